@@ -1,0 +1,205 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) lossless speculative-sampling
+ * verification library (libspecverify.so).
+ *
+ * What the library computes (pages as published):
+ *  - Token-level verification: "Speculative Decoding: The Same Distribution,
+ *    Twice as Fast" (derpx06.online), sections 3 "The loop" and 4 "The rule
+ *    that makes it exact"; "How much does a token cost" (blog.luminal.com),
+ *    section "On Speculative Sampling".
+ *  - Block verification: blog.luminal.com, section "Block verification".
+ *  - Confidence prefix scheduler: "DeepSeek Boosts Inference Speed by 85%"
+ *    (kongchang.com), section "The Third Ace"; "DeepSeek DSpark 详解"
+ *    (zskr.cn), section 04.
+ *  - Markov-head draft sampler: kongchang.com, section "The First Ace";
+ *    zskr.cn, section 03.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers on the context's device, row-major
+ *    and contiguous, owned by the caller.  Logit rows must start on a 2-byte
+ *    (bf16) or 4-byte (fp32) boundary; 16-byte alignment is faster.
+ *  - Layouts: p (target logits) [B, gamma+1, V]; q (draft logits) [B, gamma, V];
+ *    draft tokens [B, gamma] int32.  q row i pairs with p row i (i = 1..gamma);
+ *    p row gamma+1 is the bonus row.  V is innermost.
+ *  - A row's distribution is softmax(logit / temperature).
+ *  - Uniforms: Philox4x32-10 (Salmon et al., SC'11) with key = seed and
+ *    counter = (request, position | tag << 16, offset lo32, offset hi32),
+ *    u = (word0 >> 8) * 2^-24.  Tags: 0 = acceptance test u_i (block:
+ *    threshold eta_i), 1 = correction / bonus draw, 2 = Markov draft draw.
+ *    Advance `offset` every round so rounds never reuse counters.
+ *  - Every *_run call is stream-ordered: it validates its arguments on the
+ *    host (synchronously), enqueues kernels on `stream` and returns.  It never
+ *    allocates or synchronises.  Argument errors return a status and leave
+ *    outputs untouched; the message is in spec_verify_last_error().
+ *  - Data errors found on the device (token id outside [0, V), a needed row
+ *    that is all -inf or holds NaN/+inf, a verify_len outside [0, gamma]) set
+ *    accepted_len[b] = -1 and out_tokens[b, :] = -1 for that request and OR a
+ *    flag into the context's device error word (spec_verify_device_status).
+ *  - A context is not thread-safe and keeps per-call scratch: use one context
+ *    per concurrently running stream.  Calls on one context must be ordered
+ *    (same stream, or explicitly synchronised).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sv_ctx sv_ctx;
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID = 1,      /* bad argument (null pointer, size out of range, ...) */
+    SV_ERR_UNSUPPORTED = 2,  /* valid but unsupported combination (dtype, size)     */
+    SV_ERR_HIP = 3,          /* a HIP runtime call or kernel launch failed          */
+    SV_ERR_NOMEM = 4         /* device allocation failed (create only)              */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Device error word / per-request flag bits. */
+#define SV_FLAG_BAD_TOKEN      1u  /* draft or anchor token outside [0, V)              */
+#define SV_FLAG_BAD_ROW        2u  /* a needed row is all -inf or holds NaN / +inf      */
+#define SV_FLAG_RESID_ZERO     4u  /* residual mass rounded to 0: the p row was used    */
+#define SV_FLAG_BAD_VERIFY_LEN 8u  /* verify_len[b] outside [0, gamma]                  */
+
+/* Optional diagnostics: a HOST struct of nullable DEVICE pointers (fp32
+ * unless noted).  Entries of positions a request did not evaluate are NaN. */
+typedef struct {
+    float *lse_p;        /* [B, gamma+1] natural log-sum-exp of p rows (after 1/T)   */
+    float *lse_q;        /* [B, gamma]   natural log-sum-exp of q rows                */
+    float *ratio;        /* [B, gamma]   min(1, p(x_i) / q(x_i))                      */
+    float *w;            /* [B, gamma]   block: running capped ratio w_i              */
+    float *h;            /* [B, gamma]   block: acceptance threshold h_i              */
+    float *resid_mass;   /* [B]          mass Z of the correction / bonus weights     */
+    uint32_t *flags;     /* [B]          SV_FLAG_* bits of the request                */
+} sv_diag;
+
+/* Creates a context on `device` for calls with B <= max_batch,
+ * gamma <= max_gamma (<= 64), vocabulary `vocab` (1 <= V < 2^31) and, for
+ * markov_draft_run, rank `max_rank` (a multiple of 32, or 0 if unused).
+ * Allocates the context's device workspace (the only allocation the library
+ * makes).  On failure *out is NULL and the status says why. */
+sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_gamma,
+                             int64_t vocab, int max_rank);
+
+/* Frees the context and its workspace.  The caller must have synchronised
+ * every stream that used it.  NULL is accepted. */
+void spec_verify_destroy(sv_ctx *ctx);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char *spec_verify_last_error(void);
+
+/* Synchronises `stream`, returns the OR of SV_FLAG_* raised by the device
+ * since the last call in *flags, and clears the word. */
+sv_status spec_verify_device_status(sv_ctx *ctx, hipStream_t stream, uint32_t *flags);
+
+/* Token-level verification.
+ * For each request b, with L = verify_len[b] (gamma when verify_len is NULL):
+ * accept x_i with probability min(1, p_i(x_i) / q_i(x_i)), walking i = 1..L
+ * and stopping at the first rejection (tau = number accepted); on a rejection
+ * draw the correction from max(p_{tau+1} - q_{tau+1}, 0) / Z; if all L pass,
+ * draw the bonus token from p_{L+1}.  Draws are inverse-CDF over token ids in
+ * ascending order (the smallest id whose cumulative weight exceeds u * Z).
+ *   p_logits      [B, gamma+1, V], dtype p_dtype (SV_BF16 or SV_F32)
+ *   q_logits      [B, gamma, V],   dtype q_dtype (ignored when gamma == 0)
+ *   draft_tokens  [B, gamma] int32
+ *   verify_len    [B] int32 or NULL
+ *   uniforms      [B, gamma+1] fp32 or NULL: replaces the Philox draws
+ *                 (column i-1 = u_i, column gamma = correction/bonus draw)
+ *   accepted_len  [B] int32 out: tau_b, or -1 on a data error
+ *   out_tokens    [B, gamma+1] int32 out: x_1..x_tau, y, then -1
+ *   diag          NULL or diagnostics (see sv_diag)
+ * Requires 0 < B <= max_batch, 0 <= gamma <= max_gamma, V == the context's
+ * vocab, 0 < temperature < inf. */
+sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream,
+                          const void *p_logits, sv_dtype p_dtype,
+                          const void *q_logits, sv_dtype q_dtype,
+                          const int32_t *draft_tokens, const int32_t *verify_len,
+                          int B, int gamma, int64_t V, float temperature,
+                          uint64_t seed, uint64_t offset, const float *uniforms,
+                          int32_t *accepted_len, int32_t *out_tokens, const sv_diag *diag);
+
+/* Hardware-aware prefix scheduler.  Survival S_{b,i} = prod_{j<=i} conf_{b,j}
+ * (binary64); candidates are ranked by (S descending, b ascending, i
+ * ascending) and admitted one by one while E * SPS(rows) strictly rises, with
+ * SPS(n) = sps_a / (1 + n / sps_k), E starting at B and rows at B (every
+ * request verifies its correction/bonus row); the first candidate that does
+ * not raise it stops admission.
+ *   conf          [B, gamma] fp32, each in [0, 1] (values outside are clamped)
+ *   verify_len    [B] int32 out
+ *   expected      [1] fp64 out or NULL: E of the chosen allocation
+ * Requires B * gamma <= 8192 (one workgroup sorts every candidate in LDS). */
+sv_status spec_schedule_run(sv_ctx *ctx, hipStream_t stream, const float *conf,
+                            int B, int gamma, float sps_a, float sps_k,
+                            int32_t *verify_len, double *expected);
+
+/* Block verification: keeps the longest passing prefix.  With running ratio
+ * w_0 = 1, w_i = min(1, w_{i-1} p_i(x_i) / q_i(x_i)), residual masses
+ * m_i = sum_v max(w_i p_{i+1}(v) - q_{i+1}(v), 0), thresholds
+ * h_i = m_i / (m_i + 1 - w_i) for i < L (1 when 0/0) and h_L = w_L,
+ * tau = the largest i in 1..L with eta_i < h_i (else 0); the correction is
+ * drawn from max(w_tau p_{tau+1} - q_{tau+1}, 0) or, for tau = L, the bonus
+ * from p_{L+1}.  With L = 1 it takes token verification's decisions.
+ * If `conf` is non-NULL the scheduler runs first on the same stream and its
+ * verify_len (written to verify_len_out when non-NULL) drives the call;
+ * otherwise `verify_len` (or gamma) does.  Other arguments as
+ * spec_verify_run. */
+sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream,
+                               const void *p_logits, sv_dtype p_dtype,
+                               const void *q_logits, sv_dtype q_dtype,
+                               const int32_t *draft_tokens, const int32_t *verify_len,
+                               const float *conf, float sps_a, float sps_k,
+                               int32_t *verify_len_out,
+                               int B, int gamma, int64_t V, float temperature,
+                               uint64_t seed, uint64_t offset, const float *uniforms,
+                               int32_t *accepted_len, int32_t *out_tokens, const sv_diag *diag);
+
+/* Markov-head draft sampler.  For k = 1..gamma, strictly left to right:
+ * z_k = base_k + U[x_{k-1}, :] . W (bf16 inputs, fp32 accumulation),
+ * x_k = inverse-CDF draw from softmax(z_k / temperature) with uniform tag 2
+ * at position k.  x_0 is the anchor token.
+ *   base_logits   [B, gamma, V] bf16
+ *   U             [V, R] bf16, W [R, V] bf16, R == the context's max_rank
+ *   x0            [B] int32 anchor tokens
+ *   uniforms      [B, gamma] fp32 or NULL (replaces the Philox draws)
+ *   draft_tokens  [B, gamma] int32 out
+ *   q_logits      [B, gamma, V] fp32 out or NULL: z_k before 1/temperature
+ *   lse_q         [B, gamma] fp32 out or NULL: log-sum-exp of z_k / T */
+sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream,
+                           const void *base_logits, const void *U, const void *W, int R,
+                           const int32_t *x0, int B, int gamma, int64_t V, float temperature,
+                           uint64_t seed, uint64_t offset, const float *uniforms,
+                           int32_t *draft_tokens, float *q_logits, float *lse_q);
+
+/* ---- Measurement ------------------------------------------------------
+ * Per-kernel timing with HIP events recorded on the caller's stream around
+ * every kernel the library launches (the kernels themselves are unchanged).
+ * For benchmarks and profiling only; off by default. */
+typedef enum {
+    SV_KERNEL_ROWSTATS = 0,      /* row statistics: one HBM pass over every verified row */
+    SV_KERNEL_BLOCK_PASS2 = 1,   /* block verification residual masses                  */
+    SV_KERNEL_RESID = 2,         /* acceptance scan + correction / bonus sampler        */
+    SV_KERNEL_SCHEDULE = 3,      /* prefix scheduler                                    */
+    SV_KERNEL_MARKOV_GEMM = 4,   /* Markov head contraction + epilogue (per position)   */
+    SV_KERNEL_MARKOV_SELECT = 5, /* Markov head draw (per position)                     */
+    SV_KERNEL_COUNT = 6
+} sv_kernel;
+
+/* enable != 0 creates the context's event pool (up to 4096 launches per
+ * read) and starts recording; 0 stops recording and frees the pool. */
+sv_status spec_verify_profile_enable(sv_ctx *ctx, int enable);
+
+/* Waits for the recorded events, writes per-kernel totals since the last read
+ * (total_ms[SV_KERNEL_COUNT], launches[SV_KERNEL_COUNT], both host arrays) and
+ * clears them.  Launches beyond the pool's capacity are not timed. */
+sv_status spec_verify_profile_read(sv_ctx *ctx, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,399 @@
+// api.cpp -- the C ABI of libspecverify: contexts, argument validation and the
+// launch sequence of each call.  Declarations and contracts: spec_verify.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "spec_verify.h"
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sv_status fail(sv_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+sv_status ok()
+{
+    g_err[0] = '\0';
+    return SV_OK;
+}
+
+// Makes the context's device current for the scope of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev) {
+            changed = hipSetDevice(dev) == hipSuccess;
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+int esize_of(sv_dtype d) { return d == SV_BF16 ? 2 : (d == SV_F32 ? 4 : 0); }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return (((uintptr_t)p) % a) == 0; }
+
+sv_status check_launch(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return SV_OK;
+}
+
+// Shared validation of the verification calls.
+sv_status check_verify_args(const sv_ctx *ctx, const void *p, sv_dtype pd, const void *q, sv_dtype qd,
+                            const int32_t *draft, int B, int gamma, int64_t V, float T,
+                            const int32_t *accepted_len, const int32_t *out_tokens, const char *fn)
+{
+    if (!ctx) return fail(SV_ERR_INVALID, "%s: ctx is NULL", fn);
+    if (B <= 0 || B > ctx->max_batch)
+        return fail(SV_ERR_INVALID, "%s: B=%d outside [1, max_batch=%d]", fn, B, ctx->max_batch);
+    if (gamma < 0 || gamma > ctx->max_gamma)
+        return fail(SV_ERR_INVALID, "%s: gamma=%d outside [0, max_gamma=%d]", fn, gamma, ctx->max_gamma);
+    if (V != ctx->vocab)
+        return fail(SV_ERR_INVALID, "%s: V=%lld differs from the context's vocab %lld", fn, (long long)V,
+                    (long long)ctx->vocab);
+    if (!(T > 0.0f) || !std::isfinite(T)) return fail(SV_ERR_INVALID, "%s: temperature must be finite and > 0", fn);
+    if (!p || !accepted_len || !out_tokens) return fail(SV_ERR_INVALID, "%s: p, accepted_len and out_tokens are required", fn);
+    if (gamma > 0 && (!q || !draft)) return fail(SV_ERR_INVALID, "%s: q and draft_tokens are required when gamma > 0", fn);
+    if (esize_of(pd) == 0 || (gamma > 0 && esize_of(qd) == 0))
+        return fail(SV_ERR_UNSUPPORTED, "%s: dtype must be SV_BF16 or SV_F32", fn);
+    if (!aligned(p, esize_of(pd)) || (gamma > 0 && !aligned(q, esize_of(qd))))
+        return fail(SV_ERR_INVALID, "%s: logits must be aligned to their element size", fn);
+    return SV_OK;
+}
+
+svh::VerifyArgs make_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd, const int32_t *draft,
+                          const int32_t *verify_len, int B, int gamma, int64_t V, float T, uint64_t seed,
+                          uint64_t offset, const float *uniforms, int32_t *accepted_len,
+                          int32_t *out_tokens, const sv_diag *diag, bool block)
+{
+    svh::VerifyArgs a;
+    a.p = p;
+    a.q = q;
+    a.p_esize = esize_of(pd);
+    a.q_esize = gamma > 0 ? esize_of(qd) : a.p_esize;
+    a.draft = draft;
+    a.verify_len = verify_len;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.c = (float)(1.4426950408889634 / (double)T);
+    a.seed = seed;
+    a.offset = offset;
+    a.uniforms = uniforms;
+    a.accepted_len = accepted_len;
+    a.out_tokens = out_tokens;
+    if (diag) a.diag = *diag;
+    else std::memset(&a.diag, 0, sizeof(a.diag));
+    a.block = block;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_verify_last_error(void) { return g_err; }
+
+sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_gamma, int64_t vocab,
+                             int max_rank)
+{
+    if (!out) return fail(SV_ERR_INVALID, "spec_verify_create: out is NULL");
+    *out = nullptr;
+    if (max_batch <= 0) return fail(SV_ERR_INVALID, "spec_verify_create: max_batch must be > 0");
+    if (max_gamma < 0 || max_gamma > svh::kMaxGamma)
+        return fail(SV_ERR_INVALID, "spec_verify_create: max_gamma must be in [0, %d]", svh::kMaxGamma);
+    if (vocab <= 0 || vocab >= (int64_t)1 << 31)
+        return fail(SV_ERR_INVALID, "spec_verify_create: vocab must be in [1, 2^31)");
+    if (max_rank != 0 && !(max_rank == 32 || max_rank == 64 || max_rank == 128 || max_rank == 256))
+        return fail(SV_ERR_UNSUPPORTED, "spec_verify_create: max_rank must be 0, 32, 64, 128 or 256");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+        return fail(SV_ERR_INVALID, "spec_verify_create: device %d not available", device);
+    DeviceGuard guard(device);
+
+    sv_ctx *ctx = new (std::nothrow) sv_ctx();
+    if (!ctx) return fail(SV_ERR_NOMEM, "spec_verify_create: host allocation failed");
+    ctx->device = device;
+    ctx->max_batch = max_batch;
+    ctx->max_gamma = max_gamma;
+    ctx->vocab = vocab;
+    ctx->max_rank = max_rank;
+    // row-statistics chunks: about kTargetChunk1 elements, rounded to 8
+    int64_t nch1 = (vocab + svh::kTargetChunk1 / 2) / svh::kTargetChunk1;
+    if (nch1 < 1) nch1 = 1;
+    int64_t chunk1 = (vocab + nch1 - 1) / nch1;
+    chunk1 = (chunk1 + 7) / 8 * 8;
+    nch1 = (vocab + chunk1 - 1) / chunk1;
+    ctx->nch1 = (int)nch1;
+    ctx->chunk1 = chunk1;
+    ctx->nchr = (int)((vocab + svh::kChunkR - 1) / svh::kChunkR);
+    ctx->ntile = (int)((vocab + svh::kMarkovTileN - 1) / svh::kMarkovTileN);
+
+    const size_t rows_max = (size_t)max_batch * (2 * (size_t)max_gamma + 1);
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t o_part = carve(rows_max * ctx->nch1 * sizeof(float2));
+    const size_t o_csum = carve((size_t)max_batch * ctx->nchr * sizeof(float));
+    const size_t o_bm = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * ctx->nchr * sizeof(float));
+    const size_t o_counter = carve((size_t)max_batch * sizeof(uint32_t));
+    const size_t o_err = carve(sizeof(uint32_t));
+    const size_t o_sched = carve((size_t)max_batch * sizeof(int32_t));
+    size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0;
+    if (max_rank > 0) {
+        o_mkpart = carve((size_t)max_batch * ctx->ntile * sizeof(float2));
+        o_mkprev = carve((size_t)max_batch * sizeof(int32_t));
+        o_mkq = carve((size_t)max_batch * (size_t)vocab * sizeof(float));
+    }
+    void *base = nullptr;
+    if (hipMalloc(&base, off) != hipSuccess) {
+        delete ctx;
+        return fail(SV_ERR_NOMEM, "spec_verify_create: hipMalloc of %zu bytes failed", off);
+    }
+    if (hipMemset(base, 0, off) != hipSuccess) {
+        (void)hipFree(base);
+        delete ctx;
+        return fail(SV_ERR_HIP, "spec_verify_create: hipMemset failed");
+    }
+    char *b = (char *)base;
+    ctx->ws.base = base;
+    ctx->ws.bytes = off;
+    ctx->ws.part = (float2 *)(b + o_part);
+    ctx->ws.csum = (float *)(b + o_csum);
+    ctx->ws.bm = (float *)(b + o_bm);
+    ctx->ws.counter = (uint32_t *)(b + o_counter);
+    ctx->ws.errword = (uint32_t *)(b + o_err);
+    ctx->ws.sched_len = (int32_t *)(b + o_sched);
+    ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
+    ctx->ws.mk_prev = max_rank > 0 ? (int32_t *)(b + o_mkprev) : nullptr;
+    ctx->ws.mk_q = max_rank > 0 ? (float *)(b + o_mkq) : nullptr;
+    *out = ctx;
+    return ok();
+}
+
+namespace {
+
+void profile_free(sv_ctx *ctx)
+{
+    SvProfile &p = ctx->prof;
+    for (int i = 0; i < p.cap; ++i) {
+        (void)hipEventDestroy(p.ev0[i]);
+        (void)hipEventDestroy(p.ev1[i]);
+    }
+    delete[] p.ev0;
+    delete[] p.ev1;
+    delete[] p.kind;
+    p = SvProfile();
+}
+
+}  // namespace
+
+void spec_verify_destroy(sv_ctx *ctx)
+{
+    if (!ctx) return;
+    {
+        DeviceGuard guard(ctx->device);
+        profile_free(ctx);
+        if (ctx->ws.base) (void)hipFree(ctx->ws.base);
+    }
+    delete ctx;
+}
+
+sv_status spec_verify_profile_enable(sv_ctx *ctx, int enable)
+{
+    if (!ctx) return fail(SV_ERR_INVALID, "spec_verify_profile_enable: ctx is NULL");
+    DeviceGuard guard(ctx->device);
+    if (!enable) {
+        profile_free(ctx);
+        return ok();
+    }
+    if (ctx->prof.on) return ok();
+    constexpr int kCap = 4096;
+    SvProfile &p = ctx->prof;
+    p.ev0 = new (std::nothrow) hipEvent_t[kCap];
+    p.ev1 = new (std::nothrow) hipEvent_t[kCap];
+    p.kind = new (std::nothrow) int[kCap];
+    if (!p.ev0 || !p.ev1 || !p.kind) {
+        profile_free(ctx);
+        return fail(SV_ERR_NOMEM, "spec_verify_profile_enable: host allocation failed");
+    }
+    for (int i = 0; i < kCap; ++i) {
+        if (hipEventCreate(&p.ev0[i]) != hipSuccess || hipEventCreate(&p.ev1[i]) != hipSuccess) {
+            p.cap = i;
+            profile_free(ctx);
+            return fail(SV_ERR_HIP, "spec_verify_profile_enable: hipEventCreate failed");
+        }
+        p.cap = i + 1;
+    }
+    p.n = 0;
+    p.on = true;
+    return ok();
+}
+
+sv_status spec_verify_profile_read(sv_ctx *ctx, double *total_ms, int64_t *launches)
+{
+    if (!ctx || !total_ms || !launches)
+        return fail(SV_ERR_INVALID, "spec_verify_profile_read: ctx, total_ms and launches are required");
+    for (int k = 0; k < SV_KERNEL_COUNT; ++k) {
+        total_ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    SvProfile &p = ctx->prof;
+    if (!p.on) return fail(SV_ERR_INVALID, "spec_verify_profile_read: profiling is not enabled");
+    DeviceGuard guard(ctx->device);
+    for (int i = 0; i < p.n; ++i) {
+        hipError_t e = hipEventSynchronize(p.ev1[i]);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.ev0[i], p.ev1[i]);
+        if (e != hipSuccess) {
+            p.n = 0;
+            return fail(SV_ERR_HIP, "spec_verify_profile_read: %s", hipGetErrorString(e));
+        }
+        total_ms[p.kind[i]] += ms;
+        launches[p.kind[i]] += 1;
+    }
+    p.n = 0;
+    return ok();
+}
+
+sv_status spec_verify_device_status(sv_ctx *ctx, hipStream_t stream, uint32_t *flags)
+{
+    if (!ctx || !flags) return fail(SV_ERR_INVALID, "spec_verify_device_status: ctx and flags are required");
+    DeviceGuard guard(ctx->device);
+    uint32_t h = 0;
+    hipError_t e = hipMemcpyAsync(&h, ctx->ws.errword, sizeof(h), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(ctx->ws.errword, 0, sizeof(uint32_t), stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "spec_verify_device_status: %s", hipGetErrorString(e));
+    *flags = h;
+    return ok();
+}
+
+sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits, sv_dtype p_dtype,
+                          const void *q_logits, sv_dtype q_dtype, const int32_t *draft_tokens,
+                          const int32_t *verify_len, int B, int gamma, int64_t V, float temperature,
+                          uint64_t seed, uint64_t offset, const float *uniforms, int32_t *accepted_len,
+                          int32_t *out_tokens, const sv_diag *diag)
+{
+    sv_status st = check_verify_args(ctx, p_logits, p_dtype, q_logits, q_dtype, draft_tokens, B, gamma, V,
+                                     temperature, accepted_len, out_tokens, "spec_verify_run");
+    if (st != SV_OK) return st;
+    DeviceGuard guard(ctx->device);
+    const svh::VerifyArgs a = make_args(p_logits, p_dtype, q_logits, q_dtype, draft_tokens, verify_len, B,
+                                        gamma, V, temperature, seed, offset, uniforms, accepted_len,
+                                        out_tokens, diag, false);
+    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
+    if ((st = check_launch(svh::launch_resid(ctx, a, stream), "acceptance / residual sampler")) != SV_OK)
+        return st;
+    return ok();
+}
+
+sv_status spec_schedule_run(sv_ctx *ctx, hipStream_t stream, const float *conf, int B, int gamma,
+                            float sps_a, float sps_k, int32_t *verify_len, double *expected)
+{
+    if (!ctx) return fail(SV_ERR_INVALID, "spec_schedule_run: ctx is NULL");
+    if (B <= 0 || B > ctx->max_batch || gamma < 0 || gamma > ctx->max_gamma)
+        return fail(SV_ERR_INVALID, "spec_schedule_run: B=%d or gamma=%d out of range", B, gamma);
+    if (B > svh::kSchedMax || (int64_t)B * gamma > svh::kSchedMax)
+        return fail(SV_ERR_UNSUPPORTED, "spec_schedule_run: B and B*gamma must be <= %d", svh::kSchedMax);
+    if (!verify_len || (gamma > 0 && !conf))
+        return fail(SV_ERR_INVALID, "spec_schedule_run: conf and verify_len are required");
+    if (!(sps_a > 0.0f) || !(sps_k > 0.0f) || !std::isfinite(sps_a) || !std::isfinite(sps_k))
+        return fail(SV_ERR_INVALID, "spec_schedule_run: sps_a and sps_k must be finite and > 0");
+    DeviceGuard guard(ctx->device);
+    sv_status st = check_launch(svh::launch_schedule(ctx, conf, B, gamma, sps_a, sps_k, verify_len, expected,
+                                                     stream),
+                                "scheduler");
+    return st != SV_OK ? st : ok();
+}
+
+sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits, sv_dtype p_dtype,
+                               const void *q_logits, sv_dtype q_dtype, const int32_t *draft_tokens,
+                               const int32_t *verify_len, const float *conf, float sps_a, float sps_k,
+                               int32_t *verify_len_out, int B, int gamma, int64_t V, float temperature,
+                               uint64_t seed, uint64_t offset, const float *uniforms, int32_t *accepted_len,
+                               int32_t *out_tokens, const sv_diag *diag)
+{
+    sv_status st = check_verify_args(ctx, p_logits, p_dtype, q_logits, q_dtype, draft_tokens, B, gamma, V,
+                                     temperature, accepted_len, out_tokens, "spec_blockverify_run");
+    if (st != SV_OK) return st;
+    DeviceGuard guard(ctx->device);
+    const int32_t *vl = verify_len;
+    if (conf) {
+        int32_t *dst = verify_len_out ? verify_len_out : ctx->ws.sched_len;
+        st = spec_schedule_run(ctx, stream, conf, B, gamma, sps_a, sps_k, dst, nullptr);
+        if (st != SV_OK) return st;
+        vl = dst;
+    }
+    const svh::VerifyArgs a = make_args(p_logits, p_dtype, q_logits, q_dtype, draft_tokens, vl, B, gamma, V,
+                                        temperature, seed, offset, uniforms, accepted_len, out_tokens, diag,
+                                        true);
+    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
+    if ((st = check_launch(svh::launch_block_pass2(ctx, a, stream), "block pass 2")) != SV_OK) return st;
+    if ((st = check_launch(svh::launch_resid(ctx, a, stream), "block thresholds / residual sampler")) != SV_OK)
+        return st;
+    return ok();
+}
+
+sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_logits, const void *U,
+                           const void *W, int R, const int32_t *x0, int B, int gamma, int64_t V,
+                           float temperature, uint64_t seed, uint64_t offset, const float *uniforms,
+                           int32_t *draft_tokens, float *q_logits, float *lse_q)
+{
+    if (!ctx) return fail(SV_ERR_INVALID, "markov_draft_run: ctx is NULL");
+    if (ctx->max_rank == 0) return fail(SV_ERR_INVALID, "markov_draft_run: context created with max_rank 0");
+    if (R != ctx->max_rank) return fail(SV_ERR_INVALID, "markov_draft_run: R=%d differs from max_rank %d", R, ctx->max_rank);
+    if (B <= 0 || B > ctx->max_batch || gamma < 1 || gamma > ctx->max_gamma)
+        return fail(SV_ERR_INVALID, "markov_draft_run: B=%d or gamma=%d out of range", B, gamma);
+    if (V != ctx->vocab) return fail(SV_ERR_INVALID, "markov_draft_run: V differs from the context's vocab");
+    if (!(temperature > 0.0f) || !std::isfinite(temperature))
+        return fail(SV_ERR_INVALID, "markov_draft_run: temperature must be finite and > 0");
+    if (!base_logits || !U || !W || !x0 || !draft_tokens)
+        return fail(SV_ERR_INVALID, "markov_draft_run: base_logits, U, W, x0 and draft_tokens are required");
+    if (!aligned(U, 16) || !aligned(W, 2) || !aligned(base_logits, 2) || (q_logits && !aligned(q_logits, 4)))
+        return fail(SV_ERR_INVALID, "markov_draft_run: U must be 16-byte aligned, W and base 2-byte aligned");
+    DeviceGuard guard(ctx->device);
+    svh::MarkovArgs a;
+    a.base = (const uint16_t *)base_logits;
+    a.U = (const uint16_t *)U;
+    a.W = (const uint16_t *)W;
+    a.R = R;
+    a.x0 = x0;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.c = (float)(1.4426950408889634 / (double)temperature);
+    a.seed = seed;
+    a.offset = offset;
+    a.uniforms = uniforms;
+    a.draft = draft_tokens;
+    a.q_logits = q_logits;
+    a.lse_q = lse_q;
+    sv_status st = check_launch(svh::launch_markov(ctx, a, stream), "Markov sampler");
+    return st != SV_OK ? st : ok();
+}
+
+}  // extern "C"

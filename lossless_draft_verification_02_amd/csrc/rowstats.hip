@@ -1,0 +1,167 @@
+// rowstats.hip -- single-pass softmax statistics of every verified logit row.
+//
+// The acceptance ratio p(x)/q(x) and the residual max(p - q, 0) are defined on
+// normalised distributions ("Speculative Decoding: The Same Distribution,
+// Twice as Fast", section 4 "The rule that makes it exact"), so every target
+// and draft row a request verifies needs its log-sum-exp over the whole
+// vocabulary.  This kernel streams each row once from HBM and writes, per row
+// chunk, the pair (m, s) = (max x*c, sum exp2(x*c - m)) with c = log2(e)/T.
+//
+// Work decomposition: one 256-thread workgroup per (row, chunk); a chunk is
+// `chunk1` elements (a multiple of 8).  Threads read 16-byte vectors in a
+// strided, coalesced pattern, NB vectors in flight per thread, and fold each
+// batch into a running (m, s): one max, one fma, one exp2 and one add per
+// element, plus one rescale per batch.  Unaligned row starts (odd V with bf16)
+// are handled by a scalar head and tail.  Rows a request does not verify
+// (beyond verify_len) are skipped without a read.
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace {
+
+using svk::MS;
+using svk::u32x4;
+
+// (m, s) of elements [e0, e1) of one row; result valid in thread 0.
+template <int ESIZE, int NB>
+__device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64_t e0, int64_t e1,
+                                          float c, MS *red)
+{
+    constexpr int NT = svh::kRowstatsThreads;
+    constexpr int EPV = 16 / ESIZE;   // elements per 16-byte vector
+
+    // 16-byte aligned body [a0, a1) inside [e0, e1)
+    const uintptr_t addr0 = (uintptr_t)(rowptr + e0 * ESIZE);
+    int64_t head = (int64_t)(((16 - (addr0 & 15)) & 15) / ESIZE);
+    if (head > e1 - e0) head = e1 - e0;
+    const int64_t a0 = e0 + head;
+    const int64_t nvec = (e1 - a0) / EPV;
+    const int64_t a1 = a0 + nvec * EPV;
+    const u32x4 *vec = (const u32x4 *)(rowptr + a0 * ESIZE);
+
+    float mref = svk::neg_inf();   // running max, scaled by c
+    float mraw = svk::neg_inf();   // running max, raw units
+    float s = 0.0f;
+
+    for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += (int64_t)NT * NB) {
+        u32x4 raw[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int64_t idx = v0 + (int64_t)j * NT;
+            raw[j] = idx < nvec ? __builtin_nontemporal_load(vec + idx) : svk::neg_inf_vec<ESIZE>();
+        }
+        float x[NB * EPV];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) svk::widen<ESIZE>(raw[j], x + j * EPV);
+        float bm = x[0];
+#pragma unroll
+        for (int k = 1; k < NB * EPV; ++k) bm = fmaxf(bm, x[k]);
+        const float nm = fmaxf(mraw, bm);
+        if (nm == svk::neg_inf()) {
+            // everything so far is -inf; only a NaN can still matter
+#pragma unroll
+            for (int k = 0; k < NB * EPV; ++k)
+                if (x[k] != x[k]) s = x[k];
+            continue;
+        }
+        const float ref = nm * c;
+        s *= svk::fast_exp2(mref - ref);
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NB * EPV; ++k) acc += svk::fast_exp2(__builtin_fmaf(x[k], c, -ref));
+        s += acc;
+        mraw = nm;
+        mref = ref;
+    }
+
+    // scalar head [e0, a0) and tail [a1, e1): fewer than 2 * EPV elements
+    const int64_t nhead = a0 - e0;
+    const int64_t nscalar = nhead + (e1 - a1);
+    if ((int64_t)threadIdx.x < nscalar) {
+        const int64_t e = (int64_t)threadIdx.x < nhead ? e0 + threadIdx.x
+                                                        : a1 + ((int64_t)threadIdx.x - nhead);
+        const float x = svk::load_logit<ESIZE>(rowptr, e);
+        MS one;
+        if (x == svk::neg_inf()) {
+            one = {svk::neg_inf(), 0.0f};
+        } else if (x != x || x == svk::pos_inf()) {
+            one = {svk::pos_inf(), __builtin_nanf("")};
+        } else {
+            one = {x * c, 1.0f};
+        }
+        const MS a = svk::ms_merge(MS{mref, s}, one);
+        mref = a.m;
+        s = a.s;
+    }
+    return svk::block_merge<NT>(MS{mref, s}, red);
+}
+
+template <int PES, int QES, int NB>
+__global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
+    const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len,
+    int B, int gamma, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
+{
+    __shared__ MS red[svh::kRowstatsThreads / svk::kWave];
+
+    const int64_t wg = blockIdx.x;
+    const int64_t row = wg / nch1;
+    const int chunk = (int)(wg - row * nch1);
+    const int64_t rows_p = (int64_t)B * (gamma + 1);
+
+    int b, i;
+    bool is_p;
+    int64_t r;
+    if (row < rows_p) {
+        r = row;
+        b = (int)(r / (gamma + 1));
+        i = (int)(r - (int64_t)b * (gamma + 1));
+        is_p = true;
+    } else {
+        r = row - rows_p;
+        b = (int)(r / gamma);
+        i = (int)(r - (int64_t)b * gamma);
+        is_p = false;
+    }
+    const int L = verify_len ? verify_len[b] : gamma;
+    if (L < 0 || L > gamma) return;             // request is flagged downstream
+    if (is_p ? (i > L) : (i >= L)) return;       // row not verified
+
+    const int64_t e0 = (int64_t)chunk * chunk1;
+    const int64_t e1 = e0 + chunk1 < V ? e0 + chunk1 : V;
+    MS tot;
+    if (is_p)
+        tot = chunk_stats<PES, NB>((const char *)p + r * V * PES, e0, e1, c, red);
+    else
+        tot = chunk_stats<QES, NB>((const char *)q + r * V * QES, e0, e1, c, red);
+    if (threadIdx.x == 0) part[row * nch1 + chunk] = make_float2(tot.m, tot.s);
+}
+
+template <int PES, int QES>
+void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t grid)
+{
+    constexpr int NB = 8;
+    hipLaunchKernelGGL((k_rowstats<PES, QES, NB>), dim3((unsigned)grid),
+                       dim3(svh::kRowstatsThreads), 0, s, a.p, a.q, a.verify_len, a.B, a.gamma,
+                       a.V, ctx->nch1, ctx->chunk1, a.c, ctx->ws.part);
+}
+
+}  // namespace
+
+namespace svh {
+
+hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
+{
+    const int64_t rows = (int64_t)a.B * (a.gamma + 1) + (int64_t)a.B * a.gamma;
+    const int64_t grid = rows * ctx->nch1;
+    if (grid <= 0) return hipSuccess;
+    const int slot = prof_begin(ctx, s, SV_KERNEL_ROWSTATS);
+    if (a.p_esize == 2 && a.q_esize == 2) launch_typed<2, 2>(ctx, a, s, grid);
+    else if (a.p_esize == 2) launch_typed<2, 4>(ctx, a, s, grid);
+    else if (a.q_esize == 2) launch_typed<4, 2>(ctx, a, s, grid);
+    else launch_typed<4, 4>(ctx, a, s, grid);
+    const hipError_t e = hipGetLastError();
+    prof_end(ctx, s, slot);
+    return e;
+}
+
+}  // namespace svh

@@ -1,0 +1,127 @@
+// sv_internal.h -- host-side internals of libspecverify: the context, its
+// device workspace and the kernel launchers each .hip file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "spec_verify.h"
+
+namespace svh {
+
+// Row-statistics pass: a row of V logits is split into `nch1` chunks of
+// `chunk1` elements (a multiple of 8, so chunk starts keep 16-byte alignment).
+constexpr int kRowstatsThreads = 256;
+constexpr int kTargetChunk1 = 16384;
+// Residual / bonus sampler and block pass 2: chunks of kChunkR elements.
+constexpr int kResidThreads = 256;
+constexpr int kChunkR = 8192;
+// Scheduler: one workgroup sorts up to kSchedMax candidates in LDS.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedMax = 8192;
+// Markov head: output tiles of kMarkovTileN vocabulary columns.
+constexpr int kMarkovTileN = 128;
+constexpr int kMaxGamma = 64;
+
+struct Workspace {
+    float2 *part;        // [rows_max * nch1] (m, s) per row chunk
+    float *csum;         // [max_batch * nchr] correction/bonus chunk sums
+    float *bm;           // [max_batch * max_gamma * nchr] block residual-mass partials
+    uint32_t *counter;   // [max_batch] last-workgroup counters (kept at 0 between calls)
+    uint32_t *errword;   // [1] OR of SV_FLAG_* bits
+    int32_t *sched_len;  // [max_batch] scheduler output when the caller gives none
+    float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials
+    int32_t *mk_prev;    // [max_batch] Markov: token sampled at the previous position
+    float *mk_q;         // [max_batch * V] Markov logits of the current position when
+                         // the caller does not keep them
+    void *base;          // single allocation backing all of the above
+    size_t bytes;
+};
+
+}  // namespace svh
+
+// Optional per-kernel event timing (spec_verify_profile_*).
+struct SvProfile {
+    bool on = false;
+    int cap = 0;             // event pairs in the pool
+    int n = 0;               // pairs recorded since the last read
+    hipEvent_t *ev0 = nullptr, *ev1 = nullptr;
+    int *kind = nullptr;
+};
+
+struct sv_ctx {
+    int device;
+    int max_batch;
+    int max_gamma;
+    int64_t vocab;
+    int max_rank;
+    int nch1;            // row-statistics chunks per row
+    int64_t chunk1;      // elements per row-statistics chunk
+    int nchr;            // residual chunks per row
+    int ntile;           // Markov vocabulary tiles
+    svh::Workspace ws;
+    SvProfile prof;
+};
+
+namespace svh {
+
+// Records the start event of a timed launch; returns the pool slot or -1.
+inline int prof_begin(sv_ctx *ctx, hipStream_t s, int kind)
+{
+    SvProfile &p = ctx->prof;
+    if (!p.on || p.n >= p.cap) return -1;
+    const int slot = p.n++;
+    p.kind[slot] = kind;
+    (void)hipEventRecord(p.ev0[slot], s);
+    return slot;
+}
+
+inline void prof_end(sv_ctx *ctx, hipStream_t s, int slot)
+{
+    if (slot >= 0) (void)hipEventRecord(ctx->prof.ev1[slot], s);
+}
+
+// Arguments shared by the verification launchers.
+struct VerifyArgs {
+    const void *p;
+    const void *q;
+    int p_esize;          // 2 (bf16) or 4 (fp32)
+    int q_esize;
+    const int32_t *draft;
+    const int32_t *verify_len;   // may be null
+    int B, gamma;
+    int64_t V;
+    float c;              // log2(e) / T
+    uint64_t seed, offset;
+    const float *uniforms;       // may be null
+    int32_t *accepted_len;
+    int32_t *out_tokens;
+    sv_diag diag;         // device pointers, each may be null
+    bool block;           // block verification
+};
+
+hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_block_pass2(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_resid(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, float sps_a,
+                           float sps_k, int32_t *verify_len, double *expected, hipStream_t s);
+
+struct MarkovArgs {
+    const uint16_t *base;  // [B, gamma, V] bf16
+    const uint16_t *U;     // [V, R]
+    const uint16_t *W;     // [R, V]
+    int R;
+    const int32_t *x0;
+    int B, gamma;
+    int64_t V;
+    float c;               // log2(e) / T
+    uint64_t seed, offset;
+    const float *uniforms;
+    int32_t *draft;
+    float *q_logits;       // may be null
+    float *lse_q;          // may be null
+};
+
+hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s);
+
+}  // namespace svh

@@ -1,0 +1,188 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module holds none of the verification arithmetic: it only draws logits,
+draft tokens, Markov-head factors and confidence estimates, and serves both
+the GPU path and the CPU oracle with identical tensors.  Real models, suites
+and traffic are not available; these inputs stand in for them.
+
+Five workloads (sizes can be shrunk for tests, keeping the recipe):
+
+  1 tiny       B=1,   gamma=4, V=1000,    fp32, T=1.0: target ~ N(0, 3^2) with
+               one random token per row boosted by +8; draft = target + N(0, 1).
+  2 batched    B=32,  gamma=5, V=151936,  bf16, T=0.7: target ~ N(0, 3^2) with
+               1-3 random tokens per row boosted by U(6, 10); draft = target +
+               N(0, 1.5^2), rounded to bf16 after the noise is added.
+  3 headline   B=256, gamma=7, V=129280,  bf16, T=1.0: target ~ N(0, 3^2) plus a
+               Zipf(1.1) bias -1.1 ln(rank), ranks a seeded random permutation
+               per row; draft = target + N(0, 1).
+  4 markov     B=128, gamma=8, V=129280,  bf16, T=1.0, R=256: backbone logits
+               ~ N(0, 3^2); U, W ~ N(0, 0.02^2); anchor tokens uniform; target
+               rows 1..8 = backbone + N(0, 1), row 9 ~ N(0, 3^2).
+  5 block      B=512, gamma=8, V=129280,  bf16, T=1.0: logits as workload 3;
+               confidences: per-request mean mu_b ~ U(0.35, 0.95), decaying 3%
+               per position, plus N(0, 0.05^2), clipped to [0, 1].
+
+Draft tokens are drawn from softmax(q / T) of the stored (rounded) draft
+logits with the Gumbel-max trick, from a generator seeded 0.  Logit noise uses
+a generator seeded 1000 + workload id.  Generation runs on the requested
+device (torch generators are per device, so CPU and GPU draws differ; a test
+hands the same tensors to both sides).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+CONFIGS = {
+    1: dict(name="tiny", B=1, gamma=4, V=1000, dtype=torch.float32, T=1.0),
+    2: dict(name="batched", B=32, gamma=5, V=151936, dtype=torch.bfloat16, T=0.7),
+    3: dict(name="headline", B=256, gamma=7, V=129280, dtype=torch.bfloat16, T=1.0),
+    4: dict(name="markov", B=128, gamma=8, V=129280, dtype=torch.bfloat16, T=1.0, R=256),
+    5: dict(name="block", B=512, gamma=8, V=129280, dtype=torch.bfloat16, T=1.0),
+}
+
+VERIFY_SEED = 1   # Philox seed of the verification uniforms
+DRAFT_SEED = 0    # seed of the draft-token draws
+
+
+@dataclass
+class VerifyInputs:
+    cfg: int
+    B: int
+    gamma: int
+    V: int
+    T: float
+    p: torch.Tensor            # [B, gamma+1, V]
+    q: torch.Tensor            # [B, gamma, V]
+    draft: torch.Tensor        # [B, gamma] int32
+    conf: Optional[torch.Tensor] = None   # [B, gamma] fp32 (workload 5)
+    extra: dict = field(default_factory=dict)
+
+
+@dataclass
+class MarkovInputs:
+    B: int
+    gamma: int
+    V: int
+    R: int
+    T: float
+    base: torch.Tensor         # [B, gamma, V] bf16
+    U: torch.Tensor            # [V, R] bf16
+    W: torch.Tensor            # [R, V] bf16
+    x0: torch.Tensor           # [B] int32
+    p: torch.Tensor            # [B, gamma+1, V] bf16 target logits
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _target_rows(cfg: int, rows: int, V: int, g: torch.Generator, device) -> torch.Tensor:
+    """fp32 target logits for `rows` rows of a workload."""
+    x = torch.randn(rows, V, generator=g, device=device) * 3.0
+    if cfg == 1:
+        ids = torch.randint(0, V, (rows, 1), generator=g, device=device)
+        x.scatter_add_(1, ids, torch.full((rows, 1), 8.0, device=device))
+    elif cfg == 2:
+        for r in range(rows):
+            k = int(torch.randint(1, 4, (1,), generator=g, device=device).item())
+            ids = torch.randperm(V, generator=g, device=device)[:k]
+            boost = 6.0 + 4.0 * torch.rand(k, generator=g, device=device)
+            x[r, ids] += boost
+    elif cfg in (3, 5):
+        table = -1.1 * torch.log(torch.arange(1, V + 1, device=device, dtype=torch.float32))
+        keys = torch.rand(rows, V, generator=g, device=device)
+        perm = torch.argsort(keys, dim=1, stable=True)     # a random permutation per row
+        x += table[perm]
+    return x
+
+
+def _gumbel_argmax(logits_over_T: torch.Tensor, g: torch.Generator) -> torch.Tensor:
+    u = torch.rand(logits_over_T.shape, generator=g, device=logits_over_T.device)
+    u = u.clamp_(min=1e-12, max=1.0 - 1e-7)
+    return torch.argmax(logits_over_T - torch.log(-torch.log(u)), dim=-1)
+
+
+def make_verify_inputs(cfg: int, device="cpu", B: Optional[int] = None, gamma: Optional[int] = None,
+                       V: Optional[int] = None, noise: Optional[float] = None,
+                       row_block: int = 256, seed: Optional[int] = None) -> VerifyInputs:
+    """Target / draft logits and draft tokens of workload `cfg` (1, 2, 3 or 5).
+
+    seed (default 1000 + cfg) seeds the logit noise; another value gives an
+    independent batch of the same recipe."""
+    c = CONFIGS[cfg]
+    B = c["B"] if B is None else B
+    gamma = c["gamma"] if gamma is None else gamma
+    V = c["V"] if V is None else V
+    T = c["T"]
+    dt = c["dtype"]
+    sd = noise if noise is not None else (1.5 if cfg == 2 else 1.0)
+    g = _gen(device, 1000 + cfg if seed is None else seed)
+    gd = _gen(device, DRAFT_SEED)
+    p = torch.empty(B, gamma + 1, V, dtype=dt, device=device)
+    q = torch.empty(B, max(gamma, 0), V, dtype=dt, device=device)
+    draft = torch.empty(B, max(gamma, 0), dtype=torch.int32, device=device)
+    per = max(1, row_block // (gamma + 1))
+    for b0 in range(0, B, per):
+        b1 = min(B, b0 + per)
+        nb = b1 - b0
+        t = _target_rows(cfg, nb * (gamma + 1), V, g, device).view(nb, gamma + 1, V)
+        p[b0:b1] = t.to(dt)
+        if gamma > 0:
+            d = t[:, :gamma] + sd * torch.randn(nb, gamma, V, generator=g, device=device)
+            qd = d.to(dt)
+            q[b0:b1] = qd
+            draft[b0:b1] = _gumbel_argmax(qd.float() / T, gd).to(torch.int32)
+        del t
+    conf = None
+    if cfg == 5 and gamma > 0:
+        gc = _gen(device, 2000 + cfg)
+        mu = 0.35 + 0.60 * torch.rand(B, 1, generator=gc, device=device)
+        decay = 1.0 - 0.03 * torch.arange(gamma, device=device, dtype=torch.float32)[None, :]
+        conf = (mu * decay + 0.05 * torch.randn(B, gamma, generator=gc, device=device)).clamp_(0.0, 1.0)
+    return VerifyInputs(cfg, B, gamma, V, T, p, q, draft, conf)
+
+
+def make_markov_inputs(device="cpu", B: Optional[int] = None, gamma: Optional[int] = None,
+                       V: Optional[int] = None, R: Optional[int] = None, uw_std: float = 0.02,
+                       row_block: int = 256) -> MarkovInputs:
+    """Backbone logits, Markov factors, anchors and target logits of workload 4."""
+    c = CONFIGS[4]
+    B = c["B"] if B is None else B
+    gamma = c["gamma"] if gamma is None else gamma
+    V = c["V"] if V is None else V
+    R = c["R"] if R is None else R
+    g = _gen(device, 1004)
+    base = torch.empty(B, gamma, V, dtype=torch.bfloat16, device=device)
+    p = torch.empty(B, gamma + 1, V, dtype=torch.bfloat16, device=device)
+    per = max(1, row_block // (gamma + 1))
+    for b0 in range(0, B, per):
+        b1 = min(B, b0 + per)
+        nb = b1 - b0
+        bf = torch.randn(nb, gamma, V, generator=g, device=device) * 3.0
+        base[b0:b1] = bf.to(torch.bfloat16)
+        p[b0:b1, :gamma] = (bf + torch.randn(nb, gamma, V, generator=g, device=device)).to(torch.bfloat16)
+        p[b0:b1, gamma] = (torch.randn(nb, V, generator=g, device=device) * 3.0).to(torch.bfloat16)
+    U = (torch.randn(V, R, generator=g, device=device) * uw_std).to(torch.bfloat16)
+    W = (torch.randn(R, V, generator=g, device=device) * uw_std).to(torch.bfloat16)
+    x0 = torch.randint(0, V, (B,), generator=g, device=device).to(torch.int32)
+    return MarkovInputs(B, gamma, V, R, c["T"], base, U, W, x0, p)
+
+
+def bytes_single_read(inp: VerifyInputs) -> int:
+    """Bytes of every logit row read once (the row-statistics pass)."""
+    es = inp.p.element_size()
+    return inp.B * ((inp.gamma + 1) + inp.gamma) * inp.V * es
+
+
+def describe(cfg: int) -> str:
+    c = CONFIGS[cfg]
+    return f"{c['name']}: B={c['B']} gamma={c['gamma']} V={c['V']} {str(c['dtype']).split('.')[-1]} T={c['T']}"
+
+
+__all__ = ["CONFIGS", "VERIFY_SEED", "DRAFT_SEED", "VerifyInputs", "MarkovInputs", "make_verify_inputs",
+           "make_markov_inputs", "bytes_single_read", "describe"]

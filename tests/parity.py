@@ -1,0 +1,158 @@
+"""Decision-walk comparison of GPU results with the CPU oracle.
+
+Integer outputs must match bit for bit on every decision whose oracle margin
+exceeds MARGIN; the first disagreeing decision of a request whose margin is
+at most MARGIN counts as a within-margin flip and ends that request's
+comparison.  Probabilities (capped ratios, residual masses, w, h) must agree
+within PROB_ATOL; log-sum-exps within LSE_ATOL + LSE_RTOL * |lse|.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+MARGIN = 1e-4
+PROB_ATOL = 1e-5
+LSE_ATOL, LSE_RTOL = 1e-5, 1e-6
+
+
+@dataclass
+class Report:
+    requests: int = 0
+    flips: int = 0
+    failures: list = field(default_factory=list)
+    max_prob_err: float = 0.0
+    max_lse_err: float = 0.0
+
+    def ok(self) -> bool:
+        return not self.failures
+
+    def __str__(self):
+        return (f"requests={self.requests} flips={self.flips} failures={len(self.failures)} "
+                f"max_prob_err={self.max_prob_err:.2e} max_lse_err={self.max_lse_err:.2e} "
+                f"{self.failures[:5]}")
+
+
+def _close_prob(rep, g, o, what, b):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    m = ~np.isnan(o)
+    if m.any():
+        if np.isnan(g[m]).any():
+            rep.failures.append((b, what, "nan on the GPU"))
+            return
+        err = float(np.abs(g[m] - o[m]).max())
+        rep.max_prob_err = max(rep.max_prob_err, err)
+        if err > PROB_ATOL:
+            rep.failures.append((b, what, err))
+
+
+def _close_lse(rep, g, o, what, b):
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    m = ~np.isnan(o)
+    if m.any():
+        err = np.abs(g[m] - o[m])
+        rep.max_lse_err = max(rep.max_lse_err, float(err.max()))
+        if (err > LSE_ATOL + LSE_RTOL * np.abs(o[m])).any() or np.isnan(g[m]).any():
+            rep.failures.append((b, what, float(np.nanmax(err))))
+
+
+def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = False,
+                   draft=None, rep: Report | None = None) -> Report:
+    """gpu: dict of numpy arrays accepted_len, out_tokens and diag entries
+    (lse_p, lse_q, ratio, w, h, resid_mass, flags) for the same requests as
+    the oracle result `orc` (oracle.VerifyResult)."""
+    rep = rep or Report()
+    B = len(orc.accepted_len)
+    for b in range(B):
+        rep.requests += 1
+        L = gamma if verify_len is None else int(verify_len[b])
+        oa, ga = int(orc.accepted_len[b]), int(gpu["accepted_len"][b])
+        if oa < 0 or ga < 0:
+            if oa != ga:
+                rep.failures.append((b, "error status", oa, ga))
+            elif "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):
+                rep.failures.append((b, "flags", int(orc.flags[b]), int(gpu["flags"][b])))
+            elif (gpu["out_tokens"][b] != -1).any():
+                rep.failures.append((b, "error row not cleared"))
+            continue
+        flipped = False
+        if not block:
+            for i in range(1, L + 1):
+                o_acc, g_acc = i <= oa, i <= ga
+                if o_acc != g_acc:
+                    if orc.dec_margin[b, i - 1] <= MARGIN:
+                        rep.flips += 1
+                        flipped = True
+                    else:
+                        rep.failures.append((b, "accept", i, oa, ga, float(orc.dec_margin[b, i - 1])))
+                    break
+                if not o_acc:
+                    break
+        elif oa != ga:
+            i = max(oa, ga)
+            if orc.dec_margin[b, i - 1] <= MARGIN:
+                rep.flips += 1
+                flipped = True
+            else:
+                rep.failures.append((b, "block tau", oa, ga, float(orc.dec_margin[b, i - 1])))
+        if flipped or (rep.failures and rep.failures[-1][0] == b):
+            continue
+        # same tau: tokens x_1..x_tau, then the drawn token
+        if not np.array_equal(orc.out_tokens[b, :oa], gpu["out_tokens"][b, :ga]):
+            rep.failures.append((b, "prefix tokens"))
+            continue
+        if draft is not None and not np.array_equal(np.asarray(draft[b, :oa]), orc.out_tokens[b, :oa]):
+            rep.failures.append((b, "prefix is not the draft"))
+        if (gpu["out_tokens"][b, ga + 1:] != -1).any():
+            rep.failures.append((b, "padding"))
+        if int(orc.out_tokens[b, oa]) != int(gpu["out_tokens"][b, ga]):
+            if orc.icdf_margin[b] <= MARGIN:
+                rep.flips += 1
+            else:
+                rep.failures.append((b, "draw", int(orc.out_tokens[b, oa]), int(gpu["out_tokens"][b, ga]),
+                                     float(orc.icdf_margin[b])))
+            continue
+        # probabilities of the evaluated positions
+        if "lse_p" in gpu:
+            _close_lse(rep, gpu["lse_p"][b, :L + 1], orc.lse_p[b, :L + 1], "lse_p", b)
+        if "lse_q" in gpu and L > 0:
+            _close_lse(rep, gpu["lse_q"][b, :L], orc.lse_q[b, :L], "lse_q", b)
+        if "ratio" in gpu and L > 0:
+            _close_prob(rep, gpu["ratio"][b, :L], orc.ratio[b, :L], "ratio", b)
+        if block and "w" in gpu and L > 0:
+            _close_prob(rep, gpu["w"][b, :L], orc.w[b, :L], "w", b)
+            _close_prob(rep, gpu["h"][b, :L], orc.h[b, :L], "h", b)
+        if "resid_mass" in gpu:
+            _close_prob(rep, [gpu["resid_mass"][b]], [orc.resid_mass[b]], "resid_mass", b)
+        if "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):
+            rep.failures.append((b, "flags", int(orc.flags[b]), int(gpu["flags"][b])))
+    return rep
+
+
+def compare_markov(g_draft, g_lse, g_q, orc, rep: Report | None = None, q_atol: float = 2e-5) -> Report:
+    """Markov sampler: draws walked left to right per request; q logits and
+    lse compared on positions before the first (flipped) disagreement."""
+    rep = rep or Report()
+    B, gamma = orc.draft.shape
+    for b in range(B):
+        rep.requests += 1
+        for k in range(gamma):
+            o, g = int(orc.draft[b, k]), int(g_draft[b, k])
+            if g_q is not None and orc.q_logits is not None:
+                err = float(np.abs(np.asarray(g_q[b, k], np.float64) - orc.q_logits[b, k]).max())
+                rep.max_prob_err = max(rep.max_prob_err, err)
+                if err > q_atol:
+                    rep.failures.append((b, k, "q logits", err))
+                    break
+            if g_lse is not None:
+                _close_lse(rep, [g_lse[b, k]], [orc.lse_q[b, k]], f"lse_q[{k}]", b)
+            if o != g:
+                if orc.margin[b, k] <= MARGIN:
+                    rep.flips += 1
+                else:
+                    rep.failures.append((b, k, "draw", o, g, float(orc.margin[b, k])))
+                break
+    return rep
