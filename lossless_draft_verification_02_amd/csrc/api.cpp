@@ -159,7 +159,10 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_part = carve(rows_max * ctx->nch1 * sizeof(float2));
     const size_t o_csum = carve((size_t)max_batch * ctx->nchr * sizeof(float));
     const size_t o_bm = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * ctx->nchr * sizeof(float));
-    const size_t o_counter = carve((size_t)max_batch * sizeof(uint32_t));
+    const size_t o_req = carve((size_t)max_batch * svh::kReqStateBytes);
+    const size_t o_lp2 = carve((size_t)max_batch * (max_gamma + 1) * sizeof(float));
+    const size_t o_lq2 = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
+    const size_t o_wrun = carve((size_t)max_batch * (max_gamma + 1) * sizeof(float));
     const size_t o_err = carve(sizeof(uint32_t));
     const size_t o_sched = carve((size_t)max_batch * sizeof(int32_t));
     size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0;
@@ -184,7 +187,10 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.part = (float2 *)(b + o_part);
     ctx->ws.csum = (float *)(b + o_csum);
     ctx->ws.bm = (float *)(b + o_bm);
-    ctx->ws.counter = (uint32_t *)(b + o_counter);
+    ctx->ws.req = (void *)(b + o_req);
+    ctx->ws.lp2 = (float *)(b + o_lp2);
+    ctx->ws.lq2 = (float *)(b + o_lq2);
+    ctx->ws.wrun = (float *)(b + o_wrun);
     ctx->ws.errword = (uint32_t *)(b + o_err);
     ctx->ws.sched_len = (int32_t *)(b + o_sched);
     ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
@@ -306,7 +312,7 @@ sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits,
                                         gamma, V, temperature, seed, offset, uniforms, accepted_len,
                                         out_tokens, diag, false);
     if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
-    if ((st = check_launch(svh::launch_resid(ctx, a, stream), "acceptance / residual sampler")) != SV_OK)
+    if ((st = check_launch(svh::launch_token_tail(ctx, a, stream), "acceptance / residual sampler")) != SV_OK)
         return st;
     return ok();
 }
@@ -352,8 +358,7 @@ sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream, const void *p_lo
                                         temperature, seed, offset, uniforms, accepted_len, out_tokens, diag,
                                         true);
     if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
-    if ((st = check_launch(svh::launch_block_pass2(ctx, a, stream), "block pass 2")) != SV_OK) return st;
-    if ((st = check_launch(svh::launch_resid(ctx, a, stream), "block thresholds / residual sampler")) != SV_OK)
+    if ((st = check_launch(svh::launch_block_tail(ctx, a, stream), "block thresholds / residual sampler")) != SV_OK)
         return st;
     return ok();
 }

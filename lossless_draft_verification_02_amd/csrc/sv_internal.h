@@ -27,7 +27,10 @@ struct Workspace {
     float2 *part;        // [rows_max * nch1] (m, s) per row chunk
     float *csum;         // [max_batch * nchr] correction/bonus chunk sums
     float *bm;           // [max_batch * max_gamma * nchr] block residual-mass partials
-    uint32_t *counter;   // [max_batch] last-workgroup counters (kept at 0 between calls)
+    void *req;           // [max_batch] per-request state (ReqG, verify.hip)
+    float *lp2;          // [max_batch * (max_gamma + 1)] log2-sum-exp2 of verified p rows
+    float *lq2;          // [max_batch * max_gamma]       ... and q rows
+    float *wrun;         // [max_batch * (max_gamma + 1)] block running ratios w_0..w_L
     uint32_t *errword;   // [1] OR of SV_FLAG_* bits
     int32_t *sched_len;  // [max_batch] scheduler output when the caller gives none
     float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials
@@ -101,8 +104,12 @@ struct VerifyArgs {
 };
 
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
-hipError_t launch_block_pass2(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
-hipError_t launch_resid(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+// Token verification after the row statistics: accept -> chunk sums -> select.
+hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+// Block verification after the row statistics: ratios -> residual masses ->
+// thresholds -> chunk sums -> select.
+hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+constexpr size_t kReqStateBytes = 32;
 hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, float sps_a,
                            float sps_k, int32_t *verify_len, double *expected, hipStream_t s);
 

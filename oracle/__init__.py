@@ -40,34 +40,38 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def declare(lib):
+    """Declares the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    i32, i64, u64, f32, f64 = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                               ctypes.c_float, ctypes.c_double)
+    lib.orc_philox4x32_10.argtypes = [P, P, P]
+    lib.orc_philox4x32_10.restype = None
+    lib.orc_uniform.argtypes = [u64, u64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+    lib.orc_uniform.restype = f32
+    lib.orc_row_lse.argtypes = [P, i64, f32, P]
+    lib.orc_row_lse.restype = ctypes.c_uint32
+    lib.orc_icdf.argtypes = [P, i64, f32, P, P]
+    lib.orc_icdf.restype = i64
+    verify_args = [P, P, P, P, P, i32, i32, i64, f32, u64, u64, P, P, P, P, P]
+    lib.orc_token_verify.argtypes = verify_args
+    lib.orc_token_verify.restype = i32
+    lib.orc_block_verify.argtypes = verify_args
+    lib.orc_block_verify.restype = i32
+    lib.orc_schedule.argtypes = [P, i32, i32, f64, f64, P, P, P]
+    lib.orc_schedule.restype = i32
+    lib.orc_markov_draft.argtypes = [P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
+                                     P, P, P, P, P, P]
+    lib.orc_markov_draft.restype = i32
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        i32, i64, u64, f32, f64 = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
-                                   ctypes.c_float, ctypes.c_double)
-        lib.orc_philox4x32_10.argtypes = [P, P, P]
-        lib.orc_philox4x32_10.restype = None
-        lib.orc_uniform.argtypes = [u64, u64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
-        lib.orc_uniform.restype = f32
-        lib.orc_row_lse.argtypes = [P, i64, f32, P]
-        lib.orc_row_lse.restype = ctypes.c_uint32
-        lib.orc_icdf.argtypes = [P, i64, f32, P, P]
-        lib.orc_icdf.restype = i64
-        verify_args = [P, P, P, P, P, i32, i32, i64, f32, u64, u64, P, P, P, P, P]
-        lib.orc_token_verify.argtypes = verify_args
-        lib.orc_token_verify.restype = i32
-        lib.orc_block_verify.argtypes = verify_args
-        lib.orc_block_verify.restype = i32
-        lib.orc_schedule.argtypes = [P, i32, i32, f64, f64, P, P, P]
-        lib.orc_schedule.restype = i32
-        lib.orc_markov_draft.argtypes = [P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
-                                         P, P, P, P, P, P]
-        lib.orc_markov_draft.restype = i32
-        _lib = lib
+        _lib = declare(ctypes.CDLL(_LIB))
     return _lib
 
 

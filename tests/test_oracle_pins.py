@@ -122,10 +122,12 @@ def test_icdf_equals_searchsorted(orc):
         if w.sum() == 0:
             w[int(rng.integers(0, V))] = 0.5
         u = np.float32(rng.random()).item() if trial % 5 else 0.0
-        y, Z, margin = orc.icdf(w, u)
+        y, Z, _ = orc.icdf(w, u)
         c = np.cumsum(w)
-        want = int(np.searchsorted(c, u * Z, side="right"))
-        if margin > 1e-9:              # away from a float tie the two must agree
+        t = u * c[-1]
+        want = int(np.searchsorted(c, t, side="right"))
+        gap = np.min(np.abs(c - t)) / c[-1]     # this test's own distance to a CDF step
+        if gap > 1e-6:                 # away from a float tie the two must agree
             assert y == want, (trial, y, want)
         assert w[y] > 0
     assert orc.icdf(np.zeros(5), 0.3)[0] == -1
@@ -281,12 +283,14 @@ def _tables_from_enum(p, q, V, L):
     return pt, qt
 
 
-@pytest.mark.parametrize("method", ["token", "block"])
-def test_oracle_output_distribution_equals_target(orc, method):
+@pytest.mark.parametrize("method,table_seed", [("token", 5), ("block", 6), ("block", 210)])
+def test_oracle_output_distribution_equals_target(orc, method, table_seed):
     """The oracle's sampled outputs, completed with target draws, pass a
     chi-square test against the target's exact joint distribution (context-
-    dependent tables, V=3, L=2, and a temperature != 1)."""
-    rng = random.Random(5 if method == "token" else 6)
+    dependent tables, V=3, L=2, and a temperature != 1).  Table seed 210 is
+    one where the block correction's w_tau factor moves the output
+    distribution by 0.06 in total variation, so that factor is pinned too."""
+    rng = random.Random(table_seed)
     V, L, N = 3, 2, 30000
     p, q = exact_enum.random_tables(rng, V, L, zero_prob=0.15)
     pt, qt = _tables_from_enum(p, q, V, L)
