@@ -184,12 +184,13 @@ typedef enum {
     SV_KERNEL_ROWSTATS = 0,      /* row statistics: one HBM pass over every verified row  */
     SV_KERNEL_ACCEPT = 1,        /* per-request acceptance scan / block thresholds        */
     SV_KERNEL_BLOCK_PASS2 = 2,   /* block verification residual masses                   */
-    SV_KERNEL_RESID = 3,         /* correction / bonus weight sums per chunk             */
+    SV_KERNEL_RESID = 3,         /* correction / bonus weight sums per segment           */
     SV_KERNEL_SELECT = 4,        /* inverse-CDF draw of the correction / bonus token     */
-    SV_KERNEL_SCHEDULE = 5,      /* prefix scheduler                                     */
-    SV_KERNEL_MARKOV_GEMM = 6,   /* Markov head contraction + epilogue (per position)    */
-    SV_KERNEL_MARKOV_SELECT = 7, /* Markov head draw (per position)                      */
-    SV_KERNEL_COUNT = 8
+    SV_KERNEL_TAIL = 5,          /* accept + weight sums + draw fused, one workgroup per request */
+    SV_KERNEL_SCHEDULE = 6,      /* prefix scheduler                                     */
+    SV_KERNEL_MARKOV_GEMM = 7,   /* Markov head contraction + epilogue (per position)    */
+    SV_KERNEL_MARKOV_SELECT = 8, /* Markov head draw (per position)                      */
+    SV_KERNEL_COUNT = 9
 } sv_kernel;
 
 /* enable != 0 creates the context's event pool (up to 4096 launches per

@@ -23,7 +23,7 @@ EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error
             "spec_verify_device_status", "spec_verify_run", "spec_schedule_run",
             "spec_blockverify_run", "markov_draft_run", "spec_verify_profile_enable",
             "spec_verify_profile_read")
-KERNELS = ("rowstats", "accept", "block_pass2", "resid", "select", "schedule", "markov_gemm",
+KERNELS = ("rowstats", "accept", "block_pass2", "resid", "select", "tail", "schedule", "markov_gemm",
            "markov_select")
 
 

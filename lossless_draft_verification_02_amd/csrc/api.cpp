@@ -95,6 +95,8 @@ svh::VerifyArgs make_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd
     a.verify_len = verify_len;
     a.B = B;
     a.gamma = gamma;
+    a.b0 = 0;
+    a.nb = B;
     a.V = V;
     a.c = (float)(1.4426950408889634 / (double)T);
     a.seed = seed;
@@ -106,6 +108,15 @@ svh::VerifyArgs make_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd
     else std::memset(&a.diag, 0, sizeof(a.diag));
     a.block = block;
     return a;
+}
+
+// Row statistics, then the kernels that need them, on the caller's stream.
+sv_status run_verify(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s,
+                     hipError_t (*tail)(sv_ctx *, const svh::VerifyArgs &, hipStream_t), const char *what)
+{
+    sv_status st;
+    if ((st = check_launch(svh::launch_rowstats(ctx, a, s), "row statistics")) != SV_OK) return st;
+    return check_launch(tail(ctx, a, s), what);
 }
 
 }  // namespace
@@ -146,7 +157,7 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     nch1 = (vocab + chunk1 - 1) / chunk1;
     ctx->nch1 = (int)nch1;
     ctx->chunk1 = chunk1;
-    ctx->nchr = (int)((vocab + svh::kChunkR - 1) / svh::kChunkR);
+    ctx->nseg = (int)((vocab + svh::kSegR - 1) / svh::kSegR);
     ctx->ntile = (int)((vocab + svh::kMarkovTileN - 1) / svh::kMarkovTileN);
 
     const size_t rows_max = (size_t)max_batch * (2 * (size_t)max_gamma + 1);
@@ -157,8 +168,8 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
         return at;
     };
     const size_t o_part = carve(rows_max * ctx->nch1 * sizeof(float2));
-    const size_t o_csum = carve((size_t)max_batch * ctx->nchr * sizeof(float));
-    const size_t o_bm = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * ctx->nchr * sizeof(float));
+    const size_t o_csum = carve((size_t)max_batch * ctx->nseg * sizeof(float));
+    const size_t o_bm = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * ctx->nseg * sizeof(float));
     const size_t o_req = carve((size_t)max_batch * svh::kReqStateBytes);
     const size_t o_lp2 = carve((size_t)max_batch * (max_gamma + 1) * sizeof(float));
     const size_t o_lq2 = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
@@ -311,8 +322,7 @@ sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits,
     const svh::VerifyArgs a = make_args(p_logits, p_dtype, q_logits, q_dtype, draft_tokens, verify_len, B,
                                         gamma, V, temperature, seed, offset, uniforms, accepted_len,
                                         out_tokens, diag, false);
-    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
-    if ((st = check_launch(svh::launch_token_tail(ctx, a, stream), "acceptance / residual sampler")) != SV_OK)
+    if ((st = run_verify(ctx, a, stream, svh::launch_token_tail, "acceptance / residual sampler")) != SV_OK)
         return st;
     return ok();
 }
@@ -357,8 +367,7 @@ sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream, const void *p_lo
     const svh::VerifyArgs a = make_args(p_logits, p_dtype, q_logits, q_dtype, draft_tokens, vl, B, gamma, V,
                                         temperature, seed, offset, uniforms, accepted_len, out_tokens, diag,
                                         true);
-    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
-    if ((st = check_launch(svh::launch_block_tail(ctx, a, stream), "block thresholds / residual sampler")) != SV_OK)
+    if ((st = run_verify(ctx, a, stream, svh::launch_block_tail, "block thresholds / residual sampler")) != SV_OK)
         return st;
     return ok();
 }

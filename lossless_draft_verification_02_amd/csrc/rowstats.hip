@@ -25,7 +25,7 @@ using svk::u32x4;
 // (m, s) of elements [e0, e1) of one row; result valid in thread 0.
 template <int ESIZE, int NB>
 __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64_t e0, int64_t e1,
-                                          float c, MS *red)
+                                          float c, bool nontemporal, MS *red)
 {
     constexpr int NT = svh::kRowstatsThreads;
     constexpr int EPV = 16 / ESIZE;   // elements per 16-byte vector
@@ -48,7 +48,10 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int64_t idx = v0 + (int64_t)j * NT;
-            raw[j] = idx < nvec ? __builtin_nontemporal_load(vec + idx) : svk::neg_inf_vec<ESIZE>();
+            if (nontemporal)
+                raw[j] = idx < nvec ? __builtin_nontemporal_load(vec + idx) : svk::neg_inf_vec<ESIZE>();
+            else
+                raw[j] = idx < nvec ? vec[idx] : svk::neg_inf_vec<ESIZE>();
         }
         float x[NB * EPV];
 #pragma unroll
@@ -99,29 +102,28 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
 template <int PES, int QES, int NB>
 __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
     const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len,
-    int B, int gamma, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
+    int B, int gamma, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
 {
     __shared__ MS red[svh::kRowstatsThreads / svk::kWave];
 
+    // workgroup -> (row of requests [b0, b0 + nb), chunk); p rows first, then q rows
     const int64_t wg = blockIdx.x;
-    const int64_t row = wg / nch1;
-    const int chunk = (int)(wg - row * nch1);
-    const int64_t rows_p = (int64_t)B * (gamma + 1);
-
-    int b, i;
+    const int64_t slot = wg / nch1;
+    const int chunk = (int)(wg - slot * nch1);
+    const int64_t lrows_p = (int64_t)nb * (gamma + 1);
+    int bl, i;
     bool is_p;
-    int64_t r;
-    if (row < rows_p) {
-        r = row;
-        b = (int)(r / (gamma + 1));
-        i = (int)(r - (int64_t)b * (gamma + 1));
+    if (slot < lrows_p) {
+        bl = (int)(slot / (gamma + 1));
+        i = (int)(slot - (int64_t)bl * (gamma + 1));
         is_p = true;
     } else {
-        r = row - rows_p;
-        b = (int)(r / gamma);
-        i = (int)(r - (int64_t)b * gamma);
+        const int64_t r = slot - lrows_p;
+        bl = (int)(r / gamma);
+        i = (int)(r - (int64_t)bl * gamma);
         is_p = false;
     }
+    const int b = b0 + bl;
     const int L = verify_len ? verify_len[b] : gamma;
     if (L < 0 || L > gamma) return;             // request is flagged downstream
     if (is_p ? (i > L) : (i >= L)) return;       // row not verified
@@ -129,19 +131,25 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
     const int64_t e0 = (int64_t)chunk * chunk1;
     const int64_t e1 = e0 + chunk1 < V ? e0 + chunk1 : V;
     MS tot;
-    if (is_p)
-        tot = chunk_stats<PES, NB>((const char *)p + r * V * PES, e0, e1, c, red);
-    else
-        tot = chunk_stats<QES, NB>((const char *)q + r * V * QES, e0, e1, c, red);
-    if (threadIdx.x == 0) part[row * nch1 + chunk] = make_float2(tot.m, tot.s);
+    int64_t grow;   // row index in the statistics array: all p rows, then all q rows
+    const bool nontemporal = SV_ROWSTATS_NT_LOADS;
+    if (is_p) {
+        grow = (int64_t)b * (gamma + 1) + i;
+        tot = chunk_stats<PES, NB>((const char *)p + grow * V * PES, e0, e1, c, nontemporal, red);
+    } else {
+        const int64_t qr = (int64_t)b * gamma + i;
+        grow = (int64_t)B * (gamma + 1) + qr;
+        tot = chunk_stats<QES, NB>((const char *)q + qr * V * QES, e0, e1, c, nontemporal, red);
+    }
+    if (threadIdx.x == 0) part[grow * nch1 + chunk] = make_float2(tot.m, tot.s);
 }
 
 template <int PES, int QES>
 void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t grid)
 {
-    constexpr int NB = 8;
+    constexpr int NB = svh::kRowstatsNB;
     hipLaunchKernelGGL((k_rowstats<PES, QES, NB>), dim3((unsigned)grid),
-                       dim3(svh::kRowstatsThreads), 0, s, a.p, a.q, a.verify_len, a.B, a.gamma,
+                       dim3(svh::kRowstatsThreads), 0, s, a.p, a.q, a.verify_len, a.B, a.gamma, a.b0, a.nb,
                        a.V, ctx->nch1, ctx->chunk1, a.c, ctx->ws.part);
 }
 
@@ -151,7 +159,7 @@ namespace svh {
 
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 {
-    const int64_t rows = (int64_t)a.B * (a.gamma + 1) + (int64_t)a.B * a.gamma;
+    const int64_t rows = (int64_t)a.nb * (a.gamma + 1) + (int64_t)a.nb * a.gamma;
     const int64_t grid = rows * ctx->nch1;
     if (grid <= 0) return hipSuccess;
     const int slot = prof_begin(ctx, s, SV_KERNEL_ROWSTATS);

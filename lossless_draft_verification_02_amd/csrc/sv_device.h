@@ -172,25 +172,40 @@ __device__ __forceinline__ float block_sum(float v, float *lds /* NT / 64 entrie
     return r;
 }
 
-// Exclusive prefix over the block of one double per thread (thread order).
+// Inclusive prefix of one double per lane across a wavefront (lane order).
+__device__ __forceinline__ double wave_inclusive_scan_d(double v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix over the block of one double per thread (thread order):
+// wavefront scans, then the wavefront totals in order.  Deterministic.
 // Returns the exclusive prefix; *total gets the block total (all threads).
 template <int NT>
-__device__ __forceinline__ double block_exclusive_scan_d(double v, double *lds /* NT + 1 */,
+__device__ __forceinline__ double block_exclusive_scan_d(double v, double *lds /* >= NT / 64 */,
                                                          double *total)
 {
-    lds[threadIdx.x] = v;
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const double incl = wave_inclusive_scan_d(v);
+    double excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = 0.0;
+    if (lane == kWave - 1) lds[wid] = incl;
     __syncthreads();
-    // Hillis-Steele over NT entries (NT is small; fp64, deterministic order)
-    for (int o = 1; o < NT; o <<= 1) {
-        double add = (threadIdx.x >= (unsigned)o) ? lds[threadIdx.x - o] : 0.0;
-        __syncthreads();
-        lds[threadIdx.x] += add;
-        __syncthreads();
+    double base = 0.0, tot = 0.0;
+    for (int k = 0; k < NT / kWave; ++k) {
+        const double t = lds[k];
+        if (k < wid) base += t;
+        tot += t;
     }
-    const double excl = threadIdx.x ? lds[threadIdx.x - 1] : 0.0;
-    *total = lds[NT - 1];
-    __syncthreads();
-    return excl;
+    __syncthreads();   // lds may be reused after return
+    *total = tot;
+    return base + excl;
 }
 
 }  // namespace svk

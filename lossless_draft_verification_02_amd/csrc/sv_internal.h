@@ -11,11 +11,28 @@ namespace svh {
 
 // Row-statistics pass: a row of V logits is split into `nch1` chunks of
 // `chunk1` elements (a multiple of 8, so chunk starts keep 16-byte alignment).
-constexpr int kRowstatsThreads = 256;
-constexpr int kTargetChunk1 = 16384;
-// Residual / bonus sampler and block pass 2: chunks of kChunkR elements.
+// The defaults come from a sweep on MI355X; the macros exist for re-tuning.
+#ifndef SV_ROWSTATS_THREADS
+#define SV_ROWSTATS_THREADS 256
+#endif
+#ifndef SV_ROWSTATS_CHUNK
+#define SV_ROWSTATS_CHUNK 16384
+#endif
+#ifndef SV_ROWSTATS_NB
+#define SV_ROWSTATS_NB 8
+#endif
+#ifndef SV_ROWSTATS_NT_LOADS
+#define SV_ROWSTATS_NT_LOADS 1   // stream the logits with nontemporal loads
+#endif
+
+constexpr int kRowstatsThreads = SV_ROWSTATS_THREADS;
+constexpr int kTargetChunk1 = SV_ROWSTATS_CHUNK;
+constexpr int kRowstatsNB = SV_ROWSTATS_NB;   // 16-byte loads in flight per thread
+// Correction / bonus weights and block pass 2: each wavefront sums one
+// segment of kSegR elements; a workgroup covers kSegPerWG segments.
 constexpr int kResidThreads = 256;
-constexpr int kChunkR = 8192;
+constexpr int kSegR = 2048;
+constexpr int kSegPerWG = kResidThreads / 64;
 // Scheduler: one workgroup sorts up to kSchedMax candidates in LDS.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedMax = 8192;
@@ -23,10 +40,11 @@ constexpr int kSchedMax = 8192;
 constexpr int kMarkovTileN = 128;
 constexpr int kMaxGamma = 64;
 
+
 struct Workspace {
     float2 *part;        // [rows_max * nch1] (m, s) per row chunk
-    float *csum;         // [max_batch * nchr] correction/bonus chunk sums
-    float *bm;           // [max_batch * max_gamma * nchr] block residual-mass partials
+    float *csum;         // [max_batch * nseg] correction/bonus segment sums
+    float *bm;           // [max_batch * max_gamma * nseg] block residual-mass partials
     void *req;           // [max_batch] per-request state (ReqG, verify.hip)
     float *lp2;          // [max_batch * (max_gamma + 1)] log2-sum-exp2 of verified p rows
     float *lq2;          // [max_batch * max_gamma]       ... and q rows
@@ -60,7 +78,7 @@ struct sv_ctx {
     int max_rank;
     int nch1;            // row-statistics chunks per row
     int64_t chunk1;      // elements per row-statistics chunk
-    int nchr;            // residual chunks per row
+    int nseg;            // residual segments (kSegR elements) per row
     int ntile;           // Markov vocabulary tiles
     svh::Workspace ws;
     SvProfile prof;
@@ -93,6 +111,7 @@ struct VerifyArgs {
     const int32_t *draft;
     const int32_t *verify_len;   // may be null
     int B, gamma;
+    int b0, nb;           // requests [b0, b0 + nb) of the batch handled by a launch
     int64_t V;
     float c;              // log2(e) / T
     uint64_t seed, offset;

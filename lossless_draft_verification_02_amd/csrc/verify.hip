@@ -22,14 +22,16 @@
 //                 uniforms and decides tau (token rule, or block thresholds
 //                 from the residual masses); also the block "pre" stage that
 //                 only computes the running ratios.
-//  k_block_pass2  grid (request, position i, chunk): partial sums of
-//                 max(w_i p_{i+1} - q_{i+1}, 0).
-//  k_resid_sum    grid (request, chunk): partial sums of the correction /
-//                 bonus weights of row tau+1 (skipped when block pass 2
-//                 already summed exactly those weights).
-//  k_select       one workgroup per request: picks the chunk holding u * Z
-//                 from the fp64 prefix of the chunk sums, then scans inside it
-//                 for the token (inverse CDF in ascending token id order).
+//  k_block_pass2  grid (request, position i, segment group): each wavefront
+//                 sums max(w_i p_{i+1} - q_{i+1}, 0) over one segment of
+//                 kSegR consecutive tokens.
+//  k_resid_sum    grid (request, segment group): segment sums of the
+//                 correction / bonus weights of row tau+1 (skipped when
+//                 block pass 2 already summed exactly those weights).
+//  k_select       one workgroup per request: picks the segment holding u * Z
+//                 from the fp64 prefix of the segment sums, then scans inside
+//                 it, one 16-byte vector per thread, for the token (inverse CDF
+//                 in ascending token id order).
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -38,7 +40,7 @@ namespace {
 using svk::u32x4;
 
 constexpr int NT = svh::kResidThreads;
-constexpr int CHR = svh::kChunkR;
+constexpr int SEG = svh::kSegR;
 constexpr int MAXG = svh::kMaxGamma;
 constexpr double kLn2d = 0.69314718055994530942;
 
@@ -73,50 +75,82 @@ __device__ double merge_row(const float2 *__restrict__ part, int64_t row, int nc
 }
 
 // ---------------------------------------------------------------------------
-// k_accept: one 64-thread workgroup per request.
+// Per-request evaluation by one wavefront.
 // ---------------------------------------------------------------------------
+struct AcceptLDS {
+    double lp2[MAXG + 1];   // log2-sum-exp2 of the verified p rows
+    double lq2[MAXG];       // ... and q rows
+    float rr[MAXG];         // uncapped p/q ratio of each draft token
+    int32_t x[MAXG];        // the draft tokens
+};
+
+// Evaluates request b with the calling wavefront (threads 0..63 of the
+// workgroup; no workgroup barrier inside) and stores the result in *out:
+// merges the row statistics, gathers the draft tokens' logits, draws the
+// uniforms and decides tau.  Writes the request's diagnostics, and its error
+// outputs when it has a data error.  Lane j owns draft position j + 1 and p /
+// q row j (gamma <= 64); every load that does not depend on the verify length
+// is issued first, so the evaluation costs about two memory round trips.
 template <int PES, int QES>
-__global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const float2 *__restrict__ part,
-                                                       int nch1, const float *__restrict__ bm, int nchr,
-                                                       int stage, ReqG *__restrict__ req,
-                                                       float *__restrict__ lp2g, float *__restrict__ lq2g,
-                                                       float *__restrict__ wrun,
-                                                       uint32_t *__restrict__ errword)
+__device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__ part, int nch1,
+                            const float *__restrict__ bm, int nseg, int stage, int b, ReqG *out,
+                            float *__restrict__ lp2g, float *__restrict__ lq2g, float *__restrict__ wrun,
+                            uint32_t *__restrict__ errword, AcceptLDS &s)
 {
-    __shared__ double lp2[MAXG + 1];
-    __shared__ double lq2[MAXG];
-    __shared__ float rr[MAXG];
-    const int b = blockIdx.x;
+    double *lp2 = s.lp2;
+    double *lq2 = s.lq2;
+    float *rr = s.rr;
     const int lane = threadIdx.x;
     const int gamma = a.gamma;
     const int G1 = gamma + 1;
     const float nan = __builtin_nanf("");
-
-    const int L = a.verify_len ? a.verify_len[b] : gamma;
-    uint32_t flags = 0;
-    if (L < 0 || L > gamma) flags = SV_FLAG_BAD_VERIFY_LEN;
-    if (!flags) {   // tokens first: a bad token is reported alone
-        bool badtok = false;
-        for (int j = lane; j < L; j += svk::kWave) {
-            const int32_t x = a.draft[(int64_t)b * gamma + j];
-            if (x < 0 || (int64_t)x >= a.V) badtok = true;
-        }
-        if (__ballot(badtok)) flags = SV_FLAG_BAD_TOKEN;
-    }
     const int64_t prow0 = (int64_t)b * G1;
     const int64_t qrow0 = (int64_t)a.B * G1 + (int64_t)b * gamma;
-    if (!flags) {
-        bool badrow = false;
-        for (int j = lane; j <= L; j += svk::kWave) lp2[j] = merge_row(part, prow0 + j, nch1, badrow);
-        for (int j = lane; j < L; j += svk::kWave) lq2[j] = merge_row(part, qrow0 + j, nch1, badrow);
-        if (__ballot(badrow)) flags = SV_FLAG_BAD_ROW;
+
+    // ---- independent loads
+    const int L = a.verify_len ? a.verify_len[b] : gamma;
+    const bool has_tok = lane < gamma;
+    const int32_t x = has_tok ? a.draft[(int64_t)b * gamma + lane] : 0;
+    const bool x_ok = x >= 0 && (int64_t)x < a.V;
+    const int32_t xs = x_ok ? x : 0;   // in-bounds address even for a bad id
+    float gp = 0.0f, gq = 0.0f;
+    if (has_tok) {
+        gp = svk::load_logit<PES>(a.p, (prow0 + lane) * a.V + xs);
+        gq = svk::load_logit<QES>(a.q, ((int64_t)b * gamma + lane) * a.V + xs);
     }
+    // row statistics of every row the request may verify (rows beyond the
+    // verify length hold stale values and are not used)
+    bool bad_p = false, bad_q = false, bad_p64 = false;
+    const double lp = lane <= gamma ? merge_row(part, prow0 + lane, nch1, bad_p) : 0.0;
+    const double lq = has_tok ? merge_row(part, qrow0 + lane, nch1, bad_q) : 0.0;
+    const double lp64 = (gamma == svk::kWave && lane == 0) ? merge_row(part, prow0 + svk::kWave, nch1, bad_p64) : 0.0;
+    float u = 1.0f;
+    if (has_tok && stage != STAGE_BLOCK_PRE)
+        u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
+                       : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)(lane + 1), 0u);
+    // block thresholds: running ratio and residual mass of position lane + 1
+    float wi = 1.0f;
+    double mi = 0.0;
+    if (stage == STAGE_BLOCK_FINAL && lane + 1 <= gamma) {
+        wi = wrun[(int64_t)b * G1 + lane + 1];
+        if (lane + 1 < gamma) {
+            const float *bmi = bm + ((int64_t)b * gamma + lane + 1) * nseg;
+            for (int k = 0; k < nseg; ++k) mi += (double)bmi[k];
+        }
+    }
+
+    // ---- checks: verify length, then tokens (reported alone), then rows
+    uint32_t flags = 0;
+    if (L < 0 || L > gamma) flags = SV_FLAG_BAD_VERIFY_LEN;
+    if (!flags && __ballot(lane < L && !x_ok)) flags = SV_FLAG_BAD_TOKEN;
+    if (!flags && __ballot((lane <= L && bad_p) || (lane < L && bad_q) || (L == svk::kWave && bad_p64)))
+        flags = SV_FLAG_BAD_ROW;
     if (flags) {
         if (lane == 0) {
             ReqG r{};
             r.flags = flags;
             r.L = L;
-            req[b] = r;
+            *out = r;
         }
         if (stage == STAGE_BLOCK_PRE) return;   // the final stage reports it
         for (int j = lane; j < G1; j += svk::kWave) {
@@ -138,15 +172,18 @@ __global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const 
         return;
     }
 
-    // ratios of the draft tokens, log2 space, fp64
-    for (int j = lane; j < L; j += svk::kWave) {
-        const int32_t x = a.draft[(int64_t)b * gamma + j];
-        const double xp = (double)svk::load_logit<PES>(a.p, (prow0 + j) * a.V + x) * (double)a.c;
-        const double xq = (double)svk::load_logit<QES>(a.q, ((int64_t)b * gamma + j) * a.V + x) * (double)a.c;
-        const float r = (float)exp2((xp - lp2[j]) - (xq - lq2[j]));
-        rr[j] = (r != r) ? 0.0f : r;
+    // ratio of the lane's draft token, log2 space, fp64
+    if (has_tok) s.x[lane] = x;
+    if (lane <= gamma) lp2[lane] = lp;
+    if (gamma == svk::kWave && lane == 0) lp2[svk::kWave] = lp64;
+    if (has_tok) {
+        lq2[lane] = lq;
+        const double dp = (double)gp * (double)a.c - lp;
+        const double dq = (double)gq * (double)a.c - lq;
+        const float r = (float)exp2(dp - dq);
+        rr[lane] = (lane < L && r == r) ? r : 0.0f;
     }
-    // only this wavefront runs: order its LDS writes before lane 0 reads them
+    // only this wavefront runs: order its LDS writes before other lanes read them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -165,7 +202,7 @@ __global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const 
             ReqG r{};
             r.flags = 0;
             r.L = L;
-            req[b] = r;
+            *out = r;
         }
         return;
     }
@@ -173,60 +210,44 @@ __global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const 
     // diagnostics of the evaluated positions
     for (int j = lane; j < G1; j += svk::kWave)
         if (a.diag.lse_p) a.diag.lse_p[(int64_t)b * G1 + j] = j <= L ? (float)(lp2[j] * kLn2d) : nan;
-    for (int j = lane; j < gamma; j += svk::kWave) {
-        if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * gamma + j] = j < L ? (float)(lq2[j] * kLn2d) : nan;
-        if (a.diag.ratio) a.diag.ratio[(int64_t)b * gamma + j] = j < L ? fminf(rr[j], 1.0f) : nan;
+    if (has_tok) {
+        if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * gamma + lane] = lane < L ? (float)(lq * kLn2d) : nan;
+        if (a.diag.ratio) a.diag.ratio[(int64_t)b * gamma + lane] = lane < L ? fminf(rr[lane], 1.0f) : nan;
     }
-    if (lane != 0) return;
 
-    const float u2 = a.uniforms ? a.uniforms[(int64_t)b * G1 + gamma]
-                                : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, 0u, 1u);
+    // lane j takes the decision at position j + 1
+    const bool active = lane < L;
     int tau;
     float wmul = 1.0f;
     if (stage == STAGE_TOKEN) {
-        tau = L;
-        for (int j = 0; j < L; ++j) {
-            const float ratio = fminf(rr[j], 1.0f);
-            const float u = a.uniforms ? a.uniforms[(int64_t)b * G1 + j]
-                                       : svk::philox_uniform(a.seed, a.offset, (uint32_t)b,
-                                                             (uint32_t)(j + 1), 0u);
-            if (!(u < ratio)) {
-                tau = j;
-                break;
-            }
-        }
-        for (int i = 0; i < gamma; ++i) {
-            if (a.diag.w) a.diag.w[(int64_t)b * gamma + i] = nan;
-            if (a.diag.h) a.diag.h[(int64_t)b * gamma + i] = nan;
+        // accept x_{j+1} iff u < min(1, ratio); tau = first rejection
+        const uint64_t rej = __ballot(active && !(u < fminf(rr[lane], 1.0f)));
+        tau = rej ? (int)__builtin_ctzll(rej) : L;
+        if (has_tok) {
+            if (a.diag.w) a.diag.w[(int64_t)b * gamma + lane] = nan;
+            if (a.diag.h) a.diag.h[(int64_t)b * gamma + lane] = nan;
         }
     } else {
-        // thresholds from the running ratios (block pre stage) and residual masses (pass 2)
-        const float *w = wrun + (int64_t)b * G1;
-        tau = 0;
-        for (int i = 1; i <= L; ++i) {
-            float h;
+        // h_i = m_i / (m_i + 1 - w_i) for i < L, h_L = w_L
+        const int i = lane + 1;
+        float h = 0.0f;
+        if (active) {
             if (i < L) {
-                double m = 0.0;
-                const float *bmi = bm + ((int64_t)b * gamma + i) * nchr;
-                for (int k = 0; k < nchr; ++k) m += (double)bmi[k];
-                const double den = m + 1.0 - (double)w[i];
-                h = den > 0.0 ? (float)(m / den) : 1.0f;
+                const double den = mi + 1.0 - (double)wi;
+                h = den > 0.0 ? (float)(mi / den) : 1.0f;
             } else {
-                h = w[L];
+                h = wi;
             }
-            const float eta = a.uniforms ? a.uniforms[(int64_t)b * G1 + i - 1]
-                                         : svk::philox_uniform(a.seed, a.offset, (uint32_t)b,
-                                                               (uint32_t)i, 0u);
-            if (eta < h) tau = i;
-            if (a.diag.w) a.diag.w[(int64_t)b * gamma + i - 1] = w[i];
-            if (a.diag.h) a.diag.h[(int64_t)b * gamma + i - 1] = h;
         }
-        for (int i = L; i < gamma; ++i) {
-            if (a.diag.w) a.diag.w[(int64_t)b * gamma + i] = nan;
-            if (a.diag.h) a.diag.h[(int64_t)b * gamma + i] = nan;
+        const uint64_t pass = __ballot(active && u < h);    // eta_i < h_i
+        tau = pass ? 64 - (int)__builtin_clzll(pass) : 0;   // largest passing i
+        if (has_tok) {
+            if (a.diag.w) a.diag.w[(int64_t)b * gamma + lane] = active ? wi : nan;
+            if (a.diag.h) a.diag.h[(int64_t)b * gamma + lane] = active ? h : nan;
         }
-        wmul = w[tau];
+        wmul = tau == 0 ? 1.0f : __shfl(wi, tau - 1, svk::kWave);   // w_tau (w_0 = 1)
     }
+    if (lane != 0) return;
     ReqG r;
     r.flags = 0;
     r.L = L;
@@ -235,8 +256,22 @@ __global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const 
     r.wmul = wmul;
     r.lp2 = (float)lp2[tau];
     r.lq2 = tau < L ? (float)lq2[tau] : 0.0f;
-    r.u2 = u2;
-    req[b] = r;
+    r.u2 = a.uniforms ? a.uniforms[(int64_t)b * G1 + gamma]
+                      : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, 0u, 1u);
+    *out = r;
+}
+
+template <int PES, int QES>
+__global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const float2 *__restrict__ part,
+                                                       int nch1, const float *__restrict__ bm, int nseg,
+                                                       int stage, ReqG *__restrict__ req,
+                                                       float *__restrict__ lp2g, float *__restrict__ lq2g,
+                                                       float *__restrict__ wrun,
+                                                       uint32_t *__restrict__ errword)
+{
+    __shared__ AcceptLDS s;
+    const int b = a.b0 + (int)blockIdx.x;
+    accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, req + b, lp2g, lq2g, wrun, errword, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -265,62 +300,100 @@ __device__ __forceinline__ void load8(const char *row, int64_t e, float *x)
     }
 }
 
-// Sum of weights over elements [e0, e1) of the p / q rows, strided over the
-// block (thread-local partial returned).
+// Sum of the weights of tokens [s0, s1) (one segment, s1 - s0 <= SEG) by the
+// calling wavefront; every lane returns the total.  A full aligned segment is
+// read as 4 x 16-byte vectors per lane per row, all issued before any math.
 template <int PES, int QES>
-__device__ float chunk_weight_sum(const char *prow, const char *qrow, int64_t e0, int64_t e1,
-                                  int mode, float wmul, float lp2, float lq2, float c)
+__device__ float segment_weight_sum(const char *prow, const char *qrow, int64_t s0, int64_t s1, int mode,
+                                    float wmul, float lp2, float lq2, float c)
 {
+    const int lane = threadIdx.x & (svk::kWave - 1);
+    const bool aligned = (((uintptr_t)(prow + s0 * PES)) & 15) == 0 &&
+                         (mode || (((uintptr_t)(qrow + s0 * QES)) & 15) == 0);
     float acc = 0.0f;
-    const bool aligned = (((uintptr_t)(prow + e0 * PES)) & 15) == 0 &&
-                         (mode || (((uintptr_t)(qrow + e0 * QES)) & 15) == 0);
-    int64_t e_vec_end = e0;
-    if (aligned) {
-        const int64_t nunit = (e1 - e0) / 8;
-        for (int64_t u = threadIdx.x; u < nunit; u += NT) {
-            const int64_t e = e0 + u * 8;
-            float xp[8], xq[8];
-            load8<PES>(prow, e, xp);
-            if (!mode) load8<QES>(qrow, e, xq);
+    if (aligned && s1 - s0 == SEG) {
+        constexpr int U = SEG / 8 / svk::kWave;   // 8-token units per lane
+        float xp[U][8], xq[U][8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc += weight(xp[k], mode ? 0.0f : xq[k], mode, wmul, lp2, lq2, c);
+        for (int k = 0; k < U; ++k) load8<PES>(prow, s0 + (int64_t)(lane + svk::kWave * k) * 8, xp[k]);
+        if (!mode) {
+#pragma unroll
+            for (int k = 0; k < U; ++k) load8<QES>(qrow, s0 + (int64_t)(lane + svk::kWave * k) * 8, xq[k]);
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc += weight(xp[k][j], xq[k][j], 0, wmul, lp2, lq2, c);
+        } else {
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc += weight(xp[k][j], 0.0f, 1, wmul, lp2, lq2, c);
         }
-        e_vec_end = e0 + nunit * 8;
+    } else {
+        const int64_t nunit = aligned ? (s1 - s0) / 8 : 0;
+        for (int64_t u = lane; u < nunit; u += svk::kWave) {
+            float xp[8], xq[8];
+            load8<PES>(prow, s0 + u * 8, xp);
+            if (!mode) load8<QES>(qrow, s0 + u * 8, xq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += weight(xp[j], mode ? 0.0f : xq[j], mode, wmul, lp2, lq2, c);
+        }
+        for (int64_t e = s0 + nunit * 8 + lane; e < s1; e += svk::kWave) {
+            const float xp = svk::load_logit<PES>(prow, e);
+            const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
+            acc += weight(xp, xq, mode, wmul, lp2, lq2, c);
+        }
     }
-    for (int64_t e = e_vec_end + threadIdx.x; e < e1; e += NT) {
-        const float xp = svk::load_logit<PES>(prow, e);
-        const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
-        acc += weight(xp, xq, mode, wmul, lp2, lq2, c);
-    }
-    return acc;
+    return svk::wave_sum(acc);
 }
+
+constexpr int SPW = svh::kSegPerWG;   // segments (wavefronts) per workgroup
 
 template <int PES, int QES>
 __global__ __launch_bounds__(NT) void k_block_pass2(svh::VerifyArgs a, const ReqG *__restrict__ req,
                                                     const float *__restrict__ lp2g,
                                                     const float *__restrict__ lq2g,
                                                     const float *__restrict__ wrun, float *__restrict__ bm,
-                                                    int nchr)
+                                                    int nseg)
 {
-    __shared__ float red[NT / svk::kWave];
+    const int nwg = (nseg + SPW - 1) / SPW;
     const int gm1 = a.gamma - 1;
     const int64_t wg = blockIdx.x;
-    const int c = (int)(wg % nchr);
-    const int64_t bi = wg / nchr;
-    const int b = (int)(bi / gm1);
-    const int i = (int)(bi - (int64_t)b * gm1) + 1;   // 1..gamma-1
+    const int g = (int)(wg % nwg);
+    const int64_t bi = wg / nwg;
+    const int bl = (int)(bi / gm1);
+    const int i = (int)(bi - (int64_t)bl * gm1) + 1;   // 1..gamma-1
+    const int b = a.b0 + bl;
+    const int sidx = g * SPW + (int)(threadIdx.x / svk::kWave);
     const ReqG r = req[b];
-    if (r.flags || i >= r.L) return;
+    if (r.flags || i >= r.L || sidx >= nseg) return;   // whole wavefronts leave together
     const int G1 = a.gamma + 1;
     const float w = wrun[(int64_t)b * G1 + i];
-    const int64_t e0 = (int64_t)c * CHR;
-    const int64_t e1 = e0 + CHR < a.V ? e0 + CHR : a.V;
+    const int64_t s0 = (int64_t)sidx * SEG;
+    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + i) * a.V * PES;
     const char *qrow = (const char *)a.q + ((int64_t)b * a.gamma + i) * a.V * QES;
-    const float acc = chunk_weight_sum<PES, QES>(prow, qrow, e0, e1, 0, w, lp2g[(int64_t)b * G1 + i],
-                                                 lq2g[(int64_t)b * a.gamma + i], a.c);
-    const float tot = svk::block_sum<NT>(acc, red);
-    if (threadIdx.x == 0) bm[((int64_t)b * a.gamma + i) * nchr + c] = tot;
+    const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, 0, w, lp2g[(int64_t)b * G1 + i],
+                                                   lq2g[(int64_t)b * a.gamma + i], a.c);
+    if ((threadIdx.x & (svk::kWave - 1)) == 0) bm[((int64_t)b * a.gamma + i) * nseg + sidx] = tot;
+}
+
+// Writes request b's outputs, one thread per output column: x_1..x_tau, the
+// drawn token y, then -1 (all -1 and accepted_len -1 when y < 0).
+__device__ __forceinline__ void write_outputs(const svh::VerifyArgs &a, int b, int tau, int y,
+                                              const int32_t *x, uint32_t flags, double Z,
+                                              uint32_t *__restrict__ errword)
+{
+    const int G1 = a.gamma + 1;
+    const int64_t ob = (int64_t)b * G1;
+    for (int j = threadIdx.x; j < G1; j += blockDim.x)
+        a.out_tokens[ob + j] = y < 0 ? -1 : (j < tau ? x[j] : (j == tau ? y : -1));
+    if (threadIdx.x == 0) {
+        a.accepted_len[b] = y < 0 ? -1 : tau;
+        if (a.diag.flags) a.diag.flags[b] = flags;
+        if (a.diag.resid_mass) a.diag.resid_mass[b] = (float)Z;
+        if (flags) atomicOr(errword, flags);
+    }
 }
 
 // Block pass 2 already summed the correction weights when 1 <= tau < L.
@@ -331,60 +404,58 @@ __device__ __forceinline__ bool sums_from_pass2(const svh::VerifyArgs &a, const 
 
 template <int PES, int QES>
 __global__ __launch_bounds__(NT) void k_resid_sum(svh::VerifyArgs a, const ReqG *__restrict__ req,
-                                                  float *__restrict__ csum, int nchr)
+                                                  float *__restrict__ csum, int nseg)
 {
-    __shared__ float red[NT / svk::kWave];
+    const int nwg = (nseg + SPW - 1) / SPW;
     const int64_t wg = blockIdx.x;
-    const int b = (int)(wg / nchr);
-    const int c = (int)(wg - (int64_t)b * nchr);
+    const int bl = (int)(wg / nwg);
+    const int sidx = (int)(wg - (int64_t)bl * nwg) * SPW + (int)(threadIdx.x / svk::kWave);
+    const int b = a.b0 + bl;
     const ReqG r = req[b];
-    if (r.flags || sums_from_pass2(a, r)) return;
+    if (r.flags || sums_from_pass2(a, r) || sidx >= nseg) return;
     const int G1 = a.gamma + 1;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
     const char *qrow = r.mode ? nullptr : (const char *)a.q + ((int64_t)b * a.gamma + r.tau) * a.V * QES;
-    const int64_t e0 = (int64_t)c * CHR;
-    const int64_t e1 = e0 + CHR < a.V ? e0 + CHR : a.V;
-    const float acc = chunk_weight_sum<PES, QES>(prow, qrow, e0, e1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
-    const float tot = svk::block_sum<NT>(acc, red);
-    if (threadIdx.x == 0) csum[(int64_t)b * nchr + c] = tot;
+    const int64_t s0 = (int64_t)sidx * SEG;
+    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+    const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
+    if ((threadIdx.x & (svk::kWave - 1)) == 0) csum[(int64_t)b * nseg + sidx] = tot;
 }
 
 // ---------------------------------------------------------------------------
 // Inverse-CDF selection, one workgroup per request.
 // ---------------------------------------------------------------------------
 struct SelectShared {
-    double scan[NT];
-    double cbase;          // cumulative weight before the chosen chunk
-    int cstar;             // chosen chunk
-    int clast;             // last chunk with positive weight
+    double scan[16];       // one entry per wavefront (up to 1024 threads)
+    double cbase;          // cumulative weight before the chosen segment
+    int cstar;             // chosen segment
+    int clast;             // last segment with positive weight
     int ybest;             // chosen token (min over threads)
-    int ylast;             // last positive-weight token of the chunk
+    int ylast;             // last positive-weight token of the segment
 };
 
-template <int PES, int QES>
+template <int PES, int QES, int NTB = NT>
 __device__ int select_token(const svh::VerifyArgs &a, int mode, float wmul, float lp2, float lq2,
-                            const float *sums, int nchr, const char *prow, const char *qrow, float u,
+                            const float *sums, int nseg, const char *prow, const char *qrow, float u,
                             SelectShared &sh, double &Z_out)
 {
-    // chunk sums -> fp64 prefix (each thread owns a contiguous run of chunks)
-    const int per = (nchr + NT - 1) / NT;
+    // segment sums -> fp64 prefix (each thread owns a contiguous run of segments)
+    const int per = (nseg + NTB - 1) / NTB;
     const int k0 = threadIdx.x * per;
-    const int k1 = k0 + per < nchr ? k0 + per : nchr;
+    const int k1 = k0 + per < nseg ? k0 + per : nseg;
     double loc = 0.0;
     for (int k = k0; k < k1; ++k) loc += (double)sums[k];
-    double Z;
-    const double excl = svk::block_exclusive_scan_d<NT>(loc, sh.scan, &Z);
-    Z_out = Z;
-    if (!(Z > 0.0)) return -1;
-    const float tf = __fmul_rn(u, (float)Z);
-
     if (threadIdx.x == 0) {
         sh.cstar = 0x7FFFFFFF;
         sh.clast = -1;
         sh.ybest = 0x7FFFFFFF;
         sh.ylast = -1;
     }
-    __syncthreads();
+    double Z;
+    const double excl = svk::block_exclusive_scan_d<NTB>(loc, sh.scan, &Z);
+    Z_out = Z;
+    if (!(Z > 0.0)) return -1;
+    const float tf = __fmul_rn(u, (float)Z);
     {
         double run = excl;
         for (int k = k0; k < k1; ++k) {
@@ -409,27 +480,39 @@ __device__ int select_token(const svh::VerifyArgs &a, int mode, float wmul, floa
     }
     __syncthreads();
 
-    // inside the chunk: each thread owns CHR / NT contiguous elements
-    constexpr int PER = CHR / NT;
-    const int64_t c0 = (int64_t)cst * CHR;
-    const int64_t c1 = c0 + CHR < a.V ? c0 + CHR : a.V;
-    const int64_t t0 = c0 + (int64_t)threadIdx.x * PER;
+    // inside the segment: thread t owns tokens [s0 + 8t, s0 + 8t + 8)
+    constexpr int PER = SEG / NTB;
+    static_assert(PER >= 1 && SEG % NTB == 0, "segment split over the block");
+    const int64_t s0 = (int64_t)cst * SEG;
+    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+    const int64_t t0 = s0 + (int64_t)threadIdx.x * PER;
+    const bool aligned = (((uintptr_t)(prow + s0 * PES)) & 15) == 0 &&
+                         (mode || (((uintptr_t)(qrow + s0 * QES)) & 15) == 0);
     float w[PER];
+    if (PER == 8 && aligned && t0 + PER <= s1) {
+        float xp[8], xq[8];
+        load8<PES>(prow, t0, xp);
+        if (!mode) load8<QES>(qrow, t0, xq);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) w[k] = weight(xp[k], mode ? 0.0f : xq[k], mode, wmul, lp2, lq2, a.c);
+    } else {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int64_t e = t0 + k;
+            float wk = 0.0f;
+            if (e < s1) {
+                const float xp = svk::load_logit<PES>(prow, e);
+                const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
+                wk = weight(xp, xq, mode, wmul, lp2, lq2, a.c);
+            }
+            w[k] = wk;
+        }
+    }
     double lsum = 0.0;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int64_t e = t0 + k;
-        float wk = 0.0f;
-        if (e < c1) {
-            const float xp = svk::load_logit<PES>(prow, e);
-            const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
-            wk = weight(xp, xq, mode, wmul, lp2, lq2, a.c);
-        }
-        w[k] = wk;
-        lsum += (double)wk;
-    }
+    for (int k = 0; k < PER; ++k) lsum += (double)w[k];
     double dummy;
-    const double texcl = svk::block_exclusive_scan_d<NT>(lsum, sh.scan, &dummy);
+    const double texcl = svk::block_exclusive_scan_d<NTB>(lsum, sh.scan, &dummy);
     int last_pos = -1;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
@@ -437,6 +520,7 @@ __device__ int select_token(const svh::VerifyArgs &a, int mode, float wmul, floa
     if (last_pos >= 0) atomicMax(&sh.ylast, last_pos);
     if (!fallback) {
         double C = sh.cbase + texcl;
+#pragma unroll
         for (int k = 0; k < PER; ++k) {
             C += (double)w[k];
             if (w[k] > 0.0f && (float)C > tf) {
@@ -452,52 +536,105 @@ __device__ int select_token(const svh::VerifyArgs &a, int mode, float wmul, floa
 template <int PES, int QES>
 __global__ __launch_bounds__(NT) void k_select(svh::VerifyArgs a, const ReqG *__restrict__ req,
                                                float *__restrict__ csum, const float *__restrict__ bm,
-                                               int nchr, uint32_t *__restrict__ errword)
+                                               int nseg, uint32_t *__restrict__ errword)
 {
-    __shared__ float red[NT / svk::kWave];
     __shared__ SelectShared sh;
-    const int b = blockIdx.x;
+    __shared__ int32_t xs[MAXG];
+    const int b = a.b0 + (int)blockIdx.x;
     const ReqG r = req[b];
     if (r.flags) return;   // k_accept wrote the request's error outputs
     const int gamma = a.gamma;
     const int G1 = gamma + 1;
+    if ((int)threadIdx.x < r.tau) xs[threadIdx.x] = a.draft[(int64_t)b * gamma + threadIdx.x];
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
     const char *qrow = r.mode ? nullptr : (const char *)a.q + ((int64_t)b * gamma + r.tau) * a.V * QES;
-    float *own = csum + (int64_t)b * nchr;
-    const float *sums = sums_from_pass2(a, r) ? bm + ((int64_t)b * gamma + r.tau) * nchr : own;
+    float *own = csum + (int64_t)b * nseg;
+    const float *sums = sums_from_pass2(a, r) ? bm + ((int64_t)b * gamma + r.tau) * nseg : own;
 
     uint32_t flags = 0;
     double Z = 0.0;
-    int y = select_token<PES, QES>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nchr, prow, qrow, r.u2, sh, Z);
+    int y = select_token<PES, QES>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, sh, Z);
     if (y < 0 && r.mode == 0) {
         // residual mass rounded to zero (in exact arithmetic a rejection
         // implies p != q): draw from the p row instead
         flags |= SV_FLAG_RESID_ZERO;
-        for (int k = 0; k < nchr; ++k) {
-            const int64_t e0 = (int64_t)k * CHR;
-            const int64_t e1 = e0 + CHR < a.V ? e0 + CHR : a.V;
-            const float acc = chunk_weight_sum<PES, QES>(prow, nullptr, e0, e1, 1, 1.0f, r.lp2, 0.0f, a.c);
-            const float tot = svk::block_sum<NT>(acc, red);
-            if (threadIdx.x == 0) own[k] = tot;
-            __syncthreads();
+        const int wid = threadIdx.x / svk::kWave;
+        for (int k = wid; k < nseg; k += SPW) {
+            const int64_t s0 = (int64_t)k * SEG;
+            const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+            const float tot = segment_weight_sum<PES, QES>(prow, nullptr, s0, s1, 1, 1.0f, r.lp2, 0.0f, a.c);
+            if ((threadIdx.x & (svk::kWave - 1)) == 0) own[k] = tot;
         }
-        y = select_token<PES, QES>(a, 1, 1.0f, r.lp2, 0.0f, own, nchr, prow, nullptr, r.u2, sh, Z);
+        __syncthreads();
+        y = select_token<PES, QES>(a, 1, 1.0f, r.lp2, 0.0f, own, nseg, prow, nullptr, r.u2, sh, Z);
     }
     if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
-    if (threadIdx.x == 0) {
-        const int64_t ob = (int64_t)b * G1;
-        if (y >= 0) {
-            for (int j = 0; j < G1; ++j)
-                a.out_tokens[ob + j] = j < r.tau ? a.draft[(int64_t)b * gamma + j] : (j == r.tau ? y : -1);
-            a.accepted_len[b] = r.tau;
-        } else {
-            for (int j = 0; j < G1; ++j) a.out_tokens[ob + j] = -1;
-            a.accepted_len[b] = -1;
+    write_outputs(a, b, r.tau, y, xs, flags, Z, errword);
+}
+
+// ---------------------------------------------------------------------------
+// Fused tail: one workgroup of NTT threads per request evaluates the request
+// (wavefront 0), sums the correction / bonus weights of row tau+1 segment by
+// segment into LDS (all wavefronts) and selects the token, with no
+// communication between workgroups.  Used when the segment sums fit in LDS.
+// ---------------------------------------------------------------------------
+constexpr int NTT = 1024;
+constexpr int kTailMaxSeg = 4096;   // LDS segment sums: V <= 8.4M tokens
+#ifndef SV_FUSED_TAIL
+#define SV_FUSED_TAIL 1             // 0: always the accept / sum / select kernels
+#endif
+
+template <int PES, int QES>
+__global__ __launch_bounds__(NTT) void k_tail(svh::VerifyArgs a, const float2 *__restrict__ part, int nch1,
+                                              const float *__restrict__ bm, int nseg, int stage,
+                                              float *__restrict__ lp2g, float *__restrict__ lq2g,
+                                              float *__restrict__ wrun, uint32_t *__restrict__ errword)
+{
+    __shared__ AcceptLDS as;
+    __shared__ ReqG r;
+    __shared__ float segsum[kTailMaxSeg];
+    __shared__ SelectShared sh;
+    const int b = a.b0 + (int)blockIdx.x;
+    if (threadIdx.x < svk::kWave)
+        accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, &r, lp2g, lq2g, wrun, errword, as);
+    __syncthreads();
+    if (r.flags) return;   // accept_eval wrote the request's error outputs
+    const int gamma = a.gamma;
+    const int G1 = gamma + 1;
+    const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
+    const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
+    const char *qrow = r.mode ? nullptr : (const char *)a.q + ((int64_t)b * gamma + r.tau) * a.V * QES;
+
+    const float *sums = segsum;
+    if (sums_from_pass2(a, r)) {
+        sums = bm + ((int64_t)b * gamma + r.tau) * nseg;
+    } else {
+        for (int k = wid; k < nseg; k += NTT / svk::kWave) {
+            const int64_t s0 = (int64_t)k * SEG;
+            const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+            const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
+            if (lane == 0) segsum[k] = tot;
         }
-        if (a.diag.flags) a.diag.flags[b] = flags;
-        if (a.diag.resid_mass) a.diag.resid_mass[b] = (float)Z;
-        if (flags) atomicOr(errword, flags);
+        __syncthreads();
     }
+    uint32_t flags = 0;
+    double Z = 0.0;
+    int y = select_token<PES, QES, NTT>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, sh, Z);
+    if (y < 0 && r.mode == 0) {
+        // residual mass rounded to zero (in exact arithmetic a rejection
+        // implies p != q): draw from the p row instead
+        flags |= SV_FLAG_RESID_ZERO;
+        for (int k = wid; k < nseg; k += NTT / svk::kWave) {
+            const int64_t s0 = (int64_t)k * SEG;
+            const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+            const float tot = segment_weight_sum<PES, QES>(prow, nullptr, s0, s1, 1, 1.0f, r.lp2, 0.0f, a.c);
+            if (lane == 0) segsum[k] = tot;
+        }
+        __syncthreads();
+        y = select_token<PES, QES, NTT>(a, 1, 1.0f, r.lp2, 0.0f, segsum, nseg, prow, nullptr, r.u2, sh, Z);
+    }
+    if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
+    write_outputs(a, b, r.tau, y, as.x, flags, Z, errword);
 }
 
 // ---------------------------------------------------------------------------
@@ -507,8 +644,8 @@ template <int PES, int QES>
 void launch_accept(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int stage)
 {
     const int slot = svh::prof_begin(ctx, s, SV_KERNEL_ACCEPT);
-    hipLaunchKernelGGL((k_accept<PES, QES>), dim3(a.B), dim3(svk::kWave), 0, s, a,
-                       (const float2 *)ctx->ws.part, ctx->nch1, (const float *)ctx->ws.bm, ctx->nchr, stage,
+    hipLaunchKernelGGL((k_accept<PES, QES>), dim3(a.nb), dim3(svk::kWave), 0, s, a,
+                       (const float2 *)ctx->ws.part, ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage,
                        (ReqG *)ctx->ws.req, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
 }
@@ -517,22 +654,37 @@ template <int PES, int QES>
 void launch_sum_and_select(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
 {
     const ReqG *req = (const ReqG *)ctx->ws.req;
-    const int nchr = ctx->nchr;
+    const int nseg = ctx->nseg;
+    const int64_t nwg = (nseg + SPW - 1) / SPW;
     int slot = svh::prof_begin(ctx, s, SV_KERNEL_RESID);
-    hipLaunchKernelGGL((k_resid_sum<PES, QES>), dim3((unsigned)((int64_t)a.B * nchr)), dim3(NT), 0, s, a, req,
-                       ctx->ws.csum, nchr);
+    hipLaunchKernelGGL((k_resid_sum<PES, QES>), dim3((unsigned)((int64_t)a.nb * nwg)), dim3(NT), 0, s, a, req,
+                       ctx->ws.csum, nseg);
     svh::prof_end(ctx, s, slot);
     slot = svh::prof_begin(ctx, s, SV_KERNEL_SELECT);
-    hipLaunchKernelGGL((k_select<PES, QES>), dim3(a.B), dim3(NT), 0, s, a, req, ctx->ws.csum,
-                       (const float *)ctx->ws.bm, nchr, ctx->ws.errword);
+    hipLaunchKernelGGL((k_select<PES, QES>), dim3(a.nb), dim3(NT), 0, s, a, req, ctx->ws.csum,
+                       (const float *)ctx->ws.bm, nseg, ctx->ws.errword);
+    svh::prof_end(ctx, s, slot);
+}
+
+template <int PES, int QES>
+void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int stage)
+{
+    const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
+    hipLaunchKernelGGL((k_tail<PES, QES>), dim3(a.nb), dim3(NTT), 0, s, a, (const float2 *)ctx->ws.part, ctx->nch1,
+                       (const float *)ctx->ws.bm, ctx->nseg, stage, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun,
+                       ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
 }
 
 template <int PES, int QES>
 hipError_t token_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
 {
-    launch_accept<PES, QES>(ctx, a, s, STAGE_TOKEN);
-    launch_sum_and_select<PES, QES>(ctx, a, s);
+    if (SV_FUSED_TAIL && ctx->nseg <= kTailMaxSeg) {
+        launch_fused_tail<PES, QES>(ctx, a, s, STAGE_TOKEN);
+    } else {
+        launch_accept<PES, QES>(ctx, a, s, STAGE_TOKEN);
+        launch_sum_and_select<PES, QES>(ctx, a, s);
+    }
     return hipGetLastError();
 }
 
@@ -542,13 +694,18 @@ hipError_t block_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
     launch_accept<PES, QES>(ctx, a, s, STAGE_BLOCK_PRE);
     if (a.gamma >= 2) {
         const int slot = svh::prof_begin(ctx, s, SV_KERNEL_BLOCK_PASS2);
-        hipLaunchKernelGGL((k_block_pass2<PES, QES>), dim3((unsigned)((int64_t)a.B * (a.gamma - 1) * ctx->nchr)),
+        const int64_t nwg = (ctx->nseg + SPW - 1) / SPW;
+        hipLaunchKernelGGL((k_block_pass2<PES, QES>), dim3((unsigned)((int64_t)a.nb * (a.gamma - 1) * nwg)),
                            dim3(NT), 0, s, a, (const ReqG *)ctx->ws.req, (const float *)ctx->ws.lp2,
-                           (const float *)ctx->ws.lq2, (const float *)ctx->ws.wrun, ctx->ws.bm, ctx->nchr);
+                           (const float *)ctx->ws.lq2, (const float *)ctx->ws.wrun, ctx->ws.bm, ctx->nseg);
         svh::prof_end(ctx, s, slot);
     }
-    launch_accept<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
-    launch_sum_and_select<PES, QES>(ctx, a, s);
+    if (SV_FUSED_TAIL && ctx->nseg <= kTailMaxSeg) {
+        launch_fused_tail<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
+    } else {
+        launch_accept<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
+        launch_sum_and_select<PES, QES>(ctx, a, s);
+    }
     return hipGetLastError();
 }
 
@@ -558,7 +715,7 @@ namespace svh {
 
 hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 {
-    if (a.B <= 0) return hipSuccess;
+    if (a.nb <= 0) return hipSuccess;
     if (a.p_esize == 2 && a.q_esize == 2) return token_tail<2, 2>(ctx, a, s);
     if (a.p_esize == 2) return token_tail<2, 4>(ctx, a, s);
     if (a.q_esize == 2) return token_tail<4, 2>(ctx, a, s);
@@ -567,7 +724,7 @@ hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 
 hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 {
-    if (a.B <= 0) return hipSuccess;
+    if (a.nb <= 0) return hipSuccess;
     if (a.p_esize == 2 && a.q_esize == 2) return block_tail<2, 2>(ctx, a, s);
     if (a.p_esize == 2) return block_tail<2, 4>(ctx, a, s);
     if (a.q_esize == 2) return block_tail<4, 2>(ctx, a, s);

@@ -449,3 +449,17 @@ def test_full_workload4_markov_then_verify_sampled():
                           type(ov)(*[getattr(ov, f)[keep] for f in ov.__dataclass_fields__]), mi.gamma)
     _say(f"[w4 verify full] {rep2}")
     assert rep2.ok(), str(rep2)
+
+
+def test_huge_vocabulary_split_tail():
+    """V above the fused tail's LDS capacity (4096 segments of 2048 tokens):
+    the accept / segment-sum / select kernels run instead."""
+    B, gamma, V = 2, 2, 4096 * 2048 + 5003
+    _say(f"case: huge vocabulary V={V} (split tail)")
+    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V, row_block=3)
+    vi_hi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V, row_block=3, noise=0.05)
+    with make_ctx(B, gamma, V) as ctx:
+        for v in (vi, vi_hi):
+            for off in range(3):
+                check_verify(ctx, v, offset=off, label=f"huge V off={off}")
+                check_verify(ctx, v, block=True, offset=off, label=f"huge V block off={off}")
