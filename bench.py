@@ -17,6 +17,11 @@ steps.  Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
        [--copy-probe]   (also runs a plain copy of known size, for counter scaling)
+       [--workload headline|tiny|batched|block|markov|all]
+The other workloads (one JSON line each, same fields) measure the tiny and
+batched token-verification batches, scheduler + block verification
+(B=512, gamma=8) and the Markov-head sampler followed by verification
+(B=128, gamma=8, R=256; its roofline entry adds the MFMA rate).
 """
 import argparse
 import hashlib
@@ -79,6 +84,193 @@ def cpu_baseline(vi, budget_s=10.0, chunk=4):
                       f"{spent:.1f} s of single-thread oracle time"}
 
 
+def _time_steps(step, warmup, steps):
+    """Mean ms per step over exactly `steps` steps, synchronised on both sides."""
+    import torch
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(steps):
+        step(warmup + k)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3
+
+
+def _profile_steps(L, ctx, step, first, steps):
+    """Per-kernel mean durations (HIP events recorded by the library)."""
+    L.spec_verify_profile_enable(ctx, True)
+    L.spec_verify_profile_read(ctx)
+    for k in range(steps):
+        step(first + k)
+    prof = L.spec_verify_profile_read(ctx)
+    L.spec_verify_profile_enable(ctx, False)
+    return prof
+
+
+def _mean_us(prof, name):
+    ms, n = prof[name]
+    return ms / max(n, 1) * 1e3
+
+
+def _hbm_roofline(kernel, alg_bytes, mean_us, traffic=None):
+    achieved = alg_bytes / (mean_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic, "kernel": kernel,
+            "alg_bytes_per_launch": int(alg_bytes), "mean_us": round(mean_us, 2)}
+
+
+def _line(metric, value, unit, args, ms, config, roofline, **extra):
+    d = {"metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
+         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+         "vs_baseline": None, "dtype": "f32", "data": "synthetic", "config": config, "roofline": roofline}
+    d.update(extra)
+    return d
+
+
+def bench_headline(args, L, WL):
+    import torch
+    cfg = WL.CONFIGS[3]
+    # two independent batches of the headline recipe (each above the 256 MB
+    # Infinity Cache), alternated between steps
+    sets = [WL.make_verify_inputs(3, "cuda"), WL.make_verify_inputs(3, "cuda", seed=1103)]
+    vi = sets[0]
+    B, gamma, V = vi.B, vi.gamma, vi.V
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+    ctx = L.Context(0, B, gamma, V)
+
+    def step(k):
+        s = sets[k % len(sets)]
+        L.spec_verify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k)
+
+    ms, wall_ms = _time_steps(step, args.warmup, args.steps)
+    a = acc.cpu().numpy()
+    accepted = float(a[a >= 0].mean())
+    prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
+    alg = WL.bytes_single_read(vi)
+    roofline = _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats"), measured_traffic(alg))
+    if args.copy_probe:
+        # a plain streaming kernel of known traffic (1 GiB read + 1 GiB written
+        # per dispatch), to scale the FETCH_SIZE / WRITE_SIZE counters
+        n = (1 << 30) // 4
+        src = torch.zeros(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(vi)
+    ctx.close()
+    return _line(METRIC, B * gamma / (ms / 1e3), "verified positions/s", args, ms,
+                 {"workload": "token-level verification, headline batch", "B": B, "gamma": gamma, "V": V,
+                  "logits": "bf16", "temperature": cfg["T"], "input_sets": len(sets)},
+                 roofline, cpu_baseline=cpu,
+                 kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
+                 emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
+                 mean_accepted=round(accepted, 4), wall_ms_per_step=round(wall_ms, 5))
+
+
+def bench_token(args, L, WL, cfg_id, nsets):
+    """Token verification of workload 1 (tiny) or 2 (batched)."""
+    import torch
+    sets = [WL.make_verify_inputs(cfg_id, "cuda", seed=1000 + cfg_id + 100 * k) for k in range(nsets)]
+    vi = sets[0]
+    B, gamma, V = vi.B, vi.gamma, vi.V
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+    ctx = L.Context(0, B, gamma, V)
+
+    def step(k):
+        s = sets[k % len(sets)]
+        L.spec_verify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k)
+
+    ms, _ = _time_steps(step, args.warmup, args.steps)
+    prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
+    ctx.close()
+    name = WL.CONFIGS[cfg_id]["name"]
+    return _line(f"verified positions/s, {WL.describe(cfg_id)}", B * gamma / (ms / 1e3), "verified positions/s",
+                 args, ms, {"workload": f"token-level verification, {name} batch", "B": B, "gamma": gamma, "V": V,
+                            "logits": str(vi.p.dtype).split(".")[-1], "temperature": vi.T, "input_sets": nsets},
+                 _hbm_roofline("k_rowstats", WL.bytes_single_read(vi), _mean_us(prof, "rowstats")),
+                 us_per_call=round(ms * 1e3, 2),
+                 kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
+
+
+def bench_block(args, L, WL):
+    """Workload 5: scheduler + block verification, B=512, gamma=8."""
+    import torch
+    sets = [WL.make_verify_inputs(5, "cuda"), WL.make_verify_inputs(5, "cuda", seed=1105)]
+    vi = sets[0]
+    B, gamma, V = vi.B, vi.gamma, vi.V
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+    vlen = torch.empty(B, dtype=torch.int32, device="cuda")
+    ctx = L.Context(0, B, gamma, V)
+
+    def step(k):
+        s = sets[k % len(sets)]
+        L.spec_blockverify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k,
+                               conf=s.conf, sps_a=2000.0, sps_k=4096.0, verify_len_out=vlen)
+
+    ms, _ = _time_steps(step, args.warmup, args.steps)
+    prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
+    # verified positions: what the scheduler admitted (the same for every step of a set)
+    admitted = []
+    for s in sets:
+        L.spec_schedule_run(ctx, s.conf, vlen, sps_a=2000.0, sps_k=4096.0)
+        torch.cuda.synchronize()
+        admitted.append(vlen.cpu().numpy().astype("int64"))
+    ctx.close()
+    positions = sum(float(x.sum()) for x in admitted) / len(admitted)
+    rows = sum(float((2 * x + 1).sum()) for x in admitted) / len(admitted)
+    alg = rows * V * vi.p.element_size()
+    return _line("verified positions/s, B=512 gamma=8 V=129,280 bf16, scheduler + block verification",
+                 positions / (ms / 1e3), "verified positions/s", args, ms,
+                 {"workload": "block verification driven by the confidence scheduler", "B": B, "gamma": gamma,
+                  "V": V, "logits": "bf16", "sps": "2000/(1+n/4096)", "input_sets": len(sets)},
+                 _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats")),
+                 mean_verify_len=round(positions / B, 4),
+                 kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
+
+
+def bench_markov(args, L, WL):
+    """Workload 4: Markov-head draft sampling (gamma positions), then verification."""
+    import torch
+    mi = WL.make_markov_inputs("cuda")
+    B, gamma, V, R = mi.B, mi.gamma, mi.V, mi.R
+    draft = torch.empty(B, gamma, dtype=torch.int32, device="cuda")
+    ql = torch.empty(B, gamma, V, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, gamma, dtype=torch.float32, device="cuda")
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+    ctx = L.Context(0, B, gamma, V, R)
+
+    def step(k):
+        L.markov_draft_run(ctx, mi.base, mi.U, mi.W, mi.x0, draft, q_logits=ql, lse_q=lse, temperature=mi.T,
+                           seed=WL.DRAFT_SEED, offset=k)
+        L.spec_verify_run(ctx, mi.p, ql, draft, acc, out, temperature=mi.T, seed=WL.VERIFY_SEED, offset=k)
+
+    ms, _ = _time_steps(step, args.warmup, args.steps)
+    prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
+    ctx.close()
+    gemm_us = _mean_us(prof, "markov_gemm")
+    bytes_gemm = B * V * 2 + R * V * 2 + B * R * 2 + B * V * 4   # base_k + W + U rows + q_k
+    flops = 2.0 * B * R * V
+    roof = _hbm_roofline("k_markov_gemm", bytes_gemm, gemm_us)
+    roof["mfma_tflops"] = round(flops / (gemm_us * 1e-6) / 1e12, 2)
+    roof["mfma_frac_of_bf16_peak"] = round(flops / (gemm_us * 1e-6) / 2.5e15, 4)
+    return _line("verified positions/s, B=128 gamma=8 V=129,280, Markov-head draft + verification",
+                 B * gamma / (ms / 1e3), "verified positions/s", args, ms,
+                 {"workload": "Markov-head draft sampling (R=256), then token verification (p bf16, q fp32)",
+                  "B": B, "gamma": gamma, "V": V, "R": R},
+                 roof, kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
+                 markov_ms_per_call=round((prof["markov_gemm"][0] + prof["markov_select"][0]) / args.steps, 4))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +278,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "tiny", "batched", "block", "markov", "all"],
+                    help="headline (default: the one JSON line the driver reads) or another workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -96,84 +291,15 @@ def main():
     import lossless_draft_verification_02_amd as L
     from lossless_draft_verification_02_amd import workloads as WL
 
-    dev = 0
-    torch.cuda.set_device(dev)
-    cfg = WL.CONFIGS[3]
-    # two independent batches of the headline recipe, alternated between steps
-    sets = [WL.make_verify_inputs(3, "cuda"), WL.make_verify_inputs(3, "cuda", seed=1103)]
-    vi = sets[0]
-    B, gamma, V = vi.B, vi.gamma, vi.V
-    alg_bytes = WL.bytes_single_read(vi)
-    acc = torch.empty(B, dtype=torch.int32, device="cuda")
-    out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
-    ctx = L.Context(dev, B, gamma, V)
-
-    def step(k):
-        s = sets[k % len(sets)]
-        L.spec_verify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k)
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    accepted = []
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for k in range(args.steps):
-        step(args.warmup + k)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    a = acc.cpu().numpy()
-    accepted = float(a[a >= 0].mean())
-
-    # per-kernel durations from HIP events recorded by the library on its launch stream
-    L.spec_verify_profile_enable(ctx, True)
-    L.spec_verify_profile_read(ctx)
-    for k in range(args.steps):
-        step(args.warmup + args.steps + k)
-    prof = L.spec_verify_profile_read(ctx)
-    L.spec_verify_profile_enable(ctx, False)
-    rs_ms, rs_n = prof["rowstats"]
-    rs_avg_s = rs_ms / max(rs_n, 1) / 1e3
-    achieved = alg_bytes / rs_avg_s / 1e9
-    traffic = measured_traffic(alg_bytes)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                "kernel": "k_rowstats", "alg_bytes_per_launch": alg_bytes,
-                "mean_us": round(rs_avg_s * 1e6, 2)}
-    kernels_us = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in prof.items() if v[1]}
-
-    if args.copy_probe:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(vi)
-
-    value = B * gamma / (ms_per_step / 1e3)
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "verified positions/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "token-level verification, headline batch", "B": B, "gamma": gamma, "V": V,
-                   "logits": "bf16", "temperature": cfg["T"], "input_sets": len(sets)},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "kernels_mean_us": kernels_us,
-        "emitted_tokens_per_s": round(B * (accepted + 1) / (ms_per_step / 1e3), 1),
-        "mean_accepted": round(accepted, 4),
-        "wall_ms_per_step": round(wall / args.steps * 1e3, 5),
-    }
-    ctx.close()
-    print(json.dumps(line), flush=True)
+    torch.cuda.set_device(0)
+    runs = {"headline": lambda: bench_headline(args, L, WL),
+            "tiny": lambda: bench_token(args, L, WL, 1, 1),
+            "batched": lambda: bench_token(args, L, WL, 2, 4),
+            "block": lambda: bench_block(args, L, WL),
+            "markov": lambda: bench_markov(args, L, WL)}
+    names = list(runs) if args.workload == "all" else [args.workload]
+    for n in names:
+        print(json.dumps(runs[n]()), flush=True)
 
 
 if __name__ == "__main__":
