@@ -250,7 +250,7 @@ def bench_markov(args, L, WL):
     ctx = L.Context(0, B, gamma, V, R)
 
     def step(k):
-        L.markov_draft_run(ctx, mi.base, mi.U, mi.W, mi.x0, draft, q_logits=ql, lse_q=lse, temperature=mi.T,
+        L.markov_draft_run(ctx, mi.base, mi.U, mi.Wt, mi.x0, draft, q_logits=ql, lse_q=lse, temperature=mi.T,
                            seed=WL.DRAFT_SEED, offset=k)
         L.spec_verify_run(ctx, mi.p, ql, draft, acc, out, temperature=mi.T, seed=WL.VERIFY_SEED, offset=k)
 

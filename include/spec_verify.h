@@ -160,18 +160,23 @@ sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream,
                                int32_t *accepted_len, int32_t *out_tokens, const sv_diag *diag);
 
 /* Markov-head draft sampler.  For k = 1..gamma, strictly left to right:
- * z_k = base_k + U[x_{k-1}, :] . W (bf16 inputs, fp32 accumulation),
- * x_k = inverse-CDF draw from softmax(z_k / temperature) with uniform tag 2
- * at position k.  x_0 is the anchor token.
+ * z_k[n] = base_k[n] + sum_r U[x_{k-1}, r] W[r, n] (bf16 inputs, fp32
+ * accumulation), x_k = inverse-CDF draw from softmax(z_k / temperature) with
+ * uniform tag 2 at position k.  x_0 is the anchor token.
  *   base_logits   [B, gamma, V] bf16
- *   U             [V, R] bf16, W [R, V] bf16, R == the context's max_rank
+ *   U             [V, R] bf16: row x is the transition embedding of token x
+ *   Wt            [V, R] bf16: W stored vocabulary-major (Wt[n, r] = W[r, n]),
+ *                 the way a linear layer from R to V stores its weight
+ *   R             == the context's max_rank
  *   x0            [B] int32 anchor tokens
  *   uniforms      [B, gamma] fp32 or NULL (replaces the Philox draws)
  *   draft_tokens  [B, gamma] int32 out
  *   q_logits      [B, gamma, V] fp32 out or NULL: z_k before 1/temperature
- *   lse_q         [B, gamma] fp32 out or NULL: log-sum-exp of z_k / T */
+ *   lse_q         [B, gamma] fp32 out or NULL: log-sum-exp of z_k / T
+ * Requires R == the context's max_rank and V <= 262,144 (SV_ERR_UNSUPPORTED
+ * beyond); U and Wt must be 16-byte aligned. */
 sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream,
-                           const void *base_logits, const void *U, const void *W, int R,
+                           const void *base_logits, const void *U, const void *Wt, int R,
                            const int32_t *x0, int B, int gamma, int64_t V, float temperature,
                            uint64_t seed, uint64_t offset, const float *uniforms,
                            int32_t *draft_tokens, float *q_logits, float *lse_q);

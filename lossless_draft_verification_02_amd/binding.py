@@ -246,22 +246,23 @@ def spec_blockverify_run(ctx: Context, p, q, draft, accepted_len, out_tokens, *,
         ctypes.byref(d) if d else None))
 
 
-def markov_draft_run(ctx: Context, base, U, W, x0, draft_out, *, q_logits=None, lse_q=None,
+def markov_draft_run(ctx: Context, base, U, Wt, x0, draft_out, *, q_logits=None, lse_q=None,
                      temperature: float = 1.0, seed: int = 0, offset: int = 0, uniforms=None, stream=None):
-    """Markov-head sampler: base [B, gamma, V], U [V, R], W [R, V] (bf16) -> draft_out [B, gamma]."""
+    """Markov-head sampler: base [B, gamma, V], U [V, R], Wt [V, R] (bf16; W stored vocabulary-major)
+    -> draft_out [B, gamma]."""
     torch = _torch()
     B, gamma, V = base.shape
     R = U.shape[1]
     _need(base, "base", dtype=torch.bfloat16, device=ctx.device)
     _need(U, "U", dtype=torch.bfloat16, shape=(V, R), device=ctx.device)
-    _need(W, "W", dtype=torch.bfloat16, shape=(R, V), device=ctx.device)
+    _need(Wt, "Wt", dtype=torch.bfloat16, shape=(V, R), device=ctx.device)
     _need(x0, "x0", dtype=torch.int32, shape=(B,), device=ctx.device)
     _need(draft_out, "draft_out", dtype=torch.int32, shape=(B, gamma), device=ctx.device)
     _need(q_logits, "q_logits", dtype=torch.float32, shape=(B, gamma, V), device=ctx.device)
     _need(lse_q, "lse_q", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
     _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
     _check("markov_draft_run", load_library().markov_draft_run(
-        ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(W), R, _ptr(x0), B, gamma, V,
+        ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), R, _ptr(x0), B, gamma, V,
         temperature, seed, offset, _ptr(uniforms), _ptr(draft_out), _ptr(q_logits), _ptr(lse_q)))
 
 

@@ -149,6 +149,10 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->max_gamma = max_gamma;
     ctx->vocab = vocab;
     ctx->max_rank = max_rank;
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || ncu <= 0)
+        ncu = 256;
+    ctx->num_cu = ncu;
     // row-statistics chunks: about kTargetChunk1 elements, rounded to 8
     int64_t nch1 = (vocab + svh::kTargetChunk1 / 2) / svh::kTargetChunk1;
     if (nch1 < 1) nch1 = 1;
@@ -176,6 +180,8 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_wrun = carve((size_t)max_batch * (max_gamma + 1) * sizeof(float));
     const size_t o_err = carve(sizeof(uint32_t));
     const size_t o_sched = carve((size_t)max_batch * sizeof(int32_t));
+    const size_t o_srank = carve((size_t)svh::kSchedMax * sizeof(int32_t));
+    const size_t o_ssurv = carve((size_t)svh::kSchedMax * sizeof(double));
     size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0;
     if (max_rank > 0) {
         o_mkpart = carve((size_t)max_batch * ctx->ntile * sizeof(float2));
@@ -204,6 +210,8 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.wrun = (float *)(b + o_wrun);
     ctx->ws.errword = (uint32_t *)(b + o_err);
     ctx->ws.sched_len = (int32_t *)(b + o_sched);
+    ctx->ws.sched_rank = (int32_t *)(b + o_srank);
+    ctx->ws.sched_surv = (double *)(b + o_ssurv);
     ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
     ctx->ws.mk_prev = max_rank > 0 ? (int32_t *)(b + o_mkprev) : nullptr;
     ctx->ws.mk_q = max_rank > 0 ? (float *)(b + o_mkq) : nullptr;
@@ -383,12 +391,15 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_log
     if (B <= 0 || B > ctx->max_batch || gamma < 1 || gamma > ctx->max_gamma)
         return fail(SV_ERR_INVALID, "markov_draft_run: B=%d or gamma=%d out of range", B, gamma);
     if (V != ctx->vocab) return fail(SV_ERR_INVALID, "markov_draft_run: V differs from the context's vocab");
+    if (ctx->ntile > svh::kMarkovMaxTiles)
+        return fail(SV_ERR_UNSUPPORTED, "markov_draft_run: V=%lld exceeds the sampler's %d-token limit", (long long)V,
+                    svh::kMarkovMaxTiles * svh::kMarkovTileN);
     if (!(temperature > 0.0f) || !std::isfinite(temperature))
         return fail(SV_ERR_INVALID, "markov_draft_run: temperature must be finite and > 0");
     if (!base_logits || !U || !W || !x0 || !draft_tokens)
         return fail(SV_ERR_INVALID, "markov_draft_run: base_logits, U, W, x0 and draft_tokens are required");
-    if (!aligned(U, 16) || !aligned(W, 2) || !aligned(base_logits, 2) || (q_logits && !aligned(q_logits, 4)))
-        return fail(SV_ERR_INVALID, "markov_draft_run: U must be 16-byte aligned, W and base 2-byte aligned");
+    if (!aligned(U, 16) || !aligned(W, 16) || !aligned(base_logits, 2) || (q_logits && !aligned(q_logits, 4)))
+        return fail(SV_ERR_INVALID, "markov_draft_run: U and Wt must be 16-byte aligned, base 2-byte aligned");
     DeviceGuard guard(ctx->device);
     svh::MarkovArgs a;
     a.base = (const uint16_t *)base_logits;

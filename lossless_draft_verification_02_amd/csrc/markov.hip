@@ -8,20 +8,25 @@
 // token sampled at position k-1, and samples position k from the result.
 //
 // Per position k (strictly sequential; x_0 is the anchor token):
-//   k_markov_gemm    grid (vocab tiles of 128, request blocks of 128):
-//                    z[b, n] = base[b, k, n] + sum_r U[x_{k-1}(b), r] W[r, n]
-//                    with bf16 MFMA (16x16x32, fp32 accumulate); the epilogue
-//                    adds the base logits, writes z (fp32) and per (request,
-//                    tile) the pair (max z*c, sum exp2(z*c - max)).
-//   k_markov_select  one workgroup per request: merge the tile pairs into the
-//                    row's log-sum-exp, pick the tile holding u * Z, scan it
-//                    for the token (inverse CDF in ascending token order).
-//
-// Operand staging: the gathered U rows (A operand, 16 B per lane per k-step)
-// are read straight from global memory into registers; the W tile is staged
-// through LDS transposed to [n][k] so every B fragment is one 16-byte LDS read.
-// The epilogue goes back through the same LDS space so base reads and z writes
-// are row-contiguous.
+//   k_markov_gemm    z[b, n] = base[b, k, n] + sum_r U[x_{k-1}(b), r] Wt[n, r]
+//                    computed transposed, z^T = Wt . U^T, with bf16 MFMA
+//                    (16x16x32, fp32 accumulate).  Wt (the transition matrix
+//                    stored vocabulary-major, V rows of R) gives the A operand
+//                    straight from HBM: 16 bytes per lane per k-step, no LDS.
+//                    The gathered U rows of up to 128 requests sit in LDS for
+//                    the workgroup's lifetime and give the B operand.  Each
+//                    accumulator lane holds 4 consecutive vocabulary entries
+//                    of one request, so the epilogue adds the base logits and
+//                    stores 16-byte runs of z without a detour through LDS,
+//                    and reduces per (request, 128-token tile) the pair
+//                    (max z*c, sum exp2(z*c - max)).  Workgroups loop over
+//                    vocabulary tiles; the next tile's Wt fragments are
+//                    requested as soon as the current ones are consumed, so
+//                    they arrive while the epilogue runs.
+//   k_markov_select  one wavefront per request, no barriers: merge the tile
+//                    pairs into the row's log-sum-exp, pick the tile holding
+//                    u * Z by an fp64 wavefront scan, scan inside it for the
+//                    token (inverse CDF in ascending token order).
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -30,15 +35,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;                 // 4 wavefronts
-constexpr int TN = svh::kMarkovTileN;   // 128 vocabulary columns per workgroup
-constexpr int TM = 128;                 // requests per workgroup (32 per wavefront)
-constexpr int RMAX = 256;
-constexpr int WT_STRIDE_MAX = RMAX + 8;           // bf16 elements per transposed W row
-constexpr int CT_STRIDE = TN + 4;                 // floats per epilogue row
-constexpr int LDS_BYTES = (TN * WT_STRIDE_MAX * 2) > (TM * CT_STRIDE * 4)
-                              ? (TN * WT_STRIDE_MAX * 2)
-                              : (TM * CT_STRIDE * 4);
+constexpr int NT = 256;                 // 4 wavefronts, 32 vocabulary rows each per tile
+constexpr int TN = svh::kMarkovTileN;   // 128 vocabulary entries per tile
+constexpr int MC = 128;                 // requests per workgroup (8 blocks of 16)
+constexpr int MBLK = MC / 16;
+constexpr int kGemmWGs = 512;           // two resident workgroups per compute unit
+
+static_assert(TN == 4 * 32, "four wavefronts of 32 vocabulary rows per tile");
 
 __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m)
 {
@@ -46,231 +49,299 @@ __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m
     return (x < 0 || (int64_t)x >= a.V) ? 0 : x;   // invalid ids are flagged by the select
 }
 
+// The wavefront's A fragments of one tile: vocabulary rows n0 + 32 w + 16 vb + li,
+// k-chunk 8 lg of each 32-wide k-step.  Rows past V read as zero.
 template <int R>
-__global__ __launch_bounds__(NT) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
-                                                    int64_t zstride, float2 *__restrict__ tile_part,
-                                                    int ntile, int wvec)
+__device__ __forceinline__ void load_wt(const svh::MarkovArgs &a, int64_t nrow0, int li, int lg,
+                                        bf16x8 (&wa)[2][R / 32])
 {
-    constexpr int KS = R / 32;            // MFMA k-steps
-    constexpr int WTS = R + 8;            // transposed W row stride (bf16 elements)
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-    __bf16 *Wt = (__bf16 *)lds;
-    float *Ct = (float *)lds;
-
-    const int tile = blockIdx.x;
-    const int64_t n0 = (int64_t)tile * TN;
-    const int ncols = (int)((a.V - n0) < TN ? (a.V - n0) : TN);
-    const int m0 = blockIdx.y * TM;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int li = lane & 15, lg = lane >> 4;
-
-    // 1. W tile -> LDS, transposed: Wt[n][r] = W[r][n0 + n]
-    if (wvec) {
-        for (int u = threadIdx.x; u < (R / 4) * (TN / 8); u += NT) {
-            const int kq = u / (TN / 8), n8 = u % (TN / 8);
-            const int64_t col = n0 + 8 * n8;
-            uint32_t w4[4][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (col < a.V) {
-                    const svk::u32x4 v = *(const svk::u32x4 *)(a.W + (int64_t)(4 * kq + j) * a.V + col);
-                    w4[j][0] = v.x; w4[j][1] = v.y; w4[j][2] = v.z; w4[j][3] = v.w;
-                } else {
-                    w4[j][0] = w4[j][1] = w4[j][2] = w4[j][3] = 0u;
-                }
-            }
+    for (int vb = 0; vb < 2; ++vb) {
+        const int64_t n = nrow0 + 16 * vb + li;
+        const uint16_t *row = a.W + (n < a.V ? n : 0) * R + 8 * lg;
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int word = cc >> 1, hi = cc & 1;
-                uint32_t e[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) e[j] = hi ? (w4[j][word] >> 16) : (w4[j][word] & 0xFFFFu);
-                uint2 packed = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-                *(uint2 *)(Wt + (8 * n8 + cc) * WTS + 4 * kq) = packed;
-            }
-        }
-    } else {
-        for (int u = threadIdx.x; u < R * TN; u += NT) {
-            const int r = u / TN, n = u % TN;
-            const int64_t col = n0 + n;
-            const uint16_t bits = col < a.V ? a.W[(int64_t)r * a.V + col] : (uint16_t)0;
-            ((uint16_t *)Wt)[n * WTS + r] = bits;
-        }
-    }
-
-    // 2. A fragments: rows m0 + 32*wid + 16*mb + li, k = 32*ks + 8*lg .. +7
-    bf16x8 afr[2][KS];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = m0 + 32 * wid + 16 * mb + li;
-        if (m < a.B) {
-            const int x = prev_token(a, k, m);
-            const uint16_t *urow = a.U + (int64_t)x * R;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) afr[mb][ks] = *(const bf16x8 *)(urow + 32 * ks + 8 * lg);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) afr[mb][ks] = bf16x8{};
-        }
-    }
-    __syncthreads();
-
-    // 3. MFMA: each wavefront computes 32 rows x 128 columns
-    f32x4 acc[2][TN / 16];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < TN / 16; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int nb = 0; nb < TN / 16; ++nb) {
-            const bf16x8 bfr = *(const bf16x8 *)(Wt + (16 * nb + li) * WTS + 32 * ks + 8 * lg);
-            acc[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[0][ks], bfr, acc[0][nb], 0, 0, 0);
-            acc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[1][ks], bfr, acc[1][nb], 0, 0, 0);
-        }
-    }
-    __syncthreads();   // every wavefront is done with Wt
-
-    // 4. accumulators -> LDS rows (lane holds D[4*lg + r][li] of each 16x16 block)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < TN / 16; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Ct[(32 * wid + 16 * mb + 4 * lg + r) * CT_STRIDE + 16 * nb + li] = acc[mb][nb][r];
-    __syncthreads();
-
-    // 5. per row: z = base + acc, write z, tile (max, sum exp2)
-    for (int rr = 0; rr < 32; ++rr) {
-        const int mloc = 32 * wid + rr;
-        const int m = m0 + mloc;
-        if (m >= a.B) break;
-        const uint16_t *brow = a.base + ((int64_t)m * a.gamma + (k - 1)) * a.V + n0;
-        float *zrow = zout + (int64_t)m * zstride + n0;
-        float zc[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = lane + 64 * h;
-            zc[h] = svk::neg_inf();
-            if (col < ncols) {
-                const float z = Ct[mloc * CT_STRIDE + col] + __uint_as_float((uint32_t)brow[col] << 16);
-                zrow[col] = z;
-                zc[h] = z * a.c;
-            }
-        }
-        float mx = fmaxf(zc[0], zc[1]);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        float s = 0.0f;
-        if (mx != svk::neg_inf()) s = svk::fast_exp2(zc[0] - mx) + svk::fast_exp2(zc[1] - mx);
-        // a NaN z poisons s (exp2(NaN) = NaN); keep it for the select to flag
-        if (zc[0] != zc[0] || zc[1] != zc[1]) s = __builtin_nanf("");
-        s = svk::wave_sum(s);
-        if (lane == 0) tile_part[(int64_t)m * ntile + tile] = make_float2(mx, s);
+        for (int s = 0; s < R / 32; ++s) wa[vb][s] = n < a.V ? *(const bf16x8 *)(row + 32 * s) : bf16x8{};
     }
 }
 
-struct SelShared {
-    double scan[NT];
-    svk::MS red[NT / 64];
-    float lse2;
-    int tstar, tlast, ybest, ylast;
-    double tbase;
-};
-
-__global__ __launch_bounds__(NT) void k_markov_select(svh::MarkovArgs a, int k, const float *__restrict__ zin,
-                                                      int64_t zstride, const float2 *__restrict__ tile_part,
-                                                      int ntile, uint32_t *__restrict__ errword)
+template <int R>
+__global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
+                                                       int64_t zstride, float2 *__restrict__ tile_part,
+                                                       int ntile, int vec)
 {
-    __shared__ SelShared sh;
-    const int b = blockIdx.x;
+    constexpr int KS = R / 32;
+    constexpr int US = R + 8;              // LDS row stride (bf16): conflict-free 16-byte fragment reads
+    constexpr int UCH = R / 8;             // 16-byte chunks per U row
+    constexpr int UPT = MC * UCH / NT;     // chunks staged per thread
+    __shared__ __attribute__((aligned(16))) uint16_t Us[MC * US];
+    __shared__ float2 red[4][MC];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int m0 = blockIdx.y * MC;
+    const int mrows = a.B - m0 < MC ? a.B - m0 : MC;
+
+    // first tile's Wt fragments, then the gathered U rows -> LDS
+    int tile = blockIdx.x;
+    bf16x8 wa[2][KS];
+    load_wt<R>(a, (int64_t)tile * TN + 32 * wid, li, lg, wa);
+    {
+        svk::u32x4 uv[UPT];
+#pragma unroll
+        for (int q = 0; q < UPT; ++q) {
+            const int u = (int)threadIdx.x + q * NT;
+            const int row = u / UCH, ch = u % UCH;
+            uv[q] = svk::u32x4{0u, 0u, 0u, 0u};
+            if (row < mrows) uv[q] = *(const svk::u32x4 *)(a.U + (int64_t)prev_token(a, k, m0 + row) * R + 8 * ch);
+        }
+#pragma unroll
+        for (int q = 0; q < UPT; ++q) {
+            const int u = (int)threadIdx.x + q * NT;
+            *(svk::u32x4 *)(Us + (u / UCH) * US + 8 * (u % UCH)) = uv[q];
+        }
+    }
+    __syncthreads();
+
+    for (; tile < ntile; tile += gridDim.x) {
+        const int64_t n0 = (int64_t)tile * TN;
+        const int64_t nw = n0 + 32 * wid;        // this wavefront's 32 rows
+
+        // base logits of the lane's outputs: request 16 mb + li, entries nw + 16 vb + 4 lg + r
+        uint2 bv[2][MBLK];
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+            const int64_t n = nw + 16 * vb + 4 * lg;
+#pragma unroll
+            for (int mb = 0; mb < MBLK; ++mb) {
+                const int ml = 16 * mb + li;
+                bv[vb][mb] = make_uint2(0xFF80FF80u, 0xFF80FF80u);   // -inf
+                if (ml < mrows) {
+                    const uint16_t *brow = a.base + ((int64_t)(m0 + ml) * a.gamma + (k - 1)) * a.V;
+                    if (vec) {
+                        if (n < a.V) bv[vb][mb] = *(const uint2 *)(brow + n);
+                    } else {
+                        uint16_t e[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e[r] = n + r < a.V ? brow[n + r] : (uint16_t)0xFF80u;
+                        bv[vb][mb] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+                    }
+                }
+            }
+        }
+        // two halves of 64 requests: half the accumulators live at a time
+        const int next = tile + (int)gridDim.x;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            constexpr int MH = MBLK / 2;
+            f32x4 acc[2][MH];
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+                for (int j = 0; j < MH; ++j) acc[vb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int j = 0; j < MH; ++j) {
+                    const int mb = MH * h + j;
+                    const bf16x8 bfr = *(const bf16x8 *)(Us + (16 * mb + li) * US + 32 * s + 8 * lg);
+                    acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[0][s], bfr, acc[0][j], 0, 0, 0);
+                    acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[1][s], bfr, acc[1][j], 0, 0, 0);
+                }
+            }
+            // after the second half the fragments are consumed: fetch the next
+            // tile's into the same registers, so the loads overlap the epilogue
+            if (h == 1 && next < ntile) load_wt<R>(a, (int64_t)next * TN + 32 * wid, li, lg, wa);
+
+            // epilogue: lane holds z^T[nw + 16 vb + 4 lg + r][16 mb + li]
+#pragma unroll
+            for (int j = 0; j < MH; ++j) {
+                const int mb = MH * h + j;
+                const int ml = 16 * mb + li;
+                const bool rowok = ml < mrows;
+                float zc[2][4];
+                float mx = svk::neg_inf();
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    const int64_t n = nw + 16 * vb + 4 * lg;
+                    const uint32_t b01 = bv[vb][mb].x, b23 = bv[vb][mb].y;
+                    float z[4];
+                    z[0] = acc[vb][j][0] + __uint_as_float(b01 << 16);
+                    z[1] = acc[vb][j][1] + __uint_as_float(b01 & 0xFFFF0000u);
+                    z[2] = acc[vb][j][2] + __uint_as_float(b23 << 16);
+                    z[3] = acc[vb][j][3] + __uint_as_float(b23 & 0xFFFF0000u);
+                    if (rowok) {
+                        float *zrow = zout + (int64_t)(m0 + ml) * zstride;
+                        if (vec) {
+                            if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (n + r < a.V) zrow[n + r] = z[r];
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        zc[vb][r] = n + r < a.V ? z[r] * a.c : svk::neg_inf();
+                        mx = fmaxf(mx, zc[vb][r]);
+                    }
+                }
+                // the four lanes li, li + 16, li + 32, li + 48 hold this request's 32 entries
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                float sum = 0.0f;
+                bool bad = false;
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        bad |= zc[vb][r] != zc[vb][r];
+                        if (mx != svk::neg_inf()) sum += svk::fast_exp2(zc[vb][r] - mx);
+                    }
+                if (bad) sum = __builtin_nanf("");   // a NaN entry poisons the row; the draw flags it
+                sum += __shfl_xor(sum, 16, 64);
+                sum += __shfl_xor(sum, 32, 64);
+                if (lg == 0) red[wid][ml] = make_float2(mx, sum);
+            }
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < mrows) {
+            svk::MS t{red[0][threadIdx.x].x, red[0][threadIdx.x].y};
+#pragma unroll
+            for (int w = 1; w < 4; ++w) t = svk::ms_merge(t, svk::MS{red[w][threadIdx.x].x, red[w][threadIdx.x].y});
+            tile_part[(int64_t)(m0 + (int)threadIdx.x) * ntile + tile] = make_float2(t.m, t.s);
+        }
+        __syncthreads();   // red[] is rewritten by the next tile
+    }
+}
+
+constexpr int kSelWaves = 4;                                        // requests per workgroup
+constexpr int kSelTilesPerLane = svh::kMarkovMaxTiles / 64;          // tile pairs held per lane
+
+__device__ __forceinline__ int wave_min_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArgs a, int k,
+                                                                  const float *__restrict__ zin, int64_t zstride,
+                                                                  const float2 *__restrict__ tile_part, int ntile,
+                                                                  uint32_t *__restrict__ errword)
+{
+    const int lane = threadIdx.x & 63;
+    const int b = blockIdx.x * kSelWaves + (int)(threadIdx.x >> 6);
+    if (b >= a.B) return;   // whole wavefront; nothing below synchronises the workgroup
     const int64_t out = (int64_t)b * a.gamma + (k - 1);
+
+    // independent loads first: the previous token and this lane's run of tile pairs
     const int32_t xprev = k == 1 ? a.x0[b] : a.draft[(int64_t)b * a.gamma + (k - 2)];
+    const float2 *tp = tile_part + (int64_t)b * ntile;
+    const int per = (ntile + 63) / 64;
+    const int t0 = lane * per;
+    float2 mine[kSelTilesPerLane];
+#pragma unroll
+    for (int q = 0; q < kSelTilesPerLane; ++q)
+        mine[q] = (q < per && t0 + q < ntile) ? tp[t0 + q] : make_float2(svk::neg_inf(), 0.0f);
+    const float u = a.uniforms ? a.uniforms[out]
+                               : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)k, 2u);
     if (xprev < 0 || (int64_t)xprev >= a.V) {
-        if (threadIdx.x == 0) {
+        if (lane == 0) {
             a.draft[out] = -1;
             if (a.lse_q) a.lse_q[out] = __builtin_nanf("");
             atomicOr(errword, SV_FLAG_BAD_TOKEN);
         }
         return;
     }
-    const float2 *tp = tile_part + (int64_t)b * ntile;
+
     // row log-sum-exp2 from the tile pairs
     svk::MS acc{svk::neg_inf(), 0.0f};
-    for (int t = threadIdx.x; t < ntile; t += NT) acc = svk::ms_merge(acc, svk::MS{tp[t].x, tp[t].y});
-    acc = svk::block_merge<NT>(acc, sh.red);
-    if (threadIdx.x == 0) {
-        sh.lse2 = (acc.s > 0.0f && acc.m != svk::pos_inf() && acc.s == acc.s) ? acc.m + log2f(acc.s)
-                                                                                : __builtin_nanf("");
-    }
-    __syncthreads();
-    const float lse2 = sh.lse2;
+#pragma unroll
+    for (int q = 0; q < kSelTilesPerLane; ++q) acc = svk::ms_merge(acc, svk::MS{mine[q].x, mine[q].y});
+    acc = svk::wave_merge(acc);
+    const float lse2 = (acc.s > 0.0f && acc.m != svk::pos_inf() && acc.s == acc.s) ? acc.m + log2f(acc.s)
+                                                                                    : __builtin_nanf("");
     if (lse2 != lse2) {
-        if (threadIdx.x == 0) {
+        if (lane == 0) {
             a.draft[out] = -1;
             if (a.lse_q) a.lse_q[out] = __builtin_nanf("");
             atomicOr(errword, SV_FLAG_BAD_ROW);
         }
         return;
     }
-    const float u = a.uniforms ? a.uniforms[out]
-                               : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)k, 2u);
 
-    // tile masses -> fp64 prefix, each thread owning a contiguous run of tiles
-    const int per = (ntile + NT - 1) / NT;
-    const int t0 = threadIdx.x * per;
-    const int t1 = t0 + per < ntile ? t0 + per : ntile;
+    // tile masses, fp64 prefix over the lanes' contiguous runs
+    float wt[kSelTilesPerLane];
     double loc = 0.0;
-    for (int t = t0; t < t1; ++t) loc += (double)(tp[t].y * svk::fast_exp2(tp[t].x - lse2));
-    double Z;
-    const double excl = svk::block_exclusive_scan_d<NT>(loc, sh.scan, &Z);
-    const float tf = __fmul_rn(u, (float)Z);
-    if (threadIdx.x == 0) {
-        sh.tstar = 0x7FFFFFFF;
-        sh.tlast = -1;
-        sh.ybest = 0x7FFFFFFF;
-        sh.ylast = -1;
+#pragma unroll
+    for (int q = 0; q < kSelTilesPerLane; ++q) {
+        wt[q] = (q < per && t0 + q < ntile) ? mine[q].y * svk::fast_exp2(mine[q].x - lse2) : 0.0f;
+        loc += (double)wt[q];
     }
-    __syncthreads();
+    const double incl = svk::wave_inclusive_scan_d(loc);
+    const double excl = incl - loc;
+    const double Z = __shfl(incl, 63, 64);
+    const float tf = __fmul_rn(u, (float)Z);
+    int first = 0x7FFFFFFF, lastpos = -1;
     {
         double run = excl;
-        for (int t = t0; t < t1; ++t) {
-            const float wt = tp[t].y * svk::fast_exp2(tp[t].x - lse2);
-            run += (double)wt;
-            if (wt > 0.0f) {
-                atomicMax(&sh.tlast, t);
-                if ((float)run > tf) {
-                    atomicMin(&sh.tstar, t);
-                    break;
-                }
+#pragma unroll
+        for (int q = 0; q < kSelTilesPerLane; ++q) {
+            if (q < per && t0 + q < ntile && wt[q] > 0.0f) {
+                run += (double)wt[q];
+                lastpos = t0 + q;
+                if (first == 0x7FFFFFFF && (float)run > tf) first = t0 + q;
             }
         }
     }
-    __syncthreads();
-    const bool fallback = sh.tstar == 0x7FFFFFFF;
-    const int ts = fallback ? sh.tlast : sh.tstar;
-    if (t0 <= ts && ts < t1) {
-        double run = excl;
-        for (int t = t0; t < ts; ++t) run += (double)(tp[t].y * svk::fast_exp2(tp[t].x - lse2));
-        sh.tbase = run;
+    const int tstar = wave_min_i(first);
+    const int tlast = wave_max_i(lastpos);
+    const bool fallback = tstar == 0x7FFFFFFF;
+    const int ts = fallback ? tlast : tstar;
+    if (ts < 0) {   // no tile kept any mass
+        if (lane == 0) {
+            a.draft[out] = -1;
+            if (a.lse_q) a.lse_q[out] = lse2 * svk::kLn2;
+            atomicOr(errword, SV_FLAG_BAD_ROW);
+        }
+        return;
     }
-    __syncthreads();
-    // inside the tile: thread j < TN owns column j
+    // cumulative mass before tile ts, from the lane that owns it
+    double before_ts = excl;
+#pragma unroll
+    for (int q = 0; q < kSelTilesPerLane; ++q)
+        if (q < per && t0 + q < ts) before_ts += (double)wt[q];
+    const double tbase = __shfl(before_ts, ts / per, 64);
+
+    // inside the tile: lane owns columns 2 lane, 2 lane + 1
     const int64_t c0 = (int64_t)ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
-    float w = 0.0f;
-    if ((int)threadIdx.x < ncols) w = svk::fast_exp2(zin[(int64_t)b * zstride + c0 + threadIdx.x] * a.c - lse2);
-    double dummy;
-    const double wexcl = svk::block_exclusive_scan_d<NT>((double)w, sh.scan, &dummy);
-    if (w > 0.0f) {
-        atomicMax(&sh.ylast, (int)threadIdx.x);
-        if (!fallback && (float)(sh.tbase + wexcl + (double)w) > tf) atomicMin(&sh.ybest, (int)threadIdx.x);
+    const float *zr = zin + (int64_t)b * zstride + c0;
+    const int j0 = 2 * lane, j1 = 2 * lane + 1;
+    const float w0 = j0 < ncols ? svk::fast_exp2(zr[j0] * a.c - lse2) : 0.0f;
+    const float w1 = j1 < ncols ? svk::fast_exp2(zr[j1] * a.c - lse2) : 0.0f;
+    const double pair = (double)w0 + (double)w1;
+    const double pincl = svk::wave_inclusive_scan_d(pair);
+    const double pexcl = pincl - pair;
+    int yb = 0x7FFFFFFF, yl = -1;
+    if (w1 > 0.0f) {
+        yl = j1;
+        if (!fallback && (float)(tbase + pexcl + (double)w0 + (double)w1) > tf) yb = j1;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int j = sh.ybest != 0x7FFFFFFF ? sh.ybest : sh.ylast;
+    if (w0 > 0.0f) {
+        if (yl < 0) yl = j0;
+        if (!fallback && (float)(tbase + pexcl + (double)w0) > tf) yb = j0;
+    }
+    const int ybest = wave_min_i(yb);
+    const int ylast = wave_max_i(yl);
+    if (lane == 0) {
+        const int j = ybest != 0x7FFFFFFF ? ybest : ylast;
         a.draft[out] = j >= 0 ? (int32_t)(c0 + j) : -1;
         if (a.lse_q) a.lse_q[out] = lse2 * svk::kLn2;
         if (j < 0) atomicOr(errword, SV_FLAG_BAD_ROW);
@@ -281,19 +352,24 @@ template <int R>
 hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s)
 {
     const int ntile = ctx->ntile;
-    const int wvec = (a.V % 8 == 0) && ((((uintptr_t)a.W) & 15) == 0);
+    const int gy = (a.B + MC - 1) / MC;
+    int gx = kGemmWGs / gy;
+    gx = gx < 1 ? 1 : (gx > ntile ? ntile : gx);
     // z rows of position k: the caller's q_logits [B, gamma, V], else a
     // workspace row per request
     const int64_t zstride = a.q_logits ? (int64_t)a.gamma * a.V : a.V;
+    const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0) &&
+                    ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
     for (int k = 1; k <= a.gamma; ++k) {
         float *zk = a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q;
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        hipLaunchKernelGGL((k_markov_gemm<R>), dim3(ntile, (a.B + TM - 1) / TM), dim3(NT), 0, s, a, k,
-                           zk, zstride, ctx->ws.mk_part, ntile, wvec);
+        hipLaunchKernelGGL((k_markov_gemm<R>), dim3(gx, gy), dim3(NT), 0, s, a, k, zk, zstride, ctx->ws.mk_part,
+                           ntile, vec);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
-        hipLaunchKernelGGL(k_markov_select, dim3(a.B), dim3(NT), 0, s, a, k, (const float *)zk, zstride,
-                           (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword);
+        hipLaunchKernelGGL(k_markov_select, dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0, s,
+                           a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,
+                           ctx->ws.errword);
         svh::prof_end(ctx, s, slot);
     }
     return hipGetLastError();

@@ -13,7 +13,9 @@
 // batch into a running (m, s): one max, one fma, one exp2 and one add per
 // element, plus one rescale per batch.  Unaligned row starts (odd V with bf16)
 // are handled by a scalar head and tail.  Rows a request does not verify
-// (beyond verify_len) are skipped without a read.
+// (beyond verify_len) are never read: with per-request lengths on the device,
+// a fixed grid of workgroups walks a compacted list of the verified items
+// instead of dispatching a workgroup per item of the full [B, gamma] shape.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -99,40 +101,18 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
     return svk::block_merge<NT>(MS{mref, s}, red);
 }
 
+// Statistics of chunk `chunk` of row i of request b (a p row when is_p,
+// else a q row) into part[].
 template <int PES, int QES, int NB>
-__global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
-    const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len,
-    int B, int gamma, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
+__device__ __forceinline__ void rowstats_chunk(const void *__restrict__ p, const void *__restrict__ q, int B,
+                                               int gamma, int b, int i, bool is_p, int chunk, int64_t V, int nch1,
+                                               int64_t chunk1, float c, float2 *__restrict__ part, MS *red)
 {
-    __shared__ MS red[svh::kRowstatsThreads / svk::kWave];
-
-    // workgroup -> (row of requests [b0, b0 + nb), chunk); p rows first, then q rows
-    const int64_t wg = blockIdx.x;
-    const int64_t slot = wg / nch1;
-    const int chunk = (int)(wg - slot * nch1);
-    const int64_t lrows_p = (int64_t)nb * (gamma + 1);
-    int bl, i;
-    bool is_p;
-    if (slot < lrows_p) {
-        bl = (int)(slot / (gamma + 1));
-        i = (int)(slot - (int64_t)bl * (gamma + 1));
-        is_p = true;
-    } else {
-        const int64_t r = slot - lrows_p;
-        bl = (int)(r / gamma);
-        i = (int)(r - (int64_t)bl * gamma);
-        is_p = false;
-    }
-    const int b = b0 + bl;
-    const int L = verify_len ? verify_len[b] : gamma;
-    if (L < 0 || L > gamma) return;             // request is flagged downstream
-    if (is_p ? (i > L) : (i >= L)) return;       // row not verified
-
     const int64_t e0 = (int64_t)chunk * chunk1;
     const int64_t e1 = e0 + chunk1 < V ? e0 + chunk1 : V;
+    const bool nontemporal = SV_ROWSTATS_NT_LOADS;
     MS tot;
     int64_t grow;   // row index in the statistics array: all p rows, then all q rows
-    const bool nontemporal = SV_ROWSTATS_NT_LOADS;
     if (is_p) {
         grow = (int64_t)b * (gamma + 1) + i;
         tot = chunk_stats<PES, NB>((const char *)p + grow * V * PES, e0, e1, c, nontemporal, red);
@@ -144,13 +124,127 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
     if (threadIdx.x == 0) part[grow * nch1 + chunk] = make_float2(tot.m, tot.s);
 }
 
+// One workgroup per (row, chunk) item of requests [b0, b0 + nb): p rows
+// first, then q rows.  Without verify lengths every row is verified and the
+// grid is exactly the work; with them, rows past a request's length return
+// at once.
+template <int PES, int QES, int NB>
+__global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
+    const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len, int B,
+    int gamma, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
+{
+    __shared__ MS red[svh::kRowstatsThreads / svk::kWave];
+    const int64_t slot = blockIdx.x / nch1;
+    const int chunk = (int)(blockIdx.x - slot * nch1);
+    const int64_t lrows_p = (int64_t)nb * (gamma + 1);
+    int bl, i;
+    const bool is_p = slot < lrows_p;
+    if (is_p) {
+        bl = (int)(slot / (gamma + 1));
+        i = (int)(slot - (int64_t)bl * (gamma + 1));
+    } else {
+        const int64_t r = slot - lrows_p;
+        bl = (int)(r / gamma);
+        i = (int)(r - (int64_t)bl * gamma);
+    }
+    if (verify_len) {
+        const int L = verify_len[b0 + bl];
+        if (L < 0 || L > gamma || (is_p ? i > L : i >= L)) return;
+    }
+    rowstats_chunk<PES, QES, NB>(p, q, B, gamma, b0 + bl, i, is_p, chunk, V, nch1, chunk1, c, part, red);
+}
+
+// Calls with per-request verify lengths L_b (on the device): only rows
+// 0..L_b of p and 0..L_b-1 of q are read.  Every workgroup first lays out in
+// LDS the lengths and the running count of verified items (rows x chunks)
+// per request, then takes every gridDim.x-th verified item, so the work is
+// balanced and an unverified row costs nothing.  A length outside [0, gamma]
+// verifies no row (the request is flagged downstream).
+template <int PES, int QES, int NB>
+__global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats_compact(
+    const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len, int B,
+    int gamma, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
+{
+    constexpr int NT = svh::kRowstatsThreads;
+    __shared__ MS red[NT / svk::kWave];
+    __shared__ int wsum[NT / svk::kWave];
+    extern __shared__ int dyn[];
+    int *Ls = dyn;              // [nb] verify lengths, -1 for an invalid one
+    int *pre = dyn + nb;        // [nb + 1] first item of each request; pre[nb] = total
+
+    // per-request item counts (rows x chunks), thread t owning a contiguous run
+    const int t = threadIdx.x;
+    const int per = (nb + NT - 1) / NT;
+    const int r0 = t * per, r1 = r0 + per < nb ? r0 + per : nb;
+    int loc = 0;
+    for (int bl = r0; bl < r1; ++bl) {
+        int L = verify_len[b0 + bl];
+        L = (L >= 0 && L <= gamma) ? L : -1;
+        Ls[bl] = L;
+        const int cnt = L >= 0 ? (2 * L + 1) * nch1 : 0;
+        pre[bl] = cnt;
+        loc += cnt;
+    }
+    // exclusive block scan of the per-thread totals
+    const int lane = t & (svk::kWave - 1), wid = t / svk::kWave;
+    int incl = loc;
+#pragma unroll
+    for (int o = 1; o < svk::kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o, svk::kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == svk::kWave - 1) wsum[wid] = incl;
+    __syncthreads();
+    int run = incl - loc;
+    for (int w = 0; w < wid; ++w) run += wsum[w];
+    for (int bl = r0; bl < r1; ++bl) {
+        const int cnt = pre[bl];
+        pre[bl] = run;
+        run += cnt;
+    }
+    if (t == NT - 1) {
+        int tot = 0;
+        for (int w = 0; w < NT / svk::kWave; ++w) tot += wsum[w];
+        pre[nb] = tot;
+    }
+    __syncthreads();
+
+    const int total = pre[nb];
+    int lo = 0;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        // request holding the item: the largest bl >= lo with pre[bl] <= item
+        int hi = nb - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= item) lo = mid;
+            else hi = mid - 1;
+        }
+        const int r = item - pre[lo];
+        const int row = r / nch1, chunk = r - row * nch1;
+        const int L = Ls[lo];
+        const bool is_p = row <= L;
+        rowstats_chunk<PES, QES, NB>(p, q, B, gamma, b0 + lo, is_p ? row : row - (L + 1), is_p, chunk, V, nch1,
+                                     chunk1, c, part, red);
+        __syncthreads();   // red[] is reused by the next item
+    }
+}
+
 template <int PES, int QES>
-void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t grid)
+void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t items)
 {
     constexpr int NB = svh::kRowstatsNB;
-    hipLaunchKernelGGL((k_rowstats<PES, QES, NB>), dim3((unsigned)grid),
-                       dim3(svh::kRowstatsThreads), 0, s, a.p, a.q, a.verify_len, a.B, a.gamma, a.b0, a.nb,
-                       a.V, ctx->nch1, ctx->chunk1, a.c, ctx->ws.part);
+    const bool compact = a.verify_len && a.nb <= svh::kRowstatsCompactMaxReq && items <= 0x7FFFFFFF;
+    if (compact) {
+        const int64_t cap = (int64_t)svh::kRowstatsCompactWGsPerCU * ctx->num_cu;
+        const int64_t grid = items < cap ? items : cap;
+        const size_t lds = (size_t)(2 * a.nb + 1) * sizeof(int);
+        hipLaunchKernelGGL((k_rowstats_compact<PES, QES, NB>), dim3((unsigned)grid), dim3(svh::kRowstatsThreads), lds,
+                           s, a.p, a.q, a.verify_len, a.B, a.gamma, a.b0, a.nb, a.V, ctx->nch1, ctx->chunk1, a.c,
+                           ctx->ws.part);
+    } else {
+        hipLaunchKernelGGL((k_rowstats<PES, QES, NB>), dim3((unsigned)items), dim3(svh::kRowstatsThreads), 0, s,
+                           a.p, a.q, a.verify_len, a.B, a.gamma, a.b0, a.nb, a.V, ctx->nch1, ctx->chunk1, a.c, ctx->ws.part);
+    }
 }
 
 }  // namespace

@@ -13,113 +13,167 @@
 // and the verify batch at B rows.  With SPS(n) = a / (1 + n / K), admitting a
 // candidate of survival s raises E * SPS iff s * (K + n) > E.
 //
-// One workgroup of 1024 threads: survival products in fp64 (sequential per
-// request), an LDS bitonic sort of (S, candidate id) for up to 8192
-// candidates, an fp64 block scan of the sorted survivals, and a parallel
-// search for the first candidate that fails the test.
+// Two kernels, handing over at the kernel boundary:
+//   k_sched_rank   grid (candidate blocks) x (comparator blocks) of 256: the
+//                  rank of candidate e in the order (S descending, id
+//                  ascending) is the number of candidates that come before
+//                  it; every workgroup counts one block of comparators for
+//                  one block of candidates and adds its count atomically.
+//                  Survival products are recomputed per block from the
+//                  confidences, in the same sequential order everywhere.
+//   k_sched_admit  one workgroup: scatter the candidates by rank into LDS
+//                  (the sorted order), clear the ranks for the next call,
+//                  fp64 block scan of the sorted survivals, find the first
+//                  candidate that fails the test, set each request's length.
 #include "sv_device.h"
 #include "sv_internal.h"
 
 namespace {
 
-constexpr int NT = svh::kSchedThreads;
+constexpr int RB = 256;                     // candidates (and comparators) per block
+constexpr int NT = svh::kSchedThreads;      // admit workgroup
 constexpr int NMAX = svh::kSchedMax;
+constexpr int EPT = NMAX / NT;              // sorted slots per thread in the admit kernel
+constexpr int CONF_MAX = RB + svh::kMaxGamma;
 
-__device__ __forceinline__ bool before(double ka, uint32_t ia, double kb, uint32_t ib)
+__device__ __forceinline__ float clamp01(float cf)
 {
-    return ka > kb || (ka == kb && ia < ib);
+    return cf > 0.0f ? (cf < 1.0f ? cf : 1.0f) : 0.0f;   // NaN -> 0
 }
 
-__global__ __launch_bounds__(NT) void k_schedule(const float *__restrict__ conf, int B, int gamma,
-                                                 double sps_k, int32_t *__restrict__ verify_len,
-                                                 double *__restrict__ expected)
+// Survival products of candidates [e0, e0 + RB) into S[]: S(b, i) is the
+// product of the clamped confidences of positions 0..i of request b, formed
+// left to right in fp64.  sconf is scratch of CONF_MAX floats.
+__device__ void block_survival(const float *__restrict__ conf, int n, int gamma, int e0, float *sconf,
+                               double *S)
+{
+    const int c0 = (e0 / gamma) * gamma;          // first position of the first request touched
+    const int e1 = e0 + RB < n ? e0 + RB : n;
+    for (int c = c0 + (int)threadIdx.x; c < e1; c += RB) sconf[c - c0] = clamp01(conf[c]);
+    __syncthreads();
+    const int e = e0 + (int)threadIdx.x;
+    if (e < n) {
+        const int b0 = (e / gamma) * gamma;
+        double s = 1.0;
+        for (int c = b0; c <= e; ++c) s = s * (double)sconf[c - c0];
+        S[threadIdx.x] = s;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(RB) void k_sched_rank(const float *__restrict__ conf, int n, int gamma,
+                                                   int32_t *__restrict__ rank, double *__restrict__ surv)
+{
+    __shared__ double Sx[RB], Sy[RB];
+    __shared__ float sconf[CONF_MAX];
+    const int bx = blockIdx.x, by = blockIdx.y;
+    block_survival(conf, n, gamma, by * RB, sconf, Sy);
+    const int e = bx * RB + (int)threadIdx.x;
+    double s;
+    if (bx == by) {
+        s = Sy[threadIdx.x];
+    } else {
+        block_survival(conf, n, gamma, bx * RB, sconf, Sx);
+        s = Sx[threadIdx.x];
+    }
+    if (e >= n) return;
+    const int cn = n - by * RB < RB ? n - by * RB : RB;
+    int cnt = 0;
+    if (by < bx) {          // every comparator id is smaller: ties come first
+        for (int c = 0; c < cn; ++c) cnt += Sy[c] >= s;
+    } else if (by > bx) {   // every comparator id is larger: ties come after
+        for (int c = 0; c < cn; ++c) cnt += Sy[c] > s;
+    } else {
+        const int me = threadIdx.x;
+        for (int c = 0; c < cn; ++c) cnt += (Sy[c] > s) || (Sy[c] == s && c < me);
+        surv[e] = s;
+    }
+    if (cnt) atomicAdd(&rank[e], cnt);
+}
+
+__global__ __launch_bounds__(NT) void k_sched_admit(int n, int B, int gamma, double sps_k,
+                                                    int32_t *__restrict__ rank, const double *__restrict__ surv,
+                                                    int32_t *__restrict__ verify_len, double *__restrict__ expected,
+                                                    uint32_t *__restrict__ errword)
 {
     __shared__ double key[NMAX];
     __shared__ uint16_t cid[NMAX];
     __shared__ int Lb[NMAX];
-    __shared__ double scan[NT];
+    __shared__ double scan[NT / 64];
     __shared__ int kstop;
 
-    const int n = B * gamma;
-    int npow2 = 1;
-    while (npow2 < n) npow2 <<= 1;
-
-    for (int b = threadIdx.x; b < B; b += NT) {
-        double S = 1.0;
-        for (int i = 0; i < gamma; ++i) {
-            float cf = conf[(int64_t)b * gamma + i];
-            cf = cf > 0.0f ? (cf < 1.0f ? cf : 1.0f) : 0.0f;   // clamp, NaN -> 0
-            S = S * (double)cf;
-            key[b * gamma + i] = S;
-            cid[b * gamma + i] = (uint16_t)(b * gamma + i);
+    const int t = threadIdx.x;
+    for (int b = t; b < B; b += NT) Lb[b] = 0;
+    if (t == 0) kstop = n;
+    // scatter by rank: slot r of the sorted order; the ranks are a
+    // permutation of [0, n), anything else is reported and dropped
+    for (int e = t; e < n; e += NT) {
+        const int r = rank[e];
+        rank[e] = 0;
+        if ((unsigned)r < (unsigned)n) {
+            key[r] = surv[e];
+            cid[r] = (uint16_t)e;
+        } else {
+            atomicOr(errword, SV_FLAG_BAD_ROW);
         }
-        Lb[b] = 0;
     }
-    for (int k = n + threadIdx.x; k < npow2; k += NT) {
-        key[k] = -1.0;
-        cid[k] = 0xFFFF;
-    }
-    if (threadIdx.x == 0) kstop = n;
     __syncthreads();
 
-    // bitonic sort into "before" order: S descending, then candidate id ascending
-    for (int size = 2; size <= npow2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = threadIdx.x; t < npow2 / 2; t += NT) {
-                const int lo = 2 * stride * (t / stride) + (t % stride);
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const double klo = key[lo], khi = key[hi];
-                const uint32_t ilo = cid[lo], ihi = cid[hi];
-                const bool sw = up ? before(khi, ihi, klo, ilo) : before(klo, ilo, khi, ihi);
-                if (sw) {
-                    key[lo] = khi;
-                    key[hi] = klo;
-                    cid[lo] = (uint16_t)ihi;
-                    cid[hi] = (uint16_t)ilo;
-                }
-            }
-            __syncthreads();
-        }
+    double k[EPT];
+    int id[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int e = EPT * t + j;
+        k[j] = e < n ? key[e] : 0.0;
+        id[j] = e < n ? (int)cid[e] : 0;
     }
-
-    // fp64 prefix sums of sorted survivals: thread t owns [t*per, (t+1)*per)
-    const int per = (n + NT - 1) / NT;
-    const int k0 = threadIdx.x * per;
-    const int k1 = k0 + per < n ? k0 + per : n;
     double loc = 0.0;
-    for (int k = k0; k < k1; ++k) loc += key[k];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+        if (EPT * t + j < n) loc += k[j];
     double total;
     const double excl = svk::block_exclusive_scan_d<NT>(loc, scan, &total);
     {
         double E = (double)B + excl;
-        for (int k = k0; k < k1; ++k) {
-            const double rows = (double)B + (double)k;
-            if (!(key[k] * (sps_k + rows) > E)) {
-                atomicMin(&kstop, k);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int kk = EPT * t + j;
+            if (kk >= n) break;
+            const double rows = (double)B + (double)kk;
+            if (!(k[j] * (sps_k + rows) > E)) {
+                atomicMin(&kstop, kk);
                 break;
             }
-            E += key[k];
+            E += k[j];
         }
     }
     __syncthreads();
     const int ks = kstop;
-    for (int k = threadIdx.x; k < ks; k += NT) {
-        const int id = cid[k];
-        atomicMax(&Lb[id / gamma], id % gamma + 1);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int kk = EPT * t + j;
+        if (kk < ks) atomicMax(&Lb[id[j] / gamma], id[j] % gamma + 1);
     }
     if (expected) {
-        // E of the admitted set: the prefix before the stopping candidate
+        // E of the admitted set: everything before the stopping candidate
         if (ks == n) {
-            if (threadIdx.x == 0) *expected = (double)B + total;
-        } else if (k0 <= ks && ks < k1) {
+            if (t == 0) *expected = (double)B + total;
+        } else if (EPT * t <= ks && ks < EPT * t + EPT) {
             double E = (double)B + excl;
-            for (int k = k0; k < ks; ++k) E += key[k];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if (EPT * t + j < ks) E += k[j];
             *expected = E;
         }
     }
     __syncthreads();
-    for (int b = threadIdx.x; b < B; b += NT) verify_len[b] = Lb[b];
+    for (int b = t; b < B; b += NT) verify_len[b] = Lb[b];
+}
+
+__global__ void k_sched_empty(int B, int32_t *__restrict__ verify_len, double *__restrict__ expected)
+{
+    for (int b = threadIdx.x; b < B; b += blockDim.x) verify_len[b] = 0;
+    if (expected && threadIdx.x == 0) *expected = (double)B;
 }
 
 }  // namespace
@@ -130,9 +184,18 @@ hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, flo
                            float sps_k, int32_t *verify_len, double *expected, hipStream_t s)
 {
     (void)sps_a;   // a positive scale of SPS does not move the maximum
+    const int n = B * gamma;
     const int slot = prof_begin(ctx, s, SV_KERNEL_SCHEDULE);
-    hipLaunchKernelGGL(k_schedule, dim3(1), dim3(NT), 0, s, conf, B, gamma, (double)sps_k,
-                       verify_len, expected);
+    if (n == 0) {
+        hipLaunchKernelGGL(k_sched_empty, dim3(1), dim3(256), 0, s, B, verify_len, expected);
+    } else {
+        const int nb = (n + RB - 1) / RB;
+        hipLaunchKernelGGL(k_sched_rank, dim3(nb, nb), dim3(RB), 0, s, conf, n, gamma, ctx->ws.sched_rank,
+                           ctx->ws.sched_surv);
+        hipLaunchKernelGGL(k_sched_admit, dim3(1), dim3(NT), 0, s, n, B, gamma, (double)sps_k,
+                           ctx->ws.sched_rank, (const double *)ctx->ws.sched_surv, verify_len, expected,
+                           ctx->ws.errword);
+    }
     const hipError_t e = hipGetLastError();
     prof_end(ctx, s, slot);
     return e;

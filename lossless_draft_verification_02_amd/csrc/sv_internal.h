@@ -28,6 +28,8 @@ namespace svh {
 constexpr int kRowstatsThreads = SV_ROWSTATS_THREADS;
 constexpr int kTargetChunk1 = SV_ROWSTATS_CHUNK;
 constexpr int kRowstatsNB = SV_ROWSTATS_NB;   // 16-byte loads in flight per thread
+constexpr int kRowstatsCompactWGsPerCU = 4;   // grid of the verify-length (compacted) variant, per CU
+constexpr int kRowstatsCompactMaxReq = 8192;  // requests per call it lays out in LDS (64 KB)
 // Correction / bonus weights and block pass 2: each wavefront sums one
 // segment of kSegR elements; a workgroup covers kSegPerWG segments.
 constexpr int kResidThreads = 256;
@@ -38,6 +40,7 @@ constexpr int kSchedThreads = 1024;
 constexpr int kSchedMax = 8192;
 // Markov head: output tiles of kMarkovTileN vocabulary columns.
 constexpr int kMarkovTileN = 128;
+constexpr int kMarkovMaxTiles = 256 * 8;   // the draw keeps 8 tile pairs per thread: V <= 262,144
 constexpr int kMaxGamma = 64;
 
 
@@ -51,6 +54,8 @@ struct Workspace {
     float *wrun;         // [max_batch * (max_gamma + 1)] block running ratios w_0..w_L
     uint32_t *errword;   // [1] OR of SV_FLAG_* bits
     int32_t *sched_len;  // [max_batch] scheduler output when the caller gives none
+    int32_t *sched_rank; // [kSchedMax] candidate ranks, zero between calls
+    double *sched_surv;  // [kSchedMax] candidate survival products
     float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials
     int32_t *mk_prev;    // [max_batch] Markov: token sampled at the previous position
     float *mk_q;         // [max_batch * V] Markov logits of the current position when
@@ -76,6 +81,7 @@ struct sv_ctx {
     int max_gamma;
     int64_t vocab;
     int max_rank;
+    int num_cu;          // compute units of the device
     int nch1;            // row-statistics chunks per row
     int64_t chunk1;      // elements per row-statistics chunk
     int nseg;            // residual segments (kSegR elements) per row
@@ -135,7 +141,7 @@ hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, flo
 struct MarkovArgs {
     const uint16_t *base;  // [B, gamma, V] bf16
     const uint16_t *U;     // [V, R]
-    const uint16_t *W;     // [R, V]
+    const uint16_t *W;     // [V, R]: the transition matrix stored vocabulary-major
     int R;
     const int32_t *x0;
     int B, gamma;

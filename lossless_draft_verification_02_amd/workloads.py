@@ -70,9 +70,14 @@ class MarkovInputs:
     T: float
     base: torch.Tensor         # [B, gamma, V] bf16
     U: torch.Tensor            # [V, R] bf16
-    W: torch.Tensor            # [R, V] bf16
+    Wt: torch.Tensor           # [V, R] bf16: the transition matrix W [R, V], stored vocabulary-major
     x0: torch.Tensor           # [B] int32
     p: torch.Tensor            # [B, gamma+1, V] bf16 target logits
+
+    @property
+    def W(self) -> torch.Tensor:
+        """W [R, V] as a view of Wt."""
+        return self.Wt.t()
 
 
 def _gen(device, seed: int) -> torch.Generator:
@@ -168,9 +173,9 @@ def make_markov_inputs(device="cpu", B: Optional[int] = None, gamma: Optional[in
         p[b0:b1, :gamma] = (bf + torch.randn(nb, gamma, V, generator=g, device=device)).to(torch.bfloat16)
         p[b0:b1, gamma] = (torch.randn(nb, V, generator=g, device=device) * 3.0).to(torch.bfloat16)
     U = (torch.randn(V, R, generator=g, device=device) * uw_std).to(torch.bfloat16)
-    W = (torch.randn(R, V, generator=g, device=device) * uw_std).to(torch.bfloat16)
+    Wt = (torch.randn(V, R, generator=g, device=device) * uw_std).to(torch.bfloat16)
     x0 = torch.randint(0, V, (B,), generator=g, device=device).to(torch.int32)
-    return MarkovInputs(B, gamma, V, R, c["T"], base, U, W, x0, p)
+    return MarkovInputs(B, gamma, V, R, c["T"], base, U, Wt, x0, p)
 
 
 def bytes_single_read(inp: VerifyInputs) -> int:

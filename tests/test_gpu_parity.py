@@ -255,7 +255,7 @@ def test_host_argument_errors():
             L.spec_verify_run(ctx, vi.p, vi.q, vi.draft, acc4, out4, temperature=0.0)
         with pytest.raises(L.SpecVerifyError):
             L.markov_draft_run(ctx, vi.q, torch.zeros(1000, 256, dtype=torch.bfloat16, device="cuda"),
-                               torch.zeros(256, 1000, dtype=torch.bfloat16, device="cuda"),
+                               torch.zeros(1000, 256, dtype=torch.bfloat16, device="cuda"),
                                torch.zeros(4, dtype=torch.int32, device="cuda"),
                                torch.empty(4, 3, dtype=torch.int32, device="cuda"))
 
@@ -351,7 +351,7 @@ def gpu_markov(ctx, mi, uniforms=None, want_q=True, seed=WL.DRAFT_SEED):
     d = torch.full((B, gamma), -7, dtype=torch.int32, device="cuda")
     ql = torch.empty(B, gamma, V, device="cuda") if want_q else None
     lse = torch.empty(B, gamma, device="cuda")
-    L.markov_draft_run(ctx, mi.base, mi.U, mi.W, mi.x0, d, q_logits=ql, lse_q=lse, temperature=mi.T,
+    L.markov_draft_run(ctx, mi.base, mi.U, mi.Wt, mi.x0, d, q_logits=ql, lse_q=lse, temperature=mi.T,
                        seed=seed, uniforms=uniforms)
     torch.cuda.synchronize()
     return d, ql, lse
