@@ -24,12 +24,12 @@ namespace {
 using svk::MS;
 using svk::u32x4;
 
-// (m, s) of elements [e0, e1) of one row; result valid in thread 0.
-template <int ESIZE, int NB>
-__device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64_t e0, int64_t e1,
-                                          float c, bool nontemporal, MS *red)
+// This thread's (m, s) over its share of elements [e0, e1) of one row, the
+// share of thread `tid` of NT cooperating threads (a workgroup or a wavefront).
+template <int ESIZE, int NB, int NT>
+__device__ __forceinline__ MS thread_stats(const char *__restrict__ rowptr, int64_t e0, int64_t e1, float c,
+                                           bool nontemporal, int tid)
 {
-    constexpr int NT = svh::kRowstatsThreads;
     constexpr int EPV = 16 / ESIZE;   // elements per 16-byte vector
 
     // 16-byte aligned body [a0, a1) inside [e0, e1)
@@ -45,7 +45,7 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
     float mraw = svk::neg_inf();   // running max, raw units
     float s = 0.0f;
 
-    for (int64_t v0 = threadIdx.x; v0 < nvec; v0 += (int64_t)NT * NB) {
+    for (int64_t v0 = tid; v0 < nvec; v0 += (int64_t)NT * NB) {
         u32x4 raw[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -82,9 +82,8 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
     // scalar head [e0, a0) and tail [a1, e1): fewer than 2 * EPV elements
     const int64_t nhead = a0 - e0;
     const int64_t nscalar = nhead + (e1 - a1);
-    if ((int64_t)threadIdx.x < nscalar) {
-        const int64_t e = (int64_t)threadIdx.x < nhead ? e0 + threadIdx.x
-                                                        : a1 + ((int64_t)threadIdx.x - nhead);
+    if ((int64_t)tid < nscalar) {
+        const int64_t e = (int64_t)tid < nhead ? e0 + tid : a1 + ((int64_t)tid - nhead);
         const float x = svk::load_logit<ESIZE>(rowptr, e);
         MS one;
         if (x == svk::neg_inf()) {
@@ -98,12 +97,22 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
         mref = a.m;
         s = a.s;
     }
-    return svk::block_merge<NT>(MS{mref, s}, red);
+    return MS{mref, s};
+}
+
+// (m, s) of elements [e0, e1) of one row by the whole workgroup; valid in thread 0.
+template <int ESIZE, int NB>
+__device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64_t e0, int64_t e1, float c,
+                                          bool nontemporal, MS *red)
+{
+    constexpr int NT = svh::kRowstatsThreads;
+    return svk::block_merge<NT>(thread_stats<ESIZE, NB, NT>(rowptr, e0, e1, c, nontemporal, threadIdx.x), red);
 }
 
 // Statistics of chunk `chunk` of row i of request b (a p row when is_p,
-// else a q row) into part[].
-template <int PES, int QES, int NB>
+// else a q row) into part[], by the whole workgroup (WAVE false) or by one
+// wavefront on its own (WAVE true: shuffles only, no LDS, no barrier).
+template <int PES, int QES, int NB, bool WAVE>
 __device__ __forceinline__ void rowstats_chunk(const void *__restrict__ p, const void *__restrict__ q, int B,
                                                int gamma, int b, int i, bool is_p, int chunk, int64_t V, int nch1,
                                                int64_t chunk1, float c, float2 *__restrict__ part, MS *red)
@@ -111,17 +120,37 @@ __device__ __forceinline__ void rowstats_chunk(const void *__restrict__ p, const
     const int64_t e0 = (int64_t)chunk * chunk1;
     const int64_t e1 = e0 + chunk1 < V ? e0 + chunk1 : V;
     const bool nontemporal = SV_ROWSTATS_NT_LOADS;
-    MS tot;
     int64_t grow;   // row index in the statistics array: all p rows, then all q rows
+    const char *row;
+    int esize;
     if (is_p) {
         grow = (int64_t)b * (gamma + 1) + i;
-        tot = chunk_stats<PES, NB>((const char *)p + grow * V * PES, e0, e1, c, nontemporal, red);
+        row = (const char *)p + grow * V * PES;
+        esize = PES;
     } else {
         const int64_t qr = (int64_t)b * gamma + i;
         grow = (int64_t)B * (gamma + 1) + qr;
-        tot = chunk_stats<QES, NB>((const char *)q + qr * V * QES, e0, e1, c, nontemporal, red);
+        row = (const char *)q + qr * V * QES;
+        esize = QES;
     }
-    if (threadIdx.x == 0) part[grow * nch1 + chunk] = make_float2(tot.m, tot.s);
+    MS tot;
+    if constexpr (WAVE) {
+        const int lane = threadIdx.x & (svk::kWave - 1);
+        if constexpr (PES == QES)
+            tot = thread_stats<PES, NB, svk::kWave>(row, e0, e1, c, nontemporal, lane);
+        else
+            tot = esize == PES ? thread_stats<PES, NB, svk::kWave>(row, e0, e1, c, nontemporal, lane)
+                               : thread_stats<QES, NB, svk::kWave>(row, e0, e1, c, nontemporal, lane);
+        tot = svk::wave_merge(tot);
+        if (lane == 0) part[grow * nch1 + chunk] = make_float2(tot.m, tot.s);
+    } else {
+        if constexpr (PES == QES)
+            tot = chunk_stats<PES, NB>(row, e0, e1, c, nontemporal, red);
+        else
+            tot = esize == PES ? chunk_stats<PES, NB>(row, e0, e1, c, nontemporal, red)
+                               : chunk_stats<QES, NB>(row, e0, e1, c, nontemporal, red);
+        if (threadIdx.x == 0) part[grow * nch1 + chunk] = make_float2(tot.m, tot.s);
+    }
 }
 
 // One workgroup per (row, chunk) item of requests [b0, b0 + nb): p rows
@@ -151,7 +180,7 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
         const int L = verify_len[b0 + bl];
         if (L < 0 || L > gamma || (is_p ? i > L : i >= L)) return;
     }
-    rowstats_chunk<PES, QES, NB>(p, q, B, gamma, b0 + bl, i, is_p, chunk, V, nch1, chunk1, c, part, red);
+    rowstats_chunk<PES, QES, NB, false>(p, q, B, gamma, b0 + bl, i, is_p, chunk, V, nch1, chunk1, c, part, red);
 }
 
 // Calls with per-request verify lengths L_b (on the device): only rows
@@ -159,14 +188,15 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
 // LDS the lengths and the running count of verified items (rows x chunks)
 // per request, then takes every gridDim.x-th verified item, so the work is
 // balanced and an unverified row costs nothing.  A length outside [0, gamma]
-// verifies no row (the request is flagged downstream).
+// verifies no row (the request is flagged downstream).  After the layout
+// each wavefront takes whole (row, chunk) items on its own, so no barrier
+// stalls the memory pipeline between items.
 template <int PES, int QES, int NB>
 __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats_compact(
     const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len, int B,
     int gamma, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
 {
     constexpr int NT = svh::kRowstatsThreads;
-    __shared__ MS red[NT / svk::kWave];
     __shared__ int wsum[NT / svk::kWave];
     extern __shared__ int dyn[];
     int *Ls = dyn;              // [nb] verify lengths, -1 for an invalid one
@@ -209,9 +239,11 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats_compact(
     }
     __syncthreads();
 
+    // from here on every wavefront works alone: items are taken per wavefront
     const int total = pre[nb];
+    const int nw = (int)gridDim.x * (NT / svk::kWave);
     int lo = 0;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    for (int item = (int)blockIdx.x * (NT / svk::kWave) + wid; item < total; item += nw) {
         // request holding the item: the largest bl >= lo with pre[bl] <= item
         int hi = nb - 1;
         while (lo < hi) {
@@ -223,9 +255,8 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats_compact(
         const int row = r / nch1, chunk = r - row * nch1;
         const int L = Ls[lo];
         const bool is_p = row <= L;
-        rowstats_chunk<PES, QES, NB>(p, q, B, gamma, b0 + lo, is_p ? row : row - (L + 1), is_p, chunk, V, nch1,
-                                     chunk1, c, part, red);
-        __syncthreads();   // red[] is reused by the next item
+        rowstats_chunk<PES, QES, NB, true>(p, q, B, gamma, b0 + lo, is_p ? row : row - (L + 1), is_p, chunk, V,
+                                           nch1, chunk1, c, part, nullptr);
     }
 }
 

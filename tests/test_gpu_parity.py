@@ -211,6 +211,10 @@ def test_fp32_and_mixed_dtypes():
             _say(f"case: dtypes p={pd} q={qd}")
             v2 = WL.VerifyInputs(3, B, gamma, V, 1.0, vi.p.to(pd), vi.q.to(qd), vi.draft)
             check_verify(ctx, v2, label=f"{pd}/{qd}")
+            # per-request lengths take the compacted row-statistics path
+            vl = np.array([(3 * b + 1) % (gamma + 1) for b in range(B)], np.int32)
+            check_verify(ctx, v2, verify_len=vl, label=f"{pd}/{qd} verify_len")
+            check_verify(ctx, v2, verify_len=vl, block=True, label=f"{pd}/{qd} verify_len block")
 
 
 def test_data_errors_and_device_status():
