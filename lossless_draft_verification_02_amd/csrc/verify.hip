@@ -59,19 +59,55 @@ struct ReqG {
 static_assert(sizeof(ReqG) == svh::kReqStateBytes, "request state layout");
 
 // log2 sum exp2 of a row from its chunk partials (fp64 result); flags a bad row.
+// M = max m_k, S = sum s_k exp2(m_k - M), the partials loaded kMergeBatch at a
+// time (one memory round trip per batch and pass; one batch when the whole
+// row fits, the common case).
+constexpr int kMergeBatch = 8;
 __device__ double merge_row(const float2 *__restrict__ part, int64_t row, int nch1, bool &bad)
 {
     const float2 *pr = part + row * nch1;
     float M = svk::neg_inf();
-    for (int k = 0; k < nch1; ++k) M = fmaxf(M, pr[k].x);
     float S = 0.0f;
-    if (M == svk::neg_inf()) {
-        for (int k = 0; k < nch1; ++k) S += pr[k].y;   // 0, or NaN for a NaN element
-    } else {
-        for (int k = 0; k < nch1; ++k) S += pr[k].y * exp2f(pr[k].x - M);
+    float2 v[kMergeBatch];
+    for (int k0 = 0; k0 < nch1; k0 += kMergeBatch) {
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) v[j] = k0 + j < nch1 ? pr[k0 + j] : make_float2(svk::neg_inf(), 0.0f);
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) M = fmaxf(M, v[j].x);
+    }
+    for (int k0 = 0; k0 < nch1; k0 += kMergeBatch) {
+        if (k0 > 0 || nch1 > kMergeBatch) {   // the single-batch case still holds its values
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j)
+                v[j] = k0 + j < nch1 ? pr[k0 + j] : make_float2(svk::neg_inf(), 0.0f);
+        }
+        if (M == svk::neg_inf()) {
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) S += v[j].y;   // 0, or NaN for a NaN element
+        } else {
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j)
+                if (k0 + j < nch1) S += v[j].y * exp2f(v[j].x - M);
+        }
     }
     if (!(S > 0.0f) || M == svk::pos_inf() || S == svk::pos_inf()) bad = true;
     return (double)M + log2((double)S);
+}
+
+// Sum, in index order and fp64, of n floats; loads issued kSumBatch at a time.
+constexpr int kSumBatch = 16;
+__device__ double sum_in_order(const float *__restrict__ v, int n)
+{
+    double acc = 0.0;
+    for (int k0 = 0; k0 < n; k0 += kSumBatch) {
+        float x[kSumBatch];
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j) x[j] = k0 + j < n ? v[k0 + j] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j)
+            if (k0 + j < n) acc += (double)x[j];
+    }
+    return acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -133,10 +169,7 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
     double mi = 0.0;
     if (stage == STAGE_BLOCK_FINAL && lane + 1 <= gamma) {
         wi = wrun[(int64_t)b * G1 + lane + 1];
-        if (lane + 1 < gamma) {
-            const float *bmi = bm + ((int64_t)b * gamma + lane + 1) * nseg;
-            for (int k = 0; k < nseg; ++k) mi += (double)bmi[k];
-        }
+        if (lane + 1 < gamma) mi = sum_in_order(bm + ((int64_t)b * gamma + lane + 1) * nseg, nseg);
     }
 
     // ---- checks: verify length, then tokens (reported alone), then rows
@@ -347,6 +380,100 @@ __device__ float segment_weight_sum(const char *prow, const char *qrow, int64_t 
     return svk::wave_sum(acc);
 }
 
+// Raw 16-byte vectors of the lane's share of one full, aligned segment of
+// the correction / bonus rows: U units of 8 tokens per row.
+template <int PES, int QES>
+struct SegRaw {
+    static constexpr int U = SEG / 8 / svk::kWave;
+    u32x4 p[U][PES / 2];
+    u32x4 q[U][QES / 2];
+};
+
+template <int PES, int QES>
+__device__ __forceinline__ void seg_load(SegRaw<PES, QES> &r, const char *prow, const char *qrow, int64_t s0,
+                                         int mode, int lane)
+{
+    constexpr int U = SegRaw<PES, QES>::U;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int64_t e = s0 + (int64_t)(lane + svk::kWave * k) * 8;
+        const u32x4 *vp = (const u32x4 *)(prow + e * PES);
+#pragma unroll
+        for (int h = 0; h < PES / 2; ++h) r.p[k][h] = __builtin_nontemporal_load(vp + h);
+        if (!mode) {
+            const u32x4 *vq = (const u32x4 *)(qrow + e * QES);
+#pragma unroll
+            for (int h = 0; h < QES / 2; ++h) r.q[k][h] = __builtin_nontemporal_load(vq + h);
+        }
+    }
+}
+
+template <int PES, int QES>
+__device__ __forceinline__ float seg_reduce(const SegRaw<PES, QES> &r, int mode, float wmul, float lp2,
+                                            float lq2, float c)
+{
+    constexpr int U = SegRaw<PES, QES>::U;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        float xp[8], xq[8];
+#pragma unroll
+        for (int h = 0; h < PES / 2; ++h) svk::widen<PES>(r.p[k][h], xp + h * (16 / PES));
+        if (!mode) {
+#pragma unroll
+            for (int h = 0; h < QES / 2; ++h) svk::widen<QES>(r.q[k][h], xq + h * (16 / QES));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += weight(xp[j], xq[j], 0, wmul, lp2, lq2, c);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += weight(xp[j], 0.0f, 1, wmul, lp2, lq2, c);
+        }
+    }
+    return acc;
+}
+
+// Segment sums of the correction / bonus weights of rows prow / qrow into
+// sums[0, nseg), by NW wavefronts of the workgroup (wavefront wid takes
+// segments wid, wid + NW, ...).  Full segments of 16-byte aligned rows are
+// software-pipelined (unless both rows are fp32, where the second buffer would
+// spill): the next segment's vectors are requested before the current one is
+// reduced, so two segments per wavefront are in flight.
+template <int PES, int QES, int NW>
+__device__ void segment_sums(const svh::VerifyArgs &a, const char *prow, const char *qrow, int mode, float wmul,
+                             float lp2, float lq2, int nseg, float *sums)
+{
+    const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
+    const bool aligned = (((uintptr_t)prow) & 15) == 0 && (mode || (((uintptr_t)qrow) & 15) == 0);
+    const int nfull = aligned ? (int)(a.V / SEG) : 0;
+    int k = wid;
+    if constexpr (PES == 4 && QES == 4) {
+        // fp32 rows: a second register buffer does not fit; one segment at a time
+        for (; k < nfull; k += NW) {
+            SegRaw<PES, QES> cur;
+            seg_load<PES, QES>(cur, prow, qrow, (int64_t)k * SEG, mode, lane);
+            const float tot = svk::wave_sum(seg_reduce<PES, QES>(cur, mode, wmul, lp2, lq2, a.c));
+            if (lane == 0) sums[k] = tot;
+        }
+    } else if (k < nfull) {
+        SegRaw<PES, QES> cur, nxt;
+        seg_load<PES, QES>(cur, prow, qrow, (int64_t)k * SEG, mode, lane);
+        for (; k < nfull; k += NW) {
+            const int kn = k + NW;
+            if (kn < nfull) seg_load<PES, QES>(nxt, prow, qrow, (int64_t)kn * SEG, mode, lane);
+            const float tot = svk::wave_sum(seg_reduce<PES, QES>(cur, mode, wmul, lp2, lq2, a.c));
+            if (lane == 0) sums[k] = tot;
+            if (kn < nfull) cur = nxt;
+        }
+    }
+    // the partial last segment, or every segment of unaligned rows
+    for (; k < nseg; k += NW) {
+        const int64_t s0 = (int64_t)k * SEG;
+        const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+        const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, mode, wmul, lp2, lq2, a.c);
+        if (lane == 0) sums[k] = tot;
+    }
+}
+
 constexpr int SPW = svh::kSegPerWG;   // segments (wavefronts) per workgroup
 
 template <int PES, int QES>
@@ -382,11 +509,11 @@ __global__ __launch_bounds__(NT) void k_block_pass2(svh::VerifyArgs a, const Req
 // drawn token y, then -1 (all -1 and accepted_len -1 when y < 0).
 __device__ __forceinline__ void write_outputs(const svh::VerifyArgs &a, int b, int tau, int y,
                                               const int32_t *x, uint32_t flags, double Z,
-                                              uint32_t *__restrict__ errword)
+                                              uint32_t *__restrict__ errword, int nthreads)
 {
     const int G1 = a.gamma + 1;
     const int64_t ob = (int64_t)b * G1;
-    for (int j = threadIdx.x; j < G1; j += blockDim.x)
+    for (int j = threadIdx.x; j < G1; j += nthreads)
         a.out_tokens[ob + j] = y < 0 ? -1 : (j < tau ? x[j] : (j == tau ? y : -1));
     if (threadIdx.x == 0) {
         a.accepted_len[b] = y < 0 ? -1 : tau;
@@ -569,7 +696,118 @@ __global__ __launch_bounds__(NT) void k_select(svh::VerifyArgs a, const ReqG *__
         y = select_token<PES, QES>(a, 1, 1.0f, r.lp2, 0.0f, own, nseg, prow, nullptr, r.u2, sh, Z);
     }
     if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
-    write_outputs(a, b, r.tau, y, xs, flags, Z, errword);
+    write_outputs(a, b, r.tau, y, xs, flags, Z, errword, blockDim.x);
+}
+
+// Inverse-CDF selection by one wavefront (no workgroup barrier): the segment
+// sums give an fp64 wavefront prefix that picks the segment holding u * Z;
+// lane l then owns tokens [32 l, 32 l + 32) of that segment and a second
+// wavefront prefix finds the token.  Same decisions as select_token: the
+// smallest token whose fp32 cumulative weight exceeds fp32(u * fp32(Z)), else
+// the last positive-weight token.  Returns -1 when the weights sum to 0.
+__device__ __forceinline__ int wave_min_i(int v)
+{
+#pragma unroll
+    for (int o = svk::kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, svk::kWave));
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v)
+{
+#pragma unroll
+    for (int o = svk::kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, svk::kWave));
+    return v;
+}
+
+template <int PES, int QES>
+__device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul, float lp2, float lq2,
+                                 const float *sums, int nseg, const char *prow, const char *qrow, float u,
+                                 double &Z_out)
+{
+    constexpr int TPL = SEG / svk::kWave;   // tokens per lane inside the segment (32)
+    static_assert(TPL % 8 == 0, "whole 8-token units per lane");
+    const int lane = threadIdx.x & (svk::kWave - 1);
+    const int per = (nseg + svk::kWave - 1) / svk::kWave;
+    const int k0 = lane * per;
+    const int k1 = k0 + per < nseg ? k0 + per : nseg;
+    double loc = 0.0;
+    for (int k = k0; k < k1; ++k) loc += (double)sums[k];
+    const double incl = svk::wave_inclusive_scan_d(loc);
+    const double excl = incl - loc;
+    const double Z = __shfl(incl, svk::kWave - 1, svk::kWave);
+    Z_out = Z;
+    if (!(Z > 0.0)) return -1;
+    const float tf = __fmul_rn(u, (float)Z);
+    int first = 0x7FFFFFFF, lastpos = -1;
+    {
+        double run = excl;
+        for (int k = k0; k < k1; ++k) {
+            const float ck = sums[k];
+            run += (double)ck;
+            if (ck > 0.0f) {
+                lastpos = k;
+                if ((float)run > tf) {
+                    first = k;
+                    break;
+                }
+            }
+        }
+    }
+    const int cstar = wave_min_i(first);
+    const int clast = wave_max_i(lastpos);
+    const bool fallback = cstar == 0x7FFFFFFF;
+    const int cst = fallback ? clast : cstar;   // >= 0: Z > 0 needs a positive segment
+    double before = excl;
+    for (int k = k0; k < k1 && k < cst; ++k) before += (double)sums[k];
+    const double cbase = __shfl(before, cst / per, svk::kWave);
+
+    // inside the segment
+    const int64_t s0 = (int64_t)cst * SEG;
+    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+    const int64_t t0 = s0 + (int64_t)lane * TPL;
+    const bool aligned = (((uintptr_t)(prow + s0 * PES)) & 15) == 0 &&
+                         (mode || (((uintptr_t)(qrow + s0 * QES)) & 15) == 0);
+    float w[TPL];
+    if (aligned && t0 + TPL <= s1) {
+#pragma unroll
+        for (int g = 0; g < TPL / 8; ++g) {
+            float xp[8], xq[8];
+            load8<PES>(prow, t0 + 8 * g, xp);
+            if (!mode) load8<QES>(qrow, t0 + 8 * g, xq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[8 * g + j] = weight(xp[j], mode ? 0.0f : xq[j], mode, wmul, lp2, lq2, a.c);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const int64_t e = t0 + j;
+            float wj = 0.0f;
+            if (e < s1) {
+                const float xp = svk::load_logit<PES>(prow, e);
+                const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
+                wj = weight(xp, xq, mode, wmul, lp2, lq2, a.c);
+            }
+            w[j] = wj;
+        }
+    }
+    double lsum = 0.0;
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) lsum += (double)w[j];
+    const double tincl = svk::wave_inclusive_scan_d(lsum);
+    int yl = -1, yb = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < TPL; ++j)
+        if (w[j] > 0.0f) yl = (int)(t0 + j);
+    if (!fallback) {
+        double C = cbase + (tincl - lsum);
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            C += (double)w[j];
+            if (yb == 0x7FFFFFFF && w[j] > 0.0f && (float)C > tf) yb = (int)(t0 + j);
+        }
+    }
+    const int ybest = wave_min_i(yb);
+    const int ylast = wave_max_i(yl);
+    return ybest != 0x7FFFFFFF ? ybest : ylast;
 }
 
 // ---------------------------------------------------------------------------
@@ -609,18 +847,19 @@ __global__ __launch_bounds__(NTT) void k_tail(svh::VerifyArgs a, const float2 *_
     if (sums_from_pass2(a, r)) {
         sums = bm + ((int64_t)b * gamma + r.tau) * nseg;
     } else {
-        for (int k = wid; k < nseg; k += NTT / svk::kWave) {
-            const int64_t s0 = (int64_t)k * SEG;
-            const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
-            const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
-            if (lane == 0) segsum[k] = tot;
-        }
+        segment_sums<PES, QES, NTT / svk::kWave>(a, prow, qrow, r.mode, r.wmul, r.lp2, r.lq2, nseg, segsum);
         __syncthreads();
     }
+    // the draw: wavefront 0 alone
     uint32_t flags = 0;
     double Z = 0.0;
-    int y = select_token<PES, QES, NTT>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, sh, Z);
-    if (y < 0 && r.mode == 0) {
+    int y = 0;
+    if (wid == 0) {
+        y = select_token_wave<PES, QES>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, Z);
+        if (lane == 0) sh.ybest = y;
+    }
+    __syncthreads();
+    if (sh.ybest < 0 && r.mode == 0) {
         // residual mass rounded to zero (in exact arithmetic a rejection
         // implies p != q): draw from the p row instead
         flags |= SV_FLAG_RESID_ZERO;
@@ -631,10 +870,11 @@ __global__ __launch_bounds__(NTT) void k_tail(svh::VerifyArgs a, const float2 *_
             if (lane == 0) segsum[k] = tot;
         }
         __syncthreads();
-        y = select_token<PES, QES, NTT>(a, 1, 1.0f, r.lp2, 0.0f, segsum, nseg, prow, nullptr, r.u2, sh, Z);
+        if (wid == 0) y = select_token_wave<PES, QES>(a, 1, 1.0f, r.lp2, 0.0f, segsum, nseg, prow, nullptr, r.u2, Z);
     }
+    if (wid != 0) return;
     if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
-    write_outputs(a, b, r.tau, y, as.x, flags, Z, errword);
+    write_outputs(a, b, r.tau, y, as.x, flags, Z, errword, svk::kWave);
 }
 
 // ---------------------------------------------------------------------------
