@@ -19,10 +19,10 @@
 //                    of one request, so the epilogue adds the base logits and
 //                    stores 16-byte runs of z without a detour through LDS,
 //                    and reduces per (request, 128-token tile) the pair
-//                    (max z*c, sum exp2(z*c - max)).  Workgroups loop over
-//                    vocabulary tiles; the next tile's Wt fragments are
-//                    requested as soon as the current ones are consumed, so
-//                    they arrive while the epilogue runs.
+//                    (max z*c, sum exp2(z*c - max)).  Workgroups of eight
+//                    wavefronts (16 vocabulary rows each) loop over 128-token
+//                    tiles; the next tile's Wt fragments and base logits are
+//                    requested as soon as the current ones are consumed.
 //   k_markov_select  one wavefront per request, no barriers: merge the tile
 //                    pairs into the row's log-sum-exp, pick the tile holding
 //                    u * Z by an fp64 wavefront scan, scan inside it for the
@@ -35,13 +35,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;                 // 4 wavefronts, 32 vocabulary rows each per tile
+constexpr int NT = 512;                 // 8 wavefronts, 16 vocabulary rows each per tile
+constexpr int NWAVE = NT / 64;
 constexpr int TN = svh::kMarkovTileN;   // 128 vocabulary entries per tile
 constexpr int MC = 128;                 // requests per workgroup (8 blocks of 16)
 constexpr int MBLK = MC / 16;
 constexpr int kGemmWGs = 512;           // two resident workgroups per compute unit
 
-static_assert(TN == 4 * 32, "four wavefronts of 32 vocabulary rows per tile");
+static_assert(TN == NWAVE * 16, "eight wavefronts of 16 vocabulary rows per tile");
 
 __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m)
 {
@@ -49,23 +50,43 @@ __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m
     return (x < 0 || (int64_t)x >= a.V) ? 0 : x;   // invalid ids are flagged by the select
 }
 
-// The wavefront's A fragments of one tile: vocabulary rows n0 + 32 w + 16 vb + li,
+// The wavefront's A fragments of one tile: vocabulary row n = nrow0 + li,
 // k-chunk 8 lg of each 32-wide k-step.  Rows past V read as zero.
 template <int R>
 __device__ __forceinline__ void load_wt(const svh::MarkovArgs &a, int64_t nrow0, int li, int lg,
-                                        bf16x8 (&wa)[2][R / 32])
+                                        bf16x8 (&wa)[R / 32])
+{
+    const int64_t n = nrow0 + li;
+    const uint16_t *row = a.W + (n < a.V ? n : 0) * R + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < R / 32; ++s) wa[s] = n < a.V ? *(const bf16x8 *)(row + 32 * s) : bf16x8{};
+}
+
+// Base logits of the lane's outputs: requests m0 + 16 mb + li, vocabulary
+// entries n .. n + 3 (bf16, packed in a uint2); -inf past V or past the batch.
+__device__ __forceinline__ void load_base(const svh::MarkovArgs &a, int k, int m0, int mrows, int64_t n, int li,
+                                          int vec, uint2 (&bv)[MBLK])
 {
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb) {
-        const int64_t n = nrow0 + 16 * vb + li;
-        const uint16_t *row = a.W + (n < a.V ? n : 0) * R + 8 * lg;
+    for (int mb = 0; mb < MBLK; ++mb) {
+        const int ml = 16 * mb + li;
+        bv[mb] = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+        if (ml < mrows) {
+            const uint16_t *brow = a.base + ((int64_t)(m0 + ml) * a.gamma + (k - 1)) * a.V;
+            if (vec) {
+                if (n < a.V) bv[mb] = *(const uint2 *)(brow + n);
+            } else {
+                uint16_t e[4];
 #pragma unroll
-        for (int s = 0; s < R / 32; ++s) wa[vb][s] = n < a.V ? *(const bf16x8 *)(row + 32 * s) : bf16x8{};
+                for (int r = 0; r < 4; ++r) e[r] = n + r < a.V ? brow[n + r] : (uint16_t)0xFF80u;
+                bv[mb] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+            }
+        }
     }
 }
 
 template <int R>
-__global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
+__global__ __launch_bounds__(NT, 4) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
                                                        int64_t zstride, float2 *__restrict__ tile_part,
                                                        int ntile, int vec)
 {
@@ -73,18 +94,21 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
     constexpr int US = R + 8;              // LDS row stride (bf16): conflict-free 16-byte fragment reads
     constexpr int UCH = R / 8;             // 16-byte chunks per U row
     constexpr int UPT = MC * UCH / NT;     // chunks staged per thread
+    static_assert(UPT >= 1 && MC * UCH % NT == 0, "U staging split");
     __shared__ __attribute__((aligned(16))) uint16_t Us[MC * US];
-    __shared__ float2 red[4][MC];
+    __shared__ float2 red[NWAVE][MC];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int m0 = blockIdx.y * MC;
     const int mrows = a.B - m0 < MC ? a.B - m0 : MC;
 
-    // first tile's Wt fragments, then the gathered U rows -> LDS
+    // first tile's Wt fragments and base logits, then the gathered U rows -> LDS
     int tile = blockIdx.x;
-    bf16x8 wa[2][KS];
-    load_wt<R>(a, (int64_t)tile * TN + 32 * wid, li, lg, wa);
+    bf16x8 wa[KS];
+    uint2 bv[MBLK];
+    load_wt<R>(a, (int64_t)tile * TN + 16 * wid, li, lg, wa);
+    load_base(a, k, m0, mrows, (int64_t)tile * TN + 16 * wid + 4 * lg, li, vec, bv);
     {
         svk::u32x4 uv[UPT];
 #pragma unroll
@@ -103,111 +127,76 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
     __syncthreads();
 
     for (; tile < ntile; tile += gridDim.x) {
-        const int64_t n0 = (int64_t)tile * TN;
-        const int64_t nw = n0 + 32 * wid;        // this wavefront's 32 rows
-
-        // base logits of the lane's outputs: request 16 mb + li, entries nw + 16 vb + 4 lg + r
-        uint2 bv[2][MBLK];
+        const int64_t n = (int64_t)tile * TN + 16 * wid + 4 * lg;   // the lane's first vocabulary entry
+        // opaque to the optimiser, so the 16 row addresses below are rebuilt
+        // per tile rather than held (and spilled) across the loop
+        int li_t = li;
+        asm volatile("" : "+v"(li_t));
+        f32x4 acc[MBLK];
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-            const int64_t n = nw + 16 * vb + 4 * lg;
+        for (int mb = 0; mb < MBLK; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
 #pragma unroll
             for (int mb = 0; mb < MBLK; ++mb) {
-                const int ml = 16 * mb + li;
-                bv[vb][mb] = make_uint2(0xFF80FF80u, 0xFF80FF80u);   // -inf
-                if (ml < mrows) {
-                    const uint16_t *brow = a.base + ((int64_t)(m0 + ml) * a.gamma + (k - 1)) * a.V;
-                    if (vec) {
-                        if (n < a.V) bv[vb][mb] = *(const uint2 *)(brow + n);
-                    } else {
-                        uint16_t e[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) e[r] = n + r < a.V ? brow[n + r] : (uint16_t)0xFF80u;
-                        bv[vb][mb] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
-                    }
-                }
+                const bf16x8 bfr = *(const bf16x8 *)(Us + (16 * mb + li) * US + 32 * s + 8 * lg);
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], bfr, acc[mb], 0, 0, 0);
             }
         }
-        // two halves of 64 requests: half the accumulators live at a time
+        // the fragments are consumed: fetch the next tile's into the same
+        // registers, so the loads overlap the epilogue
         const int next = tile + (int)gridDim.x;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            constexpr int MH = MBLK / 2;
-            f32x4 acc[2][MH];
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-                for (int j = 0; j < MH; ++j) acc[vb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int j = 0; j < MH; ++j) {
-                    const int mb = MH * h + j;
-                    const bf16x8 bfr = *(const bf16x8 *)(Us + (16 * mb + li) * US + 32 * s + 8 * lg);
-                    acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[0][s], bfr, acc[0][j], 0, 0, 0);
-                    acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[1][s], bfr, acc[1][j], 0, 0, 0);
-                }
-            }
-            // after the second half the fragments are consumed: fetch the next
-            // tile's into the same registers, so the loads overlap the epilogue
-            if (h == 1 && next < ntile) load_wt<R>(a, (int64_t)next * TN + 32 * wid, li, lg, wa);
+        if (next < ntile) load_wt<R>(a, (int64_t)next * TN + 16 * wid, li, lg, wa);
 
-            // epilogue: lane holds z^T[nw + 16 vb + 4 lg + r][16 mb + li]
+        // epilogue: lane holds z^T[n + r][16 mb + li]
 #pragma unroll
-            for (int j = 0; j < MH; ++j) {
-                const int mb = MH * h + j;
-                const int ml = 16 * mb + li;
-                const bool rowok = ml < mrows;
-                float zc[2][4];
-                float mx = svk::neg_inf();
+        for (int mb = 0; mb < MBLK; ++mb) {
+            const int ml = 16 * mb + li_t;
+            const uint32_t b01 = bv[mb].x, b23 = bv[mb].y;
+            float z[4];
+            z[0] = acc[mb][0] + __uint_as_float(b01 << 16);
+            z[1] = acc[mb][1] + __uint_as_float(b01 & 0xFFFF0000u);
+            z[2] = acc[mb][2] + __uint_as_float(b23 << 16);
+            z[3] = acc[mb][3] + __uint_as_float(b23 & 0xFFFF0000u);
+            if (ml < mrows) {
+                float *zrow = zout + (int64_t)(m0 + ml) * zstride;
+                if (vec) {
+                    if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
+                } else {
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
-                    const int64_t n = nw + 16 * vb + 4 * lg;
-                    const uint32_t b01 = bv[vb][mb].x, b23 = bv[vb][mb].y;
-                    float z[4];
-                    z[0] = acc[vb][j][0] + __uint_as_float(b01 << 16);
-                    z[1] = acc[vb][j][1] + __uint_as_float(b01 & 0xFFFF0000u);
-                    z[2] = acc[vb][j][2] + __uint_as_float(b23 << 16);
-                    z[3] = acc[vb][j][3] + __uint_as_float(b23 & 0xFFFF0000u);
-                    if (rowok) {
-                        float *zrow = zout + (int64_t)(m0 + ml) * zstride;
-                        if (vec) {
-                            if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
-                        } else {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (n + r < a.V) zrow[n + r] = z[r];
-                        }
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        zc[vb][r] = n + r < a.V ? z[r] * a.c : svk::neg_inf();
-                        mx = fmaxf(mx, zc[vb][r]);
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < a.V) zrow[n + r] = z[r];
                 }
-                // the four lanes li, li + 16, li + 32, li + 48 hold this request's 32 entries
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                float sum = 0.0f;
-                bool bad = false;
-#pragma unroll
-                for (int vb = 0; vb < 2; ++vb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        bad |= zc[vb][r] != zc[vb][r];
-                        if (mx != svk::neg_inf()) sum += svk::fast_exp2(zc[vb][r] - mx);
-                    }
-                if (bad) sum = __builtin_nanf("");   // a NaN entry poisons the row; the draw flags it
-                sum += __shfl_xor(sum, 16, 64);
-                sum += __shfl_xor(sum, 32, 64);
-                if (lg == 0) red[wid][ml] = make_float2(mx, sum);
             }
+            float zc[4];
+            float mx = svk::neg_inf();
+            bool bad = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                zc[r] = n + r < a.V ? z[r] * a.c : svk::neg_inf();
+                mx = fmaxf(mx, zc[r]);
+                bad |= zc[r] != zc[r];
+            }
+            // the four lanes li, li + 16, li + 32, li + 48 hold this request's 16 entries
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            float sm = 0.0f;
+            if (mx != svk::neg_inf()) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[r] - mx);
+            }
+            if (bad) sm = __builtin_nanf("");   // a NaN entry poisons the row; the draw flags it
+            sm += __shfl_xor(sm, 16, 64);
+            sm += __shfl_xor(sm, 32, 64);
+            if (lg == 0) red[wid][ml] = make_float2(mx, sm);
         }
+        // the base logits are consumed: fetch the next tile's
+        if (next < ntile) load_base(a, k, m0, mrows, (int64_t)next * TN + 16 * wid + 4 * lg, li_t, vec, bv);
         __syncthreads();
         if ((int)threadIdx.x < mrows) {
             svk::MS t{red[0][threadIdx.x].x, red[0][threadIdx.x].y};
 #pragma unroll
-            for (int w = 1; w < 4; ++w) t = svk::ms_merge(t, svk::MS{red[w][threadIdx.x].x, red[w][threadIdx.x].y});
+            for (int w = 1; w < NWAVE; ++w) t = svk::ms_merge(t, svk::MS{red[w][threadIdx.x].x, red[w][threadIdx.x].y});
             tile_part[(int64_t)(m0 + (int)threadIdx.x) * ntile + tile] = make_float2(t.m, t.s);
         }
         __syncthreads();   // red[] is rewritten by the next tile

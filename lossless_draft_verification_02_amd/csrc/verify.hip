@@ -24,7 +24,9 @@
 //                 only computes the running ratios.
 //  k_block_pass2  grid (request, position i, segment group): each wavefront
 //                 sums max(w_i p_{i+1} - q_{i+1}, 0) over one segment of
-//                 kSegR consecutive tokens.
+//                 kSegR consecutive tokens.  Requests whose longest prefix
+//                 already passes (eta_L < w_L, found by the pre stage) are
+//                 skipped: tau = L for them whatever the other thresholds.
 //  k_resid_sum    grid (request, segment group): segment sums of the
 //                 correction / bonus weights of row tau+1 (skipped when
 //                 block pass 2 already summed exactly those weights).
@@ -129,7 +131,7 @@ struct AcceptLDS {
 // is issued first, so the evaluation costs about two memory round trips.
 template <int PES, int QES>
 __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__ part, int nch1,
-                            const float *__restrict__ bm, int nseg, int stage, int b, ReqG *out,
+                            const float *__restrict__ bm, int nseg, int stage, int b, const ReqG *pre, ReqG *out,
                             float *__restrict__ lp2g, float *__restrict__ lq2g, float *__restrict__ wrun,
                             uint32_t *__restrict__ errword, AcceptLDS &s)
 {
@@ -165,11 +167,13 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
         u = a.uniforms ? a.uniforms[(int64_t)b * G1 + lane]
                        : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)(lane + 1), 0u);
     // block thresholds: running ratio and residual mass of position lane + 1
+    // (not needed when the pre stage already decided tau = L)
+    const int tau_pre = stage == STAGE_BLOCK_FINAL ? pre->tau : -1;
     float wi = 1.0f;
     double mi = 0.0;
     if (stage == STAGE_BLOCK_FINAL && lane + 1 <= gamma) {
         wi = wrun[(int64_t)b * G1 + lane + 1];
-        if (lane + 1 < gamma) mi = sum_in_order(bm + ((int64_t)b * gamma + lane + 1) * nseg, nseg);
+        if (lane + 1 < gamma && tau_pre < 0) mi = sum_in_order(bm + ((int64_t)b * gamma + lane + 1) * nseg, nseg);
     }
 
     // ---- checks: verify length, then tokens (reported alone), then rows
@@ -232,9 +236,19 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
                 w = fminf(prod, 1.0f);
                 wrun[(int64_t)b * G1 + i] = w;
             }
+            // tau is the largest passing prefix, so eta_L < h_L = w_L decides
+            // tau = L whatever the other thresholds are: such a request needs
+            // no residual masses (unless the caller asked for every h_i)
+            int tau_early = -1;
+            if (L >= 1 && !a.diag.h) {
+                const float eta = a.uniforms ? a.uniforms[(int64_t)b * G1 + L - 1]
+                                             : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)L, 0u);
+                if (eta < w) tau_early = L;
+            }
             ReqG r{};
             r.flags = 0;
             r.L = L;
+            r.tau = tau_early;
             *out = r;
         }
         return;
@@ -274,6 +288,7 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
         }
         const uint64_t pass = __ballot(active && u < h);    // eta_i < h_i
         tau = pass ? 64 - (int)__builtin_clzll(pass) : 0;   // largest passing i
+        if (tau_pre >= 0) tau = tau_pre;                     // decided by the pre stage (= L)
         if (has_tok) {
             if (a.diag.w) a.diag.w[(int64_t)b * gamma + lane] = active ? wi : nan;
             if (a.diag.h) a.diag.h[(int64_t)b * gamma + lane] = active ? h : nan;
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const 
 {
     __shared__ AcceptLDS s;
     const int b = a.b0 + (int)blockIdx.x;
-    accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, req + b, lp2g, lq2g, wrun, errword, s);
+    accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, req + b, req + b, lp2g, lq2g, wrun, errword, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -493,7 +508,7 @@ __global__ __launch_bounds__(NT) void k_block_pass2(svh::VerifyArgs a, const Req
     const int b = a.b0 + bl;
     const int sidx = g * SPW + (int)(threadIdx.x / svk::kWave);
     const ReqG r = req[b];
-    if (r.flags || i >= r.L || sidx >= nseg) return;   // whole wavefronts leave together
+    if (r.flags || r.tau >= 0 || i >= r.L || sidx >= nseg) return;   // whole wavefronts leave together
     const int G1 = a.gamma + 1;
     const float w = wrun[(int64_t)b * G1 + i];
     const int64_t s0 = (int64_t)sidx * SEG;
@@ -825,6 +840,7 @@ constexpr int kTailMaxSeg = 4096;   // LDS segment sums: V <= 8.4M tokens
 template <int PES, int QES>
 __global__ __launch_bounds__(NTT) void k_tail(svh::VerifyArgs a, const float2 *__restrict__ part, int nch1,
                                               const float *__restrict__ bm, int nseg, int stage,
+                                              const ReqG *__restrict__ pre,
                                               float *__restrict__ lp2g, float *__restrict__ lq2g,
                                               float *__restrict__ wrun, uint32_t *__restrict__ errword)
 {
@@ -834,7 +850,7 @@ __global__ __launch_bounds__(NTT) void k_tail(svh::VerifyArgs a, const float2 *_
     __shared__ SelectShared sh;
     const int b = a.b0 + (int)blockIdx.x;
     if (threadIdx.x < svk::kWave)
-        accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, &r, lp2g, lq2g, wrun, errword, as);
+        accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, pre + b, &r, lp2g, lq2g, wrun, errword, as);
     __syncthreads();
     if (r.flags) return;   // accept_eval wrote the request's error outputs
     const int gamma = a.gamma;
@@ -911,8 +927,8 @@ void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int
 {
     const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
     hipLaunchKernelGGL((k_tail<PES, QES>), dim3(a.nb), dim3(NTT), 0, s, a, (const float2 *)ctx->ws.part, ctx->nch1,
-                       (const float *)ctx->ws.bm, ctx->nseg, stage, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun,
-                       ctx->ws.errword);
+                       (const float *)ctx->ws.bm, ctx->nseg, stage, (const ReqG *)ctx->ws.req, ctx->ws.lp2,
+                       ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
 }
 

@@ -124,6 +124,7 @@ def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = Fa
             _close_prob(rep, gpu["ratio"][b, :L], orc.ratio[b, :L], "ratio", b)
         if block and "w" in gpu and L > 0:
             _close_prob(rep, gpu["w"][b, :L], orc.w[b, :L], "w", b)
+        if block and "h" in gpu and L > 0:
             _close_prob(rep, gpu["h"][b, :L], orc.h[b, :L], "h", b)
         if "resid_mass" in gpu:
             _close_prob(rep, [gpu["resid_mass"][b]], [orc.resid_mass[b]], "resid_mass", b)

@@ -36,7 +36,7 @@ def _say(*a):
 # ------------------------------------------------------------- helpers -----
 
 def gpu_verify(ctx, vi, *, block=False, verify_len=None, conf=None, uniforms=None, seed=WL.VERIFY_SEED,
-               offset=0, p=None, q=None, draft=None, T=None):
+               offset=0, p=None, q=None, draft=None, T=None, skip_diag=()):
     p = vi.p if p is None else p
     q = vi.q if q is None else q
     draft = vi.draft if draft is None else draft
@@ -49,6 +49,8 @@ def gpu_verify(ctx, vi, *, block=False, verify_len=None, conf=None, uniforms=Non
                 ratio=torch.empty(B, max(gamma, 1), device=dev), w=torch.empty(B, max(gamma, 1), device=dev),
                 h=torch.empty(B, max(gamma, 1), device=dev), resid_mass=torch.empty(B, device=dev),
                 flags=torch.zeros(B, dtype=torch.int32, device=dev))
+    for k in skip_diag:
+        del diag[k]
     vlo = torch.full((B,), -7, dtype=torch.int32, device=dev) if conf is not None else None
     T = vi.T if T is None else T
     if block:
@@ -94,9 +96,10 @@ def _subset(res, req):
 
 def check_verify(ctx, vi, req=None, *, block=False, verify_len=None, uniforms=None, offset=0, label="",
                  max_flip_frac=0.02, **kw):
+    skip_diag = kw.pop("skip_diag", ())
     g = gpu_verify(ctx, vi, block=block, verify_len=None if verify_len is None else
                    torch.as_tensor(verify_len, dtype=torch.int32, device=vi.p.device),
-                   uniforms=uniforms, offset=offset, **kw)
+                   uniforms=uniforms, offset=offset, skip_diag=skip_diag, **kw)
     req = list(range(vi.B)) if req is None else list(req)
     o = oracle_verify(vi, req, block=block, verify_len=verify_len, uniforms=uniforms, offset=offset, **kw)
     vl = None if verify_len is None else np.asarray(verify_len)[req]
@@ -335,6 +338,23 @@ def test_block_recipe_small(V):
         rep = compare_verify(res, o, gamma, verify_len=ovl, block=True)
         _say(f"[block scheduled] {rep}")
         assert rep.ok(), str(rep)
+
+
+def test_block_early_decision_without_threshold_diagnostics():
+    """Without h diagnostics, requests whose longest prefix passes skip the
+    residual masses; every decision must stay the oracle's."""
+    B, gamma, V = 64, 8, 20000
+    vi = WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V)
+    vl = np.array([(5 * b + 3) % (gamma + 1) for b in range(B)], np.int32)
+    with make_ctx(B, gamma, V) as ctx:
+        for noise, label in ((None, "recipe"), (0.35, "hi-acc")):
+            v2 = vi if noise is None else WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V, noise=noise)
+            _say(f"case: block early decision, {label}")
+            full = check_verify(ctx, v2, block=True, verify_len=vl, label=f"block full {label}")[0]
+            early = check_verify(ctx, v2, block=True, verify_len=vl, label=f"block early {label}",
+                                 skip_diag=("h",))[0]
+            assert np.array_equal(full["accepted_len"], early["accepted_len"])
+            assert np.array_equal(full["out_tokens"], early["out_tokens"])
 
 
 def test_block_with_one_position_equals_token_on_gpu():
