@@ -96,20 +96,33 @@ __device__ double merge_row(const float2 *__restrict__ part, int64_t row, int nc
     return (double)M + log2((double)S);
 }
 
-// Sum, in index order and fp64, of n floats; loads issued kSumBatch at a time.
-constexpr int kSumBatch = 16;
-__device__ double sum_in_order(const float *__restrict__ v, int n)
+// Residual masses m_i = sum of the nseg segment sums of position i (i = 1 ..
+// L-1) of one request, by one wavefront: lane l adds segments l, l + 64, ...
+// of a position, then a fixed-order wavefront reduction; the loads of 8
+// positions are issued together.  Lane i - 1 returns m_i.
+__device__ double residual_masses(const float *__restrict__ bmr, int L, int nseg, int lane)
 {
-    double acc = 0.0;
-    for (int k0 = 0; k0 < n; k0 += kSumBatch) {
-        float x[kSumBatch];
+    constexpr int PB = 8;   // positions per batch
+    double mine = 0.0;
+    for (int i0 = 1; i0 < L; i0 += PB) {
+        double acc[PB];
 #pragma unroll
-        for (int j = 0; j < kSumBatch; ++j) x[j] = k0 + j < n ? v[k0 + j] : 0.0f;
+        for (int j = 0; j < PB; ++j) acc[j] = 0.0;
+        for (int k0 = 0; k0 < nseg; k0 += svk::kWave) {
+            float v[PB];
 #pragma unroll
-        for (int j = 0; j < kSumBatch; ++j)
-            if (k0 + j < n) acc += (double)x[j];
+            for (int j = 0; j < PB; ++j)
+                v[j] = (i0 + j < L && k0 + lane < nseg) ? bmr[(int64_t)(i0 + j) * nseg + k0 + lane] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < PB; ++j) acc[j] += (double)v[j];
+        }
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const double t = svk::wave_sum_d(acc[j]);
+            if (lane == i0 + j - 1) mine = t;
+        }
     }
-    return acc;
+    return mine;
 }
 
 // ---------------------------------------------------------------------------
@@ -171,9 +184,9 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
     const int tau_pre = stage == STAGE_BLOCK_FINAL ? pre->tau : -1;
     float wi = 1.0f;
     double mi = 0.0;
-    if (stage == STAGE_BLOCK_FINAL && lane + 1 <= gamma) {
-        wi = wrun[(int64_t)b * G1 + lane + 1];
-        if (lane + 1 < gamma && tau_pre < 0) mi = sum_in_order(bm + ((int64_t)b * gamma + lane + 1) * nseg, nseg);
+    if (stage == STAGE_BLOCK_FINAL) {
+        if (lane + 1 <= gamma) wi = wrun[(int64_t)b * G1 + lane + 1];
+        if (tau_pre < 0 && L >= 2) mi = residual_masses(bm + (int64_t)b * gamma * nseg, L, nseg, lane);
     }
 
     // ---- checks: verify length, then tokens (reported alone), then rows
@@ -831,14 +844,15 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
 // segment into LDS (all wavefronts) and selects the token, with no
 // communication between workgroups.  Used when the segment sums fit in LDS.
 // ---------------------------------------------------------------------------
-constexpr int NTT = 1024;
+constexpr int NTT_WIDE = 1024;      // one workgroup per CU when requests <= CUs
+constexpr int NTT_NARROW = 512;     // two per CU otherwise (<= 128 VGPRs either way)
 constexpr int kTailMaxSeg = 4096;   // LDS segment sums: V <= 8.4M tokens
 #ifndef SV_FUSED_TAIL
 #define SV_FUSED_TAIL 1             // 0: always the accept / sum / select kernels
 #endif
 
-template <int PES, int QES>
-__global__ __launch_bounds__(NTT) void k_tail(svh::VerifyArgs a, const float2 *__restrict__ part, int nch1,
+template <int PES, int QES, int NTT>
+__global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, const float2 *__restrict__ part, int nch1,
                                               const float *__restrict__ bm, int nseg, int stage,
                                               const ReqG *__restrict__ pre,
                                               float *__restrict__ lp2g, float *__restrict__ lq2g,
@@ -926,9 +940,14 @@ template <int PES, int QES>
 void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int stage)
 {
     const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
-    hipLaunchKernelGGL((k_tail<PES, QES>), dim3(a.nb), dim3(NTT), 0, s, a, (const float2 *)ctx->ws.part, ctx->nch1,
-                       (const float *)ctx->ws.bm, ctx->nseg, stage, (const ReqG *)ctx->ws.req, ctx->ws.lp2,
-                       ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
+    if (a.nb <= ctx->num_cu)
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_WIDE>), dim3(a.nb), dim3(NTT_WIDE), 0, s, a,
+                           (const float2 *)ctx->ws.part, ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage,
+                           (const ReqG *)ctx->ws.req, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
+    else
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a,
+                           (const float2 *)ctx->ws.part, ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage,
+                           (const ReqG *)ctx->ws.req, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
 }
 
