@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NT, 4) void k_markov_gemm(svh::MarkovArgs a, int k,
             *(svk::u32x4 *)(Us + (u / UCH) * US + 8 * (u % UCH)) = uv[q];
         }
     }
-    __syncthreads();
+    svk::lds_barrier();
 
     for (; tile < ntile; tile += gridDim.x) {
         const int64_t n = (int64_t)tile * TN + 16 * wid + 4 * lg;   // the lane's first vocabulary entry
@@ -192,14 +192,14 @@ __global__ __launch_bounds__(NT, 4) void k_markov_gemm(svh::MarkovArgs a, int k,
         }
         // the base logits are consumed: fetch the next tile's
         if (next < ntile) load_base(a, k, m0, mrows, (int64_t)next * TN + 16 * wid + 4 * lg, li_t, vec, bv);
-        __syncthreads();
+        svk::lds_barrier();
         if ((int)threadIdx.x < mrows) {
             svk::MS t{red[0][threadIdx.x].x, red[0][threadIdx.x].y};
 #pragma unroll
             for (int w = 1; w < NWAVE; ++w) t = svk::ms_merge(t, svk::MS{red[w][threadIdx.x].x, red[w][threadIdx.x].y});
             tile_part[(int64_t)(m0 + (int)threadIdx.x) * ntile + tile] = make_float2(t.m, t.s);
         }
-        __syncthreads();   // red[] is rewritten by the next tile
+        svk::lds_barrier();   // red[] is rewritten by the next tile
     }
 }
 

@@ -102,6 +102,18 @@ __device__ __forceinline__ u32x4 neg_inf_vec()
     return u32x4{w, w, w, w};
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
+// workgroup-scope fence on every address space: it waits for all earlier
+// global stores, and because loads and stores share one vector-memory counter
+// that also drains every load issued before them (a prefetch included).  Use
+// this where the workgroup communicates through LDS alone.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------------------
 // (max, sum-exp2) pairs.
 // ---------------------------------------------------------------------------
