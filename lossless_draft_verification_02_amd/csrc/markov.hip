@@ -35,14 +35,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 512;                 // 8 wavefronts, 16 vocabulary rows each per tile
+constexpr int NT = 512;                 // 8 wavefronts
 constexpr int NWAVE = NT / 64;
-constexpr int TN = svh::kMarkovTileN;   // 128 vocabulary entries per tile
-constexpr int MC = 128;                 // requests per workgroup (8 blocks of 16)
-constexpr int MBLK = MC / 16;
-constexpr int kGemmWGs = 512;           // two resident workgroups per compute unit
+constexpr int TN = svh::kMarkovTileN;   // 128 vocabulary rows per tile (= the draw's tile)
+constexpr int MC = 16 * NWAVE;          // 128 requests per workgroup: wavefront w owns 16 w .. 16 w + 15
+constexpr int NVB = TN / 16;            // 16-row vocabulary blocks per tile
 
-static_assert(TN == NWAVE * 16, "eight wavefronts of 16 vocabulary rows per tile");
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m)
 {
@@ -50,156 +49,163 @@ __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m
     return (x < 0 || (int64_t)x >= a.V) ? 0 : x;   // invalid ids are flagged by the select
 }
 
-// The wavefront's A fragments of one tile: vocabulary row n = nrow0 + li,
-// k-chunk 8 lg of each 32-wide k-step.  Rows past V read as zero.
+// A tile of Wt (TN rows of R bf16) in LDS: row r's 16-byte chunk c sits at
+// slot r * CH + (c ^ swz(r)), so the 16 rows of an A fragment read by one
+// 16-lane group fall in different banks.
 template <int R>
-__device__ __forceinline__ void load_wt(const svh::MarkovArgs &a, int64_t nrow0, int li, int lg,
-                                        bf16x8 (&wa)[R / 32])
+struct TileLayout {
+    static constexpr int CH = R / 8;                        // 16-byte chunks per row
+    static constexpr int SW = CH < 16 ? CH : 16;            // swizzle period
+    static constexpr int BYTES = TN * R * 2;
+    static constexpr int PER_WAVE = TN * CH / (NWAVE * 64); // copy instructions per wavefront
+    static_assert(TN * CH % (NWAVE * 64) == 0, "whole copy instructions");
+    __device__ static __forceinline__ int slot(int row, int c) { return row * CH + (c ^ (row & (SW - 1))); }
+};
+
+// Direct global -> LDS copy of Wt rows [n0, n0 + TN) into `dst`: each
+// wavefront instruction fills 64 consecutive 16-byte slots (lane i -> slot
+// base + i), fetching whichever global chunk the swizzle puts there.  Rows
+// past V copy row V - 1; their outputs are never stored.
+template <int R>
+__device__ __forceinline__ void copy_tile(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int wid, int lane)
 {
-    const int64_t n = nrow0 + li;
-    const uint16_t *row = a.W + (n < a.V ? n : 0) * R + 8 * lg;
+    using TL = TileLayout<R>;
 #pragma unroll
-    for (int s = 0; s < R / 32; ++s) wa[s] = n < a.V ? *(const bf16x8 *)(row + 32 * s) : bf16x8{};
+    for (int j = 0; j < TL::PER_WAVE; ++j) {
+        const int base = (j * NWAVE + wid) * 64;
+        const int S = base + lane;
+        const int row = S / TL::CH, p = S % TL::CH;
+        const int c = p ^ (row & (TL::SW - 1));
+        int64_t n = n0 + row;
+        n = n < a.V ? n : a.V - 1;
+        __builtin_amdgcn_global_load_lds((const void *)(a.W + n * R + 8 * c), (lds_void *)(dst + base * 16), 16, 0, 0);
+    }
 }
 
-// Base logits of the lane's outputs: requests m0 + 16 mb + li, vocabulary
-// entries n .. n + 3 (bf16, packed in a uint2); -inf past V or past the batch.
-__device__ __forceinline__ void load_base(const svh::MarkovArgs &a, int k, int m0, int mrows, int64_t n, int li,
-                                          int vec, uint2 (&bv)[MBLK])
+// Base logits of the lane's outputs in one tile: request m, vocabulary
+// entries n0 + 16 vb + 4 lg + r, as packed bf16 pairs; -inf past V or B.
+__device__ __forceinline__ void load_base(const svh::MarkovArgs &a, int k, int m, int64_t n0, int lg, int vec,
+                                          uint2 (&bv)[NVB])
 {
+    const uint16_t *brow = a.base + ((int64_t)(m < a.B ? m : 0) * a.gamma + (k - 1)) * a.V;
 #pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) {
-        const int ml = 16 * mb + li;
-        bv[mb] = make_uint2(0xFF80FF80u, 0xFF80FF80u);
-        if (ml < mrows) {
-            const uint16_t *brow = a.base + ((int64_t)(m0 + ml) * a.gamma + (k - 1)) * a.V;
+    for (int vb = 0; vb < NVB; ++vb) {
+        const int64_t n = n0 + 16 * vb + 4 * lg;
+        bv[vb] = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+        if (m < a.B) {
             if (vec) {
-                if (n < a.V) bv[mb] = *(const uint2 *)(brow + n);
+                if (n < a.V) bv[vb] = *(const uint2 *)(brow + n);
             } else {
                 uint16_t e[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) e[r] = n + r < a.V ? brow[n + r] : (uint16_t)0xFF80u;
-                bv[mb] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+                bv[vb] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
             }
         }
     }
 }
 
 template <int R>
-__global__ __launch_bounds__(NT, 4) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
+__global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
                                                        int64_t zstride, float2 *__restrict__ tile_part,
                                                        int ntile, int vec)
 {
+    using TL = TileLayout<R>;
     constexpr int KS = R / 32;
-    constexpr int US = R + 8;              // LDS row stride (bf16): conflict-free 16-byte fragment reads
-    constexpr int UCH = R / 8;             // 16-byte chunks per U row
-    constexpr int UPT = MC * UCH / NT;     // chunks staged per thread
-    static_assert(UPT >= 1 && MC * UCH % NT == 0, "U staging split");
-    __shared__ __attribute__((aligned(16))) uint16_t Us[MC * US];
-    __shared__ float2 red[NWAVE][MC];
+    __shared__ __attribute__((aligned(16))) unsigned char wtile[2 * TL::BYTES];   // double-buffered tile ring
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int m0 = blockIdx.y * MC;
-    const int mrows = a.B - m0 < MC ? a.B - m0 : MC;
+    const int m = blockIdx.y * MC + 16 * wid + li;   // the lane's request (B operand column)
+    const bool wave_on = blockIdx.y * MC + 16 * wid < a.B;
 
-    // first tile's Wt fragments and base logits, then the gathered U rows -> LDS
+    // prologue: first tile's copy, the wavefront's U fragments, first base logits
     int tile = blockIdx.x;
-    bf16x8 wa[KS];
-    uint2 bv[MBLK];
-    load_wt<R>(a, (int64_t)tile * TN + 16 * wid, li, lg, wa);
-    load_base(a, k, m0, mrows, (int64_t)tile * TN + 16 * wid + 4 * lg, li, vec, bv);
+    copy_tile<R>(a, (int64_t)tile * TN, wtile, wid, lane);
+    bf16x8 ufr[KS];
     {
-        svk::u32x4 uv[UPT];
+        const uint16_t *urow = a.U + (int64_t)(m < a.B ? prev_token(a, k, m) : 0) * R + 8 * lg;
 #pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            const int u = (int)threadIdx.x + q * NT;
-            const int row = u / UCH, ch = u % UCH;
-            uv[q] = svk::u32x4{0u, 0u, 0u, 0u};
-            if (row < mrows) uv[q] = *(const svk::u32x4 *)(a.U + (int64_t)prev_token(a, k, m0 + row) * R + 8 * ch);
-        }
-#pragma unroll
-        for (int q = 0; q < UPT; ++q) {
-            const int u = (int)threadIdx.x + q * NT;
-            *(svk::u32x4 *)(Us + (u / UCH) * US + 8 * (u % UCH)) = uv[q];
-        }
+        for (int s = 0; s < KS; ++s) ufr[s] = m < a.B ? *(const bf16x8 *)(urow + 32 * s) : bf16x8{};
     }
-    svk::lds_barrier();
+    uint2 bv[NVB];
+    load_base(a, k, m, (int64_t)tile * TN, lg, vec, bv);
 
-    for (; tile < ntile; tile += gridDim.x) {
-        const int64_t n = (int64_t)tile * TN + 16 * wid + 4 * lg;   // the lane's first vocabulary entry
-        // opaque to the optimiser, so the 16 row addresses below are rebuilt
-        // per tile rather than held (and spilled) across the loop
-        int li_t = li;
-        asm volatile("" : "+v"(li_t));
-        f32x4 acc[MBLK];
-#pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-#pragma unroll
-            for (int mb = 0; mb < MBLK; ++mb) {
-                const bf16x8 bfr = *(const bf16x8 *)(Us + (16 * mb + li) * US + 32 * s + 8 * lg);
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], bfr, acc[mb], 0, 0, 0);
-            }
-        }
-        // the fragments are consumed: fetch the next tile's into the same
-        // registers, so the loads overlap the epilogue
+    for (int it = 0; tile < ntile; ++it, tile += gridDim.x) {
+        unsigned char *buf = wtile + (it & 1) * TL::BYTES;
+        // this tile's copy (and base loads) landed for every wavefront, and
+        // every wavefront finished reading the other buffer
+        __builtin_amdgcn_s_waitcnt(0);
+        svk::lds_barrier();
         const int next = tile + (int)gridDim.x;
-        if (next < ntile) load_wt<R>(a, (int64_t)next * TN + 16 * wid, li, lg, wa);
-
-        // epilogue: lane holds z^T[n + r][16 mb + li]
+        uint2 bn[NVB];
+        if (next < ntile) {
+            copy_tile<R>(a, (int64_t)next * TN, wtile + ((it + 1) & 1) * TL::BYTES, wid, lane);
+            load_base(a, k, m, (int64_t)next * TN, lg, vec, bn);
+        }
+        if (wave_on) {
+            f32x4 acc[NVB];
 #pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb) {
-            const int ml = 16 * mb + li_t;
-            const uint32_t b01 = bv[mb].x, b23 = bv[mb].y;
-            float z[4];
-            z[0] = acc[mb][0] + __uint_as_float(b01 << 16);
-            z[1] = acc[mb][1] + __uint_as_float(b01 & 0xFFFF0000u);
-            z[2] = acc[mb][2] + __uint_as_float(b23 << 16);
-            z[3] = acc[mb][3] + __uint_as_float(b23 & 0xFFFF0000u);
-            if (ml < mrows) {
-                float *zrow = zout + (int64_t)(m0 + ml) * zstride;
-                if (vec) {
-                    if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
-                } else {
+            for (int vb = 0; vb < NVB; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < a.V) zrow[n + r] = z[r];
+            for (int s = 0; s < KS; ++s) {
+#pragma unroll
+                for (int vb = 0; vb < NVB; ++vb) {
+                    const int row = 16 * vb + li;
+                    const bf16x8 afr = *(const bf16x8 *)(buf + 16 * TL::slot(row, 4 * s + lg));
+                    acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, ufr[s], acc[vb], 0, 0, 0);
                 }
             }
-            float zc[4];
+            // epilogue: lane holds z^T[n0 + 16 vb + 4 lg + r][m]
+            const int64_t n0 = (int64_t)tile * TN;
+            float *zrow = zout + (int64_t)(m < a.B ? m : 0) * zstride;
             float mx = svk::neg_inf();
             bool bad = false;
+            float zc[NVB][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                zc[r] = n + r < a.V ? z[r] * a.c : svk::neg_inf();
-                mx = fmaxf(mx, zc[r]);
-                bad |= zc[r] != zc[r];
+            for (int vb = 0; vb < NVB; ++vb) {
+                const int64_t n = n0 + 16 * vb + 4 * lg;
+                const uint32_t b01 = bv[vb].x, b23 = bv[vb].y;
+                float z[4];
+                z[0] = acc[vb][0] + __uint_as_float(b01 << 16);
+                z[1] = acc[vb][1] + __uint_as_float(b01 & 0xFFFF0000u);
+                z[2] = acc[vb][2] + __uint_as_float(b23 << 16);
+                z[3] = acc[vb][3] + __uint_as_float(b23 & 0xFFFF0000u);
+                if (m < a.B) {
+                    if (vec) {
+                        if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < a.V) zrow[n + r] = z[r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    zc[vb][r] = n + r < a.V ? z[r] * a.c : svk::neg_inf();
+                    mx = fmaxf(mx, zc[vb][r]);
+                    bad |= zc[vb][r] != zc[vb][r];
+                }
             }
-            // the four lanes li, li + 16, li + 32, li + 48 hold this request's 16 entries
+            // lanes li, li + 16, li + 32, li + 48 hold request m's 128 entries
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             float sm = 0.0f;
             if (mx != svk::neg_inf()) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[r] - mx);
+                for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[vb][r] - mx);
             }
             if (bad) sm = __builtin_nanf("");   // a NaN entry poisons the row; the draw flags it
             sm += __shfl_xor(sm, 16, 64);
             sm += __shfl_xor(sm, 32, 64);
-            if (lg == 0) red[wid][ml] = make_float2(mx, sm);
+            if (lg == 0 && m < a.B) tile_part[(int64_t)m * ntile + tile] = make_float2(mx, sm);
         }
-        // the base logits are consumed: fetch the next tile's
-        if (next < ntile) load_base(a, k, m0, mrows, (int64_t)next * TN + 16 * wid + 4 * lg, li_t, vec, bv);
-        svk::lds_barrier();
-        if ((int)threadIdx.x < mrows) {
-            svk::MS t{red[0][threadIdx.x].x, red[0][threadIdx.x].y};
+        if (next < ntile) {
 #pragma unroll
-            for (int w = 1; w < NWAVE; ++w) t = svk::ms_merge(t, svk::MS{red[w][threadIdx.x].x, red[w][threadIdx.x].y});
-            tile_part[(int64_t)(m0 + (int)threadIdx.x) * ntile + tile] = make_float2(t.m, t.s);
+            for (int vb = 0; vb < NVB; ++vb) bv[vb] = bn[vb];
         }
-        svk::lds_barrier();   // red[] is rewritten by the next tile
     }
 }
 
@@ -342,7 +348,9 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
 {
     const int ntile = ctx->ntile;
     const int gy = (a.B + MC - 1) / MC;
-    int gx = kGemmWGs / gy;
+    const size_t lds = 2 * (size_t)TileLayout<R>::BYTES;
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;   // 160 KB of LDS per CU
+    int gx = ctx->num_cu * per_cu / gy;
     gx = gx < 1 ? 1 : (gx > ntile ? ntile : gx);
     // z rows of position k: the caller's q_logits [B, gamma, V], else a
     // workspace row per request
