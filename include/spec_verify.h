@@ -181,6 +181,33 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream,
                            uint64_t seed, uint64_t offset, const float *uniforms,
                            int32_t *draft_tokens, float *q_logits, float *lse_q);
 
+/* Markov-head draft followed by token-level verification of that draft,
+ * without materialising the draft logits.  The draft is markov_draft_run's
+ * (seed draft_seed, offset; Markov head: "DeepSeek Boosts Inference Speed by
+ * 85%" (kongchang.com), section "The First Ace"); the verification is
+ * spec_verify_run's token rule (seed verify_seed, same offset; "Speculative
+ * Decoding: The Same Distribution, Twice as Fast", section 4) with q the
+ * softmax of the draft logits at the same temperature.  The sampler supplies
+ * each draft row's normaliser and the drafted tokens' logits; the one draft
+ * row per request that the residual max(p - q, 0) needs (position tau + 1) is
+ * rebuilt after the acceptance scan with the sampler's own arithmetic, so it
+ * equals the row the token was drawn from.  Decisions equal those of
+ * markov_draft_run then spec_verify_run up to the fp32 rounding of the draft
+ * normalisers (the two paths sum them in different orders).
+ *   base_logits [B, gamma, V] bf16; U, Wt [V, R] bf16 (16-byte aligned);
+ *   x0 [B] int32 anchors; p_logits [B, gamma+1, V] (bf16 or fp32)
+ *   draft_tokens [B, gamma] int32 out; accepted_len [B], out_tokens
+ *   [B, gamma+1] int32 out, as spec_verify_run; lse_q [B, gamma] out or NULL;
+ *   diag as spec_verify_run (lse_q entries are the sampler's normalisers).
+ * Requires a context with max_rank == R; uses the context's Markov workspace. */
+sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream,
+                            const void *base_logits, const void *U, const void *Wt, int R,
+                            const int32_t *x0, const void *p_logits, sv_dtype p_dtype,
+                            int B, int gamma, int64_t V, float temperature,
+                            uint64_t draft_seed, uint64_t verify_seed, uint64_t offset,
+                            int32_t *draft_tokens, int32_t *accepted_len, int32_t *out_tokens,
+                            float *lse_q, const sv_diag *diag);
+
 /* ---- Measurement ------------------------------------------------------
  * Per-kernel timing with HIP events recorded on the caller's stream around
  * every kernel the library launches (the kernels themselves are unchanged).
@@ -195,7 +222,8 @@ typedef enum {
     SV_KERNEL_SCHEDULE = 6,      /* prefix scheduler                                     */
     SV_KERNEL_MARKOV_GEMM = 7,   /* Markov head contraction + epilogue (per position)    */
     SV_KERNEL_MARKOV_SELECT = 8, /* Markov head draw (per position)                      */
-    SV_KERNEL_COUNT = 9
+    SV_KERNEL_MARKOV_REBUILD = 9,/* fused path: correction rows rebuilt after the scan   */
+    SV_KERNEL_COUNT = 10
 } sv_kernel;
 
 /* enable != 0 creates the context's event pool (up to 4096 launches per

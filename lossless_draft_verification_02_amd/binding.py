@@ -21,10 +21,10 @@ SV_FLAG_BAD_TOKEN, SV_FLAG_BAD_ROW, SV_FLAG_RESID_ZERO, SV_FLAG_BAD_VERIFY_LEN =
 
 EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error",
             "spec_verify_device_status", "spec_verify_run", "spec_schedule_run",
-            "spec_blockverify_run", "markov_draft_run", "spec_verify_profile_enable",
+            "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "spec_verify_profile_enable",
             "spec_verify_profile_read")
 KERNELS = ("rowstats", "accept", "block_pass2", "resid", "select", "tail", "schedule", "markov_gemm",
-           "markov_select")
+           "markov_select", "markov_rebuild")
 
 
 class SpecVerifyError(RuntimeError):
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
                                          P, P, P]
     lib.spec_blockverify_run.restype = I
     lib.markov_draft_run.argtypes = [P, P, P, P, P, I, P, I, I, I64, F, U64, U64, P, P, P, P]
+    lib.markov_verify_run.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I64, F, U64, U64, U64, P, P, P, P, P]
+    lib.markov_verify_run.restype = I
     lib.markov_draft_run.restype = I
     lib.spec_verify_profile_enable.argtypes = [P, I]
     lib.spec_verify_profile_enable.restype = I
@@ -264,6 +266,29 @@ def markov_draft_run(ctx: Context, base, U, Wt, x0, draft_out, *, q_logits=None,
     _check("markov_draft_run", load_library().markov_draft_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), R, _ptr(x0), B, gamma, V,
         temperature, seed, offset, _ptr(uniforms), _ptr(draft_out), _ptr(q_logits), _ptr(lse_q)))
+
+
+def markov_verify_run(ctx: Context, base, U, Wt, x0, p, draft_out, accepted_len, out_tokens, *, lse_q=None,
+                      temperature: float = 1.0, draft_seed: int = 0, verify_seed: int = 1, offset: int = 0,
+                      diag: Optional[dict] = None, stream=None):
+    """Markov-head draft, then token verification of it against p [B, gamma+1, V], without fp32 q."""
+    torch = _torch()
+    B, gamma, V = base.shape
+    R = U.shape[1]
+    _need(base, "base", dtype=torch.bfloat16, device=ctx.device)
+    _need(U, "U", dtype=torch.bfloat16, shape=(V, R), device=ctx.device)
+    _need(Wt, "Wt", dtype=torch.bfloat16, shape=(V, R), device=ctx.device)
+    _need(x0, "x0", dtype=torch.int32, shape=(B,), device=ctx.device)
+    _need(p, "p", shape=(B, gamma + 1, V), device=ctx.device)
+    _need(draft_out, "draft_out", dtype=torch.int32, shape=(B, gamma), device=ctx.device)
+    _need(accepted_len, "accepted_len", dtype=torch.int32, shape=(B,), device=ctx.device)
+    _need(out_tokens, "out_tokens", dtype=torch.int32, shape=(B, gamma + 1), device=ctx.device)
+    _need(lse_q, "lse_q", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
+    d = _diag_struct(diag)
+    _check("markov_verify_run", load_library().markov_verify_run(
+        ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), R, _ptr(x0), _ptr(p),
+        _dtype_code(p), B, gamma, V, temperature, draft_seed, verify_seed, offset, _ptr(draft_out),
+        _ptr(accepted_len), _ptr(out_tokens), _ptr(lse_q), ctypes.byref(d) if d else None))
 
 
 def spec_verify_profile_enable(ctx: Context, enable: bool = True):

@@ -107,6 +107,9 @@ svh::VerifyArgs make_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd
     if (diag) a.diag = *diag;
     else std::memset(&a.diag, 0, sizeof(a.diag));
     a.block = block;
+    a.q_lse2 = nullptr;
+    a.q_zx = nullptr;
+    a.qrec = nullptr;
     return a;
 }
 
@@ -117,6 +120,54 @@ sv_status run_verify(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s,
     sv_status st;
     if ((st = check_launch(svh::launch_rowstats(ctx, a, s), "row statistics")) != SV_OK) return st;
     return check_launch(tail(ctx, a, s), what);
+}
+
+sv_status check_markov_args(const sv_ctx *ctx, const void *base_logits, const void *U, const void *W, int R,
+                            const int32_t *x0, int B, int gamma, int64_t V, float temperature,
+                            const int32_t *draft_tokens, const char *fn)
+{
+    if (!ctx) return fail(SV_ERR_INVALID, "%s: ctx is NULL", fn);
+    if (ctx->max_rank == 0) return fail(SV_ERR_INVALID, "%s: context created with max_rank 0", fn);
+    if (R != ctx->max_rank) return fail(SV_ERR_INVALID, "%s: R=%d differs from max_rank %d", fn, R, ctx->max_rank);
+    if (B <= 0 || B > ctx->max_batch || gamma < 1 || gamma > ctx->max_gamma)
+        return fail(SV_ERR_INVALID, "%s: B=%d or gamma=%d out of range", fn, B, gamma);
+    if (V != ctx->vocab) return fail(SV_ERR_INVALID, "%s: V differs from the context's vocab", fn);
+    if (ctx->ntile > svh::kMarkovMaxTiles)
+        return fail(SV_ERR_UNSUPPORTED, "%s: V=%lld exceeds the sampler's %d-token limit", fn, (long long)V,
+                    svh::kMarkovMaxTiles * svh::kMarkovTileN);
+    if (!(temperature > 0.0f) || !std::isfinite(temperature))
+        return fail(SV_ERR_INVALID, "%s: temperature must be finite and > 0", fn);
+    if (!base_logits || !U || !W || !x0 || !draft_tokens)
+        return fail(SV_ERR_INVALID, "%s: base_logits, U, Wt, x0 and draft_tokens are required", fn);
+    if (!aligned(U, 16) || !aligned(W, 16) || !aligned(base_logits, 2))
+        return fail(SV_ERR_INVALID, "%s: U and Wt must be 16-byte aligned, base 2-byte aligned", fn);
+    return SV_OK;
+}
+
+svh::MarkovArgs make_markov_args(const void *base_logits, const void *U, const void *W, int R, const int32_t *x0,
+                                 int B, int gamma, int64_t V, float temperature, uint64_t seed, uint64_t offset,
+                                 const float *uniforms, int32_t *draft_tokens, float *q_logits, float *lse_q)
+{
+    svh::MarkovArgs a;
+    a.base = (const uint16_t *)base_logits;
+    a.U = (const uint16_t *)U;
+    a.W = (const uint16_t *)W;
+    a.R = R;
+    a.x0 = x0;
+    a.B = B;
+    a.gamma = gamma;
+    a.V = V;
+    a.c = (float)(1.4426950408889634 / (double)temperature);
+    a.seed = seed;
+    a.offset = offset;
+    a.uniforms = uniforms;
+    a.draft = draft_tokens;
+    a.q_logits = q_logits;
+    a.lse_q = lse_q;
+    a.fused = false;
+    a.lse2_out = nullptr;
+    a.zx_out = nullptr;
+    return a;
 }
 
 }  // namespace
@@ -182,11 +233,13 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_sched = carve((size_t)max_batch * sizeof(int32_t));
     const size_t o_srank = carve((size_t)svh::kSchedMax * sizeof(int32_t));
     const size_t o_ssurv = carve((size_t)svh::kSchedMax * sizeof(double));
-    size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0;
+    size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0, o_mklse = 0, o_mkzx = 0;
     if (max_rank > 0) {
         o_mkpart = carve((size_t)max_batch * ctx->ntile * sizeof(float2));
         o_mkprev = carve((size_t)max_batch * sizeof(int32_t));
         o_mkq = carve((size_t)max_batch * (size_t)vocab * sizeof(float));
+        o_mklse = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
+        o_mkzx = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
     }
     void *base = nullptr;
     if (hipMalloc(&base, off) != hipSuccess) {
@@ -215,6 +268,8 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
     ctx->ws.mk_prev = max_rank > 0 ? (int32_t *)(b + o_mkprev) : nullptr;
     ctx->ws.mk_q = max_rank > 0 ? (float *)(b + o_mkq) : nullptr;
+    ctx->ws.mk_lse2 = max_rank > 0 ? (float *)(b + o_mklse) : nullptr;
+    ctx->ws.mk_zx = max_rank > 0 ? (float *)(b + o_mkzx) : nullptr;
     *out = ctx;
     return ok();
 }
@@ -385,40 +440,53 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_log
                            float temperature, uint64_t seed, uint64_t offset, const float *uniforms,
                            int32_t *draft_tokens, float *q_logits, float *lse_q)
 {
-    if (!ctx) return fail(SV_ERR_INVALID, "markov_draft_run: ctx is NULL");
-    if (ctx->max_rank == 0) return fail(SV_ERR_INVALID, "markov_draft_run: context created with max_rank 0");
-    if (R != ctx->max_rank) return fail(SV_ERR_INVALID, "markov_draft_run: R=%d differs from max_rank %d", R, ctx->max_rank);
-    if (B <= 0 || B > ctx->max_batch || gamma < 1 || gamma > ctx->max_gamma)
-        return fail(SV_ERR_INVALID, "markov_draft_run: B=%d or gamma=%d out of range", B, gamma);
-    if (V != ctx->vocab) return fail(SV_ERR_INVALID, "markov_draft_run: V differs from the context's vocab");
-    if (ctx->ntile > svh::kMarkovMaxTiles)
-        return fail(SV_ERR_UNSUPPORTED, "markov_draft_run: V=%lld exceeds the sampler's %d-token limit", (long long)V,
-                    svh::kMarkovMaxTiles * svh::kMarkovTileN);
-    if (!(temperature > 0.0f) || !std::isfinite(temperature))
-        return fail(SV_ERR_INVALID, "markov_draft_run: temperature must be finite and > 0");
-    if (!base_logits || !U || !W || !x0 || !draft_tokens)
-        return fail(SV_ERR_INVALID, "markov_draft_run: base_logits, U, W, x0 and draft_tokens are required");
-    if (!aligned(U, 16) || !aligned(W, 16) || !aligned(base_logits, 2) || (q_logits && !aligned(q_logits, 4)))
-        return fail(SV_ERR_INVALID, "markov_draft_run: U and Wt must be 16-byte aligned, base 2-byte aligned");
+    sv_status st = check_markov_args(ctx, base_logits, U, W, R, x0, B, gamma, V, temperature, draft_tokens,
+                                     "markov_draft_run");
+    if (st != SV_OK) return st;
+    if (q_logits && !aligned(q_logits, 4))
+        return fail(SV_ERR_INVALID, "markov_draft_run: q_logits must be 4-byte aligned");
     DeviceGuard guard(ctx->device);
-    svh::MarkovArgs a;
-    a.base = (const uint16_t *)base_logits;
-    a.U = (const uint16_t *)U;
-    a.W = (const uint16_t *)W;
-    a.R = R;
-    a.x0 = x0;
-    a.B = B;
-    a.gamma = gamma;
-    a.V = V;
-    a.c = (float)(1.4426950408889634 / (double)temperature);
-    a.seed = seed;
-    a.offset = offset;
-    a.uniforms = uniforms;
-    a.draft = draft_tokens;
-    a.q_logits = q_logits;
-    a.lse_q = lse_q;
-    sv_status st = check_launch(svh::launch_markov(ctx, a, stream), "Markov sampler");
+    svh::MarkovArgs a = make_markov_args(base_logits, U, W, R, x0, B, gamma, V, temperature, seed, offset,
+                                         uniforms, draft_tokens, q_logits, lse_q);
+    st = check_launch(svh::launch_markov(ctx, a, stream), "Markov sampler");
     return st != SV_OK ? st : ok();
+}
+
+sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream, const void *base_logits, const void *U,
+                            const void *W, int R, const int32_t *x0, const void *p_logits, sv_dtype p_dtype,
+                            int B, int gamma, int64_t V, float temperature, uint64_t draft_seed,
+                            uint64_t verify_seed, uint64_t offset, int32_t *draft_tokens, int32_t *accepted_len,
+                            int32_t *out_tokens, float *lse_q, const sv_diag *diag)
+{
+    sv_status st = check_markov_args(ctx, base_logits, U, W, R, x0, B, gamma, V, temperature, draft_tokens,
+                                     "markov_verify_run");
+    if (st != SV_OK) return st;
+    if (!p_logits || !accepted_len || !out_tokens)
+        return fail(SV_ERR_INVALID, "markov_verify_run: p_logits, accepted_len and out_tokens are required");
+    if (esize_of(p_dtype) == 0) return fail(SV_ERR_UNSUPPORTED, "markov_verify_run: p dtype must be SV_BF16 or SV_F32");
+    if (!aligned(p_logits, esize_of(p_dtype)))
+        return fail(SV_ERR_INVALID, "markov_verify_run: p_logits must be aligned to its element size");
+    DeviceGuard guard(ctx->device);
+    // 1. the draft: no z rows stored; the sampler records each row's
+    //    log2-sum-exp2 and the drafted tokens' logits
+    svh::MarkovArgs m = make_markov_args(base_logits, U, W, R, x0, B, gamma, V, temperature, draft_seed, offset,
+                                         nullptr, draft_tokens, nullptr, lse_q);
+    m.fused = true;
+    m.lse2_out = ctx->ws.mk_lse2;
+    m.zx_out = ctx->ws.mk_zx;
+    if ((st = check_launch(svh::launch_markov(ctx, m, stream), "Markov sampler")) != SV_OK) return st;
+    // 2. verification of that draft: row statistics of p only, the scan with
+    //    the sampler's q statistics, the correction rows rebuilt, the draw
+    svh::VerifyArgs a = make_args(p_logits, p_dtype, nullptr, SV_F32, draft_tokens, nullptr, B, gamma, V,
+                                  temperature, verify_seed, offset, nullptr, accepted_len, out_tokens, diag, false);
+    a.q_esize = 4;
+    a.q_lse2 = ctx->ws.mk_lse2;
+    a.q_zx = ctx->ws.mk_zx;
+    a.qrec = ctx->ws.mk_q;
+    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
+    if ((st = check_launch(svh::launch_markov_verify_tail(ctx, a, m, stream), "fused verification")) != SV_OK)
+        return st;
+    return ok();
 }
 
 }  // extern "C"

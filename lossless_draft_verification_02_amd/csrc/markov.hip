@@ -105,10 +105,14 @@ __device__ __forceinline__ void load_base(const svh::MarkovArgs &a, int k, int m
     }
 }
 
+// Position k of every request (req == null), or position tau + 1 of each
+// request whose scan ended in a rejection (req != null: the correction rows of
+// the fused draft -> verification path; other requests are skipped).  zout
+// may be null (no z rows stored) and tile_part may be null (no softmax pairs).
 template <int R>
-__global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k, float *__restrict__ zout,
-                                                       int64_t zstride, float2 *__restrict__ tile_part,
-                                                       int ntile, int vec)
+__global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k, const svh::ReqG *__restrict__ req,
+                                                       float *__restrict__ zout, int64_t zstride,
+                                                       float2 *__restrict__ tile_part, int ntile, int vec)
 {
     using TL = TileLayout<R>;
     constexpr int KS = R / 32;
@@ -118,18 +122,26 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
     const int li = lane & 15, lg = lane >> 4;
     const int m = blockIdx.y * MC + 16 * wid + li;   // the lane's request (B operand column)
     const bool wave_on = blockIdx.y * MC + 16 * wid < a.B;
+    int km = k;                                        // the lane's position
+    bool act = m < a.B;
+    if (req && act) {
+        const svh::ReqG r = req[m];
+        act = r.flags == 0 && r.mode == 0;
+        km = r.tau + 1;
+    }
 
     // prologue: first tile's copy, the wavefront's U fragments, first base logits
     int tile = blockIdx.x;
     copy_tile<R>(a, (int64_t)tile * TN, wtile, wid, lane);
     bf16x8 ufr[KS];
     {
-        const uint16_t *urow = a.U + (int64_t)(m < a.B ? prev_token(a, k, m) : 0) * R + 8 * lg;
+        const uint16_t *urow = a.U + (int64_t)(act ? prev_token(a, km, m) : 0) * R + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) ufr[s] = m < a.B ? *(const bf16x8 *)(urow + 32 * s) : bf16x8{};
+        for (int s = 0; s < KS; ++s) ufr[s] = act ? *(const bf16x8 *)(urow + 32 * s) : bf16x8{};
     }
+    const int mb = act ? m : a.B;                      // load_base reads nothing for a.B
     uint2 bv[NVB];
-    load_base(a, k, m, (int64_t)tile * TN, lg, vec, bv);
+    load_base(a, km, mb, (int64_t)tile * TN, lg, vec, bv);
 
     for (int it = 0; tile < ntile; ++it, tile += gridDim.x) {
         unsigned char *buf = wtile + (it & 1) * TL::BYTES;
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
         uint2 bn[NVB];
         if (next < ntile) {
             copy_tile<R>(a, (int64_t)next * TN, wtile + ((it + 1) & 1) * TL::BYTES, wid, lane);
-            load_base(a, k, m, (int64_t)next * TN, lg, vec, bn);
+            load_base(a, km, mb, (int64_t)next * TN, lg, vec, bn);
         }
         if (wave_on) {
             f32x4 acc[NVB];
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
             }
             // epilogue: lane holds z^T[n0 + 16 vb + 4 lg + r][m]
             const int64_t n0 = (int64_t)tile * TN;
-            float *zrow = zout + (int64_t)(m < a.B ? m : 0) * zstride;
+            float *zrow = zout ? zout + (int64_t)(act ? m : 0) * zstride : nullptr;
             float mx = svk::neg_inf();
             bool bad = false;
             float zc[NVB][4];
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
                 z[1] = acc[vb][1] + __uint_as_float(b01 & 0xFFFF0000u);
                 z[2] = acc[vb][2] + __uint_as_float(b23 << 16);
                 z[3] = acc[vb][3] + __uint_as_float(b23 & 0xFFFF0000u);
-                if (m < a.B) {
+                if (zrow && act) {
                     if (vec) {
                         if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
                     } else {
@@ -200,7 +212,7 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
             if (bad) sm = __builtin_nanf("");   // a NaN entry poisons the row; the draw flags it
             sm += __shfl_xor(sm, 16, 64);
             sm += __shfl_xor(sm, 32, 64);
-            if (lg == 0 && m < a.B) tile_part[(int64_t)m * ntile + tile] = make_float2(mx, sm);
+            if (tile_part && lg == 0 && m < a.B) tile_part[(int64_t)m * ntile + tile] = make_float2(mx, sm);
         }
         if (next < ntile) {
 #pragma unroll
@@ -225,16 +237,24 @@ __device__ __forceinline__ int wave_max_i(int v)
     return v;
 }
 
-__global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArgs a, int k,
-                                                                  const float *__restrict__ zin, int64_t zstride,
-                                                                  const float2 *__restrict__ tile_part, int ntile,
-                                                                  uint32_t *__restrict__ errword)
+// State of one request's draw after the tile choice.
+struct SelState {
+    int32_t xprev;     // token sampled at the previous position (valid)
+    float lse2;        // row log2-sum-exp2 of z * c
+    float tf;          // fp32(u * fp32(Z)), Z the fp64 sum of the tile masses
+    double tbase;      // cumulative mass before the chosen tile
+    int ts;            // chosen tile
+    int fallback;      // no cumulative mass exceeded tf: take the last positive token
+};
+
+// Tile choice for request b by one wavefront: merge the tile pairs into the
+// row's log-sum-exp, fp64 prefix of the tile masses, the tile holding u * Z.
+// Returns false when the request is finished (error outputs written).
+__device__ bool select_tile(const svh::MarkovArgs &a, int k, const float2 *__restrict__ tile_part, int ntile,
+                            uint32_t *__restrict__ errword, int b, SelState &st)
 {
     const int lane = threadIdx.x & 63;
-    const int b = blockIdx.x * kSelWaves + (int)(threadIdx.x >> 6);
-    if (b >= a.B) return;   // whole wavefront; nothing below synchronises the workgroup
     const int64_t out = (int64_t)b * a.gamma + (k - 1);
-
     // independent loads first: the previous token and this lane's run of tile pairs
     const int32_t xprev = k == 1 ? a.x0[b] : a.draft[(int64_t)b * a.gamma + (k - 2)];
     const float2 *tp = tile_part + (int64_t)b * ntile;
@@ -252,7 +272,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArg
             if (a.lse_q) a.lse_q[out] = __builtin_nanf("");
             atomicOr(errword, SV_FLAG_BAD_TOKEN);
         }
-        return;
+        return false;
     }
 
     // row log-sum-exp2 from the tile pairs
@@ -268,7 +288,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArg
             if (a.lse_q) a.lse_q[out] = __builtin_nanf("");
             atomicOr(errword, SV_FLAG_BAD_ROW);
         }
-        return;
+        return false;
     }
 
     // tile masses, fp64 prefix over the lanes' contiguous runs
@@ -305,42 +325,131 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArg
             if (a.lse_q) a.lse_q[out] = lse2 * svk::kLn2;
             atomicOr(errword, SV_FLAG_BAD_ROW);
         }
-        return;
+        return false;
     }
     // cumulative mass before tile ts, from the lane that owns it
     double before_ts = excl;
 #pragma unroll
     for (int q = 0; q < kSelTilesPerLane; ++q)
         if (q < per && t0 + q < ts) before_ts += (double)wt[q];
-    const double tbase = __shfl(before_ts, ts / per, 64);
+    st.xprev = xprev;
+    st.lse2 = lse2;
+    st.tf = tf;
+    st.tbase = __shfl(before_ts, ts / per, 64);
+    st.ts = ts;
+    st.fallback = fallback;
+    return true;
+}
 
-    // inside the tile: lane owns columns 2 lane, 2 lane + 1
-    const int64_t c0 = (int64_t)ts * TN;
+// Token of the chosen tile (z values zr[0 .. 128)) by one wavefront: lane
+// owns columns 2 lane, 2 lane + 1; fp64 prefix; outputs.
+__device__ void select_token_in_tile(const svh::MarkovArgs &a, int k, int b, const SelState &st,
+                                     const float *zr, uint32_t *__restrict__ errword)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t out = (int64_t)b * a.gamma + (k - 1);
+    const int64_t c0 = (int64_t)st.ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
-    const float *zr = zin + (int64_t)b * zstride + c0;
     const int j0 = 2 * lane, j1 = 2 * lane + 1;
-    const float w0 = j0 < ncols ? svk::fast_exp2(zr[j0] * a.c - lse2) : 0.0f;
-    const float w1 = j1 < ncols ? svk::fast_exp2(zr[j1] * a.c - lse2) : 0.0f;
+    const float w0 = j0 < ncols ? svk::fast_exp2(zr[j0] * a.c - st.lse2) : 0.0f;
+    const float w1 = j1 < ncols ? svk::fast_exp2(zr[j1] * a.c - st.lse2) : 0.0f;
     const double pair = (double)w0 + (double)w1;
     const double pincl = svk::wave_inclusive_scan_d(pair);
     const double pexcl = pincl - pair;
     int yb = 0x7FFFFFFF, yl = -1;
     if (w1 > 0.0f) {
         yl = j1;
-        if (!fallback && (float)(tbase + pexcl + (double)w0 + (double)w1) > tf) yb = j1;
+        if (!st.fallback && (float)(st.tbase + pexcl + (double)w0 + (double)w1) > st.tf) yb = j1;
     }
     if (w0 > 0.0f) {
         if (yl < 0) yl = j0;
-        if (!fallback && (float)(tbase + pexcl + (double)w0) > tf) yb = j0;
+        if (!st.fallback && (float)(st.tbase + pexcl + (double)w0) > st.tf) yb = j0;
     }
     const int ybest = wave_min_i(yb);
     const int ylast = wave_max_i(yl);
     if (lane == 0) {
         const int j = ybest != 0x7FFFFFFF ? ybest : ylast;
         a.draft[out] = j >= 0 ? (int32_t)(c0 + j) : -1;
-        if (a.lse_q) a.lse_q[out] = lse2 * svk::kLn2;
+        if (a.lse_q) a.lse_q[out] = st.lse2 * svk::kLn2;
+        if (a.lse2_out) a.lse2_out[out] = st.lse2;
+        if (a.zx_out) a.zx_out[out] = j >= 0 ? zr[j] : __builtin_nanf("");
         if (j < 0) atomicOr(errword, SV_FLAG_BAD_ROW);
     }
+}
+
+// The draw with stored z rows: one wavefront per request, no barriers.
+__global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArgs a, int k,
+                                                                  const float *__restrict__ zin, int64_t zstride,
+                                                                  const float2 *__restrict__ tile_part, int ntile,
+                                                                  uint32_t *__restrict__ errword)
+{
+    const int b = blockIdx.x * kSelWaves + (int)(threadIdx.x >> 6);
+    if (b >= a.B) return;   // whole wavefront; nothing below synchronises the workgroup
+    SelState st;
+    if (!select_tile(a, k, tile_part, ntile, errword, b, st)) return;
+    select_token_in_tile(a, k, b, st, zin + (int64_t)b * zstride + (int64_t)st.ts * TN, errword);
+}
+
+// The draw without stored z rows (fused path): one workgroup of 4 wavefronts
+// per request.  Wavefront 0 chooses the tile; all four rebuild its 128 logits
+// (two 16-row blocks each, every load issued before the MFMAs) with the
+// contraction's own arithmetic -- same A rows, same k order, same base add --
+// so they equal, bit for bit, the values reduced into the tile pairs;
+// wavefront 0 then draws the token.
+template <int R>
+__global__ __launch_bounds__(256) void k_markov_select_fused(svh::MarkovArgs a, int k,
+                                                            const float2 *__restrict__ tile_part, int ntile,
+                                                            uint32_t *__restrict__ errword)
+{
+    constexpr int KS = R / 32;
+    constexpr int VBW = NVB / 4;   // 16-row blocks per wavefront
+    __shared__ SelState st;
+    __shared__ int go;
+    __shared__ float zt[TN];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (wid == 0) {
+        SelState s0;
+        const bool ok = select_tile(a, k, tile_part, ntile, errword, b, s0);
+        if (lane == 0) {
+            go = ok;
+            if (ok) st = s0;
+        }
+    }
+    __syncthreads();
+    if (!go) return;
+    const int64_t c0 = (int64_t)st.ts * TN;
+    const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
+    const int li = lane & 15, lg = lane >> 4;
+    const uint16_t *urow = a.U + (int64_t)st.xprev * R + 8 * lg;   // the request's U row in every B column
+    bf16x8 ufr[KS], afr[VBW][KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) ufr[s] = *(const bf16x8 *)(urow + 32 * s);
+#pragma unroll
+    for (int v = 0; v < VBW; ++v) {
+        const int64_t n = c0 + 16 * (VBW * wid + v) + li;
+        const uint16_t *wrow = a.W + (n < a.V ? n : a.V - 1) * R + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) afr[v][s] = *(const bf16x8 *)(wrow + 32 * s);
+    }
+    const uint16_t *brow = a.base + ((int64_t)b * a.gamma + (k - 1)) * a.V + c0;
+#pragma unroll
+    for (int v = 0; v < VBW; ++v) {
+        const int vb = VBW * wid + v;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[v][s], ufr[s], acc, 0, 0, 0);
+        if (li == 0) {   // D[4 lg + r][0]: vocabulary row 16 vb + 4 lg + r of the tile
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int col = 16 * vb + 4 * lg + r;
+                const uint32_t bits = col < ncols ? (uint32_t)brow[col] : 0xFF80u;
+                zt[col] = acc[r] + __uint_as_float(bits << 16);
+            }
+        }
+    }
+    svk::lds_barrier();
+    if (wid == 0) select_token_in_tile(a, k, b, st, zt, errword);
 }
 
 template <int R>
@@ -358,23 +467,56 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
     const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0) &&
                     ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
     for (int k = 1; k <= a.gamma; ++k) {
-        float *zk = a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q;
+        float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        hipLaunchKernelGGL((k_markov_gemm<R>), dim3(gx, gy), dim3(NT), 0, s, a, k, zk, zstride, ctx->ws.mk_part,
-                           ntile, vec);
+        hipLaunchKernelGGL((k_markov_gemm<R>), dim3(gx, gy), dim3(NT), 0, s, a, k, (const svh::ReqG *)nullptr, zk,
+                           zstride, ctx->ws.mk_part, ntile, vec);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
-        hipLaunchKernelGGL(k_markov_select, dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0, s,
-                           a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,
-                           ctx->ws.errword);
+        if (a.fused)
+            hipLaunchKernelGGL((k_markov_select_fused<R>), dim3(a.B), dim3(256), 0, s, a, k,
+                               (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword);
+        else
+            hipLaunchKernelGGL(k_markov_select, dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0,
+                               s, a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,
+                               ctx->ws.errword);
         svh::prof_end(ctx, s, slot);
     }
+    return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_rebuild(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::ReqG *req, float *qrec, hipStream_t s)
+{
+    const int ntile = ctx->ntile;
+    const int gy = (a.B + MC - 1) / MC;
+    const size_t lds = 2 * (size_t)TileLayout<R>::BYTES;
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+    int gx = ctx->num_cu * per_cu / gy;
+    gx = gx < 1 ? 1 : (gx > ntile ? ntile : gx);
+    const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0) && ((((uintptr_t)qrec) & 15) == 0);
+    const int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_REBUILD);
+    hipLaunchKernelGGL((k_markov_gemm<R>), dim3(gx, gy), dim3(NT), 0, s, a, 0, req, qrec, a.V, (float2 *)nullptr,
+                       ntile, vec);
+    svh::prof_end(ctx, s, slot);
     return hipGetLastError();
 }
 
 }  // namespace
 
 namespace svh {
+
+hipError_t launch_markov_recompute(sv_ctx *ctx, const MarkovArgs &a, const ReqG *req, float *qrec, hipStream_t s)
+{
+    if (a.B <= 0 || a.gamma <= 0) return hipSuccess;
+    switch (a.R) {
+    case 32: return launch_rebuild<32>(ctx, a, req, qrec, s);
+    case 64: return launch_rebuild<64>(ctx, a, req, qrec, s);
+    case 128: return launch_rebuild<128>(ctx, a, req, qrec, s);
+    case 256: return launch_rebuild<256>(ctx, a, req, qrec, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s)
 {

@@ -284,7 +284,8 @@ namespace svh {
 
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 {
-    const int64_t rows = (int64_t)a.nb * (a.gamma + 1) + (int64_t)a.nb * a.gamma;
+    // p rows, then q rows unless the q statistics come from the Markov sampler
+    const int64_t rows = (int64_t)a.nb * (a.gamma + 1) + (a.q_lse2 ? 0 : (int64_t)a.nb * a.gamma);
     const int64_t grid = rows * ctx->nch1;
     if (grid <= 0) return hipSuccess;
     const int slot = prof_begin(ctx, s, SV_KERNEL_ROWSTATS);

@@ -59,7 +59,9 @@ struct Workspace {
     float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials
     int32_t *mk_prev;    // [max_batch] Markov: token sampled at the previous position
     float *mk_q;         // [max_batch * V] Markov logits of the current position when
-                         // the caller does not keep them
+                         // the caller does not keep them; fused path: rebuilt correction rows
+    float *mk_lse2;      // [max_batch * max_gamma] fused path: draft row log2-sum-exp2
+    float *mk_zx;        // [max_batch * max_gamma] fused path: drafted tokens' logits
     void *base;          // single allocation backing all of the above
     size_t bytes;
 };
@@ -126,6 +128,25 @@ struct VerifyArgs {
     int32_t *out_tokens;
     sv_diag diag;         // device pointers, each may be null
     bool block;           // block verification
+    // Draft rows that were never materialised (the fused Markov path): the
+    // sampler's per-row log2-sum-exp2 of z * c and the drafted tokens' raw
+    // logits replace the q row statistics, and qrec [B, V] fp32 holds the one
+    // correction row per request that the residual needs (row b, rebuilt
+    // after the acceptance scan).  All null otherwise.
+    const float *q_lse2;  // [B, gamma]
+    const float *q_zx;    // [B, gamma]
+    const float *qrec;    // [B, V]
+};
+
+// Per-request result of the acceptance scan, read by the kernels that follow.
+struct ReqG {
+    uint32_t flags;
+    int32_t L;
+    int32_t tau;
+    int32_t mode;      // 0: residual weights max(wmul * p - q, 0), 1: bonus weights p
+    float wmul;        // multiplier of p in the residual weights (w_tau; 1 for the token rule)
+    float lp2, lq2;    // log2-sum-exp2 of p row tau+1 and q row tau+1
+    float u2;          // correction / bonus uniform
 };
 
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
@@ -135,6 +156,7 @@ hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 // thresholds -> chunk sums -> select.
 hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 constexpr size_t kReqStateBytes = 32;
+static_assert(sizeof(ReqG) == kReqStateBytes, "request state layout");
 hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, float sps_a,
                            float sps_k, int32_t *verify_len, double *expected, hipStream_t s);
 
@@ -152,8 +174,22 @@ struct MarkovArgs {
     int32_t *draft;
     float *q_logits;       // may be null
     float *lse_q;          // may be null
+    // Fused draft -> verification: no z row is stored; the draw rebuilds the
+    // 128 logits of its chosen tile with the same MFMA sequence, and records
+    // per (request, position) the row's log2-sum-exp2 of z * c and the drawn
+    // token's raw logit.
+    bool fused;
+    float *lse2_out;       // [B, gamma] (fused)
+    float *zx_out;         // [B, gamma] (fused)
 };
 
 hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s);
+// Rebuilds, for every request whose scan ended in a rejection (req[b].mode ==
+// 0, no flags), the draft logits z of position tau + 1 into qrec + b * V.
+hipError_t launch_markov_recompute(sv_ctx *ctx, const MarkovArgs &a, const ReqG *req, float *qrec, hipStream_t s);
+// Fused Markov draft -> verification after the p row statistics: the
+// acceptance scan (token rule, q statistics from the sampler), the correction
+// rows rebuilt, then the correction / bonus draw.
+hipError_t launch_markov_verify_tail(sv_ctx *ctx, const VerifyArgs &a, const MarkovArgs &m, hipStream_t s);
 
 }  // namespace svh

@@ -46,19 +46,20 @@ constexpr int SEG = svh::kSegR;
 constexpr int MAXG = svh::kMaxGamma;
 constexpr double kLn2d = 0.69314718055994530942;
 
-enum Stage { STAGE_TOKEN = 0, STAGE_BLOCK_PRE = 1, STAGE_BLOCK_FINAL = 2 };
+// STAGE_FROM_REQ: the fused tail starts from the request state k_accept
+// stored (the fused Markov path rebuilds the correction rows in between).
+enum Stage { STAGE_TOKEN = 0, STAGE_BLOCK_PRE = 1, STAGE_BLOCK_FINAL = 2, STAGE_FROM_REQ = 3 };
 
-// Per-request result of k_accept, read by the kernels that follow.
-struct ReqG {
-    uint32_t flags;
-    int32_t L;
-    int32_t tau;
-    int32_t mode;      // 0: residual weights max(wmul * p - q, 0), 1: bonus weights p
-    float wmul;        // multiplier of p in the residual weights (w_tau; 1 for the token rule)
-    float lp2, lq2;    // log2-sum-exp2 of p row tau+1 and q row tau+1
-    float u2;          // correction / bonus uniform
-};
-static_assert(sizeof(ReqG) == svh::kReqStateBytes, "request state layout");
+// The q row of request b's correction draw (position tau + 1): a row of the
+// caller's q, or the rebuilt row b of qrec on the fused Markov path.
+template <int QES>
+__device__ __forceinline__ const char *correction_qrow(const svh::VerifyArgs &a, int b, int tau)
+{
+    if (a.qrec) return (const char *)(a.qrec + (int64_t)b * a.V);
+    return (const char *)a.q + ((int64_t)b * a.gamma + tau) * a.V * QES;
+}
+
+using svh::ReqG;
 
 // log2 sum exp2 of a row from its chunk partials (fp64 result); flags a bad row.
 // M = max m_k, S = sum s_k exp2(m_k - M), the partials loaded kMergeBatch at a
@@ -167,13 +168,23 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
     float gp = 0.0f, gq = 0.0f;
     if (has_tok) {
         gp = svk::load_logit<PES>(a.p, (prow0 + lane) * a.V + xs);
-        gq = svk::load_logit<QES>(a.q, ((int64_t)b * gamma + lane) * a.V + xs);
+        gq = a.q_zx ? a.q_zx[(int64_t)b * gamma + lane]   // the sampler's logit of the drafted token
+                    : svk::load_logit<QES>(a.q, ((int64_t)b * gamma + lane) * a.V + xs);
     }
     // row statistics of every row the request may verify (rows beyond the
     // verify length hold stale values and are not used)
     bool bad_p = false, bad_q = false, bad_p64 = false;
     const double lp = lane <= gamma ? merge_row(part, prow0 + lane, nch1, bad_p) : 0.0;
-    const double lq = has_tok ? merge_row(part, qrow0 + lane, nch1, bad_q) : 0.0;
+    double lq = 0.0;
+    if (has_tok) {
+        if (a.q_lse2) {   // the sampler's log2-sum-exp2 of the draft row
+            const float l = a.q_lse2[(int64_t)b * gamma + lane];
+            bad_q = !(l == l) || l == svk::pos_inf() || l == svk::neg_inf();
+            lq = (double)l;
+        } else {
+            lq = merge_row(part, qrow0 + lane, nch1, bad_q);
+        }
+    }
     const double lp64 = (gamma == svk::kWave && lane == 0) ? merge_row(part, prow0 + svk::kWave, nch1, bad_p64) : 0.0;
     float u = 1.0f;
     if (has_tok && stage != STAGE_BLOCK_PRE)
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(NT) void k_resid_sum(svh::VerifyArgs a, const ReqG 
     if (r.flags || sums_from_pass2(a, r) || sidx >= nseg) return;
     const int G1 = a.gamma + 1;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
-    const char *qrow = r.mode ? nullptr : (const char *)a.q + ((int64_t)b * a.gamma + r.tau) * a.V * QES;
+    const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
     const int64_t s0 = (int64_t)sidx * SEG;
     const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
     const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
@@ -702,7 +713,7 @@ __global__ __launch_bounds__(NT) void k_select(svh::VerifyArgs a, const ReqG *__
     const int G1 = gamma + 1;
     if ((int)threadIdx.x < r.tau) xs[threadIdx.x] = a.draft[(int64_t)b * gamma + threadIdx.x];
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
-    const char *qrow = r.mode ? nullptr : (const char *)a.q + ((int64_t)b * gamma + r.tau) * a.V * QES;
+    const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
     float *own = csum + (int64_t)b * nseg;
     const float *sums = sums_from_pass2(a, r) ? bm + ((int64_t)b * gamma + r.tau) * nseg : own;
 
@@ -863,15 +874,21 @@ __global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, const float2
     __shared__ float segsum[kTailMaxSeg];
     __shared__ SelectShared sh;
     const int b = a.b0 + (int)blockIdx.x;
-    if (threadIdx.x < svk::kWave)
+    if (stage == STAGE_FROM_REQ) {
+        // k_accept already evaluated the request (and wrote the outputs of a
+        // request with a data error)
+        if (threadIdx.x == 0) r = pre[b];
+        if ((int)threadIdx.x < a.gamma) as.x[threadIdx.x] = a.draft[(int64_t)b * a.gamma + threadIdx.x];
+    } else if (threadIdx.x < svk::kWave) {
         accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, pre + b, &r, lp2g, lq2g, wrun, errword, as);
+    }
     __syncthreads();
-    if (r.flags) return;   // accept_eval wrote the request's error outputs
+    if (r.flags) return;   // the request's error outputs are written
     const int gamma = a.gamma;
     const int G1 = gamma + 1;
     const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
-    const char *qrow = r.mode ? nullptr : (const char *)a.q + ((int64_t)b * gamma + r.tau) * a.V * QES;
+    const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
 
     const float *sums = segsum;
     if (sums_from_pass2(a, r)) {
@@ -984,9 +1001,28 @@ hipError_t block_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int PES>
+hipError_t markov_verify_tail(sv_ctx *ctx, const svh::VerifyArgs &a, const svh::MarkovArgs &m, hipStream_t s)
+{
+    launch_accept<PES, 4>(ctx, a, s, STAGE_TOKEN);
+    hipError_t e = svh::launch_markov_recompute(ctx, m, (const ReqG *)ctx->ws.req, ctx->ws.mk_q, s);
+    if (e != hipSuccess) return e;
+    if (SV_FUSED_TAIL && ctx->nseg <= kTailMaxSeg)
+        launch_fused_tail<PES, 4>(ctx, a, s, STAGE_FROM_REQ);
+    else
+        launch_sum_and_select<PES, 4>(ctx, a, s);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 namespace svh {
+
+hipError_t launch_markov_verify_tail(sv_ctx *ctx, const VerifyArgs &a, const MarkovArgs &m, hipStream_t s)
+{
+    if (a.nb <= 0) return hipSuccess;
+    return a.p_esize == 2 ? markov_verify_tail<2>(ctx, a, m, s) : markov_verify_tail<4>(ctx, a, m, s);
+}
 
 hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 {

@@ -415,6 +415,66 @@ def test_markov_zero_transition_is_independent():
     assert torch.equal(ql, mi.base.float())
 
 
+# ------------------------------------- fused Markov draft -> verification --
+
+def gpu_markov_verify(ctx, mi, seed_d=WL.DRAFT_SEED, seed_v=WL.VERIFY_SEED, offset=0):
+    B, gamma, V = mi.base.shape
+    d = torch.full((B, gamma), -7, dtype=torch.int32, device="cuda")
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((B, gamma + 1), -7, dtype=torch.int32, device="cuda")
+    lse = torch.empty(B, gamma, device="cuda")
+    diag = dict(lse_p=torch.empty(B, gamma + 1, device="cuda"), lse_q=torch.empty(B, gamma, device="cuda"),
+                ratio=torch.empty(B, gamma, device="cuda"), resid_mass=torch.empty(B, device="cuda"),
+                flags=torch.zeros(B, dtype=torch.int32, device="cuda"))
+    L.markov_verify_run(ctx, mi.base, mi.U, mi.Wt, mi.x0, mi.p, d, acc, out, lse_q=lse, temperature=mi.T,
+                        draft_seed=seed_d, verify_seed=seed_v, offset=offset, diag=diag)
+    torch.cuda.synchronize()
+    res = dict(accepted_len=acc.cpu().numpy(), out_tokens=out.cpu().numpy())
+    for k, v in diag.items():
+        res[k] = v.cpu().numpy()
+    res["flags"] = res["flags"].astype(np.uint32)
+    return d, lse, res
+
+
+def check_markov_verify(ctx, mi, req, label):
+    """Fused path against (a) the unfused GPU sampler, bit for bit on the
+    draft, and (b) the oracle's draft followed by the oracle's verification."""
+    d, lse, res = gpu_markov_verify(ctx, mi)
+    d2, _, lse2 = gpu_markov(ctx, mi, want_q=True)
+    assert torch.equal(d, d2), "fused and unfused samplers drew different drafts"
+    assert torch.equal(lse, lse2), "fused and unfused samplers report different normalisers"
+    o = oracle_markov(mi, req)
+    rep = compare_markov(d.cpu().numpy()[req], lse.cpu().numpy()[req], None, o)
+    _say(f"[{label} draft] {rep}")
+    assert rep.ok(), str(rep)
+    same = [i for i, b in enumerate(req) if np.array_equal(o.draft[i], d.cpu().numpy()[b])]
+    ov = oracle.token_verify(_np64(mi.p[torch.as_tensor(req, device="cuda")]), o.q_logits, o.draft, mi.gamma,
+                             temperature=mi.T, seed=WL.VERIFY_SEED, req_ids=np.asarray(req, np.int32))
+    keep = np.array(same, dtype=np.int64)
+    sub = {k: v[np.asarray(req)][keep] for k, v in res.items()}
+    rep2 = compare_verify(sub, type(ov)(*[getattr(ov, f)[keep] for f in ov.__dataclass_fields__]), mi.gamma)
+    _say(f"[{label} verify] {rep2} over {len(keep)} of {len(req)} requests")
+    assert rep2.ok(), str(rep2)
+    assert rep2.flips <= max(1, 0.02 * rep2.requests), str(rep2)
+    assert len(keep) >= 0.9 * len(req)
+
+
+@pytest.mark.parametrize("B,gamma,V,R,std", [(16, 8, 20000, 256, 0.25), (130, 3, 4999, 256, 0.25),
+                                             (24, 5, 9001, 64, 0.25), (8, 4, 5000, 256, 0.02)])
+def test_markov_verify_fused_small(B, gamma, V, R, std):
+    _say(f"case: fused Markov -> verify B={B} gamma={gamma} V={V} R={R} std={std}")
+    mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=std)
+    with make_ctx(B, gamma, V, R) as ctx:
+        check_markov_verify(ctx, mi, list(range(B)), f"fused B={B} V={V} R={R}")
+
+
+def test_markov_verify_fused_workload4_sampled():
+    _say("case: workload 4 full size, fused Markov -> verify")
+    mi = WL.make_markov_inputs("cuda")
+    with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
+        check_markov_verify(ctx, mi, _sample(mi.B, 3, 14), "fused w4")
+
+
 # ------------------------------------------ full sizes, sampled requests --
 
 def _sample(B, n, seed):
