@@ -269,7 +269,8 @@ void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t 
         const int64_t cap = (int64_t)svh::kRowstatsCompactWGsPerCU * ctx->num_cu;
         const int64_t grid = items < cap ? items : cap;
         const size_t lds = (size_t)(2 * a.nb + 1) * sizeof(int);
-        hipLaunchKernelGGL((k_rowstats_compact<PES, QES, NB>), dim3((unsigned)grid), dim3(svh::kRowstatsThreads), lds,
+        hipLaunchKernelGGL((k_rowstats_compact<PES, QES, svh::kRowstatsCompactNB>), dim3((unsigned)grid),
+                           dim3(svh::kRowstatsThreads), lds,
                            s, a.p, a.q, a.verify_len, a.B, a.gamma, a.b0, a.nb, a.V, ctx->nch1, ctx->chunk1, a.c,
                            ctx->ws.part);
     } else {

@@ -28,7 +28,14 @@ namespace svh {
 constexpr int kRowstatsThreads = SV_ROWSTATS_THREADS;
 constexpr int kTargetChunk1 = SV_ROWSTATS_CHUNK;
 constexpr int kRowstatsNB = SV_ROWSTATS_NB;   // 16-byte loads in flight per thread
-constexpr int kRowstatsCompactWGsPerCU = 4;   // grid of the verify-length (compacted) variant, per CU
+#ifndef SV_ROWSTATS_COMPACT_WGS
+#define SV_ROWSTATS_COMPACT_WGS 4
+#endif
+#ifndef SV_ROWSTATS_COMPACT_NB
+#define SV_ROWSTATS_COMPACT_NB 4
+#endif
+constexpr int kRowstatsCompactWGsPerCU = SV_ROWSTATS_COMPACT_WGS;   // grid of the compacted variant, per CU
+constexpr int kRowstatsCompactNB = SV_ROWSTATS_COMPACT_NB;          // its 16-byte loads in flight per thread
 constexpr int kRowstatsCompactMaxReq = 8192;  // requests per call it lays out in LDS (64 KB)
 // Correction / bonus weights and block pass 2: each wavefront sums one
 // segment of kSegR elements; a workgroup covers kSegPerWG segments.

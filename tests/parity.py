@@ -15,7 +15,12 @@ import numpy as np
 MARGIN = 1e-4
 PROB_ATOL = 1e-5
 LSE_ATOL, LSE_RTOL = 1e-5, 1e-6
-
+# Absolute precision of the GPU's running ratios w_i and residual masses m_i:
+# w is a product of ratios of fp32-normalised probabilities (~1e-7 relative
+# each); m = sum max(w p - q, 0) carries the fp32 rounding of every weight it
+# sums (~1e-7 of sum(w p + q) <= 2) plus its fp32 segment sums.  1e-6 bounds
+# both with room to spare.
+WM_ABS_EPS = 1e-6
 
 @dataclass
 class Report:
@@ -32,6 +37,30 @@ class Report:
         return (f"requests={self.requests} flips={self.flips} failures={len(self.failures)} "
                 f"max_prob_err={self.max_prob_err:.2e} max_lse_err={self.max_lse_err:.2e} "
                 f"{self.failures[:5]}")
+
+
+def _close_threshold(rep, g, o, w, what, b):
+    """Block thresholds h = m / (m + 1 - w).  With D = m + 1 - w,
+    dh/dm = (1 - h)^2 / (1 - w) and dh/dw = h (1 - h) / (1 - w), so absolute
+    errors eps in m and w move h by at most eps (1 - h) / (1 - w) to first
+    order -- more than the flat probability tolerance when 1 - w is small.
+    The bound used is PROB_ATOL plus that propagated error."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    w = np.asarray(w, np.float64)
+    m = ~np.isnan(o)
+    if not m.any():
+        return
+    if np.isnan(g[m]).any():
+        rep.failures.append((b, what, "nan on the GPU"))
+        return
+    err = np.abs(g[m] - o[m])
+    # w = 1 exactly gives h = 1 whatever m is: the bound then vanishes
+    tol = PROB_ATOL + WM_ABS_EPS * np.abs(1.0 - o[m]) / np.maximum(1.0 - w[m], 1e-12)
+    rep.max_prob_err = max(rep.max_prob_err, float(err.max()))
+    if (err > tol).any():
+        i = int(np.argmax(err - tol))
+        rep.failures.append((b, what, float(err[i]), float(tol[i])))
 
 
 def _close_prob(rep, g, o, what, b):
@@ -125,7 +154,7 @@ def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = Fa
         if block and "w" in gpu and L > 0:
             _close_prob(rep, gpu["w"][b, :L], orc.w[b, :L], "w", b)
         if block and "h" in gpu and L > 0:
-            _close_prob(rep, gpu["h"][b, :L], orc.h[b, :L], "h", b)
+            _close_threshold(rep, gpu["h"][b, :L], orc.h[b, :L], orc.w[b, :L], "h", b)
         if "resid_mass" in gpu:
             _close_prob(rep, [gpu["resid_mass"][b]], [orc.resid_mass[b]], "resid_mass", b)
         if "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):

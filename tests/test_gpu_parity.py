@@ -415,6 +415,45 @@ def test_markov_zero_transition_is_independent():
     assert torch.equal(ql, mi.base.float())
 
 
+# ------------------------------------------- launch shapes and edge sizes --
+
+def test_more_requests_than_compute_units():
+    """B above the CU count: the fused tail runs two 512-thread workgroups per
+    CU instead of one 1024-thread workgroup."""
+    B, gamma, V = 300, 3, 4000
+    _say(f"case: B={B} > CUs, token and block")
+    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vl = np.array([(7 * b) % (gamma + 1) for b in range(B)], np.int32)
+    with make_ctx(B, gamma, V) as ctx:
+        check_verify(ctx, vi, label="B=300 token")
+        check_verify(ctx, vi, block=True, verify_len=vl, label="B=300 block")
+
+
+def test_one_draft_position():
+    """gamma = 1 everywhere: token, block (L in {0, 1}) and the fused Markov path."""
+    B, gamma, V = 24, 1, 7001
+    _say("case: gamma = 1")
+    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vl = np.array([b % 2 for b in range(B)], np.int32)
+    with make_ctx(B, gamma, V) as ctx:
+        check_verify(ctx, vi, label="gamma=1 token")
+        check_verify(ctx, vi, block=True, verify_len=vl, label="gamma=1 block")
+    mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, uw_std=0.25)
+    with make_ctx(B, gamma, V, mi.R) as ctx:
+        check_markov_verify(ctx, mi, list(range(B)), "fused gamma=1")
+
+
+def test_compacted_row_statistics_beyond_lds_layout():
+    """More requests than the compacted row-statistics kernel lays out in LDS
+    (8192): the per-item kernel with in-kernel length checks runs instead."""
+    B, gamma, V = 8300, 1, 256
+    _say(f"case: B={B} with verify lengths")
+    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V, row_block=4096)
+    vl = np.array([(b * 5) % (gamma + 1) for b in range(B)], np.int32)
+    with make_ctx(B, gamma, V) as ctx:
+        check_verify(ctx, vi, req=_sample(B, 300, 21), verify_len=vl, label="B=8300 verify_len")
+
+
 # ------------------------------------- fused Markov draft -> verification --
 
 def gpu_markov_verify(ctx, mi, seed_d=WL.DRAFT_SEED, seed_v=WL.VERIFY_SEED, offset=0):
@@ -459,11 +498,14 @@ def check_markov_verify(ctx, mi, req, label):
     assert len(keep) >= 0.9 * len(req)
 
 
-@pytest.mark.parametrize("B,gamma,V,R,std", [(16, 8, 20000, 256, 0.25), (130, 3, 4999, 256, 0.25),
-                                             (24, 5, 9001, 64, 0.25), (8, 4, 5000, 256, 0.02)])
-def test_markov_verify_fused_small(B, gamma, V, R, std):
-    _say(f"case: fused Markov -> verify B={B} gamma={gamma} V={V} R={R} std={std}")
+@pytest.mark.parametrize("B,gamma,V,R,std,p32", [(16, 8, 20000, 256, 0.25, False), (130, 3, 4999, 256, 0.25, False),
+                                                 (24, 5, 9001, 64, 0.25, False), (8, 4, 5000, 256, 0.02, False),
+                                                 (12, 6, 6007, 128, 0.25, True)])
+def test_markov_verify_fused_small(B, gamma, V, R, std, p32):
+    _say(f"case: fused Markov -> verify B={B} gamma={gamma} V={V} R={R} std={std} p fp32={p32}")
     mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=std)
+    if p32:
+        mi.p = mi.p.float()
     with make_ctx(B, gamma, V, R) as ctx:
         check_markov_verify(ctx, mi, list(range(B)), f"fused B={B} V={V} R={R}")
 
