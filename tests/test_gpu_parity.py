@@ -310,6 +310,40 @@ def test_scheduler_matches_oracle(B, gamma, K):
         assert abs(ex - oex) <= 1e-9 * oex
 
 
+@pytest.mark.parametrize("B,gamma,K", [(300, 8, 4096.0), (1000, 4, 800.0), (2048, 4, 4096.0)])
+def test_scheduler_exact_ties(B, gamma, K):
+    """Confidences in {1/4, 1/2, 3/4, 1}: survival products are exact dyadic
+    rationals, so large groups of candidates tie across requests and across
+    the rank kernel's 256-candidate blocks; the admitted set then depends on
+    the order (survival descending, candidate id ascending) alone."""
+    _say(f"case: scheduler exact ties B={B} gamma={gamma} K={K}")
+    g = torch.Generator("cuda").manual_seed(7 * B + gamma)
+    conf = (torch.randint(1, 5, (B, gamma), generator=g, device="cuda").float() / 4.0).contiguous()
+    with make_ctx(B, gamma, 10) as ctx:
+        vl, ex = gpu_schedule(ctx, conf, sps_k=K)
+    ovl, oex, margin = _oracle_schedule(conf, sps_k=K)
+    _say(f"  mean verify_len={vl.mean():.3f} E={ex:.3f} stop margin={margin:.3e}")
+    assert np.array_equal(vl, ovl)
+    assert abs(ex - oex) <= 1e-9 * oex
+
+
+def test_scheduler_clamps_invalid_confidences():
+    """NaN and values outside [0, 1] are clamped (NaN to 0) on the device; the
+    oracle, which rejects them, is run on the clamped values."""
+    B, gamma = 64, 6
+    g = torch.Generator("cuda").manual_seed(5)
+    conf = torch.rand(B, gamma, generator=g, device="cuda")
+    conf[3, 2] = float("nan")
+    conf[5, 0] = -0.5
+    conf[7, 4] = 1.5
+    conf[9, :] = float("inf")
+    with make_ctx(B, gamma, 10) as ctx:
+        vl, ex = gpu_schedule(ctx, conf)
+    clamped = torch.nan_to_num(conf, nan=0.0).clamp(0.0, 1.0)
+    ovl, oex, _ = _oracle_schedule(clamped)
+    assert np.array_equal(vl, ovl) and abs(ex - oex) <= 1e-9 * oex
+
+
 def test_scheduler_workload5_full():
     vi = WL.make_verify_inputs(5, "cuda", B=512, gamma=8, V=1000)
     with make_ctx(512, 8, 1000) as ctx:
