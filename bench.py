@@ -16,7 +16,7 @@ steps.  Prints ONE JSON line:
             batch (rows of the first requests until ~10 s of oracle time)
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
-       [--copy-probe]   (also runs a plain copy of known size, for counter scaling)
+       [--copy-probe]   (accepted for the recorded profile commands; the copy probe always runs)
        [--workload headline|tiny|batched|block|markov|all]
 The other workloads (one JSON line each, same fields) measure the tiny and
 batched token-verification batches, scheduler + block verification
@@ -154,15 +154,36 @@ def bench_headline(args, L, WL):
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     alg = WL.bytes_single_read(vi)
     roofline = _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats"), measured_traffic(alg))
-    if args.copy_probe:
-        # a plain streaming kernel of known traffic (1 GiB read + 1 GiB written
-        # per dispatch), to scale the FETCH_SIZE / WRITE_SIZE counters
-        n = (1 << 30) // 4
-        src = torch.zeros(n, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            torch.bitwise_not(src, out=dst)
-        torch.cuda.synchronize()
+    # a plain streaming kernel of known traffic (1 GiB read + 1 GiB written per
+    # dispatch): a reference for what this part sustains on a copy, and the
+    # kernel whose FETCH_SIZE / WRITE_SIZE readings scale the counters
+    n = (1 << 30) // 4
+    src = torch.zeros(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        torch.bitwise_not(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_us = e0.elapsed_time(e1) / 5 * 1e3
+    copy_probe = {"kernel": "torch.bitwise_not over 1 GiB int32", "bytes_per_launch": 2 << 30,
+                  "mean_us": round(copy_us, 2), "gbps": round((2 << 30) / (copy_us * 1e-6) / 1e9, 1)}
+    # and a plain streaming read (a library reduction over 1 GiB)
+    torch.sum(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        torch.sum(src)
+    e1.record()
+    torch.cuda.synchronize()
+    read_us = e0.elapsed_time(e1) / 5 * 1e3
+    copy_probe["read_kernel"] = "torch.sum over 1 GiB int32"
+    copy_probe["read_mean_us"] = round(read_us, 2)
+    copy_probe["read_gbps"] = round((1 << 30) / (read_us * 1e-6) / 1e9, 1)
+    del src, dst
     cpu = None if args.no_cpu_baseline else cpu_baseline(vi)
     ctx.close()
     return _line(METRIC, B * gamma / (ms / 1e3), "verified positions/s", args, ms,
@@ -171,7 +192,9 @@ def bench_headline(args, L, WL):
                  roofline, cpu_baseline=cpu,
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
-                 mean_accepted=round(accepted, 4), wall_ms_per_step=round(wall_ms, 5))
+                 mean_accepted=round(accepted, 4), wall_ms_per_step=round(wall_ms, 5), copy_probe=copy_probe,
+                 env={"hip": torch.version.hip, "torch": torch.__version__,
+                      "device": torch.cuda.get_device_name(0)})
 
 
 def bench_token(args, L, WL, cfg_id, nsets):

@@ -7,6 +7,9 @@ in seconds (several chunks and a ragged tail), and every workload at its full
 size in the launch configuration the benchmark times, compared on a sample
 of requests the oracle evaluates one by one.
 """
+import os
+import subprocess
+
 import numpy as np
 import pytest
 import torch
@@ -447,6 +450,21 @@ def test_markov_zero_transition_is_independent():
     with make_ctx(B, gamma, V, 256) as ctx:
         d, ql, _ = gpu_markov(ctx, mi)
     assert torch.equal(ql, mi.base.float())
+
+
+# ------------------------------------------------------- the bare C ABI --
+
+def test_c_abi_program():
+    """The library driven from C alone (HIP runtime buffers, no Python or torch
+    in the process): token and block verification of a small batch against
+    the oracle, decision by decision (tests/c_abi_parity.c)."""
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_parity")
+    if not os.path.exists(exe):
+        pytest.fail("tests/c_abi_parity is not built: run the repository build step (__graft_entry__.build)")
+    _say("case: C program through the C ABI")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=90)
+    _say(r.stdout.strip())
+    assert r.returncode == 0, r.stdout + r.stderr
 
 
 # ------------------------------------------- launch shapes and edge sizes --
