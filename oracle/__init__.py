@@ -60,6 +60,8 @@ def declare(lib):
     lib.orc_block_verify.restype = i32
     lib.orc_schedule.argtypes = [P, i32, i32, f64, f64, P, P, P]
     lib.orc_schedule.restype = i32
+    lib.orc_sts_confidence.argtypes = [P, P, i32, i32, P]
+    lib.orc_sts_confidence.restype = i32
     lib.orc_markov_draft.argtypes = [P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
                                      P, P, P, P, P, P]
     lib.orc_markov_draft.restype = i32
@@ -194,6 +196,20 @@ def schedule(conf, sps_a: float = 2000.0, sps_k: float = 4096.0):
     if rc != 0:
         raise ValueError("orc_schedule: invalid arguments")
     return vl, e.value, m.value
+
+
+def sts_confidence(logits, temps):
+    """Sequentially temperature-scaled confidences [B, gamma] (float64); see
+    orc_sts_confidence in oracle.h."""
+    lg = _f64(logits)
+    t = _f64(temps).reshape(-1)
+    B, gamma = lg.shape
+    if t.shape[0] != gamma:
+        raise ValueError("sts_confidence: one temperature per position is required")
+    out = np.zeros((B, gamma), np.float64)
+    if _load().orc_sts_confidence(_ptr(lg), _ptr(t), B, gamma, _ptr(out)) != 0:
+        raise ValueError("orc_sts_confidence: invalid arguments")
+    return out
 
 
 @dataclass

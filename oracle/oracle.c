@@ -450,6 +450,26 @@ int orc_schedule(const double *conf, int B, int gamma, double sps_a, double sps_
     return 0;
 }
 
+/* Sequential temperature scaling: the logistic of logit / T_i, per position */
+/* i, written out in binary64.  A positive temperature divides the log-odds, */
+/* so T_i > 1 pulls the estimate toward 1/2 and T_i < 1 away from it.        */
+int orc_sts_confidence(const double *logits, const double *temps, int B, int gamma, double *conf)
+{
+    if (B < 0 || gamma < 0) return -1;
+    if (B > 0 && gamma > 0 && (!logits || !temps || !conf)) return -1;
+    for (int i = 0; i < gamma; ++i)
+        if (!(temps[i] > 0.0) || !isfinite(temps[i])) return -1;
+    for (int b = 0; b < B; ++b) {
+        for (int i = 0; i < gamma; ++i) {
+            const double l = logits[(int64_t)b * gamma + i];
+            if (isnan(l)) return -1;
+            const double odds = exp(-(l / temps[i]));      /* e^{-l/T} in [0, +inf] */
+            conf[(int64_t)b * gamma + i] = 1.0 / (1.0 + odds);
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Markov-head draft sampler ("The First Ace"; zskr.cn section 03): the       */
 /* parallel backbone gives base logits for every block position; going left  */

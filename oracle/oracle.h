@@ -24,6 +24,8 @@
  *  [KC]  "DeepSeek Boosts Inference Speed by 85%..." (kongchang.com),
  *        sections "The First Ace", "The Second Ace", "The Third Ace".
  *  [ZS]  "DeepSeek DSpark 详解" (zskr.cn), sections 02-04 and Fig. 1.
+ *  [AT]  "DSpark: DeepSeek's bet on speed that doesn't betray quality"
+ *        (aitalk.it), section "Verifying only what matters".
  *  [PH]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *        1, 2, 3", SC'11 -- the Philox4x32-10 generator.
  *
@@ -120,6 +122,19 @@ int orc_block_verify(const double *p, const double *q, const int32_t *draft,
  * decision that stopped admission (+inf if every candidate was admitted). */
 int orc_schedule(const double *conf, int B, int gamma, double sps_a, double sps_k,
                  int32_t *verify_len, double *expected, double *stop_margin);
+
+/* Sequential temperature scaling of the confidence head [KC "The Second
+ * Ace"], [ZS 04], [AT "Verifying only what matters"]: the head gives, for
+ * each request b and draft position i, a logit for "x_i passes given that
+ * x_1..x_{i-1} passed"; position i has its own temperature T_i (fitted
+ * offline on held-out data, left to right), and the calibrated estimate is
+ * the logistic of the logit divided by T_i:
+ *   conf[b, i] = 1 / (1 + exp(-logits[b, i] / temps[i])),   binary64.
+ * Dividing by T_i > 0 keeps the order of the candidates of one position.
+ * logits [B, gamma] (binary32 values), temps [gamma], each finite and > 0.
+ * Out: conf [B, gamma].  Returns -1 on a NaN logit or an invalid
+ * temperature. */
+int orc_sts_confidence(const double *logits, const double *temps, int B, int gamma, double *conf);
 
 /* Markov-head draft sampler [KC "The First Ace"], [ZS 03].
  * base [B, gamma, V] backbone logits, U [V, R], W [R, V], x0 [B] anchor tokens.

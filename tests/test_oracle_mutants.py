@@ -71,6 +71,15 @@ MUTANTS = [
      "if (a->s > c->s) return -1;          /* survival descending */\n    if (a->s < c->s) return 1;",
      "if (a->s < c->s) return -1;\n    if (a->s > c->s) return 1;",
      [lambda: pins.test_scheduler_equals_brute_force_optimum(oracle)]),
+    ("temperature multiplies the log-odds",
+     "exp(-(l / temps[i]))", "exp(-(l * temps[i]))",
+     [lambda: pins.test_sts_closed_forms(oracle)]),
+    ("temperature of the previous position",
+     "exp(-(l / temps[i]))", "exp(-(l / temps[i > 0 ? i - 1 : 0]))",
+     [lambda: pins.test_sts_closed_forms(oracle), lambda: pins.test_sts_equals_library_logistic(oracle)]),
+    ("logistic of the negated log-odds",
+     "exp(-(l / temps[i]))", "exp(l / temps[i])",
+     [lambda: pins.test_sts_closed_forms(oracle)]),
     ("Markov transition from the anchor only",
      "prev = (int32_t)y;", "(void)y;",
      [lambda: pins.test_markov_chain_distribution(oracle)]),

@@ -514,6 +514,55 @@ def test_scheduler_prefix_closed_and_ties(orc):
     assert vl.tolist() == [3, 1] and abs(E - (2 + 1 + 1 + 0.5 + 1)) < 1e-12
 
 
+# ------------------------------------------- sequential temperature scaling ----
+
+def test_sts_closed_forms(orc):
+    """Temperature scaling divides the head's log-odds by the position's own
+    temperature before the logistic (kongchang.com "The Second Ace"; zskr.cn
+    section 04): log-odds T_i*ln(k) give exactly k/(1+k) at every position,
+    0 gives 1/2 whatever T_i is, +-inf give 1 and 0."""
+    temps = np.array([0.5, 1.0, 2.0, 3.7])
+    ks = np.array([3.0, 9.0, 1.0 / 3.0, 19.0])
+    logits = np.stack([temps * np.log(ks), -temps * np.log(ks), np.zeros(4),
+                       np.array([np.inf, -np.inf, np.inf, -np.inf])])
+    c = orc.sts_confidence(logits, temps)
+    np.testing.assert_allclose(c[0], ks / (1 + ks), rtol=1e-14)
+    np.testing.assert_allclose(c[1], 1 / (1 + ks), rtol=1e-14)
+    assert (c[2] == 0.5).all()
+    assert c[3].tolist() == [1.0, 0.0, 1.0, 0.0]
+
+
+def test_sts_keeps_order_within_a_position(orc):
+    """Scaling by a positive temperature never reorders the candidates of one
+    position (it only changes their magnitudes); a larger temperature pulls
+    every estimate toward 1/2, a smaller one pushes it away."""
+    rng = np.random.default_rng(17)
+    logits = rng.normal(0.8, 2.0, (200, 5))
+    ones = orc.sts_confidence(logits, np.ones(5))
+    for temps in (np.array([0.3, 0.7, 1.5, 2.0, 4.0]), np.full(5, 1e6)):
+        c = orc.sts_confidence(logits, temps)
+        for i in range(5):
+            assert (np.argsort(c[:, i], kind="stable") == np.argsort(ones[:, i], kind="stable")).all()
+            flatter = np.abs(c[:, i] - 0.5) <= np.abs(ones[:, i] - 0.5) + 1e-15
+            assert flatter.all() if temps[i] >= 1 else (~flatter | (logits[:, i] == 0)).all()
+    assert np.abs(orc.sts_confidence(logits, np.full(5, 1e6)) - 0.5).max() < 1e-5
+
+
+def test_sts_equals_library_logistic(orc):
+    """Against SciPy's logistic function (scipy.special.expit) of logit / T_i."""
+    from scipy.special import expit
+    rng = np.random.default_rng(23)
+    logits = rng.normal(0.0, 6.0, (64, 7)).astype(np.float32)
+    temps = rng.uniform(0.4, 3.0, 7).astype(np.float32)
+    c = orc.sts_confidence(logits, temps)
+    ref = expit(logits.astype(np.float64) / temps.astype(np.float64)[None, :])
+    np.testing.assert_allclose(c, ref, rtol=1e-14, atol=1e-300)
+    with pytest.raises(ValueError):
+        orc.sts_confidence(logits, np.zeros(7))
+    with pytest.raises(ValueError):
+        orc.sts_confidence(np.full((2, 7), np.nan), temps)
+
+
 # --------------------------------------------------------------- Markov ----
 
 def test_markov_without_transition_is_independent_icdf(orc):
