@@ -17,11 +17,13 @@ steps.  Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
        [--copy-probe]   (accepted for the recorded profile commands; the copy probe always runs)
-       [--workload headline|tiny|batched|block|markov|all]
+       [--workload headline|tiny|batched|block|block_async|markov|all]
 The other workloads (one JSON line each, same fields) measure the tiny and
 batched token-verification batches, scheduler + block verification
-(B=512, gamma=8) and the Markov-head sampler followed by verification
-(B=128, gamma=8, R=256; its roofline entry adds the MFMA rate).
+(B=512, gamma=8), the same with temperature-scaled confidences and the
+scheduler two steps ahead on a second stream, and the Markov-head sampler
+followed by verification (B=128, gamma=8, R=256; its roofline entry adds the
+MFMA rate).
 """
 import argparse
 import hashlib
@@ -305,6 +307,87 @@ def bench_markov(args, L, WL):
                  two_call_verified_positions_per_s=round(B * gamma / (ms2 / 1e3), 1))
 
 
+def bench_block_async(args, L, WL):
+    """Workload 5 with temperature-scaled confidences and the scheduler run
+    two steps ahead: at step k a second stream (own context) schedules from
+    step k's head estimates the verify lengths that step k + 2 uses, while
+    the verification stream works on step k with the lengths scheduled at
+    step k - 2.  Three length buffers in a ring; events order the handovers
+    (schedule done -> verify, verify done reading a slot -> its next
+    schedule)."""
+    import torch
+    sets = [WL.make_verify_inputs(5, "cuda"), WL.make_verify_inputs(5, "cuda", seed=1105)]
+    vi = sets[0]
+    B, gamma, V = vi.B, vi.gamma, vi.V
+    temps = WL.sts_temperatures(gamma)
+    logits = [WL.sts_head_logits(s.conf, temps) for s in sets]
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+    ring = [torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(3)]
+    sched_done = [torch.cuda.Event() for _ in range(3)]
+    slot_free = [torch.cuda.Event() for _ in range(3)]
+    ctx = L.Context(0, B, gamma, V)
+    sctx = L.Context(0, B, gamma, 1)         # the scheduler needs no vocabulary workspace
+    main_s = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def schedule(k):                          # lengths for step k + 2 from step k's estimates
+        side.wait_event(slot_free[k % 3])
+        L.spec_schedule_sts_run(sctx, logits[k % len(sets)], temps, ring[k % 3], sps_a=2000.0, sps_k=4096.0,
+                                stream=side)
+        sched_done[k % 3].record(side)
+
+    def step(k):
+        s = sets[k % len(sets)]
+        main_s.wait_event(sched_done[(k - 2) % 3])
+        L.spec_blockverify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k,
+                               verify_len=ring[(k - 2) % 3])
+        slot_free[(k - 2) % 3].record(main_s)
+        schedule(k)
+
+    side.wait_stream(main_s)                  # inputs are written on the main stream
+    schedule(-2)
+    schedule(-1)
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(main_s)
+    for k in range(args.steps):
+        step(args.warmup + k)
+    main_s.wait_stream(side)                  # the timed region ends after the last schedule too
+    ev1.record(main_s)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    first = args.warmup + args.steps
+    L.spec_verify_profile_enable(sctx, True)
+    L.spec_verify_profile_read(sctx)
+    prof = _profile_steps(L, ctx, step, first, args.steps)
+    sprof = L.spec_verify_profile_read(sctx)
+    torch.cuda.synchronize()
+    admitted = []
+    for lg in logits:
+        L.spec_schedule_sts_run(sctx, lg, temps, ring[0], sps_a=2000.0, sps_k=4096.0)
+        torch.cuda.synchronize()
+        admitted.append(ring[0].cpu().numpy().astype("int64"))
+    ctx.close()
+    sctx.close()
+    positions = sum(float(x.sum()) for x in admitted) / len(admitted)
+    rows = sum(float((2 * x + 1).sum()) for x in admitted) / len(admitted)
+    alg = rows * V * vi.p.element_size()
+    kernels = {k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]}
+    kernels["schedule (second stream)"] = round(_mean_us(sprof, "schedule"), 2)
+    return _line("verified positions/s, B=512 gamma=8 V=129,280 bf16, block verification with the "
+                 "temperature-scaled scheduler two steps ahead",
+                 positions / (ms / 1e3), "verified positions/s", args, ms,
+                 {"workload": "block verification; scheduler on temperature-scaled confidences, two steps "
+                              "ahead on a second stream", "B": B, "gamma": gamma, "V": V, "logits": "bf16",
+                  "sps": "2000/(1+n/4096)", "temperatures": [round(t, 3) for t in temps],
+                  "input_sets": len(sets)},
+                 _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats")),
+                 mean_verify_len=round(positions / B, 4), kernels_mean_us=kernels)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,7 +396,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "tiny", "batched", "block", "markov", "all"],
+                    choices=["headline", "tiny", "batched", "block", "block_async", "markov", "all"],
                     help="headline (default: the one JSON line the driver reads) or another workload")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -330,6 +413,7 @@ def main():
             "tiny": lambda: bench_token(args, L, WL, 1, 1),
             "batched": lambda: bench_token(args, L, WL, 2, 4),
             "block": lambda: bench_block(args, L, WL),
+            "block_async": lambda: bench_block_async(args, L, WL),
             "markov": lambda: bench_markov(args, L, WL)}
     names = list(runs) if args.workload == "all" else [args.workload]
     for n in names:

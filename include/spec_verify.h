@@ -138,6 +138,27 @@ sv_status spec_schedule_run(sv_ctx *ctx, hipStream_t stream, const float *conf,
                             int B, int gamma, float sps_a, float sps_k,
                             int32_t *verify_len, double *expected);
 
+/* The prefix scheduler on temperature-scaled confidences ("DeepSeek Boosts
+ * Inference Speed by 85%", section "The Second Ace"; "DeepSeek DSpark 详解",
+ * section 04): position i of every request has its own temperature T_i, and
+ * the confidence of candidate (b, i) is 1 / (1 + exp(-conf_logits[b,i] / T_i))
+ * (binary64; NaN is taken as 0); ranking and admission then as
+ * spec_schedule_run.
+ *   conf_logits   [B, gamma] fp32 device: the confidence head's log-odds
+ *   temperatures  [gamma] fp32 HOST pointer, each finite and > 0; read
+ *                 during the call, which copies them into the launch
+ * The scheduler reads only confidences, never draft tokens or uniforms, so
+ * it may run ahead of verification: a serving loop can call it on a second
+ * stream (with a second context, a context being single-stream) on the
+ * estimates of an earlier step and hand verify_len over with an event, which
+ * takes it off the verification stream's critical path (the two-step-delayed
+ * schedule of "DeepSeek Boosts Inference Speed by 85%", section "The Third
+ * Ace", and "DSpark: DeepSeek's bet on speed that doesn't betray quality",
+ * section "Verifying only what matters"). */
+sv_status spec_schedule_sts_run(sv_ctx *ctx, hipStream_t stream, const float *conf_logits,
+                                const float *temperatures, int B, int gamma, float sps_a, float sps_k,
+                                int32_t *verify_len, double *expected);
+
 /* Block verification: keeps the longest passing prefix.  With running ratio
  * w_0 = 1, w_i = min(1, w_{i-1} p_i(x_i) / q_i(x_i)), residual masses
  * m_i = sum_v max(w_i p_{i+1}(v) - q_{i+1}(v), 0), thresholds

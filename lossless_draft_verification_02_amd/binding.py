@@ -20,7 +20,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_FLAG_BAD_TOKEN, SV_FLAG_BAD_ROW, SV_FLAG_RESID_ZERO, SV_FLAG_BAD_VERIFY_LEN = 1, 2, 4, 8
 
 EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error",
-            "spec_verify_device_status", "spec_verify_run", "spec_schedule_run",
+            "spec_verify_device_status", "spec_verify_run", "spec_schedule_run", "spec_schedule_sts_run",
             "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "spec_verify_profile_enable",
             "spec_verify_profile_read")
 KERNELS = ("rowstats", "accept", "block_pass2", "resid", "select", "tail", "schedule", "markov_gemm",
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_run.restype = I
     lib.spec_schedule_run.argtypes = [P, P, P, I, I, F, F, P, P]
     lib.spec_schedule_run.restype = I
+    lib.spec_schedule_sts_run.argtypes = [P, P, P, P, I, I, F, F, P, P]
+    lib.spec_schedule_sts_run.restype = I
     lib.spec_blockverify_run.argtypes = [P, P, P, I, P, I, P, P, P, F, F, P, I, I, I64, F, U64, U64, P,
                                          P, P, P]
     lib.spec_blockverify_run.restype = I
@@ -228,6 +230,25 @@ def spec_schedule_run(ctx: Context, conf, verify_len, *, sps_a: float = 2000.0, 
     _check("spec_schedule_run", load_library().spec_schedule_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(conf), B, gamma, sps_a, sps_k, _ptr(verify_len),
         _ptr(expected)))
+
+
+def spec_schedule_sts_run(ctx: Context, conf_logits, temperatures, verify_len, *, sps_a: float = 2000.0,
+                          sps_k: float = 4096.0, expected=None, stream=None):
+    """Prefix scheduler on temperature-scaled confidences: conf_logits [B, gamma]
+    fp32 (device) and one temperature per position (host sequence of gamma
+    floats) -> verify_len [B] int32 (+ expected [1] fp64)."""
+    torch = _torch()
+    B, gamma = conf_logits.shape
+    _need(conf_logits, "conf_logits", dtype=torch.float32, device=ctx.device)
+    _need(verify_len, "verify_len", dtype=torch.int32, shape=(B,), device=ctx.device)
+    _need(expected, "expected", dtype=torch.float64, shape=(1,), device=ctx.device)
+    temps = [float(t) for t in temperatures]
+    if len(temps) != gamma:
+        raise ValueError(f"spec_schedule_sts_run: {len(temps)} temperatures for gamma={gamma}")
+    host = (ctypes.c_float * max(gamma, 1))(*temps)
+    _check("spec_schedule_sts_run", load_library().spec_schedule_sts_run(
+        ctx.handle, _stream(ctx.device, stream), _ptr(conf_logits), ctypes.cast(host, ctypes.c_void_p), B, gamma,
+        sps_a, sps_k, _ptr(verify_len), _ptr(expected)))
 
 
 def spec_blockverify_run(ctx: Context, p, q, draft, accepted_len, out_tokens, *, temperature: float = 1.0,

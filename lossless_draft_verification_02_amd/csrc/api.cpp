@@ -390,23 +390,53 @@ sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits,
     return ok();
 }
 
-sv_status spec_schedule_run(sv_ctx *ctx, hipStream_t stream, const float *conf, int B, int gamma,
-                            float sps_a, float sps_k, int32_t *verify_len, double *expected)
+static sv_status schedule_common(sv_ctx *ctx, hipStream_t stream, const float *conf, const svh::StsTemps &sts,
+                                 int B, int gamma, float sps_a, float sps_k, int32_t *verify_len, double *expected,
+                                 const char *who)
 {
-    if (!ctx) return fail(SV_ERR_INVALID, "spec_schedule_run: ctx is NULL");
+    if (!ctx) return fail(SV_ERR_INVALID, "%s: ctx is NULL", who);
     if (B <= 0 || B > ctx->max_batch || gamma < 0 || gamma > ctx->max_gamma)
-        return fail(SV_ERR_INVALID, "spec_schedule_run: B=%d or gamma=%d out of range", B, gamma);
+        return fail(SV_ERR_INVALID, "%s: B=%d or gamma=%d out of range", who, B, gamma);
     if (B > svh::kSchedMax || (int64_t)B * gamma > svh::kSchedMax)
-        return fail(SV_ERR_UNSUPPORTED, "spec_schedule_run: B and B*gamma must be <= %d", svh::kSchedMax);
+        return fail(SV_ERR_UNSUPPORTED, "%s: B and B*gamma must be <= %d", who, svh::kSchedMax);
     if (!verify_len || (gamma > 0 && !conf))
-        return fail(SV_ERR_INVALID, "spec_schedule_run: conf and verify_len are required");
+        return fail(SV_ERR_INVALID, "%s: conf and verify_len are required", who);
     if (!(sps_a > 0.0f) || !(sps_k > 0.0f) || !std::isfinite(sps_a) || !std::isfinite(sps_k))
-        return fail(SV_ERR_INVALID, "spec_schedule_run: sps_a and sps_k must be finite and > 0");
+        return fail(SV_ERR_INVALID, "%s: sps_a and sps_k must be finite and > 0", who);
     DeviceGuard guard(ctx->device);
-    sv_status st = check_launch(svh::launch_schedule(ctx, conf, B, gamma, sps_a, sps_k, verify_len, expected,
+    sv_status st = check_launch(svh::launch_schedule(ctx, conf, sts, B, gamma, sps_a, sps_k, verify_len, expected,
                                                      stream),
                                 "scheduler");
     return st != SV_OK ? st : ok();
+}
+
+sv_status spec_schedule_run(sv_ctx *ctx, hipStream_t stream, const float *conf, int B, int gamma,
+                            float sps_a, float sps_k, int32_t *verify_len, double *expected)
+{
+    svh::StsTemps sts{};
+    return schedule_common(ctx, stream, conf, sts, B, gamma, sps_a, sps_k, verify_len, expected,
+                           "spec_schedule_run");
+}
+
+sv_status spec_schedule_sts_run(sv_ctx *ctx, hipStream_t stream, const float *conf_logits,
+                                const float *temperatures, int B, int gamma, float sps_a, float sps_k,
+                                int32_t *verify_len, double *expected)
+{
+    svh::StsTemps sts{};
+    sts.on = 1;
+    if (!ctx) return fail(SV_ERR_INVALID, "spec_schedule_sts_run: ctx is NULL");
+    if (gamma < 0 || gamma > ctx->max_gamma)
+        return fail(SV_ERR_INVALID, "spec_schedule_sts_run: gamma=%d out of range", gamma);
+    if (gamma > 0 && !temperatures)
+        return fail(SV_ERR_INVALID, "spec_schedule_sts_run: temperatures are required");
+    for (int i = 0; i < gamma; ++i) {
+        if (!(temperatures[i] > 0.0f) || !std::isfinite(temperatures[i]))
+            return fail(SV_ERR_INVALID, "spec_schedule_sts_run: temperature %d (%g) must be finite and > 0", i,
+                        (double)temperatures[i]);
+        sts.t[i] = temperatures[i];
+    }
+    return schedule_common(ctx, stream, conf_logits, sts, B, gamma, sps_a, sps_k, verify_len, expected,
+                           "spec_schedule_sts_run");
 }
 
 sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits, sv_dtype p_dtype,

@@ -13,6 +13,12 @@
 // and the verify batch at B rows.  With SPS(n) = a / (1 + n / K), admitting a
 // candidate of survival s raises E * SPS iff s * (K + n) > E.
 //
+// With sequential temperature scaling the inputs are the confidence head's
+// log-odds instead, and position i's estimate is the logistic of
+// log-odds / T_i, each position with its own temperature ("DeepSeek Boosts
+// Inference Speed by 85%", section "The Second Ace"; zskr.cn section 04);
+// it is formed in fp64 where the survival products read it.
+//
 // Two kernels, handing over at the kernel boundary:
 //   k_sched_rank   grid (candidate blocks) x (comparator blocks) of 256: the
 //                  rank of candidate e in the order (S descending, id
@@ -36,56 +42,87 @@ constexpr int NMAX = svh::kSchedMax;
 constexpr int EPT = NMAX / NT;              // sorted slots per thread in the admit kernel
 constexpr int CONF_MAX = RB + svh::kMaxGamma;
 
-__device__ __forceinline__ float clamp01(float cf)
+__device__ __forceinline__ double clamp01(double cf)
 {
-    return cf > 0.0f ? (cf < 1.0f ? cf : 1.0f) : 0.0f;   // NaN -> 0
+    return cf > 0.0 ? (cf < 1.0 ? cf : 1.0) : 0.0;   // NaN -> 0
+}
+
+// The confidence of candidate c (position c % gamma of its request): the
+// input itself, or under temperature scaling the logistic of the input
+// log-odds over that position's temperature; either is clamped to [0, 1].
+__device__ __forceinline__ double candidate_confidence(const float *__restrict__ conf, int c, int gamma,
+                                                       const svh::StsTemps &sts)
+{
+    const double v = (double)conf[c];
+    if (!sts.on) return clamp01(v);
+    const double odds = exp(-(v / (double)sts.t[c % gamma]));
+    return clamp01(1.0 / (1.0 + odds));
 }
 
 // Survival products of candidates [e0, e0 + RB) into S[]: S(b, i) is the
-// product of the clamped confidences of positions 0..i of request b, formed
-// left to right in fp64.  sconf is scratch of CONF_MAX floats.
-__device__ void block_survival(const float *__restrict__ conf, int n, int gamma, int e0, float *sconf,
-                               double *S)
+// product of the confidences of positions 0..i of request b, formed left to
+// right in fp64.  sconf is scratch of CONF_MAX doubles.
+__device__ void block_survival(const float *__restrict__ conf, int n, int gamma, int e0,
+                               const svh::StsTemps &sts, double *sconf, double *S)
 {
     const int c0 = (e0 / gamma) * gamma;          // first position of the first request touched
     const int e1 = e0 + RB < n ? e0 + RB : n;
-    for (int c = c0 + (int)threadIdx.x; c < e1; c += RB) sconf[c - c0] = clamp01(conf[c]);
+    for (int c = c0 + (int)threadIdx.x; c < e1; c += RB) sconf[c - c0] = candidate_confidence(conf, c, gamma, sts);
     __syncthreads();
     const int e = e0 + (int)threadIdx.x;
     if (e < n) {
         const int b0 = (e / gamma) * gamma;
         double s = 1.0;
-        for (int c = b0; c <= e; ++c) s = s * (double)sconf[c - c0];
+        for (int c = b0; c <= e; ++c) s = s * sconf[c - c0];
         S[threadIdx.x] = s;
     }
     __syncthreads();
 }
 
+// How many of the comparators S[0..cn) come before (s, own index me):
+// MODE 0, all earlier ids (S >= s); 1, all later ids (S > s); 2, the
+// candidate's own block (S > s, or S == s at a smaller index).  Full blocks
+// run unrolled so that many LDS reads are in flight.
+template <int MODE>
+__device__ __forceinline__ int count_before(const double *S, int cn, double s, int me)
+{
+    int cnt = 0;
+    if (cn == RB) {
+#pragma unroll 32
+        for (int c = 0; c < RB; ++c)
+            cnt += MODE == 0 ? S[c] >= s : MODE == 1 ? S[c] > s : (S[c] > s) || (S[c] == s && c < me);
+    } else {
+        for (int c = 0; c < cn; ++c)
+            cnt += MODE == 0 ? S[c] >= s : MODE == 1 ? S[c] > s : (S[c] > s) || (S[c] == s && c < me);
+    }
+    return cnt;
+}
+
 __global__ __launch_bounds__(RB) void k_sched_rank(const float *__restrict__ conf, int n, int gamma,
-                                                   int32_t *__restrict__ rank, double *__restrict__ surv)
+                                                   const svh::StsTemps sts, int32_t *__restrict__ rank,
+                                                   double *__restrict__ surv)
 {
     __shared__ double Sx[RB], Sy[RB];
-    __shared__ float sconf[CONF_MAX];
+    __shared__ double sconf[CONF_MAX];
     const int bx = blockIdx.x, by = blockIdx.y;
-    block_survival(conf, n, gamma, by * RB, sconf, Sy);
+    block_survival(conf, n, gamma, by * RB, sts, sconf, Sy);
     const int e = bx * RB + (int)threadIdx.x;
     double s;
     if (bx == by) {
         s = Sy[threadIdx.x];
     } else {
-        block_survival(conf, n, gamma, bx * RB, sconf, Sx);
+        block_survival(conf, n, gamma, bx * RB, sts, sconf, Sx);
         s = Sx[threadIdx.x];
     }
     if (e >= n) return;
     const int cn = n - by * RB < RB ? n - by * RB : RB;
-    int cnt = 0;
+    int cnt;
     if (by < bx) {          // every comparator id is smaller: ties come first
-        for (int c = 0; c < cn; ++c) cnt += Sy[c] >= s;
+        cnt = count_before<0>(Sy, cn, s, 0);
     } else if (by > bx) {   // every comparator id is larger: ties come after
-        for (int c = 0; c < cn; ++c) cnt += Sy[c] > s;
+        cnt = count_before<1>(Sy, cn, s, 0);
     } else {
-        const int me = threadIdx.x;
-        for (int c = 0; c < cn; ++c) cnt += (Sy[c] > s) || (Sy[c] == s && c < me);
+        cnt = count_before<2>(Sy, cn, s, (int)threadIdx.x);
         surv[e] = s;
     }
     if (cnt) atomicAdd(&rank[e], cnt);
@@ -180,7 +217,7 @@ __global__ void k_sched_empty(int B, int32_t *__restrict__ verify_len, double *_
 
 namespace svh {
 
-hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, float sps_a,
+hipError_t launch_schedule(sv_ctx *ctx, const float *conf, const StsTemps &sts, int B, int gamma, float sps_a,
                            float sps_k, int32_t *verify_len, double *expected, hipStream_t s)
 {
     (void)sps_a;   // a positive scale of SPS does not move the maximum
@@ -190,7 +227,7 @@ hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, flo
         hipLaunchKernelGGL(k_sched_empty, dim3(1), dim3(256), 0, s, B, verify_len, expected);
     } else {
         const int nb = (n + RB - 1) / RB;
-        hipLaunchKernelGGL(k_sched_rank, dim3(nb, nb), dim3(RB), 0, s, conf, n, gamma, ctx->ws.sched_rank,
+        hipLaunchKernelGGL(k_sched_rank, dim3(nb, nb), dim3(RB), 0, s, conf, n, gamma, sts, ctx->ws.sched_rank,
                            ctx->ws.sched_surv);
         hipLaunchKernelGGL(k_sched_admit, dim3(1), dim3(NT), 0, s, n, B, gamma, (double)sps_k,
                            ctx->ws.sched_rank, (const double *)ctx->ws.sched_surv, verify_len, expected,

@@ -164,7 +164,13 @@ hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 constexpr size_t kReqStateBytes = 32;
 static_assert(sizeof(ReqG) == kReqStateBytes, "request state layout");
-hipError_t launch_schedule(sv_ctx *ctx, const float *conf, int B, int gamma, float sps_a,
+// Per-position temperatures of sequential temperature scaling, passed by
+// value; with on == 0 the scheduler reads confidences, otherwise log-odds.
+struct StsTemps {
+    float t[kMaxGamma];
+    int on;
+};
+hipError_t launch_schedule(sv_ctx *ctx, const float *conf, const StsTemps &sts, int B, int gamma, float sps_a,
                            float sps_k, int32_t *verify_len, double *expected, hipStream_t s);
 
 struct MarkovArgs {

@@ -22,6 +22,12 @@ Five workloads (sizes can be shrunk for tests, keeping the recipe):
                confidences: per-request mean mu_b ~ U(0.35, 0.95), decaying 3%
                per position, plus N(0, 0.05^2), clipped to [0, 1].
 
+Temperature-scaled confidences (workload 5 variant): per-position temperatures
+T_i = 1 + 0.15 (i - 1), later positions hotter, and an over-confident head
+whose raw log-odds are T_i times the log-odds of workload 5's confidences
+(clipped to [1e-6, 1 - 1e-6] first), so that calibrated estimates land back
+on them.
+
 Draft tokens are drawn from softmax(q / T) of the stored (rounded) draft
 logits with the Gumbel-max trick, from a generator seeded 0.  Logit noise uses
 a generator seeded 1000 + workload id.  Generation runs on the requested
@@ -150,6 +156,19 @@ def make_verify_inputs(cfg: int, device="cpu", B: Optional[int] = None, gamma: O
         decay = 1.0 - 0.03 * torch.arange(gamma, device=device, dtype=torch.float32)[None, :]
         conf = (mu * decay + 0.05 * torch.randn(B, gamma, generator=gc, device=device)).clamp_(0.0, 1.0)
     return VerifyInputs(cfg, B, gamma, V, T, p, q, draft, conf)
+
+
+def sts_temperatures(gamma: int) -> list:
+    """Per-position temperatures of the temperature-scaled workload-5 variant."""
+    return [1.0 + 0.15 * i for i in range(gamma)]
+
+
+def sts_head_logits(conf: torch.Tensor, temps) -> torch.Tensor:
+    """Raw (over-confident) head log-odds [B, gamma] fp32 whose calibrated
+    estimates are `conf` (see the module docstring)."""
+    c = conf.double().clamp(1e-6, 1.0 - 1e-6)
+    t = torch.tensor(list(temps), dtype=torch.float64, device=conf.device)[None, :]
+    return (t * torch.log(c / (1.0 - c))).float().contiguous()
 
 
 def make_markov_inputs(device="cpu", B: Optional[int] = None, gamma: Optional[int] = None,

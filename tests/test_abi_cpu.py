@@ -57,6 +57,7 @@ def test_runs_reject_null_context():
                              None, None)
     assert st == binding.SV_ERR_INVALID and "ctx" in L.spec_verify_last_error()
     assert lib.spec_schedule_run(None, None, None, 1, 1, 1.0, 1.0, None, None) == binding.SV_ERR_INVALID
+    assert lib.spec_schedule_sts_run(None, None, None, None, 1, 1, 1.0, 1.0, None, None) == binding.SV_ERR_INVALID
     assert lib.markov_draft_run(None, None, None, None, None, 256, None, 1, 1, 10, 1.0, 0, 0, None, None,
                                 None, None) == binding.SV_ERR_INVALID
     assert lib.spec_blockverify_run(None, None, None, 1, None, 1, None, None, None, 1.0, 1.0, None, 1, 1,

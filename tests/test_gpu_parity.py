@@ -356,6 +356,139 @@ def test_scheduler_workload5_full():
     assert np.array_equal(vl, ovl) and abs(ex - oex) <= 1e-9 * oex
 
 
+def gpu_schedule_sts(ctx, logits, temps, sps_a=2000.0, sps_k=4096.0, stream=None):
+    B = logits.shape[0]
+    vl = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    ex = torch.zeros(1, dtype=torch.float64, device="cuda")
+    L.spec_schedule_sts_run(ctx, logits, temps, vl, sps_a=sps_a, sps_k=sps_k, expected=ex, stream=stream)
+    torch.cuda.synchronize()
+    return vl.cpu().numpy(), float(ex.item())
+
+
+def _oracle_schedule_sts(logits, temps, sps_k=4096.0):
+    conf = oracle.sts_confidence(logits.cpu().double().numpy(), np.asarray(temps, np.float32))
+    return oracle.schedule(conf, 2000.0, sps_k)
+
+
+@pytest.mark.parametrize("B,gamma,K", [(5, 4, 3.0), (97, 6, 200.0), (512, 8, 4096.0), (1000, 8, 4096.0),
+                                       (4096, 2, 4096.0)])
+def test_sts_scheduler_matches_oracle(B, gamma, K):
+    """Temperature-scaled confidences (one temperature per position) fused into
+    the scheduler; the first position's log-odds sit on a coarse grid, so many
+    survival products tie exactly and the id order decides."""
+    _say(f"case: temperature-scaled scheduler B={B} gamma={gamma} K={K}")
+    g = torch.Generator("cuda").manual_seed(31 * B + gamma)
+    logits = (1.5 + 2.0 * torch.randn(B, gamma, generator=g, device="cuda")).contiguous()
+    logits[:, 0] = torch.round(logits[:, 0] * 2.0) / 2.0
+    temps = [0.8 + 0.2 * i for i in range(gamma)]
+    with make_ctx(B, gamma, 10) as ctx:
+        vl, ex = gpu_schedule_sts(ctx, logits, temps, sps_k=K)
+    ovl, oex, margin = _oracle_schedule_sts(logits, temps, sps_k=K)
+    _say(f"  mean verify_len={vl.mean():.3f} E={ex:.3f} stop margin={margin:.3e}")
+    if not np.array_equal(vl, ovl):
+        assert margin <= 1e-12, (margin, vl, ovl)
+        _say(f"  within-margin flip at the stop (margin {margin:.2e})")
+    else:
+        assert abs(ex - oex) <= 1e-12 * oex
+
+
+def test_sts_scheduler_special_logits_and_bad_temperatures():
+    """NaN log-odds count as confidence 0, +inf as 1, -inf as 0; temperatures
+    must be finite and positive (checked on the host)."""
+    B, gamma = 40, 5
+    g = torch.Generator("cuda").manual_seed(3)
+    logits = torch.randn(B, gamma, generator=g, device="cuda") * 3.0
+    logits[1, 1] = float("nan")
+    logits[2, :] = float("inf")
+    logits[3, 0] = float("-inf")
+    temps = [1.0, 1.3, 1.6, 1.9, 2.2]
+    with make_ctx(B, gamma, 10) as ctx:
+        vl, ex = gpu_schedule_sts(ctx, logits, temps)
+        for bad in ([1.0, 0.0, 1.0, 1.0, 1.0], [1.0, float("nan"), 1.0, 1.0, 1.0], [-1.0] * 5):
+            with pytest.raises(L.SpecVerifyError):
+                gpu_schedule_sts(ctx, logits, bad)
+    clean = torch.nan_to_num(logits, nan=float("-inf"))
+    ovl, oex, _ = _oracle_schedule_sts(clean, temps)
+    assert np.array_equal(vl, ovl) and abs(ex - oex) <= 1e-12 * oex
+    assert vl[2] == gamma and vl[3] == 0
+
+
+def test_sts_scheduler_workload5_head_logits():
+    """Workload 5's confidences behind an over-confident head (log-odds times
+    T_i) come back, after scaling, to the plain scheduler's allocation."""
+    vi = WL.make_verify_inputs(5, "cuda", B=512, gamma=8, V=1000)
+    temps = WL.sts_temperatures(8)
+    logits = WL.sts_head_logits(vi.conf, temps)
+    with make_ctx(512, 8, 1000) as ctx:
+        vl, ex = gpu_schedule_sts(ctx, logits, temps)
+        pvl, pex = gpu_schedule(ctx, vi.conf)
+    ovl, oex, _ = _oracle_schedule_sts(logits, temps)
+    _say(f"[scheduler w5, temperature-scaled] mean verify_len={vl.mean():.3f} (plain {pvl.mean():.3f})")
+    assert np.array_equal(vl, ovl) and abs(ex - oex) <= 1e-12 * oex
+    assert abs(vl.mean() - pvl.mean()) < 0.05
+
+
+def test_two_step_ahead_schedule_on_a_second_stream():
+    """The serving pattern the scheduler's header describes: at step k a second
+    stream (own context) schedules, from step k's estimates, the lengths step
+    k + 2 verifies with; a ring of three length buffers and events order the
+    handovers.  Every step's outputs equal a one-stream run that verifies step
+    k with the allocation of step k - 2's estimates."""
+    B, gamma, V, steps = 48, 6, 7001, 7
+    sets = [WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V, seed=300 + k) for k in range(steps)]
+    temps = WL.sts_temperatures(gamma)
+    g = torch.Generator("cuda").manual_seed(77)
+    logits = [(1.0 + 2.0 * torch.randn(B, gamma, generator=g, device="cuda")).contiguous()
+              for _ in range(steps + 2)]          # logits[k + 2] are step k's estimates
+    _say(f"case: two-step-ahead schedule, B={B} gamma={gamma} V={V} steps={steps}")
+    with make_ctx(B, gamma, V) as ctx, make_ctx(B, gamma, 1) as sctx:
+        # one stream, sequential: step k uses the allocation of estimates k - 2
+        ref = []
+        for k in range(steps):
+            vl = torch.zeros(B, dtype=torch.int32, device="cuda")
+            L.spec_schedule_sts_run(ctx, logits[k], temps, vl)
+            acc = torch.empty(B, dtype=torch.int32, device="cuda")
+            out = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+            s = sets[k]
+            L.spec_blockverify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=5, offset=k,
+                                   verify_len=vl)
+            torch.cuda.synchronize()
+            ref.append((vl.cpu().numpy(), acc.cpu().numpy(), out.cpu().numpy()))
+        # two streams, pipelined
+        main_s, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        ring = [torch.full((B,), -9, dtype=torch.int32, device="cuda") for _ in range(3)]
+        sched_done = [torch.cuda.Event() for _ in range(3)]
+        slot_free = [torch.cuda.Event() for _ in range(3)]
+        accs = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(steps)]
+        outs = [torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda") for _ in range(steps)]
+        seen = [torch.empty(B, dtype=torch.int32, device="cuda") for _ in range(steps)]
+
+        def schedule(j):                      # estimates j (= step j - 2's) -> lengths for step j
+            side.wait_event(slot_free[j % 3])
+            L.spec_schedule_sts_run(sctx, logits[j], temps, ring[j % 3], stream=side)
+            sched_done[j % 3].record(side)
+
+        side.wait_stream(main_s)
+        schedule(0)
+        schedule(1)
+        for k in range(steps):
+            s = sets[k]
+            main_s.wait_event(sched_done[k % 3])
+            seen[k].copy_(ring[k % 3])
+            L.spec_blockverify_run(ctx, s.p, s.q, s.draft, accs[k], outs[k], temperature=s.T, seed=5, offset=k,
+                                   verify_len=ring[k % 3])
+            slot_free[k % 3].record(main_s)
+            schedule(k + 2)
+        torch.cuda.synchronize()
+        assert L.spec_verify_device_status(ctx) == 0 and L.spec_verify_device_status(sctx) == 0
+    for k in range(steps):
+        np.testing.assert_array_equal(seen[k].cpu().numpy(), ref[k][0])
+        np.testing.assert_array_equal(accs[k].cpu().numpy(), ref[k][1])
+        np.testing.assert_array_equal(outs[k].cpu().numpy(), ref[k][2])
+    _say(f"  {steps} pipelined steps equal the one-stream run; mean lengths "
+         f"{[round(float(r[0].mean()), 2) for r in ref]}")
+
+
 @pytest.mark.parametrize("V", [30000, 9001])
 def test_block_recipe_small(V):
     _say(f"case: block verify, workload 5 recipe, B=16 V={V}")

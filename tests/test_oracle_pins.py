@@ -495,6 +495,31 @@ def test_scheduler_equals_brute_force_optimum(orc):
         assert abs(E - (B + sum(S[b, :vl[b]].sum() for b in range(B)))) < 1e-9
 
 
+def test_scheduler_admits_exactly_where_the_gain_test_passes(orc):
+    """Along the order (survival descending, id ascending) the gain test
+    g(k) = s_k (K + B + k) - (B + sum_{j<k} s_j) never rises, since
+    g(k+1) - g(k) = (s_{k+1} - s_k)(K + B + k + 1) <= 0; so the early-stopping
+    greedy scan admits exactly the candidates with g > 0, each decidable from
+    its own rank and the survival mass ranked before it.  Checked on random
+    and heavily tied confidences with a stable sort of the survivals."""
+    rng = np.random.default_rng(97)
+    for trial in range(300):
+        B = int(rng.integers(1, 40))
+        gam = int(rng.integers(1, 9))
+        K = float(rng.choice([3.0, 50.0, 4096.0]))
+        conf = rng.random((B, gam)) ** 0.3 if trial % 2 else rng.integers(1, 5, (B, gam)) / 4.0
+        vl, _, _ = orc.schedule(conf, 2000.0, K)
+        S = np.cumprod(conf, axis=1).reshape(-1)
+        order = np.argsort(-S, kind="stable")           # ties keep id order
+        s_sorted = S[order]
+        before = np.concatenate([[0.0], np.cumsum(s_sorted)[:-1]])
+        g = s_sorted * (K + B + np.arange(S.size)) - (B + before)
+        assert (np.diff(g) <= 1e-9 * (1 + np.abs(g[:-1]))).all(), trial
+        admitted = np.zeros(S.size, bool)
+        admitted[order[g > 0]] = True
+        assert (admitted.reshape(B, gam).sum(axis=1) == vl).all(), trial
+
+
 def test_scheduler_budget_shrinks_with_load(orc):
     """Light load: long verify budgets; heavy load: the budget tightens
     (kongchang.com "The Third Ace"; zskr.cn Fig. 4)."""
