@@ -60,6 +60,11 @@ def declare(lib):
     lib.orc_block_verify.restype = i32
     lib.orc_schedule.argtypes = [P, i32, i32, f64, f64, P, P, P]
     lib.orc_schedule.restype = i32
+    lib.orc_bf16.argtypes = [f32]
+    lib.orc_bf16.restype = f32
+    lib.orc_rnn_draft.argtypes = [P, P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
+                                  P, P, P, P, P, P, P, P]
+    lib.orc_rnn_draft.restype = i32
     lib.orc_sts_confidence.argtypes = [P, P, i32, i32, P]
     lib.orc_sts_confidence.restype = i32
     lib.orc_markov_draft.argtypes = [P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
@@ -243,3 +248,47 @@ def markov_draft(base, U, W, x0, temperature=1.0, seed=0, offset=0, req_ids=None
     if rc != 0:
         raise ValueError("orc_markov_draft: invalid arguments")
     return MarkovResult(draft, ql, lse, marg, flags)
+
+
+@dataclass
+class RnnResult:
+    draft: np.ndarray         # [B, gamma] int32
+    q_logits: np.ndarray      # [B, gamma, V] float64 (before 1/T)
+    lse_q: np.ndarray         # [B, gamma]
+    margin: np.ndarray        # [B, gamma] inverse-CDF margins
+    flags: np.ndarray         # [B]
+    states: np.ndarray        # [B, gamma, R] the bf16 states hb_k (as float64)
+    state_margin: np.ndarray  # [B, gamma] ulps from the nearest bf16 rounding midpoint
+
+
+def bf16(x: float) -> float:
+    """bf16 rounding of a binary32 value; see orc_bf16 in oracle.h."""
+    return float(_load().orc_bf16(float(x)))
+
+
+def rnn_draft(base, U, W, A, x0, temperature=1.0, seed=0, offset=0, req_ids=None,
+              uniforms=None, want_q=True) -> RnnResult:
+    """RNN-head sampler; see orc_rnn_draft in oracle.h."""
+    base = _f64(base)
+    U = _f64(U)
+    W = _f64(W)
+    A = _f64(A)
+    B, gamma, V = base.shape
+    R = U.shape[1]
+    if U.shape != (V, R) or W.shape != (R, V) or A.shape != (R, R):
+        raise ValueError("U must be [V, R], W [R, V] and A [R, R]")
+    x0 = _i32(x0)
+    draft = np.zeros((B, gamma), np.int32)
+    ql = np.zeros((B, gamma, V)) if want_q else None
+    lse = np.zeros((B, gamma))
+    marg = np.zeros((B, gamma))
+    flags = np.zeros(B, np.uint32)
+    states = np.zeros((B, gamma, R))
+    smarg = np.zeros((B, gamma))
+    rc = _load().orc_rnn_draft(_ptr(base), _ptr(U), _ptr(W), _ptr(A), R, _ptr(x0), _ptr(_i32(req_ids)),
+                               B, gamma, V, temperature, seed, offset, _ptr(_f32(uniforms)),
+                               _ptr(draft), _ptr(ql), _ptr(lse), _ptr(marg), _ptr(flags), _ptr(states),
+                               _ptr(smarg))
+    if rc != 0:
+        raise ValueError("orc_rnn_draft: invalid arguments")
+    return RnnResult(draft, ql, lse, marg, flags, states, smarg)

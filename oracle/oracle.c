@@ -529,3 +529,113 @@ int orc_markov_draft(const double *base, const double *U, const double *W, int R
     free(z); free(wv);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* RNN-head draft sampler ("DeepSeek DSpark 详解", section 03: a recurrent    */
+/* head keeps an in-block state, so each draw can use more of the prefix      */
+/* than the previous token alone).  The pages give no equations; the plain    */
+/* reading taken here is an Elman recurrence with the Markov head's factors:  */
+/*   h_0 = 0,  a_k = U[x_{k-1}] + hb_{k-1} . A,  h_k = tanh(a_k),             */
+/*   hb_k = bf16(h_k),  z_k = base_k + hb_k . W,  x_k ~ softmax(z_k / T).     */
+/* The state is a bf16 activation like the factors; rounding it is a          */
+/* quantisation decision, taken in the kernels' precision: a_k accumulated    */
+/* in binary32 by sequential fused multiply-adds over r = 0..R-1 starting     */
+/* from U[x_{k-1}], tanh in binary32, then round-to-nearest-even to bf16.     */
+/* The contraction z_k is binary64 like the Markov head's.                    */
+/* ------------------------------------------------------------------------- */
+
+/* Round a binary32 value to the nearest bf16 (8 significant bits), ties to
+ * even; *dist_ulps gets the distance from the rounding midpoint in binary32
+ * units in the last place (0 = exactly halfway). */
+static float orc_bf16_round(float x, double *dist_ulps)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u) {   /* inf / NaN: unchanged */
+        if (dist_ulps) *dist_ulps = INFINITY;
+        return x;
+    }
+    const uint32_t low = u & 0xFFFFu;
+    if (dist_ulps) *dist_ulps = fabs((double)low - 32768.0);
+    uint32_t kept = u & 0xFFFF0000u;
+    if (low > 0x8000u || (low == 0x8000u && (kept & 0x10000u))) kept += 0x10000u;   /* up in magnitude */
+    float y;
+    memcpy(&y, &kept, sizeof y);
+    return y;
+}
+
+float orc_bf16(float x)
+{
+    return orc_bf16_round(x, NULL);
+}
+
+int orc_rnn_draft(const double *base, const double *U, const double *W, const double *A, int R,
+                  const int32_t *x0, const int32_t *req_ids,
+                  int B, int gamma, int64_t V, float temperature,
+                  uint64_t seed, uint64_t offset, const float *uniforms,
+                  int32_t *draft, double *q_logits, double *lse_q,
+                  double *margin, uint32_t *flags, double *states, double *state_margin)
+{
+    if (B < 0 || gamma < 0 || V <= 0 || R <= 0) return -1;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return -1;
+    if (B > 0 && gamma > 0 && (!base || !U || !W || !A || !x0 || !draft)) return -1;
+    const double T = (double)temperature;
+    double *z = (double *)malloc((size_t)V * sizeof(double));
+    double *wv = (double *)malloc((size_t)V * sizeof(double));
+    float *hb = (float *)malloc((size_t)R * sizeof(float));
+    float *hn = (float *)malloc((size_t)R * sizeof(float));
+    if (!z || !wv || !hb || !hn) { free(z); free(wv); free(hb); free(hn); return -1; }
+
+    for (int b = 0; b < B; ++b) {
+        const uint32_t req = req_ids ? (uint32_t)req_ids[b] : (uint32_t)b;
+        uint32_t fl = 0;
+        for (int k = 0; k < gamma; ++k) {
+            draft[(int64_t)b * gamma + k] = -1;
+            if (lse_q) lse_q[(int64_t)b * gamma + k] = NAN;
+            if (margin) margin[(int64_t)b * gamma + k] = NAN;
+            if (state_margin) state_margin[(int64_t)b * gamma + k] = NAN;
+        }
+        for (int r = 0; r < R; ++r) hb[r] = 0.0f;            /* h_0 = 0 */
+        int32_t prev = x0 ? x0[b] : 0;
+        if (gamma > 0 && (prev < 0 || (int64_t)prev >= V)) fl |= ORC_FLAG_BAD_TOKEN;
+        for (int k = 1; k <= gamma && !fl; ++k) {
+            /* state update: a = U[x_{k-1}] + hb_{k-1} . A, binary32 fma chain */
+            double qmin = INFINITY;
+            for (int j = 0; j < R; ++j) {
+                float acc = (float)U[(int64_t)prev * R + j];
+                for (int r = 0; r < R; ++r) acc = fmaf(hb[r], (float)A[(int64_t)r * R + j], acc);
+                double d;
+                hn[j] = orc_bf16_round(tanhf(acc), &d);
+                if (d < qmin) qmin = d;
+            }
+            for (int j = 0; j < R; ++j) hb[j] = hn[j];
+            if (states)
+                for (int j = 0; j < R; ++j) states[((int64_t)b * gamma + (k - 1)) * R + j] = (double)hb[j];
+            if (state_margin) state_margin[(int64_t)b * gamma + (k - 1)] = qmin;
+            /* logits: z = base_k + hb_k . W */
+            const double *bk = base + ((int64_t)b * gamma + (k - 1)) * V;
+            for (int64_t v = 0; v < V; ++v) {
+                double dsum = 0.0;
+                for (int r = 0; r < R; ++r) dsum += (double)hb[r] * W[(int64_t)r * V + v];
+                z[v] = bk[v] + dsum;
+            }
+            double lse;
+            fl |= orc_row_lse(z, V, temperature, &lse);
+            if (fl) break;
+            for (int64_t v = 0; v < V; ++v) wv[v] = exp(z[v] / T - lse);
+            float u = uniforms ? uniforms[(int64_t)b * gamma + (k - 1)]
+                               : orc_uniform(seed, offset, req, (uint32_t)k, 2);
+            double Z, marg;
+            int64_t y = orc_icdf(wv, V, u, &Z, &marg);
+            if (y < 0) { fl |= ORC_FLAG_BAD_ROW; break; }
+            draft[(int64_t)b * gamma + (k - 1)] = (int32_t)y;
+            if (q_logits) memcpy(q_logits + ((int64_t)b * gamma + (k - 1)) * V, z, (size_t)V * sizeof(double));
+            if (lse_q) lse_q[(int64_t)b * gamma + (k - 1)] = lse;
+            if (margin) margin[(int64_t)b * gamma + (k - 1)] = marg;
+            prev = (int32_t)y;
+        }
+        if (flags) flags[b] = fl;
+    }
+    free(z); free(wv); free(hb); free(hn);
+    return 0;
+}

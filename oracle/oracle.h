@@ -1,7 +1,8 @@
 /*
  * oracle.h -- plain, slow CPU reference of lossless speculative-sampling
- * verification, block verification, the confidence prefix scheduler and the
- * Markov-head draft sampler.
+ * verification, block verification, the confidence prefix scheduler (with
+ * temperature-scaled confidences) and the Markov- and RNN-head draft
+ * samplers.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The GPU library never
@@ -150,6 +151,24 @@ int orc_markov_draft(const double *base, const double *U, const double *W, int R
                      uint64_t seed, uint64_t offset, const float *uniforms,
                      int32_t *draft, double *q_logits, double *lse_q,
                      double *margin, uint32_t *flags);
+
+/* bf16 rounding (nearest, ties to even) of a binary32 value. */
+float orc_bf16(float x);
+
+/* RNN-head draft sampler [ZS 03] (the reading is in orc_rnn_draft's
+ * definition): h_0 = 0; a_k = U[x_{k-1}] + hb_{k-1} . A in binary32
+ * (sequential fma over r from U[x_{k-1}]); hb_k = bf16(tanhf(a_k));
+ * z_k = base_k + hb_k . W (binary64); x_k ~ softmax(z_k / T) by inverse CDF
+ * with uniform (req, k, tag 2).  A [R, R] (row r multiplies state entry r).
+ * Outputs as orc_markov_draft, plus states [B, gamma, R] (nullable) = hb_k
+ * and state_margin [B, gamma] (nullable) = the smallest distance, in binary32
+ * ulps, of any tanhf(a_k) entry from its bf16 rounding midpoint. */
+int orc_rnn_draft(const double *base, const double *U, const double *W, const double *A, int R,
+                  const int32_t *x0, const int32_t *req_ids,
+                  int B, int gamma, int64_t V, float temperature,
+                  uint64_t seed, uint64_t offset, const float *uniforms,
+                  int32_t *draft, double *q_logits, double *lse_q,
+                  double *margin, uint32_t *flags, double *states, double *state_margin);
 
 #ifdef __cplusplus
 }

@@ -80,6 +80,19 @@ MUTANTS = [
     ("logistic of the negated log-odds",
      "exp(-(l / temps[i]))", "exp(l / temps[i])",
      [lambda: pins.test_sts_closed_forms(oracle)]),
+    ("RNN state ignores the recurrent matrix",
+     "acc = fmaf(hb[r], (float)A[(int64_t)r * R + j], acc);", "acc = fmaf(hb[r], 0.0f, acc);",
+     [lambda: pins.test_rnn_state_recurrence_against_numpy(oracle),
+      lambda: pins.test_rnn_chain_distribution(oracle)]),
+    ("RNN state not carried to the next position",
+     "for (int j = 0; j < R; ++j) hb[j] = hn[j];", "for (int j = 0; j < R; ++j) (void)hn[j];",
+     [lambda: pins.test_rnn_without_recurrence_is_markov_on_tanh_embeddings(oracle)]),
+    ("RNN state without tanh",
+     "hn[j] = orc_bf16_round(tanhf(acc), &d);", "hn[j] = orc_bf16_round(acc, &d);",
+     [lambda: pins.test_rnn_without_recurrence_is_markov_on_tanh_embeddings(oracle)]),
+    ("bf16 rounding truncates",
+     "if (low > 0x8000u || (low == 0x8000u && (kept & 0x10000u))) kept += 0x10000u;", "(void)low;",
+     [lambda: pins.test_bf16_rounding_equals_torch(oracle)]),
     ("Markov transition from the anchor only",
      "prev = (int32_t)y;", "(void)y;",
      [lambda: pins.test_markov_chain_distribution(oracle)]),

@@ -651,3 +651,116 @@ def test_markov_chain_distribution(orc):
     cells = sorted(exp)
     chi2 = sum((obs.get(c, 0) - N * exp[c]) ** 2 / (N * exp[c]) for c in cells)
     assert chi2 < stats.chi2.ppf(1 - 1e-6, len(cells) - 1)
+
+
+# ------------------------------------------------------------------ RNN ----
+
+def _torch_bf16(x):
+    import torch
+    return torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _torch_tanh_bf16(a):
+    """bf16(tanh(a)) for binary32 a, by torch on the CPU (its own tanh and
+    bf16 conversion)."""
+    import torch
+    t = torch.tanh(torch.tensor(np.asarray(a, np.float32)))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_rounding_equals_torch(orc):
+    """Round-to-nearest-even to bf16 against torch's float32 -> bfloat16
+    conversion, on random values, exact halfway cases (both parities),
+    subnormals, zeros and infinities."""
+    rng = np.random.default_rng(101)
+    xs = list(rng.normal(0, 1, 3000).astype(np.float32)) + list(rng.normal(0, 1e-38, 200).astype(np.float32))
+    bits = rng.integers(0, 2 ** 31, 2000, dtype=np.int64).astype(np.uint32)
+    halfway = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    xs += list(halfway.view(np.float32)) + list((halfway | np.uint32(0x80000000)).view(np.float32))
+    xs += [0.0, -0.0, np.inf, -np.inf, 1.0, 3.0, 65504.0]
+    xs = np.array([x for x in xs if np.isfinite(x) or np.isinf(x)], np.float32)
+    got = np.array([orc.bf16(float(x)) for x in xs])
+    want = _torch_bf16(xs)
+    assert np.array_equal(got, want)
+
+
+def test_rnn_without_recurrence_is_markov_on_tanh_embeddings(orc):
+    """A = 0 removes the in-block memory: hb_k = bf16(tanh(U[x_{k-1}])), so
+    the RNN head equals the Markov head run with U' = bf16(tanh(U)) (computed
+    here by torch) -- same draws, same logits."""
+    rng = np.random.default_rng(102)
+    B, gam, V, R = 4, 5, 200, 16
+    base = rng.normal(0, 3, (B, gam, V))
+    U = _torch_bf16(rng.normal(0, 0.8, (V, R)))
+    W = _torch_bf16(rng.normal(0, 0.5, (R, V)))
+    x0 = rng.integers(0, V, B)
+    r = orc.rnn_draft(base, U, W, np.zeros((R, R)), x0, temperature=0.9, seed=5)
+    Ut = _torch_tanh_bf16(U)
+    m = orc.markov_draft(base, Ut, W, x0, temperature=0.9, seed=5)
+    assert (r.state_margin > 4).all()
+    assert np.array_equal(r.draft, m.draft)
+    assert np.allclose(r.q_logits, m.q_logits, rtol=0, atol=1e-12)
+    prev = x0.copy()
+    for k in range(gam):
+        assert np.array_equal(r.states[:, k], Ut[prev])
+        prev = r.draft[:, k]
+
+
+def test_rnn_state_recurrence_against_numpy(orc):
+    """The states chain through the sampled tokens: hb_k = bf16(tanh(U[x_{k-1}]
+    + hb_{k-1} A)) with hb_0 = 0 (numpy float64 matmul, torch tanh and bf16);
+    entries the oracle reports within 64 binary32 ulps of a rounding midpoint
+    may differ by rounding order and are skipped.  The logits are
+    base_k + hb_k W."""
+    rng = np.random.default_rng(103)
+    B, gam, V, R = 3, 6, 120, 24
+    base = rng.normal(0, 3, (B, gam, V))
+    U = _torch_bf16(rng.normal(0, 0.7, (V, R)))
+    W = _torch_bf16(rng.normal(0, 0.5, (R, V)))
+    A = _torch_bf16(rng.normal(0, 0.4, (R, R)))
+    x0 = rng.integers(0, V, B)
+    r = orc.rnn_draft(base, U, W, A, x0, seed=6)
+    hb = np.zeros((B, R))
+    prev = x0.copy()
+    checked = 0
+    for k in range(gam):
+        a = U[prev] + hb @ A
+        want = _torch_tanh_bf16(a)
+        ok = r.state_margin[:, k] > 64
+        assert np.array_equal(r.states[ok, k], want[ok])
+        checked += int(ok.sum())
+        assert np.allclose(r.q_logits[:, k] - base[:, k], r.states[:, k] @ W, rtol=0, atol=1e-10)
+        hb = r.states[:, k]
+        prev = r.draft[:, k]
+    assert checked >= B * gam - 2
+    # the recurrence matters: a later state differs from the memoryless one
+    assert not np.array_equal(r.states[:, -1], _torch_tanh_bf16(U[r.draft[:, -2]]))
+
+
+def test_rnn_chain_distribution(orc):
+    """Monte Carlo: (x_1, x_2) follows P(x1) P(x2 | x1) with
+    P(x1) = softmax(base_1 + hb_1 W), hb_1 = bf16(tanh(U[x0])), and
+    P(. | x1) = softmax(base_2 + hb_2 W), hb_2 = bf16(tanh(U[x1] + hb_1 A))."""
+    rng = np.random.default_rng(104)
+    N, gam, V, R = 40000, 2, 3, 2
+    base1 = rng.normal(0, 1, (gam, V))
+    U = _torch_bf16(rng.normal(0, 1, (V, R)))
+    W = _torch_bf16(rng.normal(0, 1.5, (R, V)))
+    A = _torch_bf16(rng.normal(0, 1.5, (R, R)))
+    x0 = 1
+    r = orc.rnn_draft(np.broadcast_to(base1, (N, gam, V)), U, W, A, np.full(N, x0), seed=8, want_q=False)
+    sm = lambda z: np.exp(z - special.logsumexp(z))
+    h1 = _torch_tanh_bf16(U[x0])
+    P1 = sm(base1[0] + h1 @ W)
+    exp = {}
+    for a in range(V):
+        h2 = _torch_tanh_bf16(U[a] + h1 @ A)
+        P2 = sm(base1[1] + h2 @ W)
+        for c in range(V):
+            exp[(a, c)] = P1[a] * P2[c]
+    obs = {}
+    for row in r.draft:
+        obs[(row[0], row[1])] = obs.get((row[0], row[1]), 0) + 1
+    cells = sorted(exp)
+    chi2 = sum((obs.get(c, 0) - N * exp[c]) ** 2 / (N * exp[c]) for c in cells)
+    assert chi2 < stats.chi2.ppf(1 - 1e-6, len(cells) - 1)
