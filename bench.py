@@ -17,13 +17,13 @@ steps.  Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
        [--copy-probe]   (accepted for the recorded profile commands; the copy probe always runs)
-       [--workload headline|tiny|batched|block|block_async|markov|all]
+       [--workload headline|tiny|batched|block|block_async|markov|rnn|all]
 The other workloads (one JSON line each, same fields) measure the tiny and
 batched token-verification batches, scheduler + block verification
 (B=512, gamma=8), the same with temperature-scaled confidences and the
 scheduler two steps ahead on a second stream, and the Markov-head sampler
 followed by verification (B=128, gamma=8, R=256; its roofline entry adds the
-MFMA rate).
+MFMA rate), and the RNN-head draft on the same inputs.
 """
 import argparse
 import hashlib
@@ -307,6 +307,39 @@ def bench_markov(args, L, WL):
                  two_call_verified_positions_per_s=round(B * gamma / (ms2 / 1e3), 1))
 
 
+def bench_rnn(args, L, WL):
+    """RNN-head draft sampling on workload 4's inputs plus a recurrent matrix:
+    gamma positions, each the contraction with the bf16 state, the draw, and
+    the next state (no logit rows stored).  Also timed: the Markov head's
+    draft alone on the same inputs, the cost the recurrence adds to."""
+    import torch
+    mi = WL.make_markov_inputs("cuda")
+    A = WL.make_rnn_recurrence(mi.R, "cuda")
+    B, gamma, V, R = mi.B, mi.gamma, mi.V, mi.R
+    draft = torch.empty(B, gamma, dtype=torch.int32, device="cuda")
+    lse = torch.empty(B, gamma, dtype=torch.float32, device="cuda")
+    ctx = L.Context(0, B, gamma, V, R)
+
+    def step(k):
+        L.rnn_draft_run(ctx, mi.base, mi.U, mi.Wt, A, mi.x0, draft, lse_q=lse, temperature=mi.T,
+                        seed=WL.DRAFT_SEED, offset=k)
+
+    ms, _ = _time_steps(step, args.warmup, args.steps)
+    prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
+    ctx.close()
+    gemm_us = _mean_us(prof, "markov_gemm")
+    bytes_gemm = B * V * 2 + R * V * 2 + B * R * 2   # base_k + W + the state rows (no z row stored)
+    flops = 2.0 * B * R * V
+    roof = _hbm_roofline("k_markov_gemm", bytes_gemm, gemm_us)
+    roof["mfma_tflops"] = round(flops / (gemm_us * 1e-6) / 1e12, 2)
+    roof["mfma_frac_of_bf16_peak"] = round(flops / (gemm_us * 1e-6) / 2.5e15, 4)
+    return _line("drafted positions/s, B=128 gamma=8 V=129,280 R=256, RNN-head draft",
+                 B * gamma / (ms / 1e3), "drafted positions/s", args, ms,
+                 {"workload": "RNN-head draft sampling (R=256, Elman state over the Markov factors; "
+                              "no logit rows stored)", "B": B, "gamma": gamma, "V": V, "R": R},
+                 roof, kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
+
+
 def bench_block_async(args, L, WL):
     """Workload 5 with temperature-scaled confidences and the scheduler run
     two steps ahead: at step k a second stream (own context) schedules from
@@ -396,7 +429,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "tiny", "batched", "block", "block_async", "markov", "all"],
+                    choices=["headline", "tiny", "batched", "block", "block_async", "markov", "rnn", "all"],
                     help="headline (default: the one JSON line the driver reads) or another workload")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -414,7 +447,8 @@ def main():
             "batched": lambda: bench_token(args, L, WL, 2, 4),
             "block": lambda: bench_block(args, L, WL),
             "block_async": lambda: bench_block_async(args, L, WL),
-            "markov": lambda: bench_markov(args, L, WL)}
+            "markov": lambda: bench_markov(args, L, WL),
+            "rnn": lambda: bench_rnn(args, L, WL)}
     names = list(runs) if args.workload == "all" else [args.workload]
     for n in names:
         print(json.dumps(runs[n]()), flush=True)

@@ -229,6 +229,31 @@ sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream,
                             int32_t *draft_tokens, int32_t *accepted_len, int32_t *out_tokens,
                             float *lse_q, const sv_diag *diag);
 
+/* RNN-head draft sampler ("DeepSeek DSpark 详解", section 03: a recurrent
+ * head keeps an in-block state and so uses more of the prefix than the
+ * previous token; the pages give no equations, and this is an Elman
+ * recurrence over the Markov head's factors).  For k = 1..gamma, strictly
+ * left to right, with h_0 = 0:
+ *   a_k[j] = U[x_{k-1}, j] + sum_r A[j, r] hb_{k-1}[r]   (fp32, sequential
+ *            fused multiply-adds over r = 0..R-1 starting from U[x_{k-1}, j])
+ *   hb_k   = bf16(tanh(a_k))   (round to nearest, ties to even)
+ *   z_k[n] = base_k[n] + sum_r hb_k[r] W[r, n]   (bf16 inputs, fp32 accumulation)
+ *   x_k    = inverse-CDF draw from softmax(z_k / temperature), uniform tag 2.
+ * With A = 0 it is the Markov head on bf16(tanh(U)).
+ *   A             [R, R] bf16 device, 16-byte aligned, in a linear layer's
+ *                 layout [out, in]: A[j, r] takes state entry r into entry j
+ *   states        [B, gamma, R] bf16 out or NULL: hb_k, the state position k
+ *                 used (not written for a request whose draw failed)
+ *   other arguments as markov_draft_run.  With q_logits NULL no logit row is
+ *   stored (the draw rebuilds the 128 logits of its chosen tile); the
+ *   context's workspace holds the state between positions, so calls on one
+ *   context must not overlap. */
+sv_status rnn_draft_run(sv_ctx *ctx, hipStream_t stream,
+                        const void *base_logits, const void *U, const void *Wt, const void *A, int R,
+                        const int32_t *x0, int B, int gamma, int64_t V, float temperature,
+                        uint64_t seed, uint64_t offset, const float *uniforms,
+                        int32_t *draft_tokens, float *q_logits, float *lse_q, uint16_t *states);
+
 /* ---- Measurement ------------------------------------------------------
  * Per-kernel timing with HIP events recorded on the caller's stream around
  * every kernel the library launches (the kernels themselves are unchanged).
@@ -241,8 +266,8 @@ typedef enum {
     SV_KERNEL_SELECT = 4,        /* inverse-CDF draw of the correction / bonus token     */
     SV_KERNEL_TAIL = 5,          /* accept + weight sums + draw fused, one workgroup per request */
     SV_KERNEL_SCHEDULE = 6,      /* prefix scheduler                                     */
-    SV_KERNEL_MARKOV_GEMM = 7,   /* Markov head contraction + epilogue (per position)    */
-    SV_KERNEL_MARKOV_SELECT = 8, /* Markov head draw (per position)                      */
+    SV_KERNEL_MARKOV_GEMM = 7,   /* Markov / RNN head contraction + epilogue (per position) */
+    SV_KERNEL_MARKOV_SELECT = 8, /* Markov / RNN head draw (+ RNN state update), per position */
     SV_KERNEL_MARKOV_REBUILD = 9,/* fused path: correction rows rebuilt after the scan   */
     SV_KERNEL_COUNT = 10
 } sv_kernel;

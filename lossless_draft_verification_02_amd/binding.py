@@ -21,7 +21,7 @@ SV_FLAG_BAD_TOKEN, SV_FLAG_BAD_ROW, SV_FLAG_RESID_ZERO, SV_FLAG_BAD_VERIFY_LEN =
 
 EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error",
             "spec_verify_device_status", "spec_verify_run", "spec_schedule_run", "spec_schedule_sts_run",
-            "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "spec_verify_profile_enable",
+            "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "rnn_draft_run", "spec_verify_profile_enable",
             "spec_verify_profile_read")
 KERNELS = ("rowstats", "accept", "block_pass2", "resid", "select", "tail", "schedule", "markov_gemm",
            "markov_select", "markov_rebuild")
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.markov_draft_run.argtypes = [P, P, P, P, P, I, P, I, I, I64, F, U64, U64, P, P, P, P]
     lib.markov_verify_run.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I64, F, U64, U64, U64, P, P, P, P, P]
     lib.markov_verify_run.restype = I
+    lib.rnn_draft_run.argtypes = [P, P, P, P, P, P, I, P, I, I, I64, F, U64, U64, P, P, P, P, P]
+    lib.rnn_draft_run.restype = I
     lib.markov_draft_run.restype = I
     lib.spec_verify_profile_enable.argtypes = [P, I]
     lib.spec_verify_profile_enable.restype = I
@@ -287,6 +289,29 @@ def markov_draft_run(ctx: Context, base, U, Wt, x0, draft_out, *, q_logits=None,
     _check("markov_draft_run", load_library().markov_draft_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), R, _ptr(x0), B, gamma, V,
         temperature, seed, offset, _ptr(uniforms), _ptr(draft_out), _ptr(q_logits), _ptr(lse_q)))
+
+
+def rnn_draft_run(ctx: Context, base, U, Wt, A, x0, draft_out, *, q_logits=None, lse_q=None, states=None,
+                  temperature: float = 1.0, seed: int = 0, offset: int = 0, uniforms=None, stream=None):
+    """RNN-head sampler: as markov_draft_run plus the recurrent matrix A [R, R]
+    (bf16); states [B, gamma, R] bf16 receives the state each position used."""
+    torch = _torch()
+    B, gamma, V = base.shape
+    R = U.shape[1]
+    _need(base, "base", dtype=torch.bfloat16, device=ctx.device)
+    _need(U, "U", dtype=torch.bfloat16, shape=(V, R), device=ctx.device)
+    _need(Wt, "Wt", dtype=torch.bfloat16, shape=(V, R), device=ctx.device)
+    _need(A, "A", dtype=torch.bfloat16, shape=(R, R), device=ctx.device)
+    _need(x0, "x0", dtype=torch.int32, shape=(B,), device=ctx.device)
+    _need(draft_out, "draft_out", dtype=torch.int32, shape=(B, gamma), device=ctx.device)
+    _need(q_logits, "q_logits", dtype=torch.float32, shape=(B, gamma, V), device=ctx.device)
+    _need(lse_q, "lse_q", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
+    _need(states, "states", dtype=torch.bfloat16, shape=(B, gamma, R), device=ctx.device)
+    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
+    _check("rnn_draft_run", load_library().rnn_draft_run(
+        ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), _ptr(A), R, _ptr(x0), B, gamma,
+        V, temperature, seed, offset, _ptr(uniforms), _ptr(draft_out), _ptr(q_logits), _ptr(lse_q),
+        _ptr(states)))
 
 
 def markov_verify_run(ctx: Context, base, U, Wt, x0, p, draft_out, accepted_len, out_tokens, *, lse_q=None,

@@ -167,6 +167,9 @@ svh::MarkovArgs make_markov_args(const void *base_logits, const void *U, const v
     a.fused = false;
     a.lse2_out = nullptr;
     a.zx_out = nullptr;
+    a.A = nullptr;
+    a.hstate = nullptr;
+    a.states_out = nullptr;
     return a;
 }
 
@@ -233,6 +236,7 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_sched = carve((size_t)max_batch * sizeof(int32_t));
     const size_t o_srank = carve((size_t)svh::kSchedMax * sizeof(int32_t));
     const size_t o_ssurv = carve((size_t)svh::kSchedMax * sizeof(double));
+    const size_t o_rnnh = carve((size_t)max_batch * (max_rank > 0 ? max_rank : 1) * sizeof(uint16_t));
     size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0, o_mklse = 0, o_mkzx = 0;
     if (max_rank > 0) {
         o_mkpart = carve((size_t)max_batch * ctx->ntile * sizeof(float2));
@@ -265,6 +269,7 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.sched_len = (int32_t *)(b + o_sched);
     ctx->ws.sched_rank = (int32_t *)(b + o_srank);
     ctx->ws.sched_surv = (double *)(b + o_ssurv);
+    ctx->ws.rnn_h = (uint16_t *)(b + o_rnnh);
     ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
     ctx->ws.mk_prev = max_rank > 0 ? (int32_t *)(b + o_mkprev) : nullptr;
     ctx->ws.mk_q = max_rank > 0 ? (float *)(b + o_mkq) : nullptr;
@@ -479,6 +484,30 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_log
     svh::MarkovArgs a = make_markov_args(base_logits, U, W, R, x0, B, gamma, V, temperature, seed, offset,
                                          uniforms, draft_tokens, q_logits, lse_q);
     st = check_launch(svh::launch_markov(ctx, a, stream), "Markov sampler");
+    return st != SV_OK ? st : ok();
+}
+
+sv_status rnn_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_logits, const void *U, const void *W,
+                        const void *A, int R, const int32_t *x0, int B, int gamma, int64_t V, float temperature,
+                        uint64_t seed, uint64_t offset, const float *uniforms, int32_t *draft_tokens,
+                        float *q_logits, float *lse_q, uint16_t *states)
+{
+    sv_status st = check_markov_args(ctx, base_logits, U, W, R, x0, B, gamma, V, temperature, draft_tokens,
+                                     "rnn_draft_run");
+    if (st != SV_OK) return st;
+    if (!A) return fail(SV_ERR_INVALID, "rnn_draft_run: A is required");
+    if (!aligned(A, 16) || (states && !aligned(states, 2)))
+        return fail(SV_ERR_INVALID, "rnn_draft_run: A must be 16-byte aligned and states 2-byte aligned");
+    if (q_logits && !aligned(q_logits, 4))
+        return fail(SV_ERR_INVALID, "rnn_draft_run: q_logits must be 4-byte aligned");
+    DeviceGuard guard(ctx->device);
+    svh::MarkovArgs a = make_markov_args(base_logits, U, W, R, x0, B, gamma, V, temperature, seed, offset,
+                                         uniforms, draft_tokens, q_logits, lse_q);
+    a.A = (const uint16_t *)A;
+    a.hstate = ctx->ws.rnn_h;
+    a.states_out = states;
+    a.fused = q_logits == nullptr;   // no z rows wanted: the draw rebuilds its tile
+    st = check_launch(svh::launch_markov(ctx, a, stream), "RNN-head sampler");
     return st != SV_OK ? st : ok();
 }
 

@@ -27,6 +27,17 @@
 //                    pairs into the row's log-sum-exp, pick the tile holding
 //                    u * Z by an fp64 wavefront scan, scan inside it for the
 //                    token (inverse CDF in ascending token order).
+//
+// RNN head ("DeepSeek DSpark 详解", section 03: a recurrent head carries an
+// in-block state, so a draw can use more of the prefix than the previous
+// token).  Same contraction and draw, with the bf16 state hb_k as the left
+// operand in place of U[x_{k-1}]: h_0 = 0, a_k = U[x_{k-1}] + A hb_{k-1}
+// (A in linear-layer layout [out, in]; fp32, sequential fused multiply-adds
+// over the state index starting from U[x_{k-1}]), hb_k = bf16(tanh(a_k)),
+// round to nearest even.  hb_1 =
+// bf16(tanh(U[x_0])) is formed wherever it is read; after drawing x_k the
+// draw's workgroup computes hb_{k+1} for its request (a 256 x 256 product,
+// A read from L2) and leaves it for the next position's contraction.
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -47,6 +58,132 @@ __device__ __forceinline__ int prev_token(const svh::MarkovArgs &a, int k, int m
 {
     const int32_t x = k == 1 ? a.x0[m] : a.draft[(int64_t)m * a.gamma + (k - 2)];
     return (x < 0 || (int64_t)x >= a.V) ? 0 : x;   // invalid ids are flagged by the select
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Nearest bf16, ties to even; infinities pass, NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t rnn_first_state(const svh::MarkovArgs &a, int m, int j)
+{
+    int32_t x = a.x0[m];
+    x = (x < 0 || (int64_t)x >= a.V) ? 0 : x;
+    return f32_to_bf16(tanhf(bf16_to_f32(a.U[(int64_t)x * a.R + j])));
+}
+
+// The contraction's left operand for request m at position k, as the KS
+// fragments of lane group lg (entries 8 lg + 32 s .. + 7): U[x_{k-1}] for the
+// Markov head, the state hb_k for the RNN head.
+template <int R>
+__device__ __forceinline__ void head_fragments(const svh::MarkovArgs &a, int k, int m, int lg, bool act,
+                                               bf16x8 (&ufr)[R / 32])
+{
+    constexpr int KS = R / 32;
+    if (!act) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ufr[s] = bf16x8{};
+        return;
+    }
+    if (!a.A) {
+        const uint16_t *urow = a.U + (int64_t)prev_token(a, k, m) * R + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ufr[s] = *(const bf16x8 *)(urow + 32 * s);
+    } else if (k == 1) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint16_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = rnn_first_state(a, m, 8 * lg + 32 * s + e);
+            ufr[s] = __builtin_bit_cast(bf16x8, h);
+        }
+    } else {
+        const uint16_t *hrow = a.hstate + (int64_t)m * R + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ufr[s] = *(const bf16x8 *)(hrow + 32 * s);
+    }
+}
+
+// RNN head, after request b's draw at position k (token xk, -1 if the draw
+// failed), in two phases separated by the caller with a barrier over the
+// NPART wavefronts that share the work (wavefront `part` takes state entries
+// [part R / NPART, (part + 1) R / NPART)):
+//   rnn_fill  hb_k (the state position k used) into the LDS scratch hs[R]
+//             as floats, and to states_out;
+//   rnn_next  for k < gamma, hb_{k+1} = bf16(tanh(U[xk] + A hb_k)) into
+//             hstate: per entry j a sequential fp32 fma chain over r from
+//             U[xk, j], A row j read as 16-byte runs (A in linear-layer
+//             layout [out, in]), batches of loads issued ahead of the fmas.
+// hstate[b] is read only in the first phase and written only in the second.
+template <int R, int NPART>
+__device__ void rnn_fill(const svh::MarkovArgs &a, int k, int b, float *hs, int part)
+{
+    constexpr int PER = R / NPART;
+    const int lane = threadIdx.x & 63;
+    const uint16_t *hrow = a.hstate + (int64_t)b * R;
+#pragma unroll
+    for (int q = 0; q < (PER + 63) / 64; ++q) {
+        const int i = lane + 64 * q;
+        if (i < PER) {
+            const int j = part * PER + i;
+            const uint16_t hbits = k == 1 ? rnn_first_state(a, b, j) : hrow[j];
+            hs[j] = bf16_to_f32(hbits);
+            if (a.states_out) a.states_out[((int64_t)b * a.gamma + (k - 1)) * R + j] = hbits;
+        }
+    }
+}
+
+template <int R, int NPART>
+__device__ void rnn_next(const svh::MarkovArgs &a, int k, int b, int32_t xk, const float *hs, int part)
+{
+    constexpr int PER = R / NPART;
+    constexpr int NC = R / 8;                     // 16-byte runs per A row
+    constexpr int BATCH = NC < 16 ? NC : 16;
+    if (k >= a.gamma) return;
+    const int lane = threadIdx.x & 63;
+    const int32_t x = (xk < 0 || (int64_t)xk >= a.V) ? 0 : xk;
+#pragma unroll
+    for (int q = 0; q < (PER + 63) / 64; ++q) {
+        const int i = lane + 64 * q;
+        if (i >= PER) break;
+        const int j = part * PER + i;
+        const uint16_t *arow = a.A + (int64_t)j * R;
+        float acc = bf16_to_f32(a.U[(int64_t)x * R + j]);
+        for (int c0 = 0; c0 < NC; c0 += BATCH) {
+            uint4 w[BATCH];
+#pragma unroll
+            for (int c = 0; c < BATCH; ++c) w[c] = *(const uint4 *)(arow + 8 * (c0 + c));
+#pragma unroll
+            for (int c = 0; c < BATCH; ++c) {
+                const uint32_t v[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+                const float *h = hs + 8 * (c0 + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc = fmaf(h[2 * e], __uint_as_float(v[e] << 16), acc);
+                    acc = fmaf(h[2 * e + 1], __uint_as_float(v[e] & 0xFFFF0000u), acc);
+                }
+            }
+        }
+        a.hstate[(int64_t)b * R + j] = f32_to_bf16(tanhf(acc));
+    }
+}
+
+// One wavefront does both phases for its request (the non-fused draw).
+template <int R>
+__device__ void rnn_advance_wave(const svh::MarkovArgs &a, int k, int b, int32_t xk, float *hs)
+{
+    rnn_fill<R, 1>(a, k, b, hs, 0);
+    // the wavefront's LDS writes are visible to its own later reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    rnn_next<R, 1>(a, k, b, xk, hs, 0);
 }
 
 // A tile of Wt (TN rows of R bf16) in LDS: row r's 16-byte chunk c sits at
@@ -134,11 +271,7 @@ __global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k,
     int tile = blockIdx.x;
     copy_tile<R>(a, (int64_t)tile * TN, wtile, wid, lane);
     bf16x8 ufr[KS];
-    {
-        const uint16_t *urow = a.U + (int64_t)(act ? prev_token(a, km, m) : 0) * R + 8 * lg;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) ufr[s] = act ? *(const bf16x8 *)(urow + 32 * s) : bf16x8{};
-    }
+    head_fragments<R>(a, km, m, lg, act, ufr);
     const int mb = act ? m : a.B;                      // load_base reads nothing for a.B
     uint2 bv[NVB];
     load_base(a, km, mb, (int64_t)tile * TN, lg, vec, bv);
@@ -342,8 +475,9 @@ __device__ bool select_tile(const svh::MarkovArgs &a, int k, const float2 *__res
 }
 
 // Token of the chosen tile (z values zr[0 .. 128)) by one wavefront: lane
-// owns columns 2 lane, 2 lane + 1; fp64 prefix; outputs.
-__device__ void select_token_in_tile(const svh::MarkovArgs &a, int k, int b, const SelState &st,
+// owns columns 2 lane, 2 lane + 1; fp64 prefix; outputs.  Returns the token
+// (the same on every lane), -1 if none.
+__device__ int32_t select_token_in_tile(const svh::MarkovArgs &a, int k, int b, const SelState &st,
                                      const float *zr, uint32_t *__restrict__ errword)
 {
     const int lane = threadIdx.x & 63;
@@ -375,6 +509,8 @@ __device__ void select_token_in_tile(const svh::MarkovArgs &a, int k, int b, con
         if (a.zx_out) a.zx_out[out] = j >= 0 ? zr[j] : __builtin_nanf("");
         if (j < 0) atomicOr(errword, SV_FLAG_BAD_ROW);
     }
+    const int jj = ybest != 0x7FFFFFFF ? ybest : ylast;
+    return jj >= 0 ? (int32_t)(c0 + jj) : -1;
 }
 
 // The draw with stored z rows: one wavefront per request, no barriers.
@@ -388,6 +524,23 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArg
     SelState st;
     if (!select_tile(a, k, tile_part, ntile, errword, b, st)) return;
     select_token_in_tile(a, k, b, st, zin + (int64_t)b * zstride + (int64_t)st.ts * TN, errword);
+}
+
+// The same draw for the RNN head, then the wavefront advances its request's
+// state.
+template <int R>
+__global__ __launch_bounds__(64 * kSelWaves) void k_rnn_select(svh::MarkovArgs a, int k,
+                                                               const float *__restrict__ zin, int64_t zstride,
+                                                               const float2 *__restrict__ tile_part, int ntile,
+                                                               uint32_t *__restrict__ errword)
+{
+    __shared__ float hs[kSelWaves][R];
+    const int b = blockIdx.x * kSelWaves + (int)(threadIdx.x >> 6);
+    if (b >= a.B) return;   // whole wavefront; nothing below synchronises the workgroup
+    SelState st;
+    if (!select_tile(a, k, tile_part, ntile, errword, b, st)) return;
+    const int32_t xk = select_token_in_tile(a, k, b, st, zin + (int64_t)b * zstride + (int64_t)st.ts * TN, errword);
+    rnn_advance_wave<R>(a, k, b, xk, hs[threadIdx.x >> 6]);
 }
 
 // The draw without stored z rows (fused path): one workgroup of 4 wavefronts
@@ -406,6 +559,8 @@ __global__ __launch_bounds__(256) void k_markov_select_fused(svh::MarkovArgs a, 
     __shared__ SelState st;
     __shared__ int go;
     __shared__ float zt[TN];
+    __shared__ float hs[R];   // RNN head: the request's state
+    __shared__ int32_t xnew;   // the token drawn (RNN head)
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     if (wid == 0) {
@@ -421,10 +576,8 @@ __global__ __launch_bounds__(256) void k_markov_select_fused(svh::MarkovArgs a, 
     const int64_t c0 = (int64_t)st.ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
     const int li = lane & 15, lg = lane >> 4;
-    const uint16_t *urow = a.U + (int64_t)st.xprev * R + 8 * lg;   // the request's U row in every B column
     bf16x8 ufr[KS], afr[VBW][KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) ufr[s] = *(const bf16x8 *)(urow + 32 * s);
+    head_fragments<R>(a, k, b, lg, true, ufr);   // the request's operand row in every B column
 #pragma unroll
     for (int v = 0; v < VBW; ++v) {
         const int64_t n = c0 + 16 * (VBW * wid + v) + li;
@@ -449,7 +602,15 @@ __global__ __launch_bounds__(256) void k_markov_select_fused(svh::MarkovArgs a, 
         }
     }
     svk::lds_barrier();
-    if (wid == 0) select_token_in_tile(a, k, b, st, zt, errword);
+    if (wid == 0) {
+        const int32_t xk = select_token_in_tile(a, k, b, st, zt, errword);
+        if (lane == 0) xnew = xk;
+    }
+    if (a.A) {   // RNN head: the four wavefronts advance the state together
+        rnn_fill<R, 4>(a, k, b, hs, wid);
+        __syncthreads();
+        rnn_next<R, 4>(a, k, b, xnew, hs, wid);
+    }
 }
 
 template <int R>
@@ -476,6 +637,10 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
         if (a.fused)
             hipLaunchKernelGGL((k_markov_select_fused<R>), dim3(a.B), dim3(256), 0, s, a, k,
                                (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword);
+        else if (a.A)
+            hipLaunchKernelGGL((k_rnn_select<R>), dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0,
+                               s, a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,
+                               ctx->ws.errword);
         else
             hipLaunchKernelGGL(k_markov_select, dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0,
                                s, a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,

@@ -63,6 +63,7 @@ struct Workspace {
     int32_t *sched_len;  // [max_batch] scheduler output when the caller gives none
     int32_t *sched_rank; // [kSchedMax] candidate ranks, zero between calls
     double *sched_surv;  // [kSchedMax] candidate survival products
+    uint16_t *rnn_h;     // [max_batch, max_rank] bf16 RNN-head state
     float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials
     int32_t *mk_prev;    // [max_batch] Markov: token sampled at the previous position
     float *mk_q;         // [max_batch * V] Markov logits of the current position when
@@ -194,6 +195,13 @@ struct MarkovArgs {
     bool fused;
     float *lse2_out;       // [B, gamma] (fused)
     float *zx_out;         // [B, gamma] (fused)
+    // RNN head (A != null): the contraction's left operand is the bf16 state
+    // hb_k instead of U[x_{k-1}]; hb_1 = bf16(tanh(U[x_0])) is formed where it
+    // is read, later states come from hstate, written by the draw of the
+    // previous position.
+    const uint16_t *A;     // [R, R] bf16, linear-layer layout: A[j][r] takes state entry r into j
+    uint16_t *hstate;      // [B, R] bf16 workspace
+    uint16_t *states_out;  // [B, gamma, R] bf16 or null
 };
 
 hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s);

@@ -22,6 +22,10 @@ Five workloads (sizes can be shrunk for tests, keeping the recipe):
                confidences: per-request mean mu_b ~ U(0.35, 0.95), decaying 3%
                per position, plus N(0, 0.05^2), clipped to [0, 1].
 
+RNN head (workload 4 variant): workload 4's backbone logits, U, W and
+anchors, plus a recurrent matrix A [R, R] ~ N(0, (0.9 / sqrt(R))^2) in bf16
+(spectral radius about 0.9, so the state neither dies nor saturates).
+
 Temperature-scaled confidences (workload 5 variant): per-position temperatures
 T_i = 1 + 0.15 (i - 1), later positions hotter, and an over-confident head
 whose raw log-odds are T_i times the log-odds of workload 5's confidences
@@ -197,6 +201,13 @@ def make_markov_inputs(device="cpu", B: Optional[int] = None, gamma: Optional[in
     return MarkovInputs(B, gamma, V, R, c["T"], base, U, Wt, x0, p)
 
 
+def make_rnn_recurrence(R: int, device="cpu", std: Optional[float] = None, seed: int = 1006) -> torch.Tensor:
+    """Recurrent matrix A [R, R] bf16 of the RNN-head variant of workload 4."""
+    g = _gen(device, seed)
+    sd = 0.9 / (R ** 0.5) if std is None else std
+    return (torch.randn(R, R, generator=g, device=device) * sd).to(torch.bfloat16)
+
+
 def bytes_single_read(inp: VerifyInputs) -> int:
     """Bytes of every logit row read once (the row-statistics pass)."""
     es = inp.p.element_size()
@@ -209,4 +220,5 @@ def describe(cfg: int) -> str:
 
 
 __all__ = ["CONFIGS", "VERIFY_SEED", "DRAFT_SEED", "VerifyInputs", "MarkovInputs", "make_verify_inputs",
-           "make_markov_inputs", "bytes_single_read", "describe"]
+           "make_markov_inputs", "make_rnn_recurrence", "sts_temperatures", "sts_head_logits", "bytes_single_read",
+           "describe"]

@@ -535,13 +535,15 @@ int orc_markov_draft(const double *base, const double *U, const double *W, int R
 /* head keeps an in-block state, so each draw can use more of the prefix      */
 /* than the previous token alone).  The pages give no equations; the plain    */
 /* reading taken here is an Elman recurrence with the Markov head's factors:  */
-/*   h_0 = 0,  a_k = U[x_{k-1}] + hb_{k-1} . A,  h_k = tanh(a_k),             */
+/*   h_0 = 0,  a_k = U[x_{k-1}] + A hb_{k-1},  h_k = tanh(a_k),               */
 /*   hb_k = bf16(h_k),  z_k = base_k + hb_k . W,  x_k ~ softmax(z_k / T).     */
 /* The state is a bf16 activation like the factors; rounding it is a          */
 /* quantisation decision, taken in the kernels' precision: a_k accumulated    */
 /* in binary32 by sequential fused multiply-adds over r = 0..R-1 starting     */
 /* from U[x_{k-1}], tanh in binary32, then round-to-nearest-even to bf16.     */
-/* The contraction z_k is binary64 like the Markov head's.                    */
+/* A is stored as a linear layer's weight, [out, in]: A[j][r] takes state     */
+/* entry r into entry j.  The contraction z_k is binary64 like the Markov     */
+/* head's.                                                                    */
 /* ------------------------------------------------------------------------- */
 
 /* Round a binary32 value to the nearest bf16 (8 significant bits), ties to
@@ -599,11 +601,11 @@ int orc_rnn_draft(const double *base, const double *U, const double *W, const do
         int32_t prev = x0 ? x0[b] : 0;
         if (gamma > 0 && (prev < 0 || (int64_t)prev >= V)) fl |= ORC_FLAG_BAD_TOKEN;
         for (int k = 1; k <= gamma && !fl; ++k) {
-            /* state update: a = U[x_{k-1}] + hb_{k-1} . A, binary32 fma chain */
+            /* state update: a = U[x_{k-1}] + A hb_{k-1}, binary32 fma chain */
             double qmin = INFINITY;
             for (int j = 0; j < R; ++j) {
                 float acc = (float)U[(int64_t)prev * R + j];
-                for (int r = 0; r < R; ++r) acc = fmaf(hb[r], (float)A[(int64_t)r * R + j], acc);
+                for (int r = 0; r < R; ++r) acc = fmaf(hb[r], (float)A[(int64_t)j * R + r], acc);
                 double d;
                 hn[j] = orc_bf16_round(tanhf(acc), &d);
                 if (d < qmin) qmin = d;

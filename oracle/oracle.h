@@ -156,10 +156,11 @@ int orc_markov_draft(const double *base, const double *U, const double *W, int R
 float orc_bf16(float x);
 
 /* RNN-head draft sampler [ZS 03] (the reading is in orc_rnn_draft's
- * definition): h_0 = 0; a_k = U[x_{k-1}] + hb_{k-1} . A in binary32
+ * definition): h_0 = 0; a_k = U[x_{k-1}] + A hb_{k-1} in binary32
  * (sequential fma over r from U[x_{k-1}]); hb_k = bf16(tanhf(a_k));
  * z_k = base_k + hb_k . W (binary64); x_k ~ softmax(z_k / T) by inverse CDF
- * with uniform (req, k, tag 2).  A [R, R] (row r multiplies state entry r).
+ * with uniform (req, k, tag 2).  A [R, R] in linear-layer layout [out, in]:
+ * A[j][r] takes state entry r into entry j.
  * Outputs as orc_markov_draft, plus states [B, gamma, R] (nullable) = hb_k
  * and state_margin [B, gamma] (nullable) = the smallest distance, in binary32
  * ulps, of any tanhf(a_k) entry from its bf16 rounding midpoint. */

@@ -186,3 +186,45 @@ def compare_markov(g_draft, g_lse, g_q, orc, rep: Report | None = None, q_atol: 
                     rep.failures.append((b, k, "draw", o, g, float(orc.margin[b, k])))
                 break
     return rep
+
+
+STATE_MARGIN_ULPS = 4.0   # bf16 state rounding: flips allowed this close (binary32 ulps) to a midpoint
+
+
+def compare_rnn(g_draft, g_lse, g_q, g_states, orc, rep: Report | None = None, q_atol: float = 2e-5) -> Report:
+    """RNN-head sampler, walked per request left to right: at each position the
+    bf16 state (bit-exact unless the oracle puts an entry within
+    STATE_MARGIN_ULPS of its rounding midpoint), then the logits, the
+    normaliser and the draw as for the Markov head; a request stops at its
+    first (flipped) disagreement."""
+    rep = rep or Report()
+    B, gamma = orc.draft.shape
+    for b in range(B):
+        rep.requests += 1
+        for k in range(gamma):
+            if g_states is not None:
+                gs = np.asarray(g_states[b, k], np.float64)
+                if not np.array_equal(gs, orc.states[b, k]):
+                    if orc.state_margin[b, k] <= STATE_MARGIN_ULPS:
+                        rep.flips += 1
+                    else:
+                        bad = int(np.argmax(gs != orc.states[b, k]))
+                        rep.failures.append((b, k, "state", bad, float(gs[bad]), float(orc.states[b, k, bad]),
+                                             float(orc.state_margin[b, k])))
+                    break
+            o, g = int(orc.draft[b, k]), int(g_draft[b, k])
+            if g_q is not None and orc.q_logits is not None:
+                err = float(np.abs(np.asarray(g_q[b, k], np.float64) - orc.q_logits[b, k]).max())
+                rep.max_prob_err = max(rep.max_prob_err, err)
+                if err > q_atol:
+                    rep.failures.append((b, k, "q logits", err))
+                    break
+            if g_lse is not None:
+                _close_lse(rep, [g_lse[b, k]], [orc.lse_q[b, k]], f"lse_q[{k}]", b)
+            if o != g:
+                if orc.margin[b, k] <= MARGIN:
+                    rep.flips += 1
+                else:
+                    rep.failures.append((b, k, "draw", o, g, float(orc.margin[b, k])))
+                break
+    return rep

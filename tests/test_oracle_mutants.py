@@ -81,7 +81,11 @@ MUTANTS = [
      "exp(-(l / temps[i]))", "exp(l / temps[i])",
      [lambda: pins.test_sts_closed_forms(oracle)]),
     ("RNN state ignores the recurrent matrix",
-     "acc = fmaf(hb[r], (float)A[(int64_t)r * R + j], acc);", "acc = fmaf(hb[r], 0.0f, acc);",
+     "acc = fmaf(hb[r], (float)A[(int64_t)j * R + r], acc);", "acc = fmaf(hb[r], 0.0f, acc);",
+     [lambda: pins.test_rnn_state_recurrence_against_numpy(oracle),
+      lambda: pins.test_rnn_chain_distribution(oracle)]),
+    ("RNN recurrent matrix transposed",
+     "acc = fmaf(hb[r], (float)A[(int64_t)j * R + r], acc);", "acc = fmaf(hb[r], (float)A[(int64_t)r * R + j], acc);",
      [lambda: pins.test_rnn_state_recurrence_against_numpy(oracle),
       lambda: pins.test_rnn_chain_distribution(oracle)]),
     ("RNN state not carried to the next position",

@@ -708,7 +708,7 @@ def test_rnn_without_recurrence_is_markov_on_tanh_embeddings(orc):
 
 def test_rnn_state_recurrence_against_numpy(orc):
     """The states chain through the sampled tokens: hb_k = bf16(tanh(U[x_{k-1}]
-    + hb_{k-1} A)) with hb_0 = 0 (numpy float64 matmul, torch tanh and bf16);
+    + A hb_{k-1})) with hb_0 = 0 (A [out, in]) (numpy float64 matmul, torch tanh and bf16);
     entries the oracle reports within 64 binary32 ulps of a rounding midpoint
     may differ by rounding order and are skipped.  The logits are
     base_k + hb_k W."""
@@ -724,7 +724,7 @@ def test_rnn_state_recurrence_against_numpy(orc):
     prev = x0.copy()
     checked = 0
     for k in range(gam):
-        a = U[prev] + hb @ A
+        a = U[prev] + hb @ A.T          # A in linear-layer layout [out, in]
         want = _torch_tanh_bf16(a)
         ok = r.state_margin[:, k] > 64
         assert np.array_equal(r.states[ok, k], want[ok])
@@ -740,7 +740,7 @@ def test_rnn_state_recurrence_against_numpy(orc):
 def test_rnn_chain_distribution(orc):
     """Monte Carlo: (x_1, x_2) follows P(x1) P(x2 | x1) with
     P(x1) = softmax(base_1 + hb_1 W), hb_1 = bf16(tanh(U[x0])), and
-    P(. | x1) = softmax(base_2 + hb_2 W), hb_2 = bf16(tanh(U[x1] + hb_1 A))."""
+    P(. | x1) = softmax(base_2 + hb_2 W), hb_2 = bf16(tanh(U[x1] + A hb_1))."""
     rng = np.random.default_rng(104)
     N, gam, V, R = 40000, 2, 3, 2
     base1 = rng.normal(0, 1, (gam, V))
@@ -754,7 +754,7 @@ def test_rnn_chain_distribution(orc):
     P1 = sm(base1[0] + h1 @ W)
     exp = {}
     for a in range(V):
-        h2 = _torch_tanh_bf16(U[a] + h1 @ A)
+        h2 = _torch_tanh_bf16(U[a] + A @ h1)
         P2 = sm(base1[1] + h2 @ W)
         for c in range(V):
             exp[(a, c)] = P1[a] * P2[c]
