@@ -229,10 +229,12 @@ sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream,
                             int32_t *draft_tokens, int32_t *accepted_len, int32_t *out_tokens,
                             float *lse_q, const sv_diag *diag);
 
-/* RNN-head draft sampler ("DeepSeek DSpark 详解", section 03: a recurrent
- * head keeps an in-block state and so uses more of the prefix than the
- * previous token; the pages give no equations, and this is an Elman
- * recurrence over the Markov head's factors).  For k = 1..gamma, strictly
+/* RNN-head draft sampler ("DeepSeek DSpark 详解", section 03; "DSpark:
+ * DeepSeek's bet on speed that doesn't betray quality", section "A drafter
+ * that learns to doubt itself": a recurrent head keeps an in-block state and
+ * so uses more of the prefix than the previous token; the pages give no
+ * equations, and this is an Elman recurrence over the Markov head's
+ * factors).  For k = 1..gamma, strictly
  * left to right, with h_0 = 0:
  *   a_k[j] = U[x_{k-1}, j] + sum_r A[j, r] hb_{k-1}[r]   (fp32, sequential
  *            fused multiply-adds over r = 0..R-1 starting from U[x_{k-1}, j])

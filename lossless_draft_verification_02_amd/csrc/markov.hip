@@ -28,9 +28,10 @@
 //                    u * Z by an fp64 wavefront scan, scan inside it for the
 //                    token (inverse CDF in ascending token order).
 //
-// RNN head ("DeepSeek DSpark 详解", section 03: a recurrent head carries an
-// in-block state, so a draw can use more of the prefix than the previous
-// token).  Same contraction and draw, with the bf16 state hb_k as the left
+// RNN head ("DeepSeek DSpark 详解", section 03, and "DSpark: DeepSeek's bet
+// on speed that doesn't betray quality", section "A drafter that learns to
+// doubt itself": the richer head variant carries a recurrent state over the
+// block's prefix, so a draw can use more of it than the previous token).  Same contraction and draw, with the bf16 state hb_k as the left
 // operand in place of U[x_{k-1}]: h_0 = 0, a_k = U[x_{k-1}] + A hb_{k-1}
 // (A in linear-layer layout [out, in]; fp32, sequential fused multiply-adds
 // over the state index starting from U[x_{k-1}]), hb_k = bf16(tanh(a_k)),
