@@ -65,6 +65,10 @@ def declare(lib):
     lib.orc_rnn_draft.argtypes = [P, P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
                                   P, P, P, P, P, P, P, P]
     lib.orc_rnn_draft.restype = i32
+    lib.orc_tree_depth.argtypes = [P, i32]
+    lib.orc_tree_depth.restype = i32
+    lib.orc_tree_verify.argtypes = [P, P, P, P, i32, P, i32, i64, f32, u64, u64, P, P, P, P, P, P, P, P]
+    lib.orc_tree_verify.restype = i32
     lib.orc_sts_confidence.argtypes = [P, P, i32, i32, P]
     lib.orc_sts_confidence.restype = i32
     lib.orc_markov_draft.argtypes = [P, P, P, i32, P, P, i32, i32, i64, f32, u64, u64,
@@ -292,3 +296,52 @@ def rnn_draft(base, U, W, A, x0, temperature=1.0, seed=0, offset=0, req_ids=None
     if rc != 0:
         raise ValueError("orc_rnn_draft: invalid arguments")
     return RnnResult(draft, ql, lse, marg, flags, states, smarg)
+
+
+@dataclass
+class TreeResult:
+    accepted_len: np.ndarray     # [B]
+    out_tokens: np.ndarray       # [B, D+1]
+    accepted_nodes: np.ndarray   # [B, D]
+    flags: np.ndarray            # [B]
+    ratio: np.ndarray            # [B, N]
+    dec_margin: np.ndarray       # [B, N]
+    icdf_margin: np.ndarray      # [B]
+
+
+def tree_depth(parents) -> int:
+    par = _i32(parents)
+    d = _load().orc_tree_depth(_ptr(par), len(par))
+    if d < 0:
+        raise ValueError("invalid tree: parents[m-1] must lie in [0, m-1]")
+    return d
+
+
+def tree_verify(p, q, tokens, parents, temperature=1.0, seed=0, offset=0, req_ids=None,
+                uniforms=None) -> TreeResult:
+    """Tree verification; see orc_tree_verify in oracle.h."""
+    p = _f64(p)
+    B, N1, V = p.shape
+    N = N1 - 1
+    par = _i32(parents)
+    if len(par) != N:
+        raise ValueError("one parent per non-root node")
+    D = tree_depth(par)
+    NQ = len(set(int(x) for x in par))
+    q = _f64(q) if NQ else np.zeros((B, 0, V))
+    if q.shape != (B, NQ, V):
+        raise ValueError(f"q must be [B, {NQ}, V]: one row per node with children")
+    tok = _i32(tokens).reshape(B, N) if N else np.zeros((B, 0), np.int32)
+    acc = np.zeros(B, np.int32)
+    out = np.zeros((B, D + 1), np.int32)
+    nodes = np.zeros((B, max(D, 1)), np.int32)
+    flags = np.zeros(B, np.uint32)
+    ratio = np.zeros((B, max(N, 1)))
+    dm = np.zeros((B, max(N, 1)))
+    im = np.zeros(B)
+    rc = _load().orc_tree_verify(_ptr(p), _ptr(q), _ptr(tok), _ptr(par), N, _ptr(_i32(req_ids)), B, V,
+                                 temperature, seed, offset, _ptr(_f32(uniforms)), _ptr(acc), _ptr(out),
+                                 _ptr(nodes), _ptr(flags), _ptr(ratio), _ptr(dm), _ptr(im))
+    if rc != 0:
+        raise ValueError("orc_tree_verify: invalid arguments")
+    return TreeResult(acc, out, nodes[:, :D], flags, ratio[:, :N], dm[:, :N], im)

@@ -641,3 +641,170 @@ int orc_rnn_draft(const double *base, const double *U, const double *W, const do
     free(z); free(wv); free(hb); free(hn);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Tree verification ("Speculative Decoding: The Same Distribution, Twice as */
+/* Fast", section 7: guess a tree of alternative continuations and check all */
+/* of them in one pass).  The page gives no rule; the plain lossless reading */
+/* is recursive rejection over the tree, whose children of a node are drawn  */
+/* independently from the draft distribution q at that node:                 */
+/*   at node n (starting at the root, 0) with residual r = p_n:              */
+/*     for each child c of n in index order, token x:                        */
+/*       accept with probability min(1, r(x) / q_n(x)); if accepted emit x   */
+/*       and continue at c;                                                   */
+/*       else r <- max(r - q_n, 0) normalised;                                */
+/*     if every child was rejected, emit a draw from r and stop;             */
+/*   at a leaf, emit a draw from p_leaf (the bonus token) and stop.          */
+/* The first child's ratio is the token rule's, in log space; a chain-shaped */
+/* tree is token verification decision for decision.                         */
+/* ------------------------------------------------------------------------- */
+int orc_tree_depth(const int32_t *parents, int N)
+{
+    if (N < 0 || (N > 0 && !parents)) return -1;
+    int *dep = (int *)malloc((size_t)(N + 1) * sizeof(int));
+    if (!dep) return -1;
+    dep[0] = 0;
+    int D = 0;
+    for (int m = 1; m <= N; ++m) {
+        const int32_t par = parents[m - 1];
+        if (par < 0 || par >= m) { free(dep); return -1; }
+        dep[m] = dep[par] + 1;
+        if (dep[m] > D) D = dep[m];
+    }
+    free(dep);
+    return D;
+}
+
+int orc_tree_verify(const double *p, const double *q, const int32_t *tokens, const int32_t *parents, int N,
+                    const int32_t *req_ids, int B, int64_t V, float temperature,
+                    uint64_t seed, uint64_t offset, const float *uniforms,
+                    int32_t *accepted_len, int32_t *out_tokens, int32_t *accepted_nodes, uint32_t *flags,
+                    double *ratio_out, double *dec_margin, double *icdf_margin)
+{
+    const int D = orc_tree_depth(parents, N);
+    if (D < 0 || B < 0 || V <= 0) return -1;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return -1;
+    if (B > 0 && (!p || !accepted_len || !out_tokens || (N > 0 && (!q || !tokens)))) return -1;
+    const double T = (double)temperature;
+    /* q row of each internal node: its rank among the nodes with children */
+    int *qrow = (int *)malloc((size_t)(N + 1) * sizeof(int));
+    double *pd = (double *)malloc((size_t)V * sizeof(double));
+    double *qd = (double *)malloc((size_t)V * sizeof(double));
+    double *r = (double *)malloc((size_t)V * sizeof(double));
+    double *lse_p = (double *)malloc((size_t)(N + 1) * sizeof(double));
+    double *lse_q = (double *)malloc((size_t)(N + 1) * sizeof(double));
+    if (!qrow || !pd || !qd || !r || !lse_p || !lse_q) {
+        free(qrow); free(pd); free(qd); free(r); free(lse_p); free(lse_q);
+        return -1;
+    }
+    int NQ = 0;
+    for (int n = 0; n <= N; ++n) {
+        qrow[n] = -1;
+        for (int m = n + 1; m <= N; ++m)
+            if (parents[m - 1] == n) { qrow[n] = NQ++; break; }
+    }
+
+    for (int b = 0; b < B; ++b) {
+        const uint32_t req = req_ids ? (uint32_t)req_ids[b] : (uint32_t)b;
+        const double *pb = p + (int64_t)b * (N + 1) * V;
+        const double *qb = NQ > 0 ? q + (int64_t)b * NQ * V : NULL;
+        const int32_t *xb = N > 0 ? tokens + (int64_t)b * N : NULL;
+        for (int j = 0; j <= D; ++j) out_tokens[(int64_t)b * (D + 1) + j] = -1;
+        if (accepted_nodes)
+            for (int j = 0; j < D; ++j) accepted_nodes[(int64_t)b * D + j] = -1;
+        for (int m = 0; m < N; ++m) {
+            if (ratio_out) ratio_out[(int64_t)b * N + m] = NAN;
+            if (dec_margin) dec_margin[(int64_t)b * N + m] = NAN;
+        }
+        if (icdf_margin) icdf_margin[b] = NAN;
+
+        /* data errors: any token out of range, then any row */
+        uint32_t fl = 0;
+        for (int m = 0; m < N; ++m)
+            if (xb[m] < 0 || (int64_t)xb[m] >= V) fl |= ORC_FLAG_BAD_TOKEN;
+        if (!fl) {
+            for (int n = 0; n <= N; ++n) fl |= orc_row_lse(pb + (int64_t)n * V, V, temperature, &lse_p[n]);
+            for (int n = 0; n <= N; ++n)
+                if (qrow[n] >= 0) fl |= orc_row_lse(qb + (int64_t)qrow[n] * V, V, temperature, &lse_q[n]);
+        }
+        if (flags) flags[b] = fl;
+        if (fl) { accepted_len[b] = -1; continue; }
+
+        int node = 0, depth = 0;
+        int64_t y = -1;
+        double Z = 0.0, marg = 0.0;
+        for (;;) {
+            const double *prow = pb + (int64_t)node * V;
+            const double lp = lse_p[node];
+            float u2 = uniforms ? uniforms[(int64_t)b * (N + 1) + N] : orc_uniform(seed, offset, req, 0, 1);
+            if (qrow[node] < 0) {                       /* leaf: the bonus token from p */
+                for (int64_t v = 0; v < V; ++v) r[v] = exp(prow[v] / T - lp);
+                y = orc_icdf(r, V, u2, &Z, &marg);
+                break;
+            }
+            const double *qr = qb + (int64_t)qrow[node] * V;
+            const double lq = lse_q[node];
+            for (int64_t v = 0; v < V; ++v) {
+                pd[v] = exp(prow[v] / T - lp);
+                qd[v] = exp(qr[v] / T - lq);
+                r[v] = pd[v];                           /* residual weights; total Zr */
+            }
+            double Zr = 1.0;
+            int accepted = -1, rejections = 0;
+            for (int c = node + 1; c <= N; ++c) {
+                if (parents[c - 1] != node) continue;
+                const int32_t x = xb[c - 1];
+                double rt;
+                if (rejections == 0) {
+                    const double lr = (prow[x] / T - lp) - (qr[x] / T - lq);
+                    rt = exp(lr);
+                    if (isnan(rt)) rt = 0.0;
+                } else if (qd[x] > 0.0) {
+                    rt = (r[x] / Zr) / qd[x];
+                } else {
+                    rt = r[x] > 0.0 ? INFINITY : 0.0;
+                }
+                const double ratio = rt < 1.0 ? rt : 1.0;
+                float u = uniforms ? uniforms[(int64_t)b * (N + 1) + (c - 1)]
+                                   : orc_uniform(seed, offset, req, (uint32_t)c, 0);
+                if (ratio_out) ratio_out[(int64_t)b * N + (c - 1)] = ratio;
+                if (dec_margin) dec_margin[(int64_t)b * N + (c - 1)] = fabs((double)u - ratio);
+                if (u < (float)ratio) { accepted = c; break; }
+                /* rejected: r <- max(r / Zr - q, 0), its total the next Zr */
+                double Zn = 0.0;
+                for (int64_t v = 0; v < V; ++v) {
+                    double diff = r[v] / Zr - qd[v];
+                    r[v] = diff > 0.0 ? diff : 0.0;
+                    Zn += r[v];
+                }
+                if (Zn == 0.0) {   /* rounded to zero (positive in exact arithmetic): fall back to p */
+                    for (int64_t v = 0; v < V; ++v) r[v] = pd[v];
+                    Zn = 1.0;
+                    fl |= ORC_FLAG_RESID_ZERO;
+                }
+                Zr = Zn;
+                ++rejections;
+            }
+            if (accepted > 0) {
+                out_tokens[(int64_t)b * (D + 1) + depth] = xb[accepted - 1];
+                if (accepted_nodes) accepted_nodes[(int64_t)b * D + depth] = accepted;
+                ++depth;
+                node = accepted;
+                continue;
+            }
+            y = orc_icdf(r, V, u2, &Z, &marg);          /* every child rejected: the residual */
+            if (y < 0) {
+                for (int64_t v = 0; v < V; ++v) r[v] = pd[v];
+                y = orc_icdf(r, V, u2, &Z, &marg);
+                fl |= ORC_FLAG_RESID_ZERO;
+            }
+            break;
+        }
+        if (flags) flags[b] = fl;
+        if (icdf_margin) icdf_margin[b] = marg;
+        accepted_len[b] = depth;
+        out_tokens[(int64_t)b * (D + 1) + depth] = (int32_t)y;
+    }
+    free(qrow); free(pd); free(qd); free(r); free(lse_p); free(lse_q);
+    return 0;
+}

@@ -1,8 +1,8 @@
 /*
  * oracle.h -- plain, slow CPU reference of lossless speculative-sampling
  * verification, block verification, the confidence prefix scheduler (with
- * temperature-scaled confidences) and the Markov- and RNN-head draft
- * samplers.
+ * temperature-scaled confidences), the Markov- and RNN-head draft samplers
+ * and tree verification.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The GPU library never
@@ -170,6 +170,30 @@ int orc_rnn_draft(const double *base, const double *U, const double *W, const do
                   uint64_t seed, uint64_t offset, const float *uniforms,
                   int32_t *draft, double *q_logits, double *lse_q,
                   double *margin, uint32_t *flags, double *states, double *state_margin);
+
+/* Depth of a tree given by parents[m-1] in [0, m-1] for nodes m = 1..N
+ * (node 0 is the root); -1 for an invalid tree. */
+int orc_tree_depth(const int32_t *parents, int N);
+
+/* Tree verification [SD 7] (the rule is in orc_tree_verify's definition):
+ * recursive rejection over a token tree whose children of a node were drawn
+ * independently from the draft distribution at that node.
+ *   p [B, N+1, V]: row n = target logits after node n (row 0: the root);
+ *   q [B, NQ, V]: draft logits at each node that has children, in node
+ *   order (NQ = their number); tokens [B, N]: token of node m at column
+ *   m-1; parents [N] (host): parent of node m, in [0, m-1].
+ *   Uniforms: node c's test (req, c, tag 0), the final draw (req, 0, tag 1);
+ *   uniforms [B, N+1] (nullable) overrides them (column c-1, column N).
+ * Out (D = the tree's depth): accepted_len [B]; out_tokens [B, D+1] = the
+ * accepted path's tokens, the drawn token, then -1; accepted_nodes [B, D]
+ * (nullable) = the accepted nodes, then -1; flags [B] (nullable); ratio and
+ * dec_margin [B, N] (nullable, NaN where unevaluated) = min(1, r(x)/q(x)) and
+ * |u - ratio| of each evaluated node; icdf_margin [B] (nullable). */
+int orc_tree_verify(const double *p, const double *q, const int32_t *tokens, const int32_t *parents, int N,
+                    const int32_t *req_ids, int B, int64_t V, float temperature,
+                    uint64_t seed, uint64_t offset, const float *uniforms,
+                    int32_t *accepted_len, int32_t *out_tokens, int32_t *accepted_nodes, uint32_t *flags,
+                    double *ratio_out, double *dec_margin, double *icdf_margin);
 
 #ifdef __cplusplus
 }

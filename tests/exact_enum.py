@@ -156,3 +156,67 @@ def random_tables(rng, V, L, zero_prob=0.25, same_prob=0.0, context_free=False):
     if context_free:
         return (lambda pre: ptab[()]), (lambda pre: qtab[()])
     return (lambda pre: ptab[pre]), (lambda pre: qtab[pre])
+
+
+def tree_children(parents):
+    """Children of every node (node 0 = root) in index order."""
+    N = len(parents)
+    ch = [[] for _ in range(N + 1)]
+    for m in range(1, N + 1):
+        ch[parents[m - 1]].append(m)
+    return ch
+
+
+def tree_round(p, q, parents, V):
+    """Exact output distribution of tree verification (recursive rejection).
+
+    The tree's children of a node are drawn independently from q(prefix of
+    the node); at a node with residual r (initially p), each child's token x
+    is accepted with probability min(1, r(x)/q(x)), continuing at that child;
+    a rejection replaces r by max(r - q, 0) normalised; when every child is
+    rejected the emitted token is drawn from r; at a leaf from p."""
+    N = len(parents)
+    ch = tree_children(parents)
+    out = defaultdict(F)
+    expected_accepted = F(0)
+    for xs in itertools.product(range(V), repeat=N):
+        # prefix of each node and the probability of this draft tree
+        pre = {0: ()}
+        pq = F(1)
+        for m in range(1, N + 1):
+            par = parents[m - 1]
+            pq *= q(pre[par])[xs[m - 1]]
+            pre[m] = pre[par] + (xs[m - 1],)
+        if not pq:
+            continue
+
+        def walk(node, prob, depth):
+            nonlocal expected_accepted
+            s = pre[node]
+            if not ch[node]:
+                pn = p(s)
+                for y in range(V):
+                    if pn[y]:
+                        out[s + (y,)] += pq * prob * pn[y]
+                expected_accepted += pq * prob * depth
+                return
+            r = list(p(s))
+            qn = q(s)
+            alive = prob
+            for c in ch[node]:
+                x = xs[c - 1]
+                a = F(1) if qn[x] == 0 else min(F(1), r[x] / qn[x])
+                if a:
+                    walk(c, alive * a, depth + 1)
+                alive *= (1 - a)
+                if not alive:
+                    return
+                resid = [max(r[v] - qn[v], F(0)) for v in range(V)]
+                r = _normalise(resid) if sum(resid) else list(p(s))
+            for y in range(V):
+                if r[y]:
+                    out[s + (y,)] += pq * alive * r[y]
+            expected_accepted += pq * alive * depth
+
+        walk(0, F(1), 0)
+    return dict(out), expected_accepted

@@ -97,6 +97,20 @@ MUTANTS = [
     ("bf16 rounding truncates",
      "if (low > 0x8000u || (low == 0x8000u && (kept & 0x10000u))) kept += 0x10000u;", "(void)low;",
      [lambda: pins.test_bf16_rounding_equals_torch(oracle)]),
+    ("tree residual restarts from p at every rejection",
+     "double diff = r[v] / Zr - qd[v];", "double diff = pd[v] - qd[v];",
+     [lambda: pins.test_oracle_tree_output_distribution_equals_target(oracle, [0, 0, 0, 1])]),
+    ("tree later children tested with the first child's ratio",
+     "if (rejections == 0) {", "if (1) {",
+     [lambda: pins.test_oracle_tree_output_distribution_equals_target(oracle, [0, 0, 0, 1])]),
+    ("tree final draw from p instead of the residual",
+     "y = orc_icdf(r, V, u2, &Z, &marg);          /* every child rejected: the residual */",
+     "y = orc_icdf(pd, V, u2, &Z, &marg);",
+     [lambda: pins.test_tree_chain_equals_token_verification(oracle),
+      lambda: pins.test_oracle_tree_output_distribution_equals_target(oracle, [0, 0, 0, 1])]),
+    ("tree first child ratio inverted",
+     "const double lr = (prow[x] / T - lp) - (qr[x] / T - lq);", "const double lr = (qr[x] / T - lq) - (prow[x] / T - lp);",
+     [lambda: pins.test_tree_chain_equals_token_verification(oracle)]),
     ("Markov transition from the anchor only",
      "prev = (int32_t)y;", "(void)y;",
      [lambda: pins.test_markov_chain_distribution(oracle)]),

@@ -764,3 +764,102 @@ def test_rnn_chain_distribution(orc):
     cells = sorted(exp)
     chi2 = sum((obs.get(c, 0) - N * exp[c]) ** 2 / (N * exp[c]) for c in cells)
     assert chi2 < stats.chi2.ppf(1 - 1e-6, len(cells) - 1)
+
+
+# ----------------------------------------------------------------- trees ----
+
+TREES = [[0], [0, 0], [0, 1], [0, 0, 1], [0, 0, 0], [0, 0, 1, 1], [0, 1, 0, 3], [0, 0, 0, 1, 2]]
+
+
+@pytest.mark.parametrize("parents", TREES, ids=[str(t) for t in TREES])
+def test_exact_enumeration_tree_is_lossless(parents):
+    """Reading pin for tree verification (the explainer's section 7 names it,
+    without a rule): recursive rejection over a tree whose children of a node
+    are drawn independently from the draft at that node.  Enumerated exactly
+    over random rational tables (context-dependent and context-free, zero
+    entries, p = q at some prefixes), the round's output completed by target
+    draws equals the target's joint distribution."""
+    rng = random.Random(300 + len(parents) * 7 + sum(parents))
+    D = exact_enum_depth(parents)
+    for trial in range(6):
+        V = rng.randint(2, 3)
+        p, q = exact_enum.random_tables(rng, V, D + 1, zero_prob=0.25, same_prob=0.3,
+                                        context_free=(trial % 3 == 0))
+        tj = exact_enum.target_joint(p, D + 1, V)
+        dist, _ = exact_enum.tree_round(p, q, parents, V)
+        assert exact_enum.complete_with_target(dist, p, D + 1, V) == {k: v for k, v in tj.items() if v}
+
+
+def exact_enum_depth(parents):
+    dep = [0]
+    for par in parents:
+        dep.append(dep[par] + 1)
+    return max(dep)
+
+
+def test_tree_chain_equals_token_verification(orc):
+    """A chain-shaped tree (node m's parent is m - 1) is token verification:
+    same uniforms, same decisions, same emitted tokens and ratios."""
+    rng = np.random.default_rng(111)
+    for noise, gam in ((1.0, 5), (0.3, 6), (2.0, 3)):
+        B, V = 40, 300
+        p = rng.normal(0, 3, (B, gam + 1, V))
+        q = p[:, :gam] + noise * rng.normal(0, 1, (B, gam, V))
+        x = np.array([[int(np.argmax(q[b, i] + rng.gumbel(size=V))) for i in range(gam)] for b in range(B)])
+        t = orc.token_verify(p, q, x, gam, seed=9, offset=4)
+        r = orc.tree_verify(p, q, x, list(range(gam)), seed=9, offset=4)
+        assert np.array_equal(r.accepted_len, t.accepted_len)
+        assert np.array_equal(r.out_tokens, t.out_tokens)
+        ok = ~np.isnan(t.ratio)
+        assert np.array_equal(np.isnan(r.ratio), ~ok) and np.array_equal(r.ratio[ok], t.ratio[ok])
+        nodes = np.where(np.arange(gam)[None, :] < r.accepted_len[:, None], np.arange(1, gam + 1)[None, :], -1)
+        assert np.array_equal(r.accepted_nodes, nodes)
+
+
+def _tree_logits(rng, parents, V, p_tab, q_tab, B):
+    """Per request: draft tokens drawn independently from q at each node, and
+    the logit rows (log of the tables) of every node / internal node."""
+    N = len(parents)
+    internal = sorted(set(parents))
+    P = np.zeros((B, N + 1, V))
+    Q = np.zeros((B, len(internal), V))
+    X = np.zeros((B, N), np.int32)
+    with np.errstate(divide="ignore"):
+        for b in range(B):
+            pre = {0: ()}
+            for m in range(1, N + 1):
+                qd = np.array([float(v) for v in q_tab(pre[parents[m - 1]])])
+                X[b, m - 1] = rng.choice(V, p=qd / qd.sum())
+                pre[m] = pre[parents[m - 1]] + (int(X[b, m - 1]),)
+            for n in range(N + 1):
+                P[b, n] = np.log([float(v) for v in p_tab(pre[n])])
+            for j, n in enumerate(internal):
+                Q[b, j] = np.log([float(v) for v in q_tab(pre[n])])
+    return P, Q, X
+
+
+@pytest.mark.parametrize("parents", [[0, 0, 0, 1], [0, 1, 0, 2, 0]], ids=["3 root children", "3 branches"])
+def test_oracle_tree_output_distribution_equals_target(orc, parents):
+    """Monte Carlo over the C oracle: the emitted tokens, completed by target
+    draws to depth + 1 tokens, follow the target's joint distribution
+    (chi-square over every sequence)."""
+    rng = np.random.default_rng(112 + len(parents))
+    prng = random.Random(7 + len(parents))
+    V = 3
+    D = exact_enum_depth(parents)
+    p_tab, q_tab = exact_enum.random_tables(prng, V, D + 1, zero_prob=0.2)
+    Nr = 30000
+    P, Q, X = _tree_logits(rng, parents, V, p_tab, q_tab, Nr)
+    r = orc.tree_verify(P, Q, X, parents, seed=13)
+    assert (r.flags == 0).all()
+    counts = {}
+    for b in range(Nr):
+        s = tuple(int(t) for t in r.out_tokens[b, :r.accepted_len[b] + 1])
+        while len(s) < D + 1:
+            pd = np.array([float(v) for v in p_tab(s)])
+            s = s + (int(rng.choice(V, p=pd / pd.sum())),)
+        counts[s] = counts.get(s, 0) + 1
+    tj = {k: float(v) for k, v in exact_enum.target_joint(p_tab, D + 1, V).items() if v}
+    assert set(counts) <= set(tj)
+    chi2 = sum((counts.get(k, 0) - Nr * v) ** 2 / (Nr * v) for k, v in tj.items())
+    assert chi2 < stats.chi2.ppf(1 - 1e-6, len(tj) - 1), chi2
