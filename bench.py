@@ -17,13 +17,14 @@ steps.  Prints ONE JSON line:
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
        [--copy-probe]   (accepted for the recorded profile commands; the copy probe always runs)
-       [--workload headline|tiny|batched|block|block_async|markov|rnn|all]
+       [--workload headline|tiny|batched|block|block_async|markov|rnn|tree|all]
 The other workloads (one JSON line each, same fields) measure the tiny and
 batched token-verification batches, scheduler + block verification
 (B=512, gamma=8), the same with temperature-scaled confidences and the
 scheduler two steps ahead on a second stream, and the Markov-head sampler
 followed by verification (B=128, gamma=8, R=256; its roofline entry adds the
-MFMA rate), and the RNN-head draft on the same inputs.
+MFMA rate), the RNN-head draft on the same inputs, and tree verification
+(B=64, 4 branches of 5 nodes).
 """
 import argparse
 import hashlib
@@ -307,6 +308,53 @@ def bench_markov(args, L, WL):
                  two_call_verified_positions_per_s=round(B * gamma / (ms2 / 1e3), 1))
 
 
+def bench_tree(args, L, WL):
+    """Tree verification: B=64 requests, 4 branches of 5 draft nodes from the
+    root (N=20, 17 nodes with children), V=129,280, bf16.  A step is one
+    tree_verify_run (row statistics of every node's rows, then the walk)."""
+    import torch
+    sets = [WL.make_tree_inputs("cuda"), WL.make_tree_inputs("cuda", seed=2007)]
+    ti = sets[0]
+    B, V, N = ti.B, ti.V, len(ti.parents)
+    NQ = ti.q.shape[1]
+    D = max(1, max(_tree_depths(ti.parents)))
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, D + 1, dtype=torch.int32, device="cuda")
+    nodes = torch.empty(B, D, dtype=torch.int32, device="cuda")
+    ctx = L.Context(0, B, N, V)
+    accepted = []
+
+    def step(k):
+        s = sets[k % len(sets)]
+        L.tree_verify_run(ctx, s.p, s.q, s.tokens, s.parents, acc, out, accepted_nodes=nodes, temperature=s.T,
+                          seed=WL.VERIFY_SEED, offset=k)
+
+    ms, _ = _time_steps(step, args.warmup, args.steps)
+    prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
+    for k in range(4):
+        step(k)
+        torch.cuda.synchronize()
+        accepted.append(float(acc.float().mean().item()))
+    ctx.close()
+    alg = B * (N + 1 + NQ) * V * ti.p.element_size()
+    mean_acc = sum(accepted) / len(accepted)
+    return _line("verified tree nodes/s, B=64 tree 4x5 (N=20) V=129,280 bf16, tree verification",
+                 B * N / (ms / 1e3), "verified tree nodes/s", args, ms,
+                 {"workload": "tree verification (recursive rejection), 4 branches of 5 nodes from the root",
+                  "B": B, "N": N, "depth": D, "V": V, "logits": "bf16", "input_sets": len(sets)},
+                 _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats")),
+                 mean_accepted_len=round(mean_acc, 4),
+                 emitted_tokens_per_s=round(B * (mean_acc + 1) / (ms / 1e3), 1),
+                 kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
+
+
+def _tree_depths(parents):
+    dep = [0]
+    for par in parents:
+        dep.append(dep[par] + 1)
+    return dep
+
+
 def bench_rnn(args, L, WL):
     """RNN-head draft sampling on workload 4's inputs plus a recurrent matrix:
     gamma positions, each the contraction with the bf16 state, the draw, and
@@ -429,7 +477,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--workload", default="headline",
-                    choices=["headline", "tiny", "batched", "block", "block_async", "markov", "rnn", "all"],
+                    choices=["headline", "tiny", "batched", "block", "block_async", "markov", "rnn", "tree",
+                             "all"],
                     help="headline (default: the one JSON line the driver reads) or another workload")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -448,7 +497,8 @@ def main():
             "block": lambda: bench_block(args, L, WL),
             "block_async": lambda: bench_block_async(args, L, WL),
             "markov": lambda: bench_markov(args, L, WL),
-            "rnn": lambda: bench_rnn(args, L, WL)}
+            "rnn": lambda: bench_rnn(args, L, WL),
+            "tree": lambda: bench_tree(args, L, WL)}
     names = list(runs) if args.workload == "all" else [args.workload]
     for n in names:
         print(json.dumps(runs[n]()), flush=True)

@@ -180,6 +180,44 @@ sv_status spec_blockverify_run(sv_ctx *ctx, hipStream_t stream,
                                uint64_t seed, uint64_t offset, const float *uniforms,
                                int32_t *accepted_len, int32_t *out_tokens, const sv_diag *diag);
 
+/* Tree verification ("Speculative Decoding: The Same Distribution, Twice as
+ * Fast", section 7: several alternative continuations arranged as a tree,
+ * checked in one pass).  The page gives no rule; this is recursive rejection,
+ * lossless when the children of each node were drawn independently from the
+ * draft distribution at that node.  From the root, at each node in turn:
+ * every child x, in node order, is accepted with probability
+ * min(1, r(x) / q(x)) for the current residual r (p at the node, and after
+ * each rejection max(r - q, 0) normalised); an accepted child is emitted and
+ * the walk continues there; if every child is rejected the final token is
+ * drawn from r, and at a leaf the bonus token from p (inverse CDF in token
+ * order).  The first child's test is spec_verify_run's, so a chain (node m's
+ * parent m - 1) gives spec_verify_run's result with gamma = N.
+ *   parents       HOST [N]: parent of node m (1..N) at index m-1, in
+ *                 [0, m-1]; node 0 is the root; one topology for the batch
+ *   p_logits      [B, N+1, V]: row n = target logits after node n
+ *   q_logits      [B, NQ, V]: draft logits at each node that has children,
+ *                 in node order (NQ = the number of such nodes)
+ *   tokens        [B, N] int32: token of node m at column m-1
+ *   uniforms      [B, N+1] fp32 or NULL: column m-1 replaces node m's test
+ *                 uniform (Philox (b, m, tag 0)), column N the final draw's
+ *                 ((b, 0, tag 1))
+ *   accepted_len  [B] int32 out: depth of the accepted path, -1 on a data error
+ *   out_tokens    [B, D+1] int32 out (D = the tree's depth): the accepted
+ *                 path's tokens, the drawn token, then -1
+ *   accepted_nodes [B, D] int32 out or NULL: the accepted nodes, then -1
+ *   diag          NULL or lse_p [B, N+1], lse_q [B, NQ], ratio [B, N]
+ *                 (min(1, r(x)/q(x)) of each tested node, NaN otherwise),
+ *                 resid_mass [B], flags [B]
+ * Requires N <= max_gamma, V == the context's vocab, V <= 8.4M; every token
+ * in [0, V) and every row finite (else accepted_len = -1 and a flag). */
+sv_status tree_verify_run(sv_ctx *ctx, hipStream_t stream,
+                          const void *p_logits, sv_dtype p_dtype,
+                          const void *q_logits, sv_dtype q_dtype,
+                          const int32_t *tokens, const int32_t *parents, int N,
+                          int B, int64_t V, float temperature, uint64_t seed, uint64_t offset,
+                          const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                          int32_t *accepted_nodes, const sv_diag *diag);
+
 /* Markov-head draft sampler.  For k = 1..gamma, strictly left to right:
  * z_k[n] = base_k[n] + sum_r U[x_{k-1}, r] W[r, n] (bf16 inputs, fp32
  * accumulation), x_k = inverse-CDF draw from softmax(z_k / temperature) with

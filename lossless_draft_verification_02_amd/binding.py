@@ -21,7 +21,8 @@ SV_FLAG_BAD_TOKEN, SV_FLAG_BAD_ROW, SV_FLAG_RESID_ZERO, SV_FLAG_BAD_VERIFY_LEN =
 
 EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error",
             "spec_verify_device_status", "spec_verify_run", "spec_schedule_run", "spec_schedule_sts_run",
-            "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "rnn_draft_run", "spec_verify_profile_enable",
+            "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "rnn_draft_run", "tree_verify_run",
+            "spec_verify_profile_enable",
             "spec_verify_profile_read")
 KERNELS = ("rowstats", "accept", "block_pass2", "resid", "select", "tail", "schedule", "markov_gemm",
            "markov_select", "markov_rebuild")
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH):
     lib.markov_draft_run.argtypes = [P, P, P, P, P, I, P, I, I, I64, F, U64, U64, P, P, P, P]
     lib.markov_verify_run.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I64, F, U64, U64, U64, P, P, P, P, P]
     lib.markov_verify_run.restype = I
+    lib.tree_verify_run.argtypes = [P, P, P, I, P, I, P, P, I, I, I64, F, U64, U64, P, P, P, P, P]
+    lib.tree_verify_run.restype = I
     lib.rnn_draft_run.argtypes = [P, P, P, P, P, P, I, P, I, I, I64, F, U64, U64, P, P, P, P, P]
     lib.rnn_draft_run.restype = I
     lib.markov_draft_run.restype = I
@@ -289,6 +292,43 @@ def markov_draft_run(ctx: Context, base, U, Wt, x0, draft_out, *, q_logits=None,
     _check("markov_draft_run", load_library().markov_draft_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), R, _ptr(x0), B, gamma, V,
         temperature, seed, offset, _ptr(uniforms), _ptr(draft_out), _ptr(q_logits), _ptr(lse_q)))
+
+
+def tree_verify_run(ctx: Context, p, q, tokens, parents, accepted_len, out_tokens, *, accepted_nodes=None,
+                    temperature: float = 1.0, seed: int = 1, offset: int = 0, uniforms=None,
+                    diag: Optional[dict] = None, stream=None):
+    """Tree verification: p [B, N+1, V], q [B, NQ, V] (rows of the nodes with
+    children, node order), tokens [B, N], parents (host sequence of N ints,
+    parents[m-1] in [0, m-1]) -> accepted_len [B], out_tokens [B, D+1]
+    (+ accepted_nodes [B, D])."""
+    torch = _torch()
+    par = [int(x) for x in parents]
+    N = len(par)
+    if p.dim() != 3 or p.shape[1] != N + 1:
+        raise ValueError("p must be [B, N+1, V]")
+    B, _, V = p.shape
+    NQ = len(set(par))
+    depth = [0] * (N + 1)
+    for m in range(1, N + 1):
+        if not 0 <= par[m - 1] < m:
+            raise ValueError(f"parents[{m - 1}]={par[m - 1]} must lie in [0, {m - 1}]")
+        depth[m] = depth[par[m - 1]] + 1
+    D = max(depth)
+    _need(p, "p", shape=(B, N + 1, V), device=ctx.device)
+    if N > 0:
+        _need(q, "q", shape=(B, NQ, V), device=ctx.device)
+        _need(tokens, "tokens", dtype=torch.int32, shape=(B, N), device=ctx.device)
+    _need(accepted_len, "accepted_len", dtype=torch.int32, shape=(B,), device=ctx.device)
+    _need(out_tokens, "out_tokens", dtype=torch.int32, shape=(B, D + 1), device=ctx.device)
+    _need(accepted_nodes, "accepted_nodes", dtype=torch.int32, shape=(B, D), device=ctx.device)
+    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, N + 1), device=ctx.device)
+    d = _diag_struct(diag)
+    host = (ctypes.c_int32 * max(N, 1))(*par)
+    _check("tree_verify_run", load_library().tree_verify_run(
+        ctx.handle, _stream(ctx.device, stream), _ptr(p), _dtype_code(p), _ptr(q) if N > 0 else None,
+        _dtype_code(q) if N > 0 else SV_F32, _ptr(tokens) if N > 0 else None, ctypes.cast(host, ctypes.c_void_p),
+        N, B, V, temperature, seed, offset, _ptr(uniforms), _ptr(accepted_len), _ptr(out_tokens),
+        _ptr(accepted_nodes), ctypes.byref(d) if d else None))
 
 
 def rnn_draft_run(ctx: Context, base, U, Wt, A, x0, draft_out, *, q_logits=None, lse_q=None, states=None,

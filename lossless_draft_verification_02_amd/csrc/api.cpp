@@ -110,6 +110,8 @@ svh::VerifyArgs make_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd
     a.q_lse2 = nullptr;
     a.q_zx = nullptr;
     a.qrec = nullptr;
+    a.np_rows = 0;
+    a.nq_rows = 0;
     return a;
 }
 
@@ -485,6 +487,62 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_log
                                          uniforms, draft_tokens, q_logits, lse_q);
     st = check_launch(svh::launch_markov(ctx, a, stream), "Markov sampler");
     return st != SV_OK ? st : ok();
+}
+
+sv_status tree_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits, sv_dtype p_dtype,
+                          const void *q_logits, sv_dtype q_dtype, const int32_t *tokens, const int32_t *parents,
+                          int N, int B, int64_t V, float temperature, uint64_t seed, uint64_t offset,
+                          const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                          int32_t *accepted_nodes, const sv_diag *diag)
+{
+    const char *fn = "tree_verify_run";
+    if (!ctx) return fail(SV_ERR_INVALID, "%s: ctx is NULL", fn);
+    if (N < 0 || N > ctx->max_gamma)
+        return fail(SV_ERR_INVALID, "%s: N=%d nodes out of range [0, max_gamma=%d]", fn, N, ctx->max_gamma);
+    if (N > 0 && !parents) return fail(SV_ERR_INVALID, "%s: parents are required", fn);
+    // topology: parents come first; children in index order; q rows of the
+    // nodes with children in node order
+    svh::TreeTopo t;
+    std::memset(&t, 0, sizeof t);
+    t.N = N;
+    int depth[svh::kMaxGamma + 1];
+    depth[0] = 0;
+    int8_t last[svh::kMaxGamma + 1];
+    for (int n = 0; n <= N; ++n) {
+        t.first_child[n] = -1;
+        t.next_sib[n] = -1;
+        t.qrow[n] = -1;
+        last[n] = -1;
+    }
+    t.parent[0] = -1;
+    for (int m = 1; m <= N; ++m) {
+        const int32_t par = parents[m - 1];
+        if (par < 0 || par >= m)
+            return fail(SV_ERR_INVALID, "%s: parents[%d]=%d must lie in [0, %d]", fn, m - 1, par, m - 1);
+        t.parent[m] = (int8_t)par;
+        depth[m] = depth[par] + 1;
+        t.D = depth[m] > t.D ? depth[m] : t.D;
+        if (last[par] < 0) t.first_child[par] = (int8_t)m;
+        else t.next_sib[last[par]] = (int8_t)m;
+        last[par] = (int8_t)m;
+    }
+    for (int n = 0; n <= N; ++n)
+        if (t.first_child[n] >= 0) t.qrow[n] = (int8_t)t.NQ++;
+    // the row checks of a draft call with gamma = N (q has NQ <= N rows)
+    sv_status st = check_verify_args(ctx, p_logits, p_dtype, q_logits, q_dtype, tokens, B, N, V, temperature,
+                                     accepted_len, out_tokens, fn);
+    if (st != SV_OK) return st;
+    if (ctx->nseg > svh::kTailMaxSeg)
+        return fail(SV_ERR_UNSUPPORTED, "%s: V=%lld exceeds the tree walk's segment table", fn, (long long)V);
+    DeviceGuard guard(ctx->device);
+    svh::VerifyArgs a = make_args(p_logits, p_dtype, q_logits, q_dtype, tokens, nullptr, B, N, V, temperature,
+                                  seed, offset, uniforms, accepted_len, out_tokens, diag, false);
+    a.np_rows = N + 1;
+    a.nq_rows = t.NQ;
+    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
+    if ((st = check_launch(svh::launch_tree_tail(ctx, a, t, accepted_nodes, stream), "tree walk")) != SV_OK)
+        return st;
+    return ok();
 }
 
 sv_status rnn_draft_run(sv_ctx *ctx, hipStream_t stream, const void *base_logits, const void *U, const void *W,

@@ -111,11 +111,12 @@ __device__ __forceinline__ MS chunk_stats(const char *__restrict__ rowptr, int64
 
 // Statistics of chunk `chunk` of row i of request b (a p row when is_p,
 // else a q row) into part[], by the whole workgroup (WAVE false) or by one
-// wavefront on its own (WAVE true: shuffles only, no LDS, no barrier).
+// wavefront on its own (WAVE true: shuffles only, no LDS, no barrier).  A
+// request has np p rows and nq q rows (gamma + 1 and gamma for a draft).
 template <int PES, int QES, int NB, bool WAVE>
 __device__ __forceinline__ void rowstats_chunk(const void *__restrict__ p, const void *__restrict__ q, int B,
-                                               int gamma, int b, int i, bool is_p, int chunk, int64_t V, int nch1,
-                                               int64_t chunk1, float c, float2 *__restrict__ part, MS *red)
+                                               int np, int nq, int b, int i, bool is_p, int chunk, int64_t V,
+                                               int nch1, int64_t chunk1, float c, float2 *__restrict__ part, MS *red)
 {
     const int64_t e0 = (int64_t)chunk * chunk1;
     const int64_t e1 = e0 + chunk1 < V ? e0 + chunk1 : V;
@@ -124,12 +125,12 @@ __device__ __forceinline__ void rowstats_chunk(const void *__restrict__ p, const
     const char *row;
     int esize;
     if (is_p) {
-        grow = (int64_t)b * (gamma + 1) + i;
+        grow = (int64_t)b * np + i;
         row = (const char *)p + grow * V * PES;
         esize = PES;
     } else {
-        const int64_t qr = (int64_t)b * gamma + i;
-        grow = (int64_t)B * (gamma + 1) + qr;
+        const int64_t qr = (int64_t)b * nq + i;
+        grow = (int64_t)B * np + qr;
         row = (const char *)q + qr * V * QES;
         esize = QES;
     }
@@ -154,33 +155,34 @@ __device__ __forceinline__ void rowstats_chunk(const void *__restrict__ p, const
 }
 
 // One workgroup per (row, chunk) item of requests [b0, b0 + nb): p rows
-// first, then q rows.  Without verify lengths every row is verified and the
-// grid is exactly the work; with them, rows past a request's length return
-// at once.
+// first (np per request), then q rows (nq per request).  Without verify
+// lengths every row is read and the grid is exactly the work; with them
+// (draft layout, np = gamma + 1, nq = gamma), rows past a request's length
+// return at once.
 template <int PES, int QES, int NB>
 __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats(
     const void *__restrict__ p, const void *__restrict__ q, const int32_t *__restrict__ verify_len, int B,
-    int gamma, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
+    int np, int nq, int b0, int nb, int64_t V, int nch1, int64_t chunk1, float c, float2 *__restrict__ part)
 {
     __shared__ MS red[svh::kRowstatsThreads / svk::kWave];
     const int64_t slot = blockIdx.x / nch1;
     const int chunk = (int)(blockIdx.x - slot * nch1);
-    const int64_t lrows_p = (int64_t)nb * (gamma + 1);
+    const int64_t lrows_p = (int64_t)nb * np;
     int bl, i;
     const bool is_p = slot < lrows_p;
     if (is_p) {
-        bl = (int)(slot / (gamma + 1));
-        i = (int)(slot - (int64_t)bl * (gamma + 1));
+        bl = (int)(slot / np);
+        i = (int)(slot - (int64_t)bl * np);
     } else {
         const int64_t r = slot - lrows_p;
-        bl = (int)(r / gamma);
-        i = (int)(r - (int64_t)bl * gamma);
+        bl = (int)(r / nq);
+        i = (int)(r - (int64_t)bl * nq);
     }
     if (verify_len) {
         const int L = verify_len[b0 + bl];
-        if (L < 0 || L > gamma || (is_p ? i > L : i >= L)) return;
+        if (L < 0 || L > nq || (is_p ? i > L : i >= L)) return;
     }
-    rowstats_chunk<PES, QES, NB, false>(p, q, B, gamma, b0 + bl, i, is_p, chunk, V, nch1, chunk1, c, part, red);
+    rowstats_chunk<PES, QES, NB, false>(p, q, B, np, nq, b0 + bl, i, is_p, chunk, V, nch1, chunk1, c, part, red);
 }
 
 // Calls with per-request verify lengths L_b (on the device): only rows
@@ -255,13 +257,13 @@ __global__ __launch_bounds__(svh::kRowstatsThreads) void k_rowstats_compact(
         const int row = r / nch1, chunk = r - row * nch1;
         const int L = Ls[lo];
         const bool is_p = row <= L;
-        rowstats_chunk<PES, QES, NB, true>(p, q, B, gamma, b0 + lo, is_p ? row : row - (L + 1), is_p, chunk, V,
-                                           nch1, chunk1, c, part, nullptr);
+        rowstats_chunk<PES, QES, NB, true>(p, q, B, gamma + 1, gamma, b0 + lo, is_p ? row : row - (L + 1), is_p,
+                                           chunk, V, nch1, chunk1, c, part, nullptr);
     }
 }
 
 template <int PES, int QES>
-void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t items)
+void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t items, int np, int nq)
 {
     constexpr int NB = svh::kRowstatsNB;
     const bool compact = a.verify_len && a.nb <= svh::kRowstatsCompactMaxReq && items <= 0x7FFFFFFF;
@@ -275,7 +277,8 @@ void launch_typed(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int64_t 
                            ctx->ws.part);
     } else {
         hipLaunchKernelGGL((k_rowstats<PES, QES, NB>), dim3((unsigned)items), dim3(svh::kRowstatsThreads), 0, s,
-                           a.p, a.q, a.verify_len, a.B, a.gamma, a.b0, a.nb, a.V, ctx->nch1, ctx->chunk1, a.c, ctx->ws.part);
+                           a.p, a.q, a.verify_len, a.B, np, nq, a.b0, a.nb, a.V, ctx->nch1, ctx->chunk1, a.c,
+                           ctx->ws.part);
     }
 }
 
@@ -286,14 +289,16 @@ namespace svh {
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
 {
     // p rows, then q rows unless the q statistics come from the Markov sampler
-    const int64_t rows = (int64_t)a.nb * (a.gamma + 1) + (a.q_lse2 ? 0 : (int64_t)a.nb * a.gamma);
+    const int np = a.np_rows ? a.np_rows : a.gamma + 1;
+    const int nq = a.np_rows ? a.nq_rows : a.gamma;
+    const int64_t rows = (int64_t)a.nb * np + (a.q_lse2 ? 0 : (int64_t)a.nb * nq);
     const int64_t grid = rows * ctx->nch1;
     if (grid <= 0) return hipSuccess;
     const int slot = prof_begin(ctx, s, SV_KERNEL_ROWSTATS);
-    if (a.p_esize == 2 && a.q_esize == 2) launch_typed<2, 2>(ctx, a, s, grid);
-    else if (a.p_esize == 2) launch_typed<2, 4>(ctx, a, s, grid);
-    else if (a.q_esize == 2) launch_typed<4, 2>(ctx, a, s, grid);
-    else launch_typed<4, 4>(ctx, a, s, grid);
+    if (a.p_esize == 2 && a.q_esize == 2) launch_typed<2, 2>(ctx, a, s, grid, np, nq);
+    else if (a.p_esize == 2) launch_typed<2, 4>(ctx, a, s, grid, np, nq);
+    else if (a.q_esize == 2) launch_typed<4, 2>(ctx, a, s, grid, np, nq);
+    else launch_typed<4, 4>(ctx, a, s, grid, np, nq);
     const hipError_t e = hipGetLastError();
     prof_end(ctx, s, slot);
     return e;

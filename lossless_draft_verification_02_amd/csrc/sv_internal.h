@@ -42,6 +42,9 @@ constexpr int kRowstatsCompactMaxReq = 8192;  // requests per call it lays out i
 constexpr int kResidThreads = 256;
 constexpr int kSegR = 2048;
 constexpr int kSegPerWG = kResidThreads / 64;
+// Fused tails: per-request segment sums of the correction / bonus weights in
+// LDS, V <= kTailMaxSeg * kSegR tokens.
+constexpr int kTailMaxSeg = 4096;
 // Scheduler: one workgroup sorts up to kSchedMax candidates in LDS.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedMax = 8192;
@@ -144,6 +147,10 @@ struct VerifyArgs {
     const float *q_lse2;  // [B, gamma]
     const float *q_zx;    // [B, gamma]
     const float *qrec;    // [B, V]
+    // Row counts per request when they are not gamma + 1 and gamma (tree
+    // verification: N + 1 node rows of p, one q row per node with children);
+    // 0 for a draft.
+    int np_rows, nq_rows;
 };
 
 // Per-request result of the acceptance scan, read by the kernels that follow.
@@ -163,6 +170,19 @@ hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 // Block verification after the row statistics: ratios -> residual masses ->
 // thresholds -> chunk sums -> select.
 hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+// Tree topology (node 0 the root, nodes 1..N in an order where parents come
+// first), shared by every request of a call.
+struct TreeTopo {
+    int N, NQ, D;                       // nodes, nodes with children, depth
+    int8_t parent[kMaxGamma + 1];       // parent of node m >= 1
+    int8_t first_child[kMaxGamma + 1];  // -1 for a leaf
+    int8_t next_sib[kMaxGamma + 1];     // next child of the same parent, -1 for the last
+    int8_t qrow[kMaxGamma + 1];         // q row of a node with children, else -1
+};
+// Tree verification after the row statistics (a.np_rows = N + 1, a.nq_rows =
+// NQ): one workgroup per request walks the tree and draws the final token.
+hipError_t launch_tree_tail(sv_ctx *ctx, const VerifyArgs &a, const TreeTopo &t, int32_t *nodes_out,
+                            hipStream_t s);
 constexpr size_t kReqStateBytes = 32;
 static_assert(sizeof(ReqG) == kReqStateBytes, "request state layout");
 // Per-position temperatures of sequential temperature scaling, passed by

@@ -857,7 +857,7 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
 // ---------------------------------------------------------------------------
 constexpr int NTT_WIDE = 1024;      // one workgroup per CU when requests <= CUs
 constexpr int NTT_NARROW = 512;     // two per CU otherwise (<= 128 VGPRs either way)
-constexpr int kTailMaxSeg = 4096;   // LDS segment sums: V <= 8.4M tokens
+constexpr int kTailMaxSeg = svh::kTailMaxSeg;   // LDS segment sums: V <= 8.4M tokens
 #ifndef SV_FUSED_TAIL
 #define SV_FUSED_TAIL 1             // 0: always the accept / sum / select kernels
 #endif
@@ -1014,6 +1014,281 @@ hipError_t markov_verify_tail(sv_ctx *ctx, const svh::VerifyArgs &a, const svh::
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Tree verification ("Speculative Decoding: The Same Distribution, Twice as
+// Fast", section 7: several alternative continuations arranged as a tree and
+// checked in one pass), by recursive rejection: the children of a node were
+// drawn independently from the draft q at that node; each child is accepted
+// with probability min(1, r(x)/q(x)) for the current residual r, which is p
+// at the node and after each rejection becomes max(r - q, 0) normalised; if
+// every child is rejected the token is drawn from r, at a leaf from p.
+// After j >= 1 rejections r is proportional to max(p - A_j q, 0), A_1 = 1,
+// A_{j+1} = A_j (1 + Z_j) with Z_j the mass of max(p / A_j - q, 0): the
+// residual stays the correction weights max(wmul p - q, 0) of the token
+// sampler with wmul = 1 / A_j, and each rejection costs one pass over the
+// node's p and q rows for the next Z.  The first child takes the token rule's
+// log-space ratio, so a chain-shaped tree is token verification.
+//
+// One workgroup per request.  Wavefront 0 walks the tree: its lanes first
+// gather every node's token logits under the node's parent rows (one memory
+// round trip for the whole tree, independent of the decisions); lane 0 then
+// decides.
+// Between decisions that need a residual mass, and for the final draw, all
+// wavefronts sum the current weights over the node's rows into LDS segment
+// sums (the fused tail's segment sums and wavefront draw).
+// ---------------------------------------------------------------------------
+struct TreeLDS {
+    double lp[MAXG + 1];        // log2-sum-exp2 of every p row (node order)
+    double lq[MAXG + 1];        // ... of every q row (order of the nodes with children)
+    float zp[MAXG + 1];         // node m's token logit in its parent's p row ...
+    float zq[MAXG + 1];         // ... and q row (gathered when the parent is reached)
+    float u[MAXG + 1];          // node m's acceptance uniform
+    int32_t x[MAXG];            // token of node m at x[m - 1]
+    int32_t path_x[MAXG], path_n[MAXG];
+    double zr;                  // mass of the current residual weights
+    double wmul;                // residual weights max(wmul p - q, 0)
+    int node, child, depth, act, mode, first, resid_p;
+    uint32_t flags;
+};
+enum { TREE_PASS = 0, TREE_DRAW = 1, TREE_DONE = 2 };
+
+__device__ __forceinline__ int64_t tree_prow(const svh::TreeTopo &t, int b, int n) { return (int64_t)b * (t.N + 1) + n; }
+__device__ __forceinline__ int64_t tree_qrow(const svh::TreeTopo &t, int b, int n) { return (int64_t)b * t.NQ + t.qrow[n]; }
+
+// Wavefront 0, lane 0: decisions at st.node from st.child on, until a pass
+// or the draw is needed (st.act says which).
+__device__ void tree_decide(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st)
+{
+    for (;;) {
+    const int node = st.node;
+    if (t.first_child[node] < 0) {   // a leaf: the bonus token from p
+        st.mode = 1;
+        st.wmul = 1.0;
+        st.act = TREE_DRAW;
+        return;
+    }
+    const double lp = st.lp[node], lq = st.lq[t.qrow[node]];
+    const float lp2 = (float)lp, lq2 = (float)lq;
+    {
+        const int c = st.child;
+        const float zp = st.zp[c], zq = st.zq[c];
+        float ratio;
+        if (st.first) {   // the token rule's ratio, log2 space in fp64
+            const double dp = (double)zp * (double)a.c - lp;
+            const double dq = (double)zq * (double)a.c - lq;
+            const float r = (float)exp2(dp - dq);
+            ratio = r == r ? fminf(r, 1.0f) : 0.0f;
+        } else {
+            const float pw = svk::fast_exp2(__builtin_fmaf(zp, a.c, -lp2));
+            const float qw = svk::fast_exp2(__builtin_fmaf(zq, a.c, -lq2));
+            const double d = st.resid_p ? (double)pw : (double)((float)st.wmul * pw - qw);
+            const double r = d > 0.0 ? (qw > 0.0f ? d / (st.zr * (double)qw) : __builtin_inf()) : 0.0;
+            ratio = r < 1.0 ? (float)r : 1.0f;
+        }
+        if (a.diag.ratio) a.diag.ratio[(int64_t)b * t.N + (c - 1)] = ratio;
+        if (st.u[c] < ratio) {   // accepted: continue at c
+            st.path_x[st.depth] = st.x[c - 1];
+            st.path_n[st.depth] = c;
+            st.depth += 1;
+            st.node = c;
+            st.child = t.first_child[c];
+            st.first = 1;
+            st.resid_p = 1;
+            continue;
+        }
+        // rejected: the residual becomes max(r - q, 0)
+        st.wmul = st.resid_p ? 1.0 : st.wmul / (1.0 + st.zr);
+        st.resid_p = 0;
+        st.first = 0;
+        st.mode = 0;
+        const int nxt = t.next_sib[c];
+        st.act = nxt >= 0 ? TREE_PASS : TREE_DRAW;
+        st.child = nxt;
+        return;
+    }
+    }
+}
+
+// Wavefront 0: decisions until a pass or the draw is needed.
+template <int PES, int QES>
+__device__ void tree_walk(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st)
+{
+    if ((threadIdx.x & (svk::kWave - 1)) == 0) tree_decide(a, t, b, st);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wavefront 0: data checks, row statistics, uniforms; then the walk from the
+// root.  A request with a data error gets its error outputs here.
+template <int PES, int QES>
+__device__ void tree_begin(const svh::VerifyArgs &a, const svh::TreeTopo &t, const float2 *__restrict__ part,
+                           int nch1, int b, int32_t *__restrict__ nodes_out, uint32_t *__restrict__ errword,
+                           TreeLDS &st)
+{
+    const int lane = threadIdx.x & (svk::kWave - 1);
+    const int N = t.N, NQ = t.NQ, D = t.D;
+    const float nan = __builtin_nanf("");
+    const int32_t x = lane < N ? a.draft[(int64_t)b * N + lane] : 0;
+    const bool x_ok = x >= 0 && (int64_t)x < a.V;
+    // node lane + 1's token logits under its parent's rows (decision-independent)
+    if (lane < N && x_ok) {
+        const int par = t.parent[lane + 1];
+        st.zp[lane + 1] = svk::load_logit<PES>(a.p, tree_prow(t, b, par) * a.V + x);
+        st.zq[lane + 1] = svk::load_logit<QES>(a.q, tree_qrow(t, b, par) * a.V + x);
+    }
+    bool bad = false;
+    for (int n = lane; n <= N; n += svk::kWave) {
+        bool bn = false;
+        st.lp[n] = merge_row(part, tree_prow(t, b, n), nch1, bn);
+        bad |= bn;
+    }
+    for (int j = lane; j < NQ; j += svk::kWave) {
+        bool bq = false;
+        st.lq[j] = merge_row(part, (int64_t)a.B * (N + 1) + (int64_t)b * NQ + j, nch1, bq);
+        bad |= bq;
+    }
+    if (lane < N) {
+        st.x[lane] = x;
+        st.u[lane + 1] = a.uniforms ? a.uniforms[(int64_t)b * (N + 1) + lane]
+                                    : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)(lane + 1), 0u);
+    }
+    uint32_t flags = 0;
+    if (__ballot(lane < N && !x_ok)) flags = SV_FLAG_BAD_TOKEN;
+    else if (__ballot(bad)) flags = SV_FLAG_BAD_ROW;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int n = lane; n <= N; n += svk::kWave)
+        if (a.diag.lse_p) a.diag.lse_p[(int64_t)b * (N + 1) + n] = flags ? nan : (float)(st.lp[n] * kLn2d);
+    for (int j = lane; j < NQ; j += svk::kWave)
+        if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * NQ + j] = flags ? nan : (float)(st.lq[j] * kLn2d);
+    for (int m = lane; m < N; m += svk::kWave)
+        if (a.diag.ratio) a.diag.ratio[(int64_t)b * N + m] = nan;
+    if (flags) {
+        for (int j = lane; j <= D; j += svk::kWave) a.out_tokens[(int64_t)b * (D + 1) + j] = -1;
+        if (nodes_out)
+            for (int j = lane; j < D; j += svk::kWave) nodes_out[(int64_t)b * D + j] = -1;
+        if (lane == 0) {
+            a.accepted_len[b] = -1;
+            if (a.diag.flags) a.diag.flags[b] = flags;
+            atomicOr(errword, flags);
+            st.act = TREE_DONE;
+        }
+        return;
+    }
+    if (lane == 0) {
+        st.node = 0;
+        st.child = t.first_child[0];
+        st.depth = 0;
+        st.first = 1;
+        st.resid_p = 1;
+        st.flags = 0;
+        st.zr = 1.0;
+        st.wmul = 1.0;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    tree_walk<PES, QES>(a, t, b, st);
+}
+
+template <int PES, int QES, int NTT>
+__global__ __launch_bounds__(NTT, 1) void k_tree(svh::VerifyArgs a, const svh::TreeTopo t,
+                                              const float2 *__restrict__ part, int nch1, int nseg,
+                                              int32_t *__restrict__ nodes_out, uint32_t *__restrict__ errword)
+{
+    __shared__ TreeLDS st;
+    __shared__ float segsum[kTailMaxSeg];
+    const int b = a.b0 + (int)blockIdx.x;
+    const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
+    if (wid == 0) tree_begin<PES, QES>(a, t, part, nch1, b, nodes_out, errword, st);
+    __syncthreads();
+    // every pass consumes one rejection or makes the draw (at most one retry
+    // of the draw, from p): the loop ends well within this bound
+    for (int it = 0; it < 2 * MAXG + 4; ++it) {
+        const int act = st.act;
+        if (act == TREE_DONE) return;
+        const int node = st.node;
+        const char *prow = (const char *)a.p + tree_prow(t, b, node) * a.V * PES;
+        const char *qrow = st.mode ? nullptr : (const char *)a.q + tree_qrow(t, b, node) * a.V * QES;
+        const float lp2 = (float)st.lp[node];
+        const float lq2 = st.mode ? 0.0f : (float)st.lq[t.qrow[node]];
+        const float wm = (float)st.wmul;
+        const int mode = st.mode;
+        segment_sums<PES, QES, NTT / svk::kWave>(a, prow, qrow, mode, wm, lp2, lq2, nseg, segsum);
+        __syncthreads();
+        if (wid == 0) {
+            if (act == TREE_PASS) {
+                // mass of the residual weights: fixed-order fp64 sum of the segment sums
+                const int per = (nseg + svk::kWave - 1) / svk::kWave;
+                const int k0 = lane * per, k1 = k0 + per < nseg ? k0 + per : nseg;
+                double loc = 0.0;
+                for (int k = k0; k < k1; ++k) loc += (double)segsum[k];
+                const double Z = __shfl(svk::wave_inclusive_scan_d(loc), svk::kWave - 1, svk::kWave);
+                if (lane == 0) {
+                    if (Z > 0.0) {
+                        st.zr = Z;
+                    } else {   // rounded to zero (positive in exact arithmetic): fall back to p
+                        st.flags |= SV_FLAG_RESID_ZERO;
+                        st.resid_p = 1;
+                        st.mode = 1;
+                        st.zr = 1.0;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                tree_walk<PES, QES>(a, t, b, st);
+            } else {
+                const float u2 = a.uniforms ? a.uniforms[(int64_t)b * (t.N + 1) + t.N]
+                                            : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, 0u, 1u);
+                double Z = 0.0;
+                const int y = select_token_wave<PES, QES>(a, mode, wm, lp2, lq2, segsum, nseg, prow, qrow, u2, Z);
+                if (y < 0 && mode == 0) {
+                    // residual mass rounded to zero: draw from the node's p row
+                    if (lane == 0) {
+                        st.flags |= SV_FLAG_RESID_ZERO;
+                        st.mode = 1;
+                        st.wmul = 1.0;
+                    }
+                } else {
+                    uint32_t flags = st.flags | (y < 0 ? SV_FLAG_BAD_ROW : 0u);
+                    const int depth = st.depth, D = t.D;
+                    for (int j = lane; j <= D; j += svk::kWave)
+                        a.out_tokens[(int64_t)b * (D + 1) + j] =
+                            y < 0 ? -1 : (j < depth ? st.path_x[j] : (j == depth ? y : -1));
+                    if (nodes_out)
+                        for (int j = lane; j < D; j += svk::kWave)
+                            nodes_out[(int64_t)b * D + j] = (y >= 0 && j < depth) ? st.path_n[j] : -1;
+                    if (lane == 0) {
+                        a.accepted_len[b] = y < 0 ? -1 : depth;
+                        if (a.diag.flags) a.diag.flags[b] = flags;
+                        if (a.diag.resid_mass) a.diag.resid_mass[b] = (float)Z;
+                        if (flags) atomicOr(errword, flags);
+                        st.act = TREE_DONE;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int PES, int QES>
+hipError_t tree_tail(sv_ctx *ctx, const svh::VerifyArgs &a, const svh::TreeTopo &t, int32_t *nodes_out,
+                     hipStream_t s)
+{
+    // 512 threads: the walk, the segment sums and the draw together hold
+    // about 200 VGPRs, which a 1024-thread workgroup (4 wavefronts per SIMD)
+    // would spill
+    const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
+    hipLaunchKernelGGL((k_tree<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a, t,
+                       (const float2 *)ctx->ws.part, ctx->nch1, ctx->nseg, nodes_out, ctx->ws.errword);
+    svh::prof_end(ctx, s, slot);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 namespace svh {
@@ -1040,6 +1315,16 @@ hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
     if (a.p_esize == 2) return block_tail<2, 4>(ctx, a, s);
     if (a.q_esize == 2) return block_tail<4, 2>(ctx, a, s);
     return block_tail<4, 4>(ctx, a, s);
+}
+
+hipError_t launch_tree_tail(sv_ctx *ctx, const VerifyArgs &a, const TreeTopo &t, int32_t *nodes_out, hipStream_t s)
+{
+    if (a.nb <= 0) return hipSuccess;
+    if (ctx->nseg > kTailMaxSeg) return hipErrorInvalidValue;
+    if (a.p_esize == 2 && a.q_esize == 2) return tree_tail<2, 2>(ctx, a, t, nodes_out, s);
+    if (a.p_esize == 2) return tree_tail<2, 4>(ctx, a, t, nodes_out, s);
+    if (a.q_esize == 2) return tree_tail<4, 2>(ctx, a, t, nodes_out, s);
+    return tree_tail<4, 4>(ctx, a, t, nodes_out, s);
 }
 
 }  // namespace svh

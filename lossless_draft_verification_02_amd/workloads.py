@@ -22,6 +22,13 @@ Five workloads (sizes can be shrunk for tests, keeping the recipe):
                confidences: per-request mean mu_b ~ U(0.35, 0.95), decaying 3%
                per position, plus N(0, 0.05^2), clipped to [0, 1].
 
+Tree verification: B=64 requests, a tree of 4 branches of 5 nodes each
+(the root's 4 children start 4 chains; N = 20 nodes, depth 5, 17 nodes with
+children), V=129280, bf16, T=1.0.  Target rows as workload 3 (one per node and
+the root); the draft row of a node with children = its target row + N(0, 1);
+each child's token is drawn from softmax(draft row of its parent / T) with its
+own Gumbel noise, so siblings are independent draws.
+
 RNN head (workload 4 variant): workload 4's backbone logits, U, W and
 anchors, plus a recurrent matrix A [R, R] ~ N(0, (0.9 / sqrt(R))^2) in bf16
 (spectral radius about 0.9, so the state neither dies nor saturates).
@@ -201,6 +208,57 @@ def make_markov_inputs(device="cpu", B: Optional[int] = None, gamma: Optional[in
     return MarkovInputs(B, gamma, V, R, c["T"], base, U, Wt, x0, p)
 
 
+def tree_parents(branches: int = 4, depth: int = 5) -> list:
+    """Parents (node m at index m-1) of `branches` chains of `depth` nodes
+    hanging from the root."""
+    par = []
+    for k in range(branches):
+        first = k * depth + 1
+        par.append(0)
+        par.extend(range(first, first + depth - 1))
+    return par
+
+
+@dataclass
+class TreeInputs:
+    B: int
+    V: int
+    T: float
+    parents: list
+    p: torch.Tensor         # [B, N+1, V]
+    q: torch.Tensor         # [B, NQ, V]
+    tokens: torch.Tensor    # [B, N] int32
+
+
+def make_tree_inputs(device="cpu", B: int = 64, V: int = 129280, parents: Optional[list] = None,
+                     dtype=torch.bfloat16, noise: float = 1.0, seed: int = 1007, row_block: int = 256,
+                     T: float = 1.0) -> TreeInputs:
+    """Target / draft logits and node tokens of the tree-verification workload."""
+    par = tree_parents() if parents is None else list(parents)
+    N = len(par)
+    internal = sorted(set(par))
+    qidx = {n: j for j, n in enumerate(internal)}
+    g = _gen(device, seed)
+    gd = _gen(device, DRAFT_SEED)
+    p = torch.empty(B, N + 1, V, dtype=dtype, device=device)
+    q = torch.empty(B, len(internal), V, dtype=dtype, device=device)
+    tokens = torch.empty(B, N, dtype=torch.int32, device=device)
+    per = max(1, row_block // (N + 1))
+    for b0 in range(0, B, per):
+        b1 = min(B, b0 + per)
+        nb = b1 - b0
+        t = _target_rows(3, nb * (N + 1), V, g, device).view(nb, N + 1, V)
+        p[b0:b1] = t.to(dtype)
+        if internal:
+            d = t[:, internal] + noise * torch.randn(nb, len(internal), V, generator=g, device=device)
+            qd = d.to(dtype)
+            q[b0:b1] = qd
+            for m in range(1, N + 1):
+                tokens[b0:b1, m - 1] = _gumbel_argmax(qd[:, qidx[par[m - 1]]].float() / T, gd).to(torch.int32)
+        del t
+    return TreeInputs(B, V, T, par, p, q, tokens)
+
+
 def make_rnn_recurrence(R: int, device="cpu", std: Optional[float] = None, seed: int = 1006) -> torch.Tensor:
     """Recurrent matrix A [R, R] bf16 of the RNN-head variant of workload 4."""
     g = _gen(device, seed)
@@ -220,5 +278,5 @@ def describe(cfg: int) -> str:
 
 
 __all__ = ["CONFIGS", "VERIFY_SEED", "DRAFT_SEED", "VerifyInputs", "MarkovInputs", "make_verify_inputs",
-           "make_markov_inputs", "make_rnn_recurrence", "sts_temperatures", "sts_head_logits", "bytes_single_read",
+           "make_markov_inputs", "make_rnn_recurrence", "TreeInputs", "make_tree_inputs", "tree_parents", "sts_temperatures", "sts_head_logits", "bytes_single_read",
            "describe"]

@@ -228,3 +228,83 @@ def compare_rnn(g_draft, g_lse, g_q, g_states, orc, rep: Report | None = None, q
                     rep.failures.append((b, k, "draw", o, g, float(orc.margin[b, k])))
                 break
     return rep
+
+
+def tree_tested(parents, accepted_nodes, depth, N):
+    """(node, accepted) decisions of a tree walk in the order they were taken,
+    reconstructed from the accepted path: at each node on the path every child
+    up to the accepted one (all children where none was)."""
+    ch = [[] for _ in range(N + 1)]
+    for m in range(1, N + 1):
+        ch[parents[m - 1]].append(m)
+    out, node = [], 0
+    for level in range(depth + 1):
+        nxt = int(accepted_nodes[level]) if level < depth else -1
+        for c in ch[node]:
+            out.append((c, c == nxt))
+            if c == nxt:
+                break
+        if nxt < 0:
+            break
+        node = nxt
+    return out
+
+
+def compare_tree(gpu: dict, orc, parents, rep: Report | None = None) -> Report:
+    """Tree verification, per request: the sequence of (node, decision) pairs
+    must match the oracle's unless the first disagreement sits on a decision
+    whose oracle margin is at most MARGIN (a within-margin flip); with the
+    same path the drawn token must match unless its inverse-CDF margin is
+    within MARGIN; ratios of the tested nodes within PROB_ATOL."""
+    rep = rep or Report()
+    N = len(parents)
+    B = len(orc.accepted_len)
+    for b in range(B):
+        rep.requests += 1
+        oa, ga = int(orc.accepted_len[b]), int(gpu["accepted_len"][b])
+        if oa < 0 or ga < 0:
+            if oa != ga:
+                rep.failures.append((b, "error status", oa, ga))
+            elif "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):
+                rep.failures.append((b, "flags", int(orc.flags[b]), int(gpu["flags"][b])))
+            continue
+        od = tree_tested(parents, orc.accepted_nodes[b], oa, N)
+        gd = tree_tested(parents, gpu["accepted_nodes"][b], ga, N)
+        diverged = False
+        for i in range(max(len(od), len(gd))):
+            if i < len(od) and i < len(gd) and od[i] == gd[i]:
+                continue
+            node = od[i][0] if i < len(od) else gd[i][0]
+            if orc.dec_margin[b, node - 1] <= MARGIN:
+                rep.flips += 1
+            else:
+                rep.failures.append((b, "decision", node, od[i:i + 1], gd[i:i + 1],
+                                     float(orc.dec_margin[b, node - 1])))
+            diverged = True
+            break
+        if diverged:
+            continue
+        if not np.array_equal(orc.out_tokens[b, :oa], gpu["out_tokens"][b, :ga]):
+            rep.failures.append((b, "path tokens"))
+            continue
+        if (gpu["out_tokens"][b, ga + 1:] != -1).any():
+            rep.failures.append((b, "padding"))
+        if int(orc.out_tokens[b, oa]) != int(gpu["out_tokens"][b, ga]):
+            if orc.icdf_margin[b] <= MARGIN:
+                rep.flips += 1
+            else:
+                rep.failures.append((b, "draw", int(orc.out_tokens[b, oa]), int(gpu["out_tokens"][b, ga]),
+                                     float(orc.icdf_margin[b])))
+            continue
+        if "ratio" in gpu:
+            tested = [n for n, _ in od]
+            g = np.asarray(gpu["ratio"][b], np.float64)
+            if np.isnan(g[[n - 1 for n in tested]]).any():
+                rep.failures.append((b, "ratio missing"))
+            _close_prob(rep, g[[n - 1 for n in tested]], orc.ratio[b, [n - 1 for n in tested]], "ratio", b)
+            untested = sorted(set(range(1, N + 1)) - set(tested))
+            if untested and not np.isnan(g[[n - 1 for n in untested]]).all():
+                rep.failures.append((b, "ratio of an untested node"))
+        if "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):
+            rep.failures.append((b, "flags", int(orc.flags[b]), int(gpu["flags"][b])))
+    return rep

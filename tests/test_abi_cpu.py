@@ -18,7 +18,7 @@ def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
-    keep = [n for n in names if n.startswith(("spec_", "markov_", "rnn_"))]
+    keep = [n for n in names if n.startswith(("spec_", "markov_", "rnn_", "tree_"))]
     return sorted(set(keep))
 
 
@@ -64,6 +64,8 @@ def test_runs_reject_null_context():
                                     10, 1.0, 0, 0, None, None, None, None) == binding.SV_ERR_INVALID
     assert lib.rnn_draft_run(None, None, None, None, None, None, 256, None, 1, 1, 10, 1.0, 0, 0, None, None,
                              None, None, None) == binding.SV_ERR_INVALID
+    assert lib.tree_verify_run(None, None, None, 1, None, 1, None, None, 0, 1, 10, 1.0, 0, 0, None, None, None,
+                               None, None) == binding.SV_ERR_INVALID
     lib.spec_verify_destroy(None)   # accepted
 
 
