@@ -174,16 +174,18 @@ def bench_headline(args, L, WL):
     copy_us = e0.elapsed_time(e1) / 5 * 1e3
     copy_probe = {"kernel": "torch.bitwise_not over 1 GiB int32", "bytes_per_launch": 2 << 30,
                   "mean_us": round(copy_us, 2), "gbps": round((2 << 30) / (copy_us * 1e-6) / 1e9, 1)}
-    # and a plain streaming read (a library reduction over 1 GiB)
-    torch.sum(src)
+    # and a plain streaming read (a library reduction over 1 GiB of fp32; the
+    # int32 reduction widens to int64 and runs far below the memory rate)
+    srcf = src.view(torch.float32)
+    torch.sum(srcf)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(5):
-        torch.sum(src)
+        torch.sum(srcf)
     e1.record()
     torch.cuda.synchronize()
     read_us = e0.elapsed_time(e1) / 5 * 1e3
-    copy_probe["read_kernel"] = "torch.sum over 1 GiB int32"
+    copy_probe["read_kernel"] = "torch.sum over 1 GiB float32"
     copy_probe["read_mean_us"] = round(read_us, 2)
     copy_probe["read_gbps"] = round((1 << 30) / (read_us * 1e-6) / 1e9, 1)
     del src, dst
@@ -501,6 +503,19 @@ def main():
             "tree": lambda: bench_tree(args, L, WL)}
     names = list(runs) if args.workload == "all" else [args.workload]
     for n in names:
+        if n == "block_async" and len(names) > 1:
+            # its cross-stream handoffs stall when earlier work in the same
+            # process has taken the hardware queues (measured 4x slower):
+            # it runs in a fresh child process
+            import subprocess
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", n, "--steps", str(args.steps),
+                   "--warmup", str(args.warmup), "--no-cpu-baseline"]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                print(r.stderr, file=sys.stderr)
+                sys.exit(r.returncode)
+            print(r.stdout.strip().splitlines()[-1], flush=True)
+            continue
         print(json.dumps(runs[n]()), flush=True)
 
 
