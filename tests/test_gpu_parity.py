@@ -698,6 +698,29 @@ def test_tree_uniform_overrides_force_rejections():
             check_tree(ctx, ti, list(range(B)), f"tree forced u={val}", uniforms=u)
 
 
+@pytest.mark.parametrize("shape", ["chain", "wide"])
+def test_tree_largest_trees(shape):
+    """N = 64 nodes (the most a context allows): a 64-node chain equals token
+    verification with gamma = 64 on the GPU; a root with 64 leaf children
+    (63 residual passes at most) matches the oracle."""
+    B, V = 8, 4099
+    N = 64
+    with make_ctx(B, N, V) as ctx:
+        if shape == "chain":
+            vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=N, V=V, noise=0.3)
+            ti = WL.TreeInputs(B, V, vi.T, list(range(N)), vi.p, vi.q, vi.draft)
+            for off in range(3):
+                t = gpu_verify(ctx, vi, offset=off)
+                g = gpu_tree(ctx, ti, offset=off)
+                assert np.array_equal(t["accepted_len"], g["accepted_len"])
+                assert np.array_equal(t["out_tokens"], g["out_tokens"])
+        else:
+            ti = WL.make_tree_inputs("cuda", B=B, V=V, parents=[0] * N, noise=2.0)
+            u = torch.full((B, N + 1), 0.999, device="cuda")   # reject (almost) every child
+            check_tree(ctx, ti, list(range(B)), "tree 64 children, forced rejections", uniforms=u)
+            check_tree(ctx, ti, list(range(B)), "tree 64 children")
+
+
 def test_tree_workload_full_sampled():
     """The tree workload at full size (B=64, 4 branches x 5, V=129,280, bf16);
     the oracle on sampled requests."""
