@@ -10,19 +10,24 @@
 // Per position k (strictly sequential; x_0 is the anchor token):
 //   k_markov_gemm    z[b, n] = base[b, k, n] + sum_r U[x_{k-1}(b), r] Wt[n, r]
 //                    computed transposed, z^T = Wt . U^T, with bf16 MFMA
-//                    (16x16x32, fp32 accumulate).  Wt (the transition matrix
-//                    stored vocabulary-major, V rows of R) gives the A operand
-//                    straight from HBM: 16 bytes per lane per k-step, no LDS.
-//                    The gathered U rows of up to 128 requests sit in LDS for
-//                    the workgroup's lifetime and give the B operand.  Each
-//                    accumulator lane holds 4 consecutive vocabulary entries
-//                    of one request, so the epilogue adds the base logits and
-//                    stores 16-byte runs of z without a detour through LDS,
-//                    and reduces per (request, 128-token tile) the pair
-//                    (max z*c, sum exp2(z*c - max)).  Workgroups of eight
-//                    wavefronts (16 vocabulary rows each) loop over 128-token
-//                    tiles; the next tile's Wt fragments and base logits are
-//                    requested as soon as the current ones are consumed.
+//                    (16x16x32, fp32 accumulate).  Workgroups of eight
+//                    wavefronts loop over 128-token tiles; each tile of Wt
+//                    (the transition matrix stored vocabulary-major, V rows
+//                    of R) is copied into a two-slot LDS ring by direct
+//                    global -> LDS loads and gives the A operand; the U rows
+//                    (or states) of the workgroup's 128 requests give the B
+//                    operand and stay in registers for the whole launch.  At
+//                    rank 256 a wavefront covers 32 requests x 64 rows of a
+//                    tile, so each A fragment read from LDS feeds two MFMAs.
+//                    Each accumulator lane holds 4 consecutive vocabulary
+//                    entries of one request, so the epilogue adds the base
+//                    logits and stores 16-byte runs of z without a detour
+//                    through LDS, and reduces per (request, 128-token tile)
+//                    the pair (max z*c, sum exp2(z*c - max)).  The next
+//                    tile's copy and base logits are requested a few
+//                    instructions at a time through the MFMAs and the
+//                    epilogue, so the small per-CU miss queue never blocks
+//                    the wavefront's arithmetic for long.
 //   k_markov_select  one wavefront per request, no barriers: merge the tile
 //                    pairs into the row's log-sum-exp, pick the tile holding
 //                    u * Z by an fp64 wavefront scan, scan inside it for the
@@ -39,6 +44,8 @@
 // bf16(tanh(U[x_0])) is formed wherever it is read; after drawing x_k the
 // draw's workgroup computes hb_{k+1} for its request (a 256 x 256 product,
 // A read from L2) and leaves it for the next position's contraction.
+#include <type_traits>
+
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -205,153 +212,331 @@ struct TileLayout {
 // base + i), fetching whichever global chunk the swizzle puts there.  Rows
 // past V copy row V - 1; their outputs are never stored.
 template <int R>
-__device__ __forceinline__ void copy_tile(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int wid, int lane)
+__device__ __forceinline__ void copy_chunk(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int wid, int lane,
+                                           int j)
 {
     using TL = TileLayout<R>;
-#pragma unroll
-    for (int j = 0; j < TL::PER_WAVE; ++j) {
-        const int base = (j * NWAVE + wid) * 64;
-        const int S = base + lane;
-        const int row = S / TL::CH, p = S % TL::CH;
-        const int c = p ^ (row & (TL::SW - 1));
-        int64_t n = n0 + row;
-        n = n < a.V ? n : a.V - 1;
-        __builtin_amdgcn_global_load_lds((const void *)(a.W + n * R + 8 * c), (lds_void *)(dst + base * 16), 16, 0, 0);
-    }
+    const int base = (j * NWAVE + wid) * 64;
+    const int S = base + lane;
+    const int row = S / TL::CH, p = S % TL::CH;
+    const int c = p ^ (row & (TL::SW - 1));
+    int64_t n = n0 + row;
+    n = n < a.V ? n : a.V - 1;
+    __builtin_amdgcn_global_load_lds((const void *)(a.W + n * R + 8 * c), (lds_void *)(dst + base * 16), 16, 0, 0);
 }
 
-// Base logits of the lane's outputs in one tile: request m, vocabulary
-// entries n0 + 16 vb + 4 lg + r, as packed bf16 pairs; -inf past V or B.
-__device__ __forceinline__ void load_base(const svh::MarkovArgs &a, int k, int m, int64_t n0, int lg, int vec,
-                                          uint2 (&bv)[NVB])
+template <int R>
+__device__ __forceinline__ void copy_tile(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int wid, int lane)
 {
-    const uint16_t *brow = a.base + ((int64_t)(m < a.B ? m : 0) * a.gamma + (k - 1)) * a.V;
 #pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-        const int64_t n = n0 + 16 * vb + 4 * lg;
-        bv[vb] = make_uint2(0xFF80FF80u, 0xFF80FF80u);
-        if (m < a.B) {
-            if (vec) {
-                if (n < a.V) bv[vb] = *(const uint2 *)(brow + n);
-            } else {
-                uint16_t e[4];
+    for (int j = 0; j < TileLayout<R>::PER_WAVE; ++j) copy_chunk<R>(a, n0, dst, wid, lane, j);
+}
+
+// Max and sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48):
+// each swap hands a lane its own row's value and the partner row's, so the
+// symmetric combination leaves the same result in every lane of the pair.
+__device__ __forceinline__ float rows4_max(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// How a workgroup's eight wavefronts share one tile x 128 requests.  A
+// wavefront holds the B fragments of G request groups of 16 in registers for
+// the whole launch and covers NVB / G of the tile's 16-row blocks, so every A
+// fragment it reads from LDS feeds G MFMAs; the G wavefronts of one request
+// set split the tile's rows and combine their softmax pairs through LDS.
+// G = 2 halves the LDS reads per MFMA; it needs the register room of one
+// workgroup per CU, which the largest rank has anyway (its tile ring fills
+// the LDS).
+template <int R>
+struct GemmShape {
+    static constexpr int G = R == 256 ? 2 : 1;   // request groups per wavefront
+    static constexpr int NSET = NWAVE / G;       // request sets of 16 G
+    static constexpr int VBW = NVB / G;          // 16-row blocks per wavefront
+    static constexpr int MINB = G == 1 ? 2 : 1;  // workgroups per CU the registers are sized for
+};
+
+// Base logits of the lane's outputs in one tile: request m, vocabulary
+// entries n0 + 16 (vb0 + j) + 4 lg + r, as packed bf16 pairs; -inf past V or B.
+__device__ __forceinline__ const uint16_t *base_row(const svh::MarkovArgs &a, int k, int m)
+{
+    return m < a.B ? a.base + ((int64_t)m * a.gamma + (k - 1)) * a.V : nullptr;
+}
+
+__device__ __forceinline__ uint2 base_quad(const uint16_t *brow, int n, int Vi, int vec)
+{
+    uint2 r = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+    if (brow) {
+        if (vec) {
+            if (n < Vi) r = *(const uint2 *)(brow + n);
+        } else {
+            uint16_t e[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) e[r] = n + r < a.V ? brow[n + r] : (uint16_t)0xFF80u;
-                bv[vb] = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
-            }
+            for (int q = 0; q < 4; ++q) e[q] = n + q < Vi ? brow[n + q] : (uint16_t)0xFF80u;
+            r = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
         }
     }
+    return r;
 }
 
 // Position k of every request (req == null), or position tau + 1 of each
 // request whose scan ended in a rejection (req != null: the correction rows of
 // the fused draft -> verification path; other requests are skipped).  zout
 // may be null (no z rows stored) and tile_part may be null (no softmax pairs).
+//
+// Per tile: wait for the tile's copy, barrier, request the next tile's copy
+// and base logits, then the MFMAs with the next k-step's A fragments read
+// from LDS while the current k-step's run; per output the k-steps accumulate
+// in ascending order (the draw rebuilds its chosen tile the same way).
 template <int R>
-__global__ __launch_bounds__(NT, 2) void k_markov_gemm(svh::MarkovArgs a, int k, const svh::ReqG *__restrict__ req,
-                                                       float *__restrict__ zout, int64_t zstride,
-                                                       float2 *__restrict__ tile_part, int ntile, int vec)
+__global__ __launch_bounds__(NT, GemmShape<R>::MINB)
+void k_markov_gemm(
+    svh::MarkovArgs a, int k, const svh::ReqG *__restrict__ req, float *__restrict__ zout, int64_t zstride,
+    float2 *__restrict__ tile_part, int ntile, int vec)
 {
     using TL = TileLayout<R>;
+    using GS = GemmShape<R>;
+    constexpr int G = GS::G, VBW = GS::VBW;
     constexpr int KS = R / 32;
     __shared__ __attribute__((aligned(16))) unsigned char wtile[2 * TL::BYTES];   // double-buffered tile ring
+    __shared__ svk::MS parts[G > 1 ? 2 * G * MC : 1];  // [tile parity][row part][request]: partial pairs
 
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15, lg = lane >> 4;
-    const int m = blockIdx.y * MC + 16 * wid + li;   // the lane's request (B operand column)
-    const bool wave_on = blockIdx.y * MC + 16 * wid < a.B;
-    int km = k;                                        // the lane's position
-    bool act = m < a.B;
-    if (req && act) {
-        const svh::ReqG r = req[m];
-        act = r.flags == 0 && r.mode == 0;
-        km = r.tau + 1;
+    const int set = wid % GS::NSET, rp = wid / GS::NSET;   // request set, row part
+    const int vb0 = rp * VBW;                              // first 16-row block of the wavefront
+    const int q0 = 16 * G * set;                           // first request of the set within the workgroup
+    const bool wave_on = blockIdx.y * MC + q0 < a.B;
+    const int Vi = (int)a.V;
+
+    int m[G], km[G];
+    bool act[G];
+    const uint16_t *brow[G];   // base row of (request, position); null reads -inf
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = blockIdx.y * MC + q0 + 16 * g + li;     // the lane's requests (B operand columns)
+        km[g] = k;                                      // and their positions
+        act[g] = m[g] < a.B;
+        if (req && act[g]) {
+            const svh::ReqG r = req[m[g]];
+            act[g] = r.flags == 0 && r.mode == 0;
+            km[g] = r.tau + 1;
+        }
+        brow[g] = act[g] ? base_row(a, km[g], m[g]) : nullptr;
     }
 
-    // prologue: first tile's copy, the wavefront's U fragments, first base logits
+    // prologue: first tile's copy, the lane's B fragments, first base logits
     int tile = blockIdx.x;
     copy_tile<R>(a, (int64_t)tile * TN, wtile, wid, lane);
-    bf16x8 ufr[KS];
-    head_fragments<R>(a, km, m, lg, act, ufr);
-    const int mb = act ? m : a.B;                      // load_base reads nothing for a.B
-    uint2 bv[NVB];
-    load_base(a, km, mb, (int64_t)tile * TN, lg, vec, bv);
+    bf16x8 ufr[G][KS];
+    uint2 bv[G][VBW];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        head_fragments<R>(a, km[g], m[g], lg, act[g], ufr[g]);
+#pragma unroll
+        for (int j = 0; j < VBW; ++j) bv[g][j] = base_quad(brow[g], tile * TN + 16 * (vb0 + j) + 4 * lg, Vi, vec);
+    }
+
+    // G > 1: the softmax pair of (request, tile) from the row parts' partials,
+    // written by the row-part-0 wavefronts once a barrier has passed
+    auto merge_parts = [&](int par, int t) {
+        if (G > 1 && tile_part && rp == 0 && lane < 16 * G) {
+            const int mm = blockIdx.y * MC + q0 + lane;
+            if (mm < a.B) {
+                svk::MS v = parts[(par * G + 0) * MC + q0 + lane];
+#pragma unroll
+                for (int r = 1; r < G; ++r) v = svk::ms_merge(v, parts[(par * G + r) * MC + q0 + lane]);
+                tile_part[(int64_t)mm * ntile + t] = make_float2(v.m, v.s);
+            }
+        }
+    };
+
+    // The next tile's loads (PER_WAVE = KS copy instructions and NVB base
+    // quads per wavefront) are spread over the tile's work so that the
+    // memory queue drains as fast as it fills and no issue stalls the
+    // VALU/MFMA stream behind it.  G = 1: over the k-steps (one copy
+    // instruction and NVB / KS base quads per k-step).  G > 1 (KS = NVB = 8):
+    // sixteen issue points, op i a copy instruction (i even) or a base quad
+    // (i odd), ops 0..7 at the k-steps and 8..15 through the epilogue.
+    constexpr int BPS = (NVB + KS - 1) / KS;   // base quads per k-step (G = 1)
+    static_assert(TL::PER_WAVE == KS, "one copy instruction per k-step");
+    static_assert(G == 1 || (KS == 8 && NVB == 8), "sixteen issue points");
 
     for (int it = 0; tile < ntile; ++it, tile += gridDim.x) {
         unsigned char *buf = wtile + (it & 1) * TL::BYTES;
-        // this tile's copy (and base loads) landed for every wavefront, and
-        // every wavefront finished reading the other buffer
+        unsigned char *nbuf = wtile + ((it + 1) & 1) * TL::BYTES;
+        // this tile's copy (and base loads) landed for every wavefront, every
+        // wavefront finished reading the other buffer and wrote its partials
         __builtin_amdgcn_s_waitcnt(0);
         svk::lds_barrier();
+        if (it > 0) merge_parts((it - 1) & 1, tile - (int)gridDim.x);
         const int next = tile + (int)gridDim.x;
-        uint2 bn[NVB];
-        if (next < ntile) {
-            copy_tile<R>(a, (int64_t)next * TN, wtile + ((it + 1) & 1) * TL::BYTES, wid, lane);
-            load_base(a, km, mb, (int64_t)next * TN, lg, vec, bn);
-        }
-        if (wave_on) {
-            f32x4 acc[NVB];
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) acc[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-#pragma unroll
-                for (int vb = 0; vb < NVB; ++vb) {
-                    const int row = 16 * vb + li;
-                    const bf16x8 afr = *(const bf16x8 *)(buf + 16 * TL::slot(row, 4 * s + lg));
-                    acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, ufr[s], acc[vb], 0, 0, 0);
-                }
+        const bool has_next = next < ntile;
+        const int64_t nn0 = (int64_t)next * TN;
+        uint2 bn[G][VBW];
+        auto issue = [&](int i) {   // G > 1: op i of the next tile's loads
+            if (!has_next) return;
+            if ((i & 1) == 0) {
+                copy_chunk<R>(a, nn0, nbuf, wid, lane, i >> 1);
+            } else {
+                const int f = i >> 1;
+                bn[f / VBW][f % VBW] = base_quad(brow[f / VBW], next * TN + 16 * (vb0 + f % VBW) + 4 * lg, Vi, vec);
             }
-            // epilogue: lane holds z^T[n0 + 16 vb + 4 lg + r][m]
-            const int64_t n0 = (int64_t)tile * TN;
-            float *zrow = zout ? zout + (int64_t)(act ? m : 0) * zstride : nullptr;
-            float mx = svk::neg_inf();
-            bool bad = false;
-            float zc[NVB][4];
+        };
+        if (!wave_on) {
+            if (has_next) copy_tile<R>(a, nn0, nbuf, wid, lane);
+            continue;
+        }
+        f32x4 acc[G][VBW];
 #pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) {
-                const int64_t n = n0 + 16 * vb + 4 * lg;
-                const uint32_t b01 = bv[vb].x, b23 = bv[vb].y;
-                float z[4];
-                z[0] = acc[vb][0] + __uint_as_float(b01 << 16);
-                z[1] = acc[vb][1] + __uint_as_float(b01 & 0xFFFF0000u);
-                z[2] = acc[vb][2] + __uint_as_float(b23 << 16);
-                z[3] = acc[vb][3] + __uint_as_float(b23 & 0xFFFF0000u);
-                if (zrow && act) {
-                    if (vec) {
-                        if (n < a.V) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
-                    } else {
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (n + r < a.V) zrow[n + r] = z[r];
+            for (int j = 0; j < VBW; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // A fragments: with G > 1 the next k-step's are read while the
+        // current k-step's MFMAs run (registers allow it at one workgroup per
+        // CU); with G = 1 each k-step reads its own
+        constexpr int NBUF = G > 1 ? 2 : 1;
+        bf16x8 af[NBUF][VBW];
+        if (NBUF == 2) {
+#pragma unroll
+            for (int j = 0; j < VBW; ++j) af[0][j] = *(const bf16x8 *)(buf + 16 * TL::slot(16 * (vb0 + j) + li, lg));
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (G > 1) {
+                issue(s);
+            } else if (has_next) {
+                copy_chunk<R>(a, nn0, nbuf, wid, lane, s);
+#pragma unroll
+                for (int f = s * BPS; f < (s + 1) * BPS && f < NVB; ++f)
+                    bn[f / VBW][f % VBW] =
+                        base_quad(brow[f / VBW], next * TN + 16 * (vb0 + f % VBW) + 4 * lg, Vi, vec);
+            }
+            const int cur = NBUF == 2 ? (s & 1) : 0;
+            if (NBUF == 2 && s + 1 < KS) {
+#pragma unroll
+                for (int j = 0; j < VBW; ++j)
+                    af[(s + 1) % NBUF][j] =
+                        *(const bf16x8 *)(buf + 16 * TL::slot(16 * (vb0 + j) + li, 4 * (s + 1) + lg));
+            } else if (NBUF == 1) {
+#pragma unroll
+                for (int j = 0; j < VBW; ++j)
+                    af[0][j] = *(const bf16x8 *)(buf + 16 * TL::slot(16 * (vb0 + j) + li, 4 * s + lg));
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int j = 0; j < VBW; ++j)
+                    acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cur][j], ufr[g][s], acc[g][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // epilogue: lane holds z^T[n0 + 16 (vb0 + j) + 4 lg + r][m[g]]; at the
+        // largest rank the common case (a full tile, no z rows stored) runs
+        // without per-entry checks
+        const int n0 = tile * TN;
+        auto epilogue = [&](auto fast_c) {
+            constexpr bool FAST = decltype(fast_c)::value;
+            constexpr bool FULL = FAST;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const bool STORE = !FAST && zout != nullptr;
+                float *zrow = STORE ? zout + (int64_t)(act[g] ? m[g] : 0) * zstride : nullptr;
+                float mx = svk::neg_inf();
+                float zc[VBW][4];
+#pragma unroll
+                for (int j = 0; j < VBW; ++j) {
+                    const int n = n0 + 16 * (vb0 + j) + 4 * lg;
+                    const uint32_t b01 = bv[g][j].x, b23 = bv[g][j].y;
+                    float z[4];
+                    z[0] = acc[g][j][0] + __uint_as_float(b01 << 16);
+                    z[1] = acc[g][j][1] + __uint_as_float(b01 & 0xFFFF0000u);
+                    z[2] = acc[g][j][2] + __uint_as_float(b23 << 16);
+                    z[3] = acc[g][j][3] + __uint_as_float(b23 & 0xFFFF0000u);
+                    if (STORE && act[g]) {
+                        if (FULL && vec) {
+                            *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
+                        } else if (vec) {
+                            if (n < Vi) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (FULL || n + r < Vi) zrow[n + r] = z[r];
+                        }
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        zc[j][r] = (FULL || n + r < Vi) ? z[r] * a.c : svk::neg_inf();
+                        mx = fmaxf(mx, zc[j][r]);
                     }
                 }
+                auto point = [&](int pt) {   // issue points 8 + 4 g + pt
+                    if (G > 1) {
+                        issue(8 + 4 * g + pt);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                };
+                if (!tile_part) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    zc[vb][r] = n + r < a.V ? z[r] * a.c : svk::neg_inf();
-                    mx = fmaxf(mx, zc[vb][r]);
-                    bad |= zc[vb][r] != zc[vb][r];
+                    for (int pt = 0; pt < 4; ++pt) point(pt);
+                    continue;
+                }
+                point(0);
+                mx = rows4_max(mx);   // over the request's 4 lanes: the wavefront's rows of the tile
+                point(1);
+                // a NaN entry poisons the row (the draw flags it): through the
+                // exponentials when the maximum is finite, explicitly otherwise
+                float sm = 0.0f;
+                if (mx != svk::neg_inf()) {
+#pragma unroll
+                    for (int j = 0; j < VBW; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[j][r] - mx);
+                } else {
+                    bool bad = false;
+#pragma unroll
+                    for (int j = 0; j < VBW; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) bad |= zc[j][r] != zc[j][r];
+                    if (bad) sm = __builtin_nanf("");
+                }
+                point(2);
+                sm = rows4_sum(sm);
+                point(3);
+                if (lg == 0) {
+                    if (G > 1)
+                        parts[((it & 1) * G + rp) * MC + q0 + 16 * g + li] = svk::MS{mx, sm};
+                    else if (m[g] < a.B)
+                        tile_part[(int64_t)m[g] * ntile + tile] = make_float2(mx, sm);
                 }
             }
-            // lanes li, li + 16, li + 32, li + 48 hold request m's 128 entries
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            float sm = 0.0f;
-            if (mx != svk::neg_inf()) {
+        };
+        if (G > 1 && n0 + TN <= Vi && !zout)
+            epilogue(std::true_type{});
+        else
+            epilogue(std::false_type{});
+        if (has_next) {
 #pragma unroll
-                for (int vb = 0; vb < NVB; ++vb)
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[vb][r] - mx);
-            }
-            if (bad) sm = __builtin_nanf("");   // a NaN entry poisons the row; the draw flags it
-            sm += __shfl_xor(sm, 16, 64);
-            sm += __shfl_xor(sm, 32, 64);
-            if (tile_part && lg == 0 && m < a.B) tile_part[(int64_t)m * ntile + tile] = make_float2(mx, sm);
+                for (int j = 0; j < VBW; ++j) bv[g][j] = bn[g][j];
         }
-        if (next < ntile) {
-#pragma unroll
-            for (int vb = 0; vb < NVB; ++vb) bv[vb] = bn[vb];
-        }
+    }
+    if (G > 1 && tile_part) {
+        // the last tile's partials
+        const int it = (ntile - 1 - (int)blockIdx.x) / (int)gridDim.x;   // index of the workgroup's last tile
+        svk::lds_barrier();
+        merge_parts(it & 1, tile - (int)gridDim.x);
     }
 }
 
