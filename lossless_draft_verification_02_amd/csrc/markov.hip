@@ -28,10 +28,12 @@
 //                    instructions at a time through the MFMAs and the
 //                    epilogue, so the small per-CU miss queue never blocks
 //                    the wavefront's arithmetic for long.
-//   k_markov_select  one wavefront per request, no barriers: merge the tile
-//                    pairs into the row's log-sum-exp, pick the tile holding
-//                    u * Z by an fp64 wavefront scan, scan inside it for the
-//                    token (inverse CDF in ascending token order).
+//   k_markov_draw    one 256-thread workgroup per request: the row maximum
+//                    of the tile pairs, the tile masses relative to it and
+//                    their fp64 prefix over the workgroup, the tile holding
+//                    u * Z, then that tile's 128 logits (read back, or rebuilt
+//                    by MFMA when no z rows are stored) scanned for the token
+//                    (inverse CDF in ascending token order).
 //
 // RNN head ("DeepSeek DSpark 详解", section 03, and "DSpark: DeepSeek's bet
 // on speed that doesn't betray quality", section "A drafter that learns to
@@ -180,18 +182,6 @@ __device__ void rnn_next(const svh::MarkovArgs &a, int k, int b, int32_t xk, con
         }
         a.hstate[(int64_t)b * R + j] = f32_to_bf16(tanhf(acc));
     }
-}
-
-// One wavefront does both phases for its request (the non-fused draw).
-template <int R>
-__device__ void rnn_advance_wave(const svh::MarkovArgs &a, int k, int b, int32_t xk, float *hs)
-{
-    rnn_fill<R, 1>(a, k, b, hs, 0);
-    // the wavefront's LDS writes are visible to its own later reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    rnn_next<R, 1>(a, k, b, xk, hs, 0);
 }
 
 // A tile of Wt (TN rows of R bf16) in LDS: row r's 16-byte chunk c sits at
@@ -540,8 +530,9 @@ void k_markov_gemm(
     }
 }
 
-constexpr int kSelWaves = 4;                                        // requests per workgroup
-constexpr int kSelTilesPerLane = svh::kMarkovMaxTiles / 64;          // tile pairs held per lane
+constexpr int kDrawThreads = 256;                                        // one workgroup per request
+constexpr int kDrawWaves = kDrawThreads / 64;
+constexpr int kDrawTilesPerThread = svh::kMarkovMaxTiles / kDrawThreads;  // tile pairs held per thread
 
 __device__ __forceinline__ int wave_min_i(int v)
 {
@@ -555,38 +546,58 @@ __device__ __forceinline__ int wave_max_i(int v)
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
     return v;
 }
+__device__ __forceinline__ float wave_max_f(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
 
 // State of one request's draw after the tile choice.
 struct SelState {
     int32_t xprev;     // token sampled at the previous position (valid)
     float lse2;        // row log2-sum-exp2 of z * c
+    float ref;         // row max of z * c: masses are exp2(z * c - ref)
     float tf;          // fp32(u * fp32(Z)), Z the fp64 sum of the tile masses
     double tbase;      // cumulative mass before the chosen tile
     int ts;            // chosen tile
     int fallback;      // no cumulative mass exceeded tf: take the last positive token
 };
 
-// Tile choice for request b by one wavefront: merge the tile pairs into the
-// row's log-sum-exp, fp64 prefix of the tile masses, the tile holding u * Z.
+// Workgroup scratch of the tile choice.
+struct DrawLDS {
+    float wmax[kDrawWaves];
+    int wbad[kDrawWaves];
+    double scan[kDrawWaves];
+    int wfirst[kDrawWaves], wlast[kDrawWaves];
+    double wfirstb[kDrawWaves], wlastb[kDrawWaves];
+};
+
+// Tile choice for request b by the whole workgroup (every thread returns the
+// same result): thread t holds tiles [t per, (t + 1) per); the row maximum
+// M of the tile maxima; tile masses s exp2(m - M), their fp64 prefix in tile
+// order (thread runs, then a deterministic block scan) and total Z; the row
+// log2-sum-exp2 M + log2(Z); the first tile whose cumulative mass, rounded
+// to binary32, exceeds fp32(u fp32(Z)) (else the last tile with mass).
 // Returns false when the request is finished (error outputs written).
-__device__ bool select_tile(const svh::MarkovArgs &a, int k, const float2 *__restrict__ tile_part, int ntile,
-                            uint32_t *__restrict__ errword, int b, SelState &st)
+__device__ bool select_tile_wg(const svh::MarkovArgs &a, int k, const float2 *__restrict__ tile_part, int ntile,
+                               uint32_t *__restrict__ errword, int b, DrawLDS &L, SelState &st)
 {
-    const int lane = threadIdx.x & 63;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int64_t out = (int64_t)b * a.gamma + (k - 1);
-    // independent loads first: the previous token and this lane's run of tile pairs
+    // independent loads first: the previous token and this thread's run of tile pairs
     const int32_t xprev = k == 1 ? a.x0[b] : a.draft[(int64_t)b * a.gamma + (k - 2)];
     const float2 *tp = tile_part + (int64_t)b * ntile;
-    const int per = (ntile + 63) / 64;
-    const int t0 = lane * per;
-    float2 mine[kSelTilesPerLane];
+    const int per = (ntile + kDrawThreads - 1) / kDrawThreads;
+    const int t0 = t * per;
+    float2 mine[kDrawTilesPerThread];
 #pragma unroll
-    for (int q = 0; q < kSelTilesPerLane; ++q)
+    for (int q = 0; q < kDrawTilesPerThread; ++q)
         mine[q] = (q < per && t0 + q < ntile) ? tp[t0 + q] : make_float2(svk::neg_inf(), 0.0f);
     const float u = a.uniforms ? a.uniforms[out]
                                : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)k, 2u);
     if (xprev < 0 || (int64_t)xprev >= a.V) {
-        if (lane == 0) {
+        if (t == 0) {
             a.draft[out] = -1;
             if (a.lse_q) a.lse_q[out] = __builtin_nanf("");
             atomicOr(errword, SV_FLAG_BAD_TOKEN);
@@ -594,15 +605,42 @@ __device__ bool select_tile(const svh::MarkovArgs &a, int k, const float2 *__res
         return false;
     }
 
-    // row log-sum-exp2 from the tile pairs
-    svk::MS acc{svk::neg_inf(), 0.0f};
+    // row maximum; a NaN sum or a +inf maximum poisons the row
+    float mloc = svk::neg_inf();
+    bool bad = false;
 #pragma unroll
-    for (int q = 0; q < kSelTilesPerLane; ++q) acc = svk::ms_merge(acc, svk::MS{mine[q].x, mine[q].y});
-    acc = svk::wave_merge(acc);
-    const float lse2 = (acc.s > 0.0f && acc.m != svk::pos_inf() && acc.s == acc.s) ? acc.m + log2f(acc.s)
-                                                                                    : __builtin_nanf("");
+    for (int q = 0; q < kDrawTilesPerThread; ++q) {
+        mloc = fmaxf(mloc, mine[q].x);
+        bad |= (mine[q].y != mine[q].y) || mine[q].x == svk::pos_inf();
+    }
+    mloc = wave_max_f(mloc);
+    const bool wbad = __any(bad);
+    if (lane == 0) {
+        L.wmax[wid] = mloc;
+        L.wbad[wid] = wbad;
+    }
+    __syncthreads();
+    float M = L.wmax[0];
+    bad = L.wbad[0];
+#pragma unroll
+    for (int w = 1; w < kDrawWaves; ++w) {
+        M = fmaxf(M, L.wmax[w]);
+        bad |= L.wbad[w] != 0;
+    }
+
+    // tile masses relative to M, fp64 prefix over the block
+    float wt[kDrawTilesPerThread];
+    double loc = 0.0;
+#pragma unroll
+    for (int q = 0; q < kDrawTilesPerThread; ++q) {
+        wt[q] = mine[q].y > 0.0f ? mine[q].y * svk::fast_exp2(mine[q].x - M) : 0.0f;
+        loc += (double)wt[q];
+    }
+    double Z;
+    const double excl = svk::block_exclusive_scan_d<kDrawThreads>(loc, L.scan, &Z);
+    const float lse2 = (!bad && M != svk::neg_inf() && Z > 0.0) ? M + log2f((float)Z) : __builtin_nanf("");
     if (lse2 != lse2) {
-        if (lane == 0) {
+        if (t == 0) {
             a.draft[out] = -1;
             if (a.lse_q) a.lse_q[out] = __builtin_nanf("");
             atomicOr(errword, SV_FLAG_BAD_ROW);
@@ -610,69 +648,89 @@ __device__ bool select_tile(const svh::MarkovArgs &a, int k, const float2 *__res
         return false;
     }
 
-    // tile masses, fp64 prefix over the lanes' contiguous runs
-    float wt[kSelTilesPerLane];
-    double loc = 0.0;
-#pragma unroll
-    for (int q = 0; q < kSelTilesPerLane; ++q) {
-        wt[q] = (q < per && t0 + q < ntile) ? mine[q].y * svk::fast_exp2(mine[q].x - lse2) : 0.0f;
-        loc += (double)wt[q];
-    }
-    const double incl = svk::wave_inclusive_scan_d(loc);
-    const double excl = incl - loc;
-    const double Z = __shfl(incl, 63, 64);
+    // the first tile past the threshold, and the last tile with mass, each
+    // with the cumulative mass before it
     const float tf = __fmul_rn(u, (float)Z);
-    int first = 0x7FFFFFFF, lastpos = -1;
+    int first = 0x7FFFFFFF, last = -1;
+    double firstb = 0.0, lastb = 0.0;
     {
         double run = excl;
 #pragma unroll
-        for (int q = 0; q < kSelTilesPerLane; ++q) {
-            if (q < per && t0 + q < ntile && wt[q] > 0.0f) {
+        for (int q = 0; q < kDrawTilesPerThread; ++q) {
+            if (wt[q] > 0.0f) {
+                const double before = run;
                 run += (double)wt[q];
-                lastpos = t0 + q;
-                if (first == 0x7FFFFFFF && (float)run > tf) first = t0 + q;
+                last = t0 + q;
+                lastb = before;
+                if (first == 0x7FFFFFFF && (float)run > tf) {
+                    first = t0 + q;
+                    firstb = before;
+                }
             }
         }
     }
-    const int tstar = wave_min_i(first);
-    const int tlast = wave_max_i(lastpos);
-    const bool fallback = tstar == 0x7FFFFFFF;
-    const int ts = fallback ? tlast : tstar;
-    if (ts < 0) {   // no tile kept any mass
+    // runs are contiguous in thread order: the lowest thread with a first
+    // tile holds the workgroup's first, the highest with mass its last
+    {
+        const uint64_t hasf = __ballot(first != 0x7FFFFFFF), hasl = __ballot(last >= 0);
+        const int lf = hasf ? __builtin_ctzll(hasf) : 0;
+        const int ll = hasl ? 63 - __builtin_clzll(hasl) : 0;
+        const int fw = __shfl(first, lf, 64), lw = __shfl(last, ll, 64);
+        const double fbw = __shfl(firstb, lf, 64), lbw = __shfl(lastb, ll, 64);
         if (lane == 0) {
+            L.wfirst[wid] = hasf ? fw : 0x7FFFFFFF;
+            L.wfirstb[wid] = fbw;
+            L.wlast[wid] = hasl ? lw : -1;
+            L.wlastb[wid] = lbw;
+        }
+    }
+    __syncthreads();
+    int ts = 0x7FFFFFFF, tl = -1;
+    double tb = 0.0, tlb = 0.0;
+#pragma unroll
+    for (int w = 0; w < kDrawWaves; ++w) {
+        if (ts == 0x7FFFFFFF && L.wfirst[w] != 0x7FFFFFFF) {
+            ts = L.wfirst[w];
+            tb = L.wfirstb[w];
+        }
+        if (L.wlast[w] >= 0) {
+            tl = L.wlast[w];
+            tlb = L.wlastb[w];
+        }
+    }
+    const bool fallback = ts == 0x7FFFFFFF;
+    if (tl < 0) {   // no tile kept any mass
+        if (t == 0) {
             a.draft[out] = -1;
             if (a.lse_q) a.lse_q[out] = lse2 * svk::kLn2;
             atomicOr(errword, SV_FLAG_BAD_ROW);
         }
         return false;
     }
-    // cumulative mass before tile ts, from the lane that owns it
-    double before_ts = excl;
-#pragma unroll
-    for (int q = 0; q < kSelTilesPerLane; ++q)
-        if (q < per && t0 + q < ts) before_ts += (double)wt[q];
     st.xprev = xprev;
     st.lse2 = lse2;
+    st.ref = M;
     st.tf = tf;
-    st.tbase = __shfl(before_ts, ts / per, 64);
-    st.ts = ts;
+    st.tbase = fallback ? tlb : tb;
+    st.ts = fallback ? tl : ts;
     st.fallback = fallback;
     return true;
 }
 
 // Token of the chosen tile (z values zr[0 .. 128)) by one wavefront: lane
-// owns columns 2 lane, 2 lane + 1; fp64 prefix; outputs.  Returns the token
-// (the same on every lane), -1 if none.
+// owns columns 2 lane, 2 lane + 1; masses exp2(z c - ref) as the tile
+// choice's; fp64 prefix; outputs.  Returns the token (the same on every
+// lane), -1 if none.
 __device__ int32_t select_token_in_tile(const svh::MarkovArgs &a, int k, int b, const SelState &st,
-                                     const float *zr, uint32_t *__restrict__ errword)
+                                        const float *zr, uint32_t *__restrict__ errword)
 {
     const int lane = threadIdx.x & 63;
     const int64_t out = (int64_t)b * a.gamma + (k - 1);
     const int64_t c0 = (int64_t)st.ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
     const int j0 = 2 * lane, j1 = 2 * lane + 1;
-    const float w0 = j0 < ncols ? svk::fast_exp2(zr[j0] * a.c - st.lse2) : 0.0f;
-    const float w1 = j1 < ncols ? svk::fast_exp2(zr[j1] * a.c - st.lse2) : 0.0f;
+    const float w0 = j0 < ncols ? svk::fast_exp2(zr[j0] * a.c - st.ref) : 0.0f;
+    const float w1 = j1 < ncols ? svk::fast_exp2(zr[j1] * a.c - st.ref) : 0.0f;
     const double pair = (double)w0 + (double)w1;
     const double pincl = svk::wave_inclusive_scan_d(pair);
     const double pexcl = pincl - pair;
@@ -699,91 +757,61 @@ __device__ int32_t select_token_in_tile(const svh::MarkovArgs &a, int k, int b, 
     return jj >= 0 ? (int32_t)(c0 + jj) : -1;
 }
 
-// The draw with stored z rows: one wavefront per request, no barriers.
-__global__ __launch_bounds__(64 * kSelWaves) void k_markov_select(svh::MarkovArgs a, int k,
-                                                                  const float *__restrict__ zin, int64_t zstride,
-                                                                  const float2 *__restrict__ tile_part, int ntile,
-                                                                  uint32_t *__restrict__ errword)
-{
-    const int b = blockIdx.x * kSelWaves + (int)(threadIdx.x >> 6);
-    if (b >= a.B) return;   // whole wavefront; nothing below synchronises the workgroup
-    SelState st;
-    if (!select_tile(a, k, tile_part, ntile, errword, b, st)) return;
-    select_token_in_tile(a, k, b, st, zin + (int64_t)b * zstride + (int64_t)st.ts * TN, errword);
-}
-
-// The same draw for the RNN head, then the wavefront advances its request's
-// state.
+// The draw at position k: one workgroup of four wavefronts per request.  All
+// threads choose the tile; its 128 logits come from the stored z rows (zin)
+// or, without them (fused path), are rebuilt by the four wavefronts (two
+// 16-row blocks each) with the contraction's own arithmetic -- same A rows,
+// same k order, same base add -- so they equal, bit for bit, the values
+// reduced into the tile pairs; the B fragments of that rebuild are requested
+// before the tile choice.  Wavefront 0 then draws the token; for the RNN head
+// the four wavefronts advance the request's state.
 template <int R>
-__global__ __launch_bounds__(64 * kSelWaves) void k_rnn_select(svh::MarkovArgs a, int k,
-                                                               const float *__restrict__ zin, int64_t zstride,
-                                                               const float2 *__restrict__ tile_part, int ntile,
-                                                               uint32_t *__restrict__ errword)
-{
-    __shared__ float hs[kSelWaves][R];
-    const int b = blockIdx.x * kSelWaves + (int)(threadIdx.x >> 6);
-    if (b >= a.B) return;   // whole wavefront; nothing below synchronises the workgroup
-    SelState st;
-    if (!select_tile(a, k, tile_part, ntile, errword, b, st)) return;
-    const int32_t xk = select_token_in_tile(a, k, b, st, zin + (int64_t)b * zstride + (int64_t)st.ts * TN, errword);
-    rnn_advance_wave<R>(a, k, b, xk, hs[threadIdx.x >> 6]);
-}
-
-// The draw without stored z rows (fused path): one workgroup of 4 wavefronts
-// per request.  Wavefront 0 chooses the tile; all four rebuild its 128 logits
-// (two 16-row blocks each, every load issued before the MFMAs) with the
-// contraction's own arithmetic -- same A rows, same k order, same base add --
-// so they equal, bit for bit, the values reduced into the tile pairs;
-// wavefront 0 then draws the token.
-template <int R>
-__global__ __launch_bounds__(256) void k_markov_select_fused(svh::MarkovArgs a, int k,
-                                                            const float2 *__restrict__ tile_part, int ntile,
-                                                            uint32_t *__restrict__ errword)
+__global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a, int k,
+                                                              const float *__restrict__ zin, int64_t zstride,
+                                                              const float2 *__restrict__ tile_part, int ntile,
+                                                              uint32_t *__restrict__ errword)
 {
     constexpr int KS = R / 32;
-    constexpr int VBW = NVB / 4;   // 16-row blocks per wavefront
-    __shared__ SelState st;
-    __shared__ int go;
+    constexpr int VBW = NVB / kDrawWaves;   // 16-row blocks per wavefront
+    __shared__ DrawLDS L;
     __shared__ float zt[TN];
-    __shared__ float hs[R];   // RNN head: the request's state
+    __shared__ float hs[R];    // RNN head: the request's state
     __shared__ int32_t xnew;   // the token drawn (RNN head)
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    if (wid == 0) {
-        SelState s0;
-        const bool ok = select_tile(a, k, tile_part, ntile, errword, b, s0);
-        if (lane == 0) {
-            go = ok;
-            if (ok) st = s0;
-        }
-    }
-    __syncthreads();
-    if (!go) return;
+    const int li = lane & 15, lg = lane >> 4;
+    bf16x8 ufr[KS];
+    if (!zin) head_fragments<R>(a, k, b, lg, true, ufr);   // the request's operand row in every B column
+    SelState st;
+    if (!select_tile_wg(a, k, tile_part, ntile, errword, b, L, st)) return;   // the same in every thread
     const int64_t c0 = (int64_t)st.ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
-    const int li = lane & 15, lg = lane >> 4;
-    bf16x8 ufr[KS], afr[VBW][KS];
-    head_fragments<R>(a, k, b, lg, true, ufr);   // the request's operand row in every B column
+    if (zin) {
+        if ((int)threadIdx.x < ncols) zt[threadIdx.x] = zin[(int64_t)b * zstride + c0 + threadIdx.x];
+    } else {
+        bf16x8 afr[VBW][KS];
 #pragma unroll
-    for (int v = 0; v < VBW; ++v) {
-        const int64_t n = c0 + 16 * (VBW * wid + v) + li;
-        const uint16_t *wrow = a.W + (n < a.V ? n : a.V - 1) * R + 8 * lg;
+        for (int v = 0; v < VBW; ++v) {
+            const int64_t n = c0 + 16 * (VBW * wid + v) + li;
+            const uint16_t *wrow = a.W + (n < a.V ? n : a.V - 1) * R + 8 * lg;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) afr[v][s] = *(const bf16x8 *)(wrow + 32 * s);
-    }
-    const uint16_t *brow = a.base + ((int64_t)b * a.gamma + (k - 1)) * a.V + c0;
+            for (int s = 0; s < KS; ++s) afr[v][s] = *(const bf16x8 *)(wrow + 32 * s);
+        }
+        const uint16_t *brow = a.base + ((int64_t)b * a.gamma + (k - 1)) * a.V + c0;
 #pragma unroll
-    for (int v = 0; v < VBW; ++v) {
-        const int vb = VBW * wid + v;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < VBW; ++v) {
+            const int vb = VBW * wid + v;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[v][s], ufr[s], acc, 0, 0, 0);
-        if (li == 0) {   // D[4 lg + r][0]: vocabulary row 16 vb + 4 lg + r of the tile
+            for (int s = 0; s < KS; ++s)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[v][s], ufr[s], acc, 0, 0, 0);
+            if (li == 0) {   // D[4 lg + r][0]: vocabulary row 16 vb + 4 lg + r of the tile
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int col = 16 * vb + 4 * lg + r;
-                const uint32_t bits = col < ncols ? (uint32_t)brow[col] : 0xFF80u;
-                zt[col] = acc[r] + __uint_as_float(bits << 16);
+                for (int r = 0; r < 4; ++r) {
+                    const int col = 16 * vb + 4 * lg + r;
+                    const uint32_t bits = col < ncols ? (uint32_t)brow[col] : 0xFF80u;
+                    zt[col] = acc[r] + __uint_as_float(bits << 16);
+                }
             }
         }
     }
@@ -793,9 +821,9 @@ __global__ __launch_bounds__(256) void k_markov_select_fused(svh::MarkovArgs a, 
         if (lane == 0) xnew = xk;
     }
     if (a.A) {   // RNN head: the four wavefronts advance the state together
-        rnn_fill<R, 4>(a, k, b, hs, wid);
+        rnn_fill<R, kDrawWaves>(a, k, b, hs, wid);
         __syncthreads();
-        rnn_next<R, 4>(a, k, b, xnew, hs, wid);
+        rnn_next<R, kDrawWaves>(a, k, b, xnew, hs, wid);
     }
 }
 
@@ -820,17 +848,8 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
                            zstride, ctx->ws.mk_part, ntile, vec);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
-        if (a.fused)
-            hipLaunchKernelGGL((k_markov_select_fused<R>), dim3(a.B), dim3(256), 0, s, a, k,
-                               (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword);
-        else if (a.A)
-            hipLaunchKernelGGL((k_rnn_select<R>), dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0,
-                               s, a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,
-                               ctx->ws.errword);
-        else
-            hipLaunchKernelGGL(k_markov_select, dim3((a.B + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0,
-                               s, a, k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile,
-                               ctx->ws.errword);
+        hipLaunchKernelGGL((k_markov_draw<R>), dim3(a.B), dim3(kDrawThreads), 0, s, a, k, (const float *)zk, zstride,
+                           (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword);
         svh::prof_end(ctx, s, slot);
     }
     return hipGetLastError();
