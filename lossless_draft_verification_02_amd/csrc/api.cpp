@@ -239,6 +239,8 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_srank = carve((size_t)svh::kSchedMax * sizeof(int32_t));
     const size_t o_ssurv = carve((size_t)svh::kSchedMax * sizeof(double));
     const size_t o_rnnh = carve((size_t)max_batch * (max_rank > 0 ? max_rank : 1) * sizeof(uint16_t));
+    const size_t o_tstate = carve(2 * (size_t)max_batch * svh::kTreeStateBytes);
+    const size_t o_tseg = carve(2 * (size_t)max_batch * ctx->nseg * sizeof(float));
     size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0, o_mklse = 0, o_mkzx = 0;
     if (max_rank > 0) {
         o_mkpart = carve((size_t)max_batch * ctx->ntile * sizeof(float2));
@@ -272,6 +274,8 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.sched_rank = (int32_t *)(b + o_srank);
     ctx->ws.sched_surv = (double *)(b + o_ssurv);
     ctx->ws.rnn_h = (uint16_t *)(b + o_rnnh);
+    ctx->ws.tree_state = (void *)(b + o_tstate);
+    ctx->ws.tree_seg = (float *)(b + o_tseg);
     ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
     ctx->ws.mk_prev = max_rank > 0 ? (int32_t *)(b + o_mkprev) : nullptr;
     ctx->ws.mk_q = max_rank > 0 ? (float *)(b + o_mkq) : nullptr;
@@ -528,6 +532,22 @@ sv_status tree_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits,
     }
     for (int n = 0; n <= N; ++n)
         if (t.first_child[n] >= 0) t.qrow[n] = (int8_t)t.NQ++;
+    // passes a walk can need: at each node on the path c - 1 rejections that
+    // leave a sibling to try (c its children), then the draw and one retry of
+    // the draw from p; one more round consumes the last sums
+    {
+        int nch[svh::kMaxGamma + 1] = {0};
+        for (int m = 1; m <= N; ++m) nch[t.parent[m]] += 1;
+        int above[svh::kMaxGamma + 1];
+        above[0] = 0;
+        int most = 0;
+        for (int v = 0; v <= N; ++v) {
+            if (v > 0) above[v] = above[t.parent[v]] + nch[t.parent[v]] - 1;
+            const int here = above[v] + (nch[v] > 0 ? nch[v] - 1 : 0);
+            most = here > most ? here : most;
+        }
+        t.rounds = most + 2 + 1;
+    }
     // the row checks of a draft call with gamma = N (q has NQ <= N rows)
     sv_status st = check_verify_args(ctx, p_logits, p_dtype, q_logits, q_dtype, tokens, B, N, V, temperature,
                                      accepted_len, out_tokens, fn);

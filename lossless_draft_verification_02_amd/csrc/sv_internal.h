@@ -73,6 +73,8 @@ struct Workspace {
                          // the caller does not keep them; fused path: rebuilt correction rows
     float *mk_lse2;      // [max_batch * max_gamma] fused path: draft row log2-sum-exp2
     float *mk_zx;        // [max_batch * max_gamma] fused path: drafted tokens' logits
+    void *tree_state;    // [2][max_batch] kTreeStateBytes: tree walk state by round parity
+    float *tree_seg;     // [2][max_batch * nseg] tree walk segment sums by round parity
     void *base;          // single allocation backing all of the above
     size_t bytes;
 };
@@ -178,7 +180,10 @@ struct TreeTopo {
     int8_t first_child[kMaxGamma + 1];  // -1 for a leaf
     int8_t next_sib[kMaxGamma + 1];     // next child of the same parent, -1 for the last
     int8_t qrow[kMaxGamma + 1];         // q row of a node with children, else -1
+    int rounds;                         // walk rounds covering the longest sequence of passes
 };
+// Bytes of one request's walk state in the tree workspace.
+constexpr size_t kTreeStateBytes = 3072;
 // Tree verification after the row statistics (a.np_rows = N + 1, a.nq_rows =
 // NQ): one workgroup per request walks the tree and draws the final token.
 hipError_t launch_tree_tail(sv_ctx *ctx, const VerifyArgs &a, const TreeTopo &t, int32_t *nodes_out,

@@ -472,19 +472,20 @@ __device__ __forceinline__ float seg_reduce(const SegRaw<PES, QES> &r, int mode,
 }
 
 // Segment sums of the correction / bonus weights of rows prow / qrow into
-// sums[0, nseg), by NW wavefronts of the workgroup (wavefront wid takes
-// segments wid, wid + NW, ...).  Full segments of 16-byte aligned rows are
+// sums[kfirst, nseg), by NW wavefronts of the workgroup (wavefront wid takes
+// segments kfirst + wid, kfirst + wid + NW, ...).  Full segments of 16-byte aligned rows are
 // software-pipelined (unless both rows are fp32, where the second buffer would
 // spill): the next segment's vectors are requested before the current one is
 // reduced, so two segments per wavefront are in flight.
 template <int PES, int QES, int NW>
 __device__ void segment_sums(const svh::VerifyArgs &a, const char *prow, const char *qrow, int mode, float wmul,
-                             float lp2, float lq2, int nseg, float *sums)
+                             float lp2, float lq2, int nseg, float *sums, int kfirst = 0)
 {
     const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
     const bool aligned = (((uintptr_t)prow) & 15) == 0 && (mode || (((uintptr_t)qrow) & 15) == 0);
-    const int nfull = aligned ? (int)(a.V / SEG) : 0;
-    int k = wid;
+    const int nf = aligned ? (int)(a.V / SEG) : 0;
+    const int nfull = nf < nseg ? nf : nseg;   // segments [kfirst, nseg) only
+    int k = kfirst + wid;
     if constexpr (PES == 4 && QES == 4) {
         // fp32 rows: a second register buffer does not fit; one segment at a time
         for (; k < nfull; k += NW) {
@@ -1057,7 +1058,7 @@ __device__ __forceinline__ int64_t tree_qrow(const svh::TreeTopo &t, int b, int 
 
 // Wavefront 0, lane 0: decisions at st.node from st.child on, until a pass
 // or the draw is needed (st.act says which).
-__device__ void tree_decide(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st)
+__device__ void tree_decide(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st, bool writer)
 {
     for (;;) {
     const int node = st.node;
@@ -1085,7 +1086,7 @@ __device__ void tree_decide(const svh::VerifyArgs &a, const svh::TreeTopo &t, in
             const double r = d > 0.0 ? (qw > 0.0f ? d / (st.zr * (double)qw) : __builtin_inf()) : 0.0;
             ratio = r < 1.0 ? (float)r : 1.0f;
         }
-        if (a.diag.ratio) a.diag.ratio[(int64_t)b * t.N + (c - 1)] = ratio;
+        if (writer && a.diag.ratio) a.diag.ratio[(int64_t)b * t.N + (c - 1)] = ratio;
         if (st.u[c] < ratio) {   // accepted: continue at c
             st.path_x[st.depth] = st.x[c - 1];
             st.path_n[st.depth] = c;
@@ -1111,20 +1112,22 @@ __device__ void tree_decide(const svh::VerifyArgs &a, const svh::TreeTopo &t, in
 
 // Wavefront 0: decisions until a pass or the draw is needed.
 template <int PES, int QES>
-__device__ void tree_walk(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st)
+__device__ void tree_walk(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st, bool writer)
 {
-    if ((threadIdx.x & (svk::kWave - 1)) == 0) tree_decide(a, t, b, st);
+    if ((threadIdx.x & (svk::kWave - 1)) == 0) tree_decide(a, t, b, st, writer);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Wavefront 0: data checks, row statistics, uniforms; then the walk from the
-// root.  A request with a data error gets its error outputs here.
+// root.  A request with a data error gets its error outputs here.  Only the
+// writer stores outputs and diagnostics (other workgroups of a request
+// repeat the same steps for their own state).
 template <int PES, int QES>
 __device__ void tree_begin(const svh::VerifyArgs &a, const svh::TreeTopo &t, const float2 *__restrict__ part,
                            int nch1, int b, int32_t *__restrict__ nodes_out, uint32_t *__restrict__ errword,
-                           TreeLDS &st)
+                           TreeLDS &st, bool writer)
 {
     const int lane = threadIdx.x & (svk::kWave - 1);
     const int N = t.N, NQ = t.NQ, D = t.D;
@@ -1159,20 +1162,26 @@ __device__ void tree_begin(const svh::VerifyArgs &a, const svh::TreeTopo &t, con
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int n = lane; n <= N; n += svk::kWave)
-        if (a.diag.lse_p) a.diag.lse_p[(int64_t)b * (N + 1) + n] = flags ? nan : (float)(st.lp[n] * kLn2d);
-    for (int j = lane; j < NQ; j += svk::kWave)
-        if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * NQ + j] = flags ? nan : (float)(st.lq[j] * kLn2d);
-    for (int m = lane; m < N; m += svk::kWave)
-        if (a.diag.ratio) a.diag.ratio[(int64_t)b * N + m] = nan;
+    if (writer) {
+        for (int n = lane; n <= N; n += svk::kWave)
+            if (a.diag.lse_p) a.diag.lse_p[(int64_t)b * (N + 1) + n] = flags ? nan : (float)(st.lp[n] * kLn2d);
+        for (int j = lane; j < NQ; j += svk::kWave)
+            if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * NQ + j] = flags ? nan : (float)(st.lq[j] * kLn2d);
+        for (int m = lane; m < N; m += svk::kWave)
+            if (a.diag.ratio) a.diag.ratio[(int64_t)b * N + m] = nan;
+    }
     if (flags) {
-        for (int j = lane; j <= D; j += svk::kWave) a.out_tokens[(int64_t)b * (D + 1) + j] = -1;
-        if (nodes_out)
-            for (int j = lane; j < D; j += svk::kWave) nodes_out[(int64_t)b * D + j] = -1;
+        if (writer) {
+            for (int j = lane; j <= D; j += svk::kWave) a.out_tokens[(int64_t)b * (D + 1) + j] = -1;
+            if (nodes_out)
+                for (int j = lane; j < D; j += svk::kWave) nodes_out[(int64_t)b * D + j] = -1;
+        }
         if (lane == 0) {
-            a.accepted_len[b] = -1;
-            if (a.diag.flags) a.diag.flags[b] = flags;
-            atomicOr(errword, flags);
+            if (writer) {
+                a.accepted_len[b] = -1;
+                if (a.diag.flags) a.diag.flags[b] = flags;
+                atomicOr(errword, flags);
+            }
             st.act = TREE_DONE;
         }
         return;
@@ -1190,9 +1199,103 @@ __device__ void tree_begin(const svh::VerifyArgs &a, const svh::TreeTopo &t, con
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    tree_walk<PES, QES>(a, t, b, st);
+    tree_walk<PES, QES>(a, t, b, st, writer);
 }
 
+// Wavefront 0, after the segment sums of the node's current weights are in
+// sums[0, nseg): a pass gives the residual mass and the walk continues; the
+// draw picks the token (or falls back to p once) and, if the writer, stores
+// request b's outputs.
+template <int PES, int QES>
+__device__ void tree_consume(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b, TreeLDS &st,
+                             const float *sums, int nseg, int32_t *__restrict__ nodes_out,
+                             uint32_t *__restrict__ errword, bool writer)
+{
+    const int lane = threadIdx.x & (svk::kWave - 1);
+    const int node = st.node;
+    const int mode = st.mode;
+    if (st.act == TREE_PASS) {
+        // mass of the residual weights: fixed-order fp64 sum of the segment sums
+        const int per = (nseg + svk::kWave - 1) / svk::kWave;
+        const int k0 = lane * per, k1 = k0 + per < nseg ? k0 + per : nseg;
+        double loc = 0.0;
+        for (int k = k0; k < k1; ++k) loc += (double)sums[k];
+        const double Z = __shfl(svk::wave_inclusive_scan_d(loc), svk::kWave - 1, svk::kWave);
+        if (lane == 0) {
+            if (Z > 0.0) {
+                st.zr = Z;
+            } else {   // rounded to zero (positive in exact arithmetic): fall back to p
+                st.flags |= SV_FLAG_RESID_ZERO;
+                st.resid_p = 1;
+                st.mode = 1;
+                st.zr = 1.0;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        tree_walk<PES, QES>(a, t, b, st, writer);
+        return;
+    }
+    const char *prow = (const char *)a.p + tree_prow(t, b, node) * a.V * PES;
+    const char *qrow = mode ? nullptr : (const char *)a.q + tree_qrow(t, b, node) * a.V * QES;
+    const float lp2 = (float)st.lp[node];
+    const float lq2 = mode ? 0.0f : (float)st.lq[t.qrow[node]];
+    const float wm = (float)st.wmul;
+    const float u2 = a.uniforms ? a.uniforms[(int64_t)b * (t.N + 1) + t.N]
+                                : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, 0u, 1u);
+    double Z = 0.0;
+    const int y = select_token_wave<PES, QES>(a, mode, wm, lp2, lq2, sums, nseg, prow, qrow, u2, Z);
+    if (y < 0 && mode == 0) {
+        // residual mass rounded to zero: draw from the node's p row
+        if (lane == 0) {
+            st.flags |= SV_FLAG_RESID_ZERO;
+            st.mode = 1;
+            st.wmul = 1.0;
+        }
+    } else {
+        if (writer) {
+            const uint32_t flags = st.flags | (y < 0 ? SV_FLAG_BAD_ROW : 0u);
+            const int depth = st.depth, D = t.D;
+            for (int j = lane; j <= D; j += svk::kWave)
+                a.out_tokens[(int64_t)b * (D + 1) + j] =
+                    y < 0 ? -1 : (j < depth ? st.path_x[j] : (j == depth ? y : -1));
+            if (nodes_out)
+                for (int j = lane; j < D; j += svk::kWave)
+                    nodes_out[(int64_t)b * D + j] = (y >= 0 && j < depth) ? st.path_n[j] : -1;
+            if (lane == 0) {
+                a.accepted_len[b] = y < 0 ? -1 : depth;
+                if (a.diag.flags) a.diag.flags[b] = flags;
+                if (a.diag.resid_mass) a.diag.resid_mass[b] = (float)Z;
+                if (flags) atomicOr(errword, flags);
+            }
+        }
+        if (lane == 0) st.act = TREE_DONE;
+    }
+}
+
+// The node's current weights: prow / qrow, mode, wmul and the row statistics.
+struct TreeRows {
+    const char *prow, *qrow;
+    int mode;
+    float wm, lp2, lq2;
+};
+template <int PES, int QES>
+__device__ __forceinline__ TreeRows tree_rows(const svh::VerifyArgs &a, const svh::TreeTopo &t, int b,
+                                              const TreeLDS &st)
+{
+    TreeRows r;
+    const int node = st.node;
+    r.mode = st.mode;
+    r.prow = (const char *)a.p + tree_prow(t, b, node) * a.V * PES;
+    r.qrow = r.mode ? nullptr : (const char *)a.q + tree_qrow(t, b, node) * a.V * QES;
+    r.lp2 = (float)st.lp[node];
+    r.lq2 = r.mode ? 0.0f : (float)st.lq[t.qrow[node]];
+    r.wm = (float)st.wmul;
+    return r;
+}
+
+// One workgroup per request walks its whole tree.
 template <int PES, int QES, int NTT>
 __global__ __launch_bounds__(NTT, 1) void k_tree(svh::VerifyArgs a, const svh::TreeTopo t,
                                               const float2 *__restrict__ part, int nch1, int nseg,
@@ -1201,78 +1304,75 @@ __global__ __launch_bounds__(NTT, 1) void k_tree(svh::VerifyArgs a, const svh::T
     __shared__ TreeLDS st;
     __shared__ float segsum[kTailMaxSeg];
     const int b = a.b0 + (int)blockIdx.x;
-    const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
-    if (wid == 0) tree_begin<PES, QES>(a, t, part, nch1, b, nodes_out, errword, st);
+    const int wid = threadIdx.x / svk::kWave;
+    if (wid == 0) tree_begin<PES, QES>(a, t, part, nch1, b, nodes_out, errword, st, true);
     __syncthreads();
     // every pass consumes one rejection or makes the draw (at most one retry
     // of the draw, from p): the loop ends well within this bound
     for (int it = 0; it < 2 * MAXG + 4; ++it) {
-        const int act = st.act;
-        if (act == TREE_DONE) return;
-        const int node = st.node;
-        const char *prow = (const char *)a.p + tree_prow(t, b, node) * a.V * PES;
-        const char *qrow = st.mode ? nullptr : (const char *)a.q + tree_qrow(t, b, node) * a.V * QES;
-        const float lp2 = (float)st.lp[node];
-        const float lq2 = st.mode ? 0.0f : (float)st.lq[t.qrow[node]];
-        const float wm = (float)st.wmul;
-        const int mode = st.mode;
-        segment_sums<PES, QES, NTT / svk::kWave>(a, prow, qrow, mode, wm, lp2, lq2, nseg, segsum);
+        if (st.act == TREE_DONE) return;
+        const TreeRows r = tree_rows<PES, QES>(a, t, b, st);
+        segment_sums<PES, QES, NTT / svk::kWave>(a, r.prow, r.qrow, r.mode, r.wm, r.lp2, r.lq2, nseg, segsum);
         __syncthreads();
-        if (wid == 0) {
-            if (act == TREE_PASS) {
-                // mass of the residual weights: fixed-order fp64 sum of the segment sums
-                const int per = (nseg + svk::kWave - 1) / svk::kWave;
-                const int k0 = lane * per, k1 = k0 + per < nseg ? k0 + per : nseg;
-                double loc = 0.0;
-                for (int k = k0; k < k1; ++k) loc += (double)segsum[k];
-                const double Z = __shfl(svk::wave_inclusive_scan_d(loc), svk::kWave - 1, svk::kWave);
-                if (lane == 0) {
-                    if (Z > 0.0) {
-                        st.zr = Z;
-                    } else {   // rounded to zero (positive in exact arithmetic): fall back to p
-                        st.flags |= SV_FLAG_RESID_ZERO;
-                        st.resid_p = 1;
-                        st.mode = 1;
-                        st.zr = 1.0;
-                    }
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                tree_walk<PES, QES>(a, t, b, st);
-            } else {
-                const float u2 = a.uniforms ? a.uniforms[(int64_t)b * (t.N + 1) + t.N]
-                                            : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, 0u, 1u);
-                double Z = 0.0;
-                const int y = select_token_wave<PES, QES>(a, mode, wm, lp2, lq2, segsum, nseg, prow, qrow, u2, Z);
-                if (y < 0 && mode == 0) {
-                    // residual mass rounded to zero: draw from the node's p row
-                    if (lane == 0) {
-                        st.flags |= SV_FLAG_RESID_ZERO;
-                        st.mode = 1;
-                        st.wmul = 1.0;
-                    }
-                } else {
-                    uint32_t flags = st.flags | (y < 0 ? SV_FLAG_BAD_ROW : 0u);
-                    const int depth = st.depth, D = t.D;
-                    for (int j = lane; j <= D; j += svk::kWave)
-                        a.out_tokens[(int64_t)b * (D + 1) + j] =
-                            y < 0 ? -1 : (j < depth ? st.path_x[j] : (j == depth ? y : -1));
-                    if (nodes_out)
-                        for (int j = lane; j < D; j += svk::kWave)
-                            nodes_out[(int64_t)b * D + j] = (y >= 0 && j < depth) ? st.path_n[j] : -1;
-                    if (lane == 0) {
-                        a.accepted_len[b] = y < 0 ? -1 : depth;
-                        if (a.diag.flags) a.diag.flags[b] = flags;
-                        if (a.diag.resid_mass) a.diag.resid_mass[b] = (float)Z;
-                        if (flags) atomicOr(errword, flags);
-                        st.act = TREE_DONE;
-                    }
-                }
-            }
-        }
+        if (wid == 0) tree_consume<PES, QES>(a, t, b, st, segsum, nseg, nodes_out, errword, true);
         __syncthreads();
     }
+}
+
+// One round of the walk with S workgroups per request (blockIdx.x = S
+// (b - b0) + s), for batches that leave most CUs idle with one workgroup per
+// request.  Every workgroup of a request holds the same walk state: round 0
+// starts the walk; a later round loads the state the previous round stored,
+// reads the previous round's segment sums of all S workgroups and makes the
+// same decisions.  Then, while a pass or the draw is pending, workgroup s
+// sums its share of the segments.  State and segment sums are double
+// buffered by round parity (a round reads one buffer and writes the other),
+// workgroup 0 stores the state and writes every output.  The host launches
+// enough rounds for the topology's longest sequence of passes.
+template <int PES, int QES, int NTT>
+__global__ __launch_bounds__(NTT, 1) void k_tree_round(svh::VerifyArgs a, const svh::TreeTopo t,
+                                                    const float2 *__restrict__ part, int nch1, int nseg, int S,
+                                                    int round, int max_batch, unsigned char *__restrict__ state_g,
+                                                    float *__restrict__ seg_g, int32_t *__restrict__ nodes_out,
+                                                    uint32_t *__restrict__ errword)
+{
+    __shared__ TreeLDS st;
+    __shared__ float segsum[kTailMaxSeg];
+    constexpr int W32 = (int)(sizeof(TreeLDS) / 4);
+    static_assert(sizeof(TreeLDS) % 4 == 0 && sizeof(TreeLDS) <= svh::kTreeStateBytes, "tree state layout");
+    const int s = (int)blockIdx.x % S;
+    const int b = a.b0 + (int)blockIdx.x / S;
+    const bool writer = s == 0;
+    const int wid = threadIdx.x / svk::kWave;
+    const int rd = (round + 1) & 1, wr = round & 1;   // buffers read and written by this round
+    if (round == 0) {
+        if (wid == 0) tree_begin<PES, QES>(a, t, part, nch1, b, nodes_out, errword, st, writer);
+        __syncthreads();
+    } else {
+        const uint32_t *src = (const uint32_t *)(state_g + ((size_t)rd * max_batch + b) * svh::kTreeStateBytes);
+        for (int i = threadIdx.x; i < W32; i += NTT) ((uint32_t *)&st)[i] = src[i];
+        __syncthreads();
+        if (st.act != TREE_DONE) {   // the same in every thread
+            const float *sg = seg_g + ((size_t)rd * max_batch + b) * nseg;
+            for (int k = threadIdx.x; k < nseg; k += NTT) segsum[k] = sg[k];
+            __syncthreads();
+            if (wid == 0) tree_consume<PES, QES>(a, t, b, st, segsum, nseg, nodes_out, errword, writer);
+            __syncthreads();
+        }
+    }
+    // stored every round, final states too, so the next round reads this one
+    if (writer) {
+        uint32_t *dst = (uint32_t *)(state_g + ((size_t)wr * max_batch + b) * svh::kTreeStateBytes);
+        for (int i = threadIdx.x; i < W32; i += NTT) dst[i] = ((const uint32_t *)&st)[i];
+    }
+    if (st.act == TREE_DONE) return;
+    // this round's pass (or draw): workgroup s sums segments [k0, k1)
+    const int per = (nseg + S - 1) / S;
+    const int k0 = s * per, k1 = k0 + per < nseg ? k0 + per : nseg;
+    if (k0 >= k1) return;
+    const TreeRows r = tree_rows<PES, QES>(a, t, b, st);
+    segment_sums<PES, QES, NTT / svk::kWave>(a, r.prow, r.qrow, r.mode, r.wm, r.lp2, r.lq2, k1,
+                                             seg_g + ((size_t)wr * max_batch + b) * nseg, k0);
 }
 
 template <int PES, int QES>
@@ -1283,8 +1383,21 @@ hipError_t tree_tail(sv_ctx *ctx, const svh::VerifyArgs &a, const svh::TreeTopo 
     // about 200 VGPRs, which a 1024-thread workgroup (4 wavefronts per SIMD)
     // would spill
     const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
-    hipLaunchKernelGGL((k_tree<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a, t,
-                       (const float2 *)ctx->ws.part, ctx->nch1, ctx->nseg, nodes_out, ctx->ws.errword);
+    // workgroups per request that one workgroup per CU allows, up to 8 (two
+    // per CU measured no faster: the rounds' fixed costs dominate)
+    int S = a.nb > 0 ? ctx->num_cu / a.nb : 1;
+    S = S > 8 ? 8 : S;
+    S = S > ctx->nseg ? ctx->nseg : S;
+    if (S < 2) {
+        hipLaunchKernelGGL((k_tree<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a, t,
+                           (const float2 *)ctx->ws.part, ctx->nch1, ctx->nseg, nodes_out, ctx->ws.errword);
+    } else {
+        for (int round = 0; round < t.rounds; ++round)
+            hipLaunchKernelGGL((k_tree_round<PES, QES, NTT_NARROW>), dim3(a.nb * S), dim3(NTT_NARROW), 0, s, a, t,
+                               (const float2 *)ctx->ws.part, ctx->nch1, ctx->nseg, S, round, ctx->max_batch,
+                               (unsigned char *)ctx->ws.tree_state, ctx->ws.tree_seg, nodes_out,
+                               ctx->ws.errword);
+    }
     svh::prof_end(ctx, s, slot);
     return hipGetLastError();
 }

@@ -684,6 +684,29 @@ def test_tree_root_only_and_data_errors():
         assert flags & L.binding.SV_FLAG_BAD_TOKEN and flags & L.binding.SV_FLAG_BAD_ROW
 
 
+def test_tree_one_workgroup_walk_matches_rounds():
+    """A batch too large for several workgroups per request (B = 160 on 256
+    CUs) walks with one workgroup per request; the same requests in a small
+    batch walk in rounds with several workgroups each.  Both give the same
+    outputs bit for bit, and the large batch matches the oracle."""
+    B, V = 160, 5003
+    ti = WL.make_tree_inputs("cuda", B=B, V=V, parents=TREE_SHAPES["mixed"], noise=1.0)
+    with make_ctx(B, len(ti.parents), V) as ctx:
+        big = gpu_tree(ctx, ti)
+        sub = 40
+        small = WL.TreeInputs(sub, V, ti.T, ti.parents, ti.p[:sub].contiguous(), ti.q[:sub].contiguous(),
+                              ti.tokens[:sub].contiguous())
+        g = gpu_tree(ctx, small)
+    for k in ("accepted_len", "out_tokens", "accepted_nodes", "ratio", "lse_p", "lse_q", "flags"):
+        assert np.array_equal(big[k][:sub], g[k], equal_nan=k in ("ratio", "lse_p", "lse_q")), k
+    req = list(range(0, B, 8))
+    o = oracle_tree(ti, req)
+    rep = compare_tree({k: v[req] for k, v in big.items()}, o, ti.parents)
+    _say(f"[tree B=160 one workgroup per request] {rep}")
+    assert rep.ok(), str(rep)
+    assert rep.flips <= 1
+
+
 def test_tree_uniform_overrides_force_rejections():
     """Uniforms forced to just below 1 reject every child whose ratio is
     below 1, so the walk runs through many residual passes; forced to 0 it
