@@ -969,10 +969,20 @@ void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int
     svh::prof_end(ctx, s, slot);
 }
 
+// The fused tail puts each request's segment sums on one CU, where they are
+// VALU-bound (two exp2 per token); a batch that would leave most CUs idle
+// spreads them over workgroups per segment group instead (k_resid_sum), at
+// the price of two more launches.
+inline bool fused_tail_fits(const sv_ctx *ctx, const svh::VerifyArgs &a)
+{
+    if (!SV_FUSED_TAIL || ctx->nseg > kTailMaxSeg) return false;
+    return !(4 * (int64_t)a.nb <= ctx->num_cu && ctx->nseg >= 16);
+}
+
 template <int PES, int QES>
 hipError_t token_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
 {
-    if (SV_FUSED_TAIL && ctx->nseg <= kTailMaxSeg) {
+    if (fused_tail_fits(ctx, a)) {
         launch_fused_tail<PES, QES>(ctx, a, s, STAGE_TOKEN);
     } else {
         launch_accept<PES, QES>(ctx, a, s, STAGE_TOKEN);
@@ -993,7 +1003,7 @@ hipError_t block_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
                            (const float *)ctx->ws.lq2, (const float *)ctx->ws.wrun, ctx->ws.bm, ctx->nseg);
         svh::prof_end(ctx, s, slot);
     }
-    if (SV_FUSED_TAIL && ctx->nseg <= kTailMaxSeg) {
+    if (fused_tail_fits(ctx, a)) {
         launch_fused_tail<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
     } else {
         launch_accept<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
@@ -1008,7 +1018,7 @@ hipError_t markov_verify_tail(sv_ctx *ctx, const svh::VerifyArgs &a, const svh::
     launch_accept<PES, 4>(ctx, a, s, STAGE_TOKEN);
     hipError_t e = svh::launch_markov_recompute(ctx, m, (const ReqG *)ctx->ws.req, ctx->ws.mk_q, s);
     if (e != hipSuccess) return e;
-    if (SV_FUSED_TAIL && ctx->nseg <= kTailMaxSeg)
+    if (fused_tail_fits(ctx, a))
         launch_fused_tail<PES, 4>(ctx, a, s, STAGE_FROM_REQ);
     else
         launch_sum_and_select<PES, 4>(ctx, a, s);
