@@ -969,10 +969,10 @@ void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int
     svh::prof_end(ctx, s, slot);
 }
 
-// The fused tail puts each request's segment sums on one CU, where they are
-// VALU-bound (two exp2 per token); a batch that would leave most CUs idle
-// spreads them over workgroups per segment group instead (k_resid_sum), at
-// the price of two more launches.
+// The fused tail puts each request's segment sums on one CU, which streams
+// a 2-row pass at its share of the bandwidth; a batch that would leave most
+// CUs idle spreads them over workgroups per segment group instead
+// (k_resid_sum), at the price of two more launches.
 inline bool fused_tail_fits(const sv_ctx *ctx, const svh::VerifyArgs &a)
 {
     if (!SV_FUSED_TAIL || ctx->nseg > kTailMaxSeg) return false;
