@@ -1,0 +1,162 @@
+"""The *_run entry points allocate nothing, clear nothing with a memset and
+never synchronise, so a caller can capture them in a HIP graph: each test
+captures a call once, then for several input sets written in place runs the
+same call eagerly (fresh outputs, synchronised) and replays the graph, and
+requires every replay's outputs to equal the eager ones bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import lossless_draft_verification_02_amd as L
+from lossless_draft_verification_02_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+DEV = 0
+
+
+def _capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _outputs(B, gamma, n_ratio):
+    return dict(acc=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+                out=torch.full((B, gamma + 1), -7, dtype=torch.int32, device="cuda"),
+                lse_p=torch.full((B, gamma + 1), -7.0, device="cuda"),
+                ratio=torch.full((B, max(n_ratio, 1)), -7.0, device="cuda"),
+                resid=torch.full((B,), -7.0, device="cuda"),
+                flags=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+
+
+def _diag(o):
+    return dict(lse_p=o["lse_p"], ratio=o["ratio"], resid_mass=o["resid"], flags=o["flags"])
+
+
+def _equal(a, b, label):
+    for k in a:
+        x, y = a[k].cpu().numpy(), b[k].cpu().numpy()
+        assert np.array_equal(x, y, equal_nan=x.dtype.kind == "f"), f"{label}: {k} differs after replay"
+
+
+def test_token_verification_replays_in_a_graph():
+    B, gamma, V = 16, 5, 20011
+    src = WL.make_verify_inputs(3, "cuda", B=3 * B, gamma=gamma, V=V)
+    p = src.p[:B].clone()
+    q = src.q[:B].clone()
+    d = src.draft[:B].clone()
+    gout = _outputs(B, gamma, gamma)
+    with L.Context(DEV, B, gamma, V) as ctx:
+        def call(o):
+            L.spec_verify_run(ctx, p, q, d, o["acc"], o["out"], temperature=src.T, seed=WL.VERIFY_SEED,
+                              offset=3, diag=_diag(o))
+        g = _capture(lambda: call(gout))
+        for k in range(3):
+            p.copy_(src.p[k * B:(k + 1) * B])
+            q.copy_(src.q[k * B:(k + 1) * B])
+            d.copy_(src.draft[k * B:(k + 1) * B])
+            ref = _outputs(B, gamma, gamma)
+            call(ref)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            _equal(ref, gout, f"token verification, input set {k}")
+            assert (gout["acc"] >= 0).all()
+
+
+def test_scheduled_block_verification_replays_in_a_graph():
+    B, gamma, V = 16, 8, 20011
+    src = WL.make_verify_inputs(5, "cuda", B=3 * B, gamma=gamma, V=V)
+    p = src.p[:B].clone()
+    q = src.q[:B].clone()
+    d = src.draft[:B].clone()
+    conf = src.conf[:B].clone()
+    gout = _outputs(B, gamma, gamma)
+    gout["vlen"] = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    with L.Context(DEV, B, gamma, V) as ctx:
+        def call(o):
+            L.spec_blockverify_run(ctx, p, q, d, o["acc"], o["out"], temperature=src.T, seed=WL.VERIFY_SEED,
+                                   offset=1, conf=conf, sps_k=40.0, verify_len_out=o["vlen"], diag=_diag(o))
+        g = _capture(lambda: call(gout))
+        for k in range(3):
+            p.copy_(src.p[k * B:(k + 1) * B])
+            q.copy_(src.q[k * B:(k + 1) * B])
+            d.copy_(src.draft[k * B:(k + 1) * B])
+            conf.copy_(src.conf[k * B:(k + 1) * B])
+            ref = _outputs(B, gamma, gamma)
+            ref["vlen"] = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+            call(ref)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            _equal(ref, gout, f"block verification, input set {k}")
+            assert (gout["vlen"] >= 0).all() and (gout["vlen"] <= gamma).all()
+
+
+def test_fused_markov_draft_and_verification_replays_in_a_graph():
+    B, gamma, V = 16, 4, 5003
+    mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, uw_std=0.25)
+    base = mi.base.clone()
+    x0 = mi.x0.clone()
+    p = mi.p.clone()
+    gout = _outputs(B, gamma, gamma)
+    gout["draft"] = torch.full((B, gamma), -7, dtype=torch.int32, device="cuda")
+    gout["lse_q"] = torch.full((B, gamma), -7.0, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    with L.Context(DEV, B, gamma, V, mi.U.shape[1]) as ctx:
+        def call(o):
+            L.markov_verify_run(ctx, base, mi.U, mi.Wt, x0, p, o["draft"], o["acc"], o["out"], lse_q=o["lse_q"],
+                                temperature=mi.T, draft_seed=WL.DRAFT_SEED, verify_seed=WL.VERIFY_SEED, offset=2,
+                                diag=_diag(o))
+        g = _capture(lambda: call(gout))
+        for k in range(3):
+            if k:
+                base.copy_((base.float() + 0.5 * torch.randn(base.shape, generator=gen, device="cuda")).to(base.dtype))
+                p.copy_((p.float() + 0.5 * torch.randn(p.shape, generator=gen, device="cuda")).to(p.dtype))
+                x0.copy_(torch.randint(0, V, (B,), generator=gen, device="cuda", dtype=torch.int32))
+            ref = _outputs(B, gamma, gamma)
+            ref["draft"] = torch.full((B, gamma), -7, dtype=torch.int32, device="cuda")
+            ref["lse_q"] = torch.full((B, gamma), -7.0, device="cuda")
+            call(ref)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            _equal(ref, gout, f"fused Markov path, input set {k}")
+
+
+def test_tree_verification_rounds_replay_in_a_graph():
+    B, V = 16, 9001
+    parents = [0, 0, 0, 1, 1, 2, 4, 0]
+    src = WL.make_tree_inputs("cuda", B=3 * B, V=V, parents=parents)
+    N, D = len(parents), 3
+    p = src.p[:B].clone()
+    q = src.q[:B].clone()
+    t = src.tokens[:B].clone()
+    gout = dict(acc=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+                out=torch.full((B, D + 1), -7, dtype=torch.int32, device="cuda"),
+                nodes=torch.full((B, D), -7, dtype=torch.int32, device="cuda"))
+    with L.Context(DEV, B, N, V) as ctx:
+        def call(o):
+            L.tree_verify_run(ctx, p, q, t, parents, o["acc"], o["out"], accepted_nodes=o["nodes"],
+                              temperature=src.T, seed=WL.VERIFY_SEED, offset=5)
+        g = _capture(lambda: call(gout))
+        for k in range(3):
+            p.copy_(src.p[k * B:(k + 1) * B])
+            q.copy_(src.q[k * B:(k + 1) * B])
+            t.copy_(src.tokens[k * B:(k + 1) * B])
+            ref = {n: torch.full_like(v, -7) for n, v in gout.items()}
+            call(ref)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            _equal(ref, gout, f"tree verification, input set {k}")
+            assert (gout["acc"] >= 0).all()
