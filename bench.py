@@ -174,20 +174,6 @@ def bench_headline(args, L, WL):
     copy_us = e0.elapsed_time(e1) / 5 * 1e3
     copy_probe = {"kernel": "torch.bitwise_not over 1 GiB int32", "bytes_per_launch": 2 << 30,
                   "mean_us": round(copy_us, 2), "gbps": round((2 << 30) / (copy_us * 1e-6) / 1e9, 1)}
-    # and a plain streaming read (a library reduction over 1 GiB of fp32; the
-    # int32 reduction widens to int64 and runs far below the memory rate)
-    srcf = src.view(torch.float32)
-    torch.sum(srcf)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        torch.sum(srcf)
-    e1.record()
-    torch.cuda.synchronize()
-    read_us = e0.elapsed_time(e1) / 5 * 1e3
-    copy_probe["read_kernel"] = "torch.sum over 1 GiB float32"
-    copy_probe["read_mean_us"] = round(read_us, 2)
-    copy_probe["read_gbps"] = round((1 << 30) / (read_us * 1e-6) / 1e9, 1)
     del src, dst
     cpu = None if args.no_cpu_baseline else cpu_baseline(vi)
     ctx.close()
