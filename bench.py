@@ -137,10 +137,10 @@ def _line(metric, value, unit, args, ms, config, roofline, **extra):
 
 def bench_headline(args, L, WL):
     import torch
-    cfg = WL.CONFIGS[3]
+    cfg = WL.WORKLOADS["headline"]
     # two independent batches of the headline recipe (each above the 256 MB
     # Infinity Cache), alternated between steps
-    sets = [WL.make_verify_inputs(3, "cuda"), WL.make_verify_inputs(3, "cuda", seed=1103)]
+    sets = [WL.make_verify_inputs("headline", "cuda"), WL.make_verify_inputs("headline", "cuda", seed=1103)]
     vi = sets[0]
     B, gamma, V = vi.B, vi.gamma, vi.V
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -188,10 +188,11 @@ def bench_headline(args, L, WL):
                       "device": torch.cuda.get_device_name(0)})
 
 
-def bench_token(args, L, WL, cfg_id, nsets):
-    """Token verification of workload 1 (tiny) or 2 (batched)."""
+def bench_token(args, L, WL, name, nsets):
+    """Token verification of the tiny or the batched workload."""
     import torch
-    sets = [WL.make_verify_inputs(cfg_id, "cuda", seed=1000 + cfg_id + 100 * k) for k in range(nsets)]
+    seed0 = WL.WORKLOADS[name]["seed"]
+    sets = [WL.make_verify_inputs(name, "cuda", seed=seed0 + 100 * k) for k in range(nsets)]
     vi = sets[0]
     B, gamma, V = vi.B, vi.gamma, vi.V
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -205,8 +206,7 @@ def bench_token(args, L, WL, cfg_id, nsets):
     ms, _ = _time_steps(step, args.warmup, args.steps)
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     ctx.close()
-    name = WL.CONFIGS[cfg_id]["name"]
-    return _line(f"verified positions/s, {WL.describe(cfg_id)}", B * gamma / (ms / 1e3), "verified positions/s",
+    return _line(f"verified positions/s, {WL.describe(name)}", B * gamma / (ms / 1e3), "verified positions/s",
                  args, ms, {"workload": f"token-level verification, {name} batch", "B": B, "gamma": gamma, "V": V,
                             "logits": str(vi.p.dtype).split(".")[-1], "temperature": vi.T, "input_sets": nsets},
                  _hbm_roofline("k_rowstats", WL.bytes_single_read(vi), _mean_us(prof, "rowstats")),
@@ -215,9 +215,9 @@ def bench_token(args, L, WL, cfg_id, nsets):
 
 
 def bench_block(args, L, WL):
-    """Workload 5: scheduler + block verification, B=512, gamma=8."""
+    """The block workload: scheduler + block verification, B=512, gamma=8."""
     import torch
-    sets = [WL.make_verify_inputs(5, "cuda"), WL.make_verify_inputs(5, "cuda", seed=1105)]
+    sets = [WL.make_verify_inputs("block", "cuda"), WL.make_verify_inputs("block", "cuda", seed=1105)]
     vi = sets[0]
     B, gamma, V = vi.B, vi.gamma, vi.V
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -252,7 +252,7 @@ def bench_block(args, L, WL):
 
 
 def bench_markov(args, L, WL):
-    """Workload 4: Markov-head draft sampling (gamma positions), then verification of
+    """The markov workload: Markov-head draft sampling (gamma positions), then verification of
     that draft.  The timed step is the fused path (markov_verify_run: no fp32 draft
     logits materialised); the two-call path (markov_draft_run writing q, then
     spec_verify_run reading it) is timed alongside for comparison."""
@@ -344,7 +344,7 @@ def _tree_depths(parents):
 
 
 def bench_rnn(args, L, WL):
-    """RNN-head draft sampling on workload 4's inputs plus a recurrent matrix:
+    """RNN-head draft sampling on the markov workload's inputs plus a recurrent matrix:
     gamma positions, each the contraction with the bf16 state, the draw, and
     the next state (no logit rows stored).  Also timed: the Markov head's
     draft alone on the same inputs, the cost the recurrence adds to."""
@@ -377,7 +377,7 @@ def bench_rnn(args, L, WL):
 
 
 def bench_block_async(args, L, WL):
-    """Workload 5 with temperature-scaled confidences and the scheduler run
+    """The block workload with temperature-scaled confidences and the scheduler run
     two steps ahead: at step k a second stream (own context) schedules from
     step k's head estimates the verify lengths that step k + 2 uses, while
     the verification stream works on step k with the lengths scheduled at
@@ -385,7 +385,7 @@ def bench_block_async(args, L, WL):
     (schedule done -> verify, verify done reading a slot -> its next
     schedule)."""
     import torch
-    sets = [WL.make_verify_inputs(5, "cuda"), WL.make_verify_inputs(5, "cuda", seed=1105)]
+    sets = [WL.make_verify_inputs("block", "cuda"), WL.make_verify_inputs("block", "cuda", seed=1105)]
     vi = sets[0]
     B, gamma, V = vi.B, vi.gamma, vi.V
     temps = WL.sts_temperatures(gamma)
@@ -467,10 +467,10 @@ def main():
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "tiny", "batched", "block", "block_async", "markov", "rnn", "tree",
                              "all"],
-                    help="headline (default: the one JSON line the driver reads) or another workload")
+                    help="headline (default: one JSON line for the headline workload) or another workload")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(batch sharding across GPUs needs no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
@@ -480,8 +480,8 @@ def main():
 
     torch.cuda.set_device(0)
     runs = {"headline": lambda: bench_headline(args, L, WL),
-            "tiny": lambda: bench_token(args, L, WL, 1, 1),
-            "batched": lambda: bench_token(args, L, WL, 2, 4),
+            "tiny": lambda: bench_token(args, L, WL, "tiny", 1),
+            "batched": lambda: bench_token(args, L, WL, "batched", 4),
             "block": lambda: bench_block(args, L, WL),
             "block_async": lambda: bench_block_async(args, L, WL),
             "markov": lambda: bench_markov(args, L, WL),

@@ -50,7 +50,7 @@ def _equal(a, b, label):
 
 def test_token_verification_replays_in_a_graph():
     B, gamma, V = 16, 5, 20011
-    src = WL.make_verify_inputs(3, "cuda", B=3 * B, gamma=gamma, V=V)
+    src = WL.make_verify_inputs("headline", "cuda", B=3 * B, gamma=gamma, V=V)
     p = src.p[:B].clone()
     q = src.q[:B].clone()
     d = src.draft[:B].clone()
@@ -75,7 +75,7 @@ def test_token_verification_replays_in_a_graph():
 
 def test_scheduled_block_verification_replays_in_a_graph():
     B, gamma, V = 16, 8, 20011
-    src = WL.make_verify_inputs(5, "cuda", B=3 * B, gamma=gamma, V=V)
+    src = WL.make_verify_inputs("block", "cuda", B=3 * B, gamma=gamma, V=V)
     p = src.p[:B].clone()
     q = src.q[:B].clone()
     d = src.draft[:B].clone()

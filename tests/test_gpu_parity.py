@@ -121,9 +121,9 @@ def make_ctx(B, gamma, V, R=0):
 # ------------------------------------------------- token verification ----
 
 def test_tiny_config_many_rounds():
-    """Workload 1 (B=1, gamma=4, V=1000, fp32) over 300 rounds (offsets)."""
-    _say("case: workload 1, 300 offsets")
-    vi = WL.make_verify_inputs(1, "cuda")
+    """The tiny workload (B=1, gamma=4, V=1000, fp32) over 300 offsets."""
+    _say("case: tiny workload, 300 offsets")
+    vi = WL.make_verify_inputs("tiny", "cuda")
     tot = Report()
     with make_ctx(1, 4, 1000) as ctx:
         for off in range(300):
@@ -136,33 +136,33 @@ def test_tiny_config_many_rounds():
 
 
 def test_tiny_recipe_batched():
-    _say("case: workload 1 recipe, B=64")
-    vi = WL.make_verify_inputs(1, "cuda", B=64)
+    _say("case: tiny recipe, B=64")
+    vi = WL.make_verify_inputs("tiny", "cuda", B=64)
     with make_ctx(64, 4, 1000) as ctx:
         check_verify(ctx, vi, label="tiny B=64")
 
 
 @pytest.mark.parametrize("V", [20011, 40000])
 def test_batched_recipe_small(V):
-    """Workload 2 recipe (bf16, T=0.7, peaked targets); V odd exercises unaligned rows."""
-    _say(f"case: workload 2 recipe, B=8 V={V}")
-    vi = WL.make_verify_inputs(2, "cuda", B=8, V=V)
+    """The batched recipe (bf16, T=0.7, peaked targets); V odd exercises unaligned rows."""
+    _say(f"case: batched recipe, B=8 V={V}")
+    vi = WL.make_verify_inputs("batched", "cuda", B=8, V=V)
     with make_ctx(8, 5, V) as ctx:
         check_verify(ctx, vi, label=f"w2 V={V}")
 
 
 @pytest.mark.parametrize("V,gamma", [(40000, 7), (16385, 3), (8192, 7)])
 def test_headline_recipe_small(V, gamma):
-    _say(f"case: workload 3 recipe, B=16 gamma={gamma} V={V}")
-    vi = WL.make_verify_inputs(3, "cuda", B=16, gamma=gamma, V=V)
+    _say(f"case: headline recipe, B=16 gamma={gamma} V={V}")
+    vi = WL.make_verify_inputs("headline", "cuda", B=16, gamma=gamma, V=V)
     with make_ctx(16, gamma, V) as ctx:
         check_verify(ctx, vi, label=f"w3 V={V} g={gamma}")
 
 
 def test_headline_high_acceptance_variant():
     """Draft noise 0.35: long accepted runs, many bonus draws."""
-    _say("case: workload 3 recipe, noise 0.35")
-    vi = WL.make_verify_inputs(3, "cuda", B=32, V=30000, noise=0.35)
+    _say("case: headline recipe, noise 0.35")
+    vi = WL.make_verify_inputs("headline", "cuda", B=32, V=30000, noise=0.35)
     with make_ctx(32, 7, 30000) as ctx:
         g, _, _ = check_verify(ctx, vi, label="w3 hi-acc")
     assert (g["accepted_len"] == 7).any()
@@ -171,7 +171,7 @@ def test_headline_high_acceptance_variant():
 def test_verify_len_and_uniform_override():
     _say("case: verify_len + uniforms override")
     B, gamma, V = 24, 6, 12000
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     vl = np.array([b % (gamma + 1) for b in range(B)], np.int32)
     un = torch.rand(B, gamma + 1, generator=torch.Generator("cuda").manual_seed(5), device="cuda")
     un = (un * 2**24).floor() / 2**24
@@ -210,7 +210,7 @@ def test_special_cases():
 
 def test_fp32_and_mixed_dtypes():
     B, gamma, V = 8, 4, 5001
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     with make_ctx(B, gamma, V) as ctx:
         for pd, qd in ((torch.float32, torch.float32), (torch.bfloat16, torch.float32),
                        (torch.float32, torch.bfloat16)):
@@ -225,7 +225,7 @@ def test_fp32_and_mixed_dtypes():
 
 def test_data_errors_and_device_status():
     B, gamma, V = 6, 3, 4000
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     p, q, x = vi.p.clone(), vi.q.clone(), vi.draft.clone()
     x[1, 2] = V                      # token out of range
     p[2, 1, 77] = float("nan")       # NaN in a verified row
@@ -251,11 +251,11 @@ def test_data_errors_and_device_status():
 
 
 def test_host_argument_errors():
-    vi = WL.make_verify_inputs(3, "cuda", B=4, gamma=3, V=1000)
+    vi = WL.make_verify_inputs("headline", "cuda", B=4, gamma=3, V=1000)
     with make_ctx(4, 3, 1000) as ctx:
         acc = torch.empty(8, dtype=torch.int32, device="cuda")
         out = torch.empty(8, 4, dtype=torch.int32, device="cuda")
-        big = WL.make_verify_inputs(3, "cuda", B=8, gamma=3, V=1000)
+        big = WL.make_verify_inputs("headline", "cuda", B=8, gamma=3, V=1000)
         with pytest.raises(L.SpecVerifyError) as e:
             L.spec_verify_run(ctx, big.p, big.q, big.draft, acc, out)
         assert e.value.status == L.binding.SV_ERR_INVALID and "max_batch" in str(e.value)
@@ -271,7 +271,7 @@ def test_host_argument_errors():
 
 
 def test_determinism_run_to_run():
-    vi = WL.make_verify_inputs(3, "cuda", B=32, V=50000)
+    vi = WL.make_verify_inputs("headline", "cuda", B=32, V=50000)
     with make_ctx(32, 7, 50000) as ctx:
         a = gpu_verify(ctx, vi)
         b = gpu_verify(ctx, vi)
@@ -347,8 +347,8 @@ def test_scheduler_clamps_invalid_confidences():
     assert np.array_equal(vl, ovl) and abs(ex - oex) <= 1e-9 * oex
 
 
-def test_scheduler_workload5_full():
-    vi = WL.make_verify_inputs(5, "cuda", B=512, gamma=8, V=1000)
+def test_scheduler_block_workload_full():
+    vi = WL.make_verify_inputs("block", "cuda", B=512, gamma=8, V=1000)
     with make_ctx(512, 8, 1000) as ctx:
         vl, ex = gpu_schedule(ctx, vi.conf)
     ovl, oex, _ = _oracle_schedule(vi.conf)
@@ -413,10 +413,10 @@ def test_sts_scheduler_special_logits_and_bad_temperatures():
     assert vl[2] == gamma and vl[3] == 0
 
 
-def test_sts_scheduler_workload5_head_logits():
-    """Workload 5's confidences behind an over-confident head (log-odds times
+def test_sts_scheduler_block_workload_head_logits():
+    """The block workload's confidences behind an over-confident head (log-odds times
     T_i) come back, after scaling, to the plain scheduler's allocation."""
-    vi = WL.make_verify_inputs(5, "cuda", B=512, gamma=8, V=1000)
+    vi = WL.make_verify_inputs("block", "cuda", B=512, gamma=8, V=1000)
     temps = WL.sts_temperatures(8)
     logits = WL.sts_head_logits(vi.conf, temps)
     with make_ctx(512, 8, 1000) as ctx:
@@ -435,7 +435,7 @@ def test_two_step_ahead_schedule_on_a_second_stream():
     handovers.  Every step's outputs equal a one-stream run that verifies step
     k with the allocation of step k - 2's estimates."""
     B, gamma, V, steps = 48, 6, 7001, 7
-    sets = [WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V, seed=300 + k) for k in range(steps)]
+    sets = [WL.make_verify_inputs("block", "cuda", B=B, gamma=gamma, V=V, seed=300 + k) for k in range(steps)]
     temps = WL.sts_temperatures(gamma)
     g = torch.Generator("cuda").manual_seed(77)
     logits = [(1.0 + 2.0 * torch.randn(B, gamma, generator=g, device="cuda")).contiguous()
@@ -491,10 +491,10 @@ def test_two_step_ahead_schedule_on_a_second_stream():
 
 @pytest.mark.parametrize("V", [30000, 9001])
 def test_block_recipe_small(V):
-    _say(f"case: block verify, workload 5 recipe, B=16 V={V}")
+    _say(f"case: block verify, block recipe, B=16 V={V}")
     B, gamma = 16, 8
-    vi = WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V)
-    vi_hi = WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V, noise=0.35)
+    vi = WL.make_verify_inputs("block", "cuda", B=B, gamma=gamma, V=V)
+    vi_hi = WL.make_verify_inputs("block", "cuda", B=B, gamma=gamma, V=V, noise=0.35)
     with make_ctx(B, gamma, V) as ctx:
         check_verify(ctx, vi, block=True, label=f"block V={V}")
         check_verify(ctx, vi_hi, block=True, label=f"block hi-acc V={V}")
@@ -514,11 +514,11 @@ def test_block_early_decision_without_threshold_diagnostics():
     """Without h diagnostics, requests whose longest prefix passes skip the
     residual masses; every decision must stay the oracle's."""
     B, gamma, V = 64, 8, 20000
-    vi = WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("block", "cuda", B=B, gamma=gamma, V=V)
     vl = np.array([(5 * b + 3) % (gamma + 1) for b in range(B)], np.int32)
     with make_ctx(B, gamma, V) as ctx:
         for noise, label in ((None, "recipe"), (0.35, "hi-acc")):
-            v2 = vi if noise is None else WL.make_verify_inputs(5, "cuda", B=B, gamma=gamma, V=V, noise=noise)
+            v2 = vi if noise is None else WL.make_verify_inputs("block", "cuda", B=B, gamma=gamma, V=V, noise=noise)
             _say(f"case: block early decision, {label}")
             full = check_verify(ctx, v2, block=True, verify_len=vl, label=f"block full {label}")[0]
             early = check_verify(ctx, v2, block=True, verify_len=vl, label=f"block early {label}",
@@ -529,7 +529,7 @@ def test_block_early_decision_without_threshold_diagnostics():
 
 def test_block_with_one_position_equals_token_on_gpu():
     B, gamma, V = 32, 6, 20000
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     vl = torch.ones(B, dtype=torch.int32, device="cuda")
     with make_ctx(B, gamma, V) as ctx:
         a = gpu_verify(ctx, vi, verify_len=vl)
@@ -649,7 +649,7 @@ def test_tree_chain_is_token_verification_on_gpu():
     """A chain-shaped tree through tree_verify_run gives spec_verify_run's
     outputs bit for bit (same rows, same uniforms)."""
     B, gamma, V = 32, 6, 20000
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     ti = WL.TreeInputs(B, V, vi.T, list(range(gamma)), vi.p, vi.q, vi.draft)
     with make_ctx(B, gamma, V) as ctx:
         for off in range(4):
@@ -730,7 +730,7 @@ def test_tree_largest_trees(shape):
     N = 64
     with make_ctx(B, N, V) as ctx:
         if shape == "chain":
-            vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=N, V=V, noise=0.3)
+            vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=N, V=V, noise=0.3)
             ti = WL.TreeInputs(B, V, vi.T, list(range(N)), vi.p, vi.q, vi.draft)
             for off in range(3):
                 t = gpu_verify(ctx, vi, offset=off)
@@ -826,10 +826,10 @@ def test_rnn_zero_recurrence_is_markov_on_tanh_embeddings():
     assert torch.equal(d, dm) and torch.equal(ql, qm) and torch.equal(lse, lm)
 
 
-def test_rnn_workload4_sampled():
-    """Workload 4 at full size (B=128, gamma=8, V=129,280, R=256) with the
+def test_rnn_markov_workload_sampled():
+    """The markov workload at full size (B=128, gamma=8, V=129,280, R=256) with the
     recurrent matrix of the RNN variant; the oracle on sampled requests."""
-    _say("case: RNN head, workload 4 full size")
+    _say("case: RNN head, markov workload at full size")
     mi = WL.make_markov_inputs("cuda")
     A = WL.make_rnn_recurrence(mi.R, "cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
@@ -858,7 +858,7 @@ def test_more_requests_than_compute_units():
     CU instead of one 1024-thread workgroup."""
     B, gamma, V = 300, 3, 4000
     _say(f"case: B={B} > CUs, token and block")
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     vl = np.array([(7 * b) % (gamma + 1) for b in range(B)], np.int32)
     with make_ctx(B, gamma, V) as ctx:
         check_verify(ctx, vi, label="B=300 token")
@@ -869,7 +869,7 @@ def test_one_draft_position():
     """gamma = 1 everywhere: token, block (L in {0, 1}) and the fused Markov path."""
     B, gamma, V = 24, 1, 7001
     _say("case: gamma = 1")
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     vl = np.array([b % 2 for b in range(B)], np.int32)
     with make_ctx(B, gamma, V) as ctx:
         check_verify(ctx, vi, label="gamma=1 token")
@@ -884,7 +884,7 @@ def test_compacted_row_statistics_beyond_lds_layout():
     (8192): the per-item kernel with in-kernel length checks runs instead."""
     B, gamma, V = 8300, 1, 256
     _say(f"case: B={B} with verify lengths")
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V, row_block=4096)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V, row_block=4096)
     vl = np.array([(b * 5) % (gamma + 1) for b in range(B)], np.int32)
     with make_ctx(B, gamma, V) as ctx:
         check_verify(ctx, vi, req=_sample(B, 300, 21), verify_len=vl, label="B=8300 verify_len")
@@ -946,8 +946,8 @@ def test_markov_verify_fused_small(B, gamma, V, R, std, p32):
         check_markov_verify(ctx, mi, list(range(B)), f"fused B={B} V={V} R={R}")
 
 
-def test_markov_verify_fused_workload4_sampled():
-    _say("case: workload 4 full size, fused Markov -> verify")
+def test_markov_verify_fused_full_size_sampled():
+    _say("case: markov workload at full size, fused Markov -> verify")
     mi = WL.make_markov_inputs("cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
         check_markov_verify(ctx, mi, _sample(mi.B, 3, 14), "fused w4")
@@ -960,24 +960,24 @@ def _sample(B, n, seed):
     return sorted(set([0, B - 1] + rng.choice(B, size=min(n, B), replace=False).tolist()))
 
 
-def test_full_workload3_headline_sampled():
+def test_full_headline_sampled():
     """B=256, gamma=7, V=129280 bf16, the benchmark's launch configuration."""
-    _say("case: workload 3 full size")
-    vi = WL.make_verify_inputs(3, "cuda")
+    _say("case: headline workload at full size")
+    vi = WL.make_verify_inputs("headline", "cuda")
     with make_ctx(vi.B, vi.gamma, vi.V) as ctx:
         check_verify(ctx, vi, req=_sample(vi.B, 14, 3), label="w3 full")
 
 
-def test_full_workload2_sampled():
-    _say("case: workload 2 full size")
-    vi = WL.make_verify_inputs(2, "cuda")
+def test_full_batched_sampled():
+    _say("case: batched workload at full size")
+    vi = WL.make_verify_inputs("batched", "cuda")
     with make_ctx(vi.B, vi.gamma, vi.V) as ctx:
         check_verify(ctx, vi, req=_sample(vi.B, 10, 2), label="w2 full")
 
 
-def test_full_workload5_block_scheduled_sampled():
-    _say("case: workload 5 full size (scheduler + block verification)")
-    vi = WL.make_verify_inputs(5, "cuda")
+def test_full_block_scheduled_sampled():
+    _say("case: block workload at full size (scheduler + block verification)")
+    vi = WL.make_verify_inputs("block", "cuda")
     with make_ctx(vi.B, vi.gamma, vi.V) as ctx:
         res = gpu_verify(ctx, vi, block=True, conf=vi.conf)
     ovl, _, _ = _oracle_schedule(vi.conf)
@@ -989,8 +989,8 @@ def test_full_workload5_block_scheduled_sampled():
     assert rep.ok(), str(rep)
 
 
-def test_full_workload4_markov_then_verify_sampled():
-    _say("case: workload 4 full size (Markov sampler, then verification)")
+def test_full_markov_then_verify_sampled():
+    _say("case: markov workload at full size (Markov sampler, then verification)")
     mi = WL.make_markov_inputs("cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
         d, ql, lse = gpu_markov(ctx, mi)
@@ -1018,8 +1018,8 @@ def test_huge_vocabulary_split_tail():
     the accept / segment-sum / select kernels run instead."""
     B, gamma, V = 2, 2, 4096 * 2048 + 5003
     _say(f"case: huge vocabulary V={V} (split tail)")
-    vi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V, row_block=3)
-    vi_hi = WL.make_verify_inputs(3, "cuda", B=B, gamma=gamma, V=V, row_block=3, noise=0.05)
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V, row_block=3)
+    vi_hi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V, row_block=3, noise=0.05)
     with make_ctx(B, gamma, V) as ctx:
         for v in (vi, vi_hi):
             for off in range(3):
