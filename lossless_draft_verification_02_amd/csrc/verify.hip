@@ -62,35 +62,49 @@ __device__ __forceinline__ const char *correction_qrow(const svh::VerifyArgs &a,
 using svh::ReqG;
 
 // log2 sum exp2 of a row from its chunk partials (fp64 result); flags a bad row.
-// M = max m_k, S = sum s_k exp2(m_k - M), the partials loaded kMergeBatch at a
-// time (one memory round trip per batch and pass; one batch when the whole
-// row fits, the common case).
+// M = max m_k, S = sum s_k exp2(m_k - M) in chunk order.  A row of up to
+// kMergeHeld chunks is loaded at once (one memory round trip); longer rows
+// load kMergeBatch partials at a time (one round trip per batch and pass).
 constexpr int kMergeBatch = 8;
+constexpr int kMergeHeld = 16;
 __device__ double merge_row(const float2 *__restrict__ part, int64_t row, int nch1, bool &bad)
 {
     const float2 *pr = part + row * nch1;
     float M = svk::neg_inf();
     float S = 0.0f;
-    float2 v[kMergeBatch];
-    for (int k0 = 0; k0 < nch1; k0 += kMergeBatch) {
+    if (nch1 <= kMergeHeld) {
+        float2 v[kMergeHeld];
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) v[j] = k0 + j < nch1 ? pr[k0 + j] : make_float2(svk::neg_inf(), 0.0f);
+        for (int j = 0; j < kMergeHeld; ++j) v[j] = j < nch1 ? pr[j] : make_float2(svk::neg_inf(), 0.0f);
 #pragma unroll
-        for (int j = 0; j < kMergeBatch; ++j) M = fmaxf(M, v[j].x);
-    }
-    for (int k0 = 0; k0 < nch1; k0 += kMergeBatch) {
-        if (k0 > 0 || nch1 > kMergeBatch) {   // the single-batch case still holds its values
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j)
-                v[j] = k0 + j < nch1 ? pr[k0 + j] : make_float2(svk::neg_inf(), 0.0f);
-        }
+        for (int j = 0; j < kMergeHeld; ++j) M = fmaxf(M, v[j].x);
         if (M == svk::neg_inf()) {
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) S += v[j].y;   // 0, or NaN for a NaN element
+            for (int j = 0; j < kMergeHeld; ++j) S += v[j].y;   // 0, or NaN for a NaN element
         } else {
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j)
-                if (k0 + j < nch1) S += v[j].y * exp2f(v[j].x - M);
+            for (int j = 0; j < kMergeHeld; ++j)
+                if (j < nch1) S += v[j].y * exp2f(v[j].x - M);
+        }
+    } else {
+        float2 v[kMergeBatch];
+        for (int k0 = 0; k0 < nch1; k0 += kMergeBatch) {
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) v[j] = k0 + j < nch1 ? pr[k0 + j] : make_float2(svk::neg_inf(), 0.0f);
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) M = fmaxf(M, v[j].x);
+        }
+        for (int k0 = 0; k0 < nch1; k0 += kMergeBatch) {
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) v[j] = k0 + j < nch1 ? pr[k0 + j] : make_float2(svk::neg_inf(), 0.0f);
+            if (M == svk::neg_inf()) {
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) S += v[j].y;
+            } else {
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j)
+                    if (k0 + j < nch1) S += v[j].y * exp2f(v[j].x - M);
+            }
         }
     }
     if (!(S > 0.0f) || M == svk::pos_inf() || S == svk::pos_inf()) bad = true;

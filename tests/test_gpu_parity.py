@@ -181,17 +181,19 @@ def test_verify_len_and_uniform_override():
         check_verify(ctx, vi, verify_len=vl, uniforms=un, label="both")
 
 
-def test_special_cases():
-    B, gamma, V = 16, 5, 3000
+@pytest.mark.parametrize("V", [3000, 33000])
+def test_special_cases(V):
+    """V = 33000 (17 segments, 16 requests) takes the split tail."""
+    B, gamma = 16, 5
     g = torch.Generator("cuda").manual_seed(11)
     p = (torch.randn(B, gamma + 1, V, generator=g, device="cuda") * 2).to(torch.bfloat16)
     x = torch.randint(0, V, (B, gamma), generator=g, device="cuda", dtype=torch.int32)
     with make_ctx(B, gamma, V) as ctx:
-        _say("case: p == q")
+        _say(f"case: p == q V={V}")
         vi = WL.VerifyInputs(0, B, gamma, V, 1.0, p, p[:, :gamma].contiguous(), x)
         res, _, _ = check_verify(ctx, vi, label="p==q")
         assert (res["accepted_len"] == gamma).all()
-        _say("case: disjoint supports")
+        _say(f"case: disjoint supports V={V}")
         pd = torch.full((B, gamma + 1, V), float("-inf"), device="cuda")
         qd = torch.full((B, gamma, V), float("-inf"), device="cuda")
         pd[:, :, : V // 2] = torch.randn(B, gamma + 1, V // 2, generator=g, device="cuda")
@@ -202,7 +204,7 @@ def test_special_cases():
         assert (res["accepted_len"] == 0).all() and (res["out_tokens"][:, 0] < V // 2).all()
         for blk in (False, True):
             check_verify(ctx, vi, block=blk, label=f"disjoint block={blk}")
-    _say("case: gamma = 0 (bonus draw only)")
+    _say(f"case: gamma = 0 (bonus draw only) V={V}")
     with make_ctx(B, 0, V) as ctx:
         vi = WL.VerifyInputs(0, B, 0, V, 1.0, p[:, :1].contiguous(), p[:, :0].contiguous(), x[:, :0].contiguous())
         check_verify(ctx, vi, label="gamma=0")
@@ -223,8 +225,10 @@ def test_fp32_and_mixed_dtypes():
             check_verify(ctx, v2, verify_len=vl, block=True, label=f"{pd}/{qd} verify_len block")
 
 
-def test_data_errors_and_device_status():
-    B, gamma, V = 6, 3, 4000
+@pytest.mark.parametrize("V", [4000, 40000])
+def test_data_errors_and_device_status(V):
+    """V = 40000 (20 segments, 6 requests) takes the split tail."""
+    B, gamma = 6, 3
     vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
     p, q, x = vi.p.clone(), vi.q.clone(), vi.draft.clone()
     x[1, 2] = V                      # token out of range
@@ -235,7 +239,7 @@ def test_data_errors_and_device_status():
     with make_ctx(B, gamma, V) as ctx:
         assert L.spec_verify_device_status(ctx) == 0
         for blk in (False, True):
-            _say(f"case: data errors block={blk}")
+            _say(f"case: data errors block={blk} V={V}")
             res, o, _ = check_verify(ctx, bad, block=blk, label=f"errors block={blk}")
             assert res["accepted_len"].tolist()[1:5] == [-1, -1, -1, -1]
             assert res["accepted_len"][0] >= 0 and res["accepted_len"][5] >= 0
