@@ -822,11 +822,33 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
                          (mode || (((uintptr_t)(qrow + s0 * QES)) & 15) == 0);
     float w[TPL];
     if (aligned && t0 + TPL <= s1) {
+        // every vector of the lane's 32 tokens is requested before any is
+        // used: one memory round trip
+        constexpr int U = TPL / 8;
+        u32x4 rp[U][PES / 2], rq[U][QES / 2];
 #pragma unroll
-        for (int g = 0; g < TPL / 8; ++g) {
+        for (int g = 0; g < U; ++g) {
+            const u32x4 *vp = (const u32x4 *)(prow + (t0 + 8 * g) * PES);
+#pragma unroll
+            for (int h = 0; h < PES / 2; ++h) rp[g][h] = __builtin_nontemporal_load(vp + h);
+        }
+        if (!mode) {
+#pragma unroll
+            for (int g = 0; g < U; ++g) {
+                const u32x4 *vq = (const u32x4 *)(qrow + (t0 + 8 * g) * QES);
+#pragma unroll
+                for (int h = 0; h < QES / 2; ++h) rq[g][h] = __builtin_nontemporal_load(vq + h);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < U; ++g) {
             float xp[8], xq[8];
-            load8<PES>(prow, t0 + 8 * g, xp);
-            if (!mode) load8<QES>(qrow, t0 + 8 * g, xq);
+#pragma unroll
+            for (int h = 0; h < PES / 2; ++h) svk::widen<PES>(rp[g][h], xp + h * (16 / PES));
+            if (!mode) {
+#pragma unroll
+                for (int h = 0; h < QES / 2; ++h) svk::widen<QES>(rq[g][h], xq + h * (16 / QES));
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) w[8 * g + j] = weight(xp[j], mode ? 0.0f : xq[j], mode, wmul, lp2, lq2, a.c);
         }
