@@ -797,7 +797,17 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
 #pragma unroll
             for (int s = 0; s < KS; ++s) afr[v][s] = *(const bf16x8 *)(wrow + 32 * s);
         }
+        // base logits of the lane's outputs, requested with the A rows (an
+        // in-row address for every column; -inf replaces those past V)
         const uint16_t *brow = a.base + ((int64_t)b * a.gamma + (k - 1)) * a.V + c0;
+        uint32_t bbits[VBW][4];
+#pragma unroll
+        for (int v = 0; v < VBW; ++v)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int col = 16 * (VBW * wid + v) + 4 * lg + r;
+                bbits[v][r] = brow[col < ncols ? col : 0];
+            }
 #pragma unroll
         for (int v = 0; v < VBW; ++v) {
             const int vb = VBW * wid + v;
@@ -809,7 +819,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int col = 16 * vb + 4 * lg + r;
-                    const uint32_t bits = col < ncols ? (uint32_t)brow[col] : 0xFF80u;
+                    const uint32_t bits = col < ncols ? bbits[v][r] : 0xFF80u;
                     zt[col] = acc[r] + __uint_as_float(bits << 16);
                 }
             }
