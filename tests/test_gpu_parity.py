@@ -190,7 +190,7 @@ def test_special_cases(V):
     x = torch.randint(0, V, (B, gamma), generator=g, device="cuda", dtype=torch.int32)
     with make_ctx(B, gamma, V) as ctx:
         _say(f"case: p == q V={V}")
-        vi = WL.VerifyInputs(0, B, gamma, V, 1.0, p, p[:, :gamma].contiguous(), x)
+        vi = WL.VerifyInputs("p equals q", B, gamma, V, 1.0, p, p[:, :gamma].contiguous(), x)
         res, _, _ = check_verify(ctx, vi, label="p==q")
         assert (res["accepted_len"] == gamma).all()
         _say(f"case: disjoint supports V={V}")
@@ -199,14 +199,14 @@ def test_special_cases(V):
         pd[:, :, : V // 2] = torch.randn(B, gamma + 1, V // 2, generator=g, device="cuda")
         qd[:, :, V // 2:] = torch.randn(B, gamma, V - V // 2, generator=g, device="cuda")
         xd = torch.randint(V // 2, V, (B, gamma), generator=g, device="cuda", dtype=torch.int32)
-        vi = WL.VerifyInputs(0, B, gamma, V, 1.0, pd.to(torch.bfloat16), qd.to(torch.bfloat16), xd)
+        vi = WL.VerifyInputs("disjoint supports", B, gamma, V, 1.0, pd.to(torch.bfloat16), qd.to(torch.bfloat16), xd)
         res, _, _ = check_verify(ctx, vi, label="disjoint")
         assert (res["accepted_len"] == 0).all() and (res["out_tokens"][:, 0] < V // 2).all()
         for blk in (False, True):
             check_verify(ctx, vi, block=blk, label=f"disjoint block={blk}")
     _say(f"case: gamma = 0 (bonus draw only) V={V}")
     with make_ctx(B, 0, V) as ctx:
-        vi = WL.VerifyInputs(0, B, 0, V, 1.0, p[:, :1].contiguous(), p[:, :0].contiguous(), x[:, :0].contiguous())
+        vi = WL.VerifyInputs("bonus only", B, 0, V, 1.0, p[:, :1].contiguous(), p[:, :0].contiguous(), x[:, :0].contiguous())
         check_verify(ctx, vi, label="gamma=0")
 
 
@@ -217,7 +217,7 @@ def test_fp32_and_mixed_dtypes():
         for pd, qd in ((torch.float32, torch.float32), (torch.bfloat16, torch.float32),
                        (torch.float32, torch.bfloat16)):
             _say(f"case: dtypes p={pd} q={qd}")
-            v2 = WL.VerifyInputs(3, B, gamma, V, 1.0, vi.p.to(pd), vi.q.to(qd), vi.draft)
+            v2 = WL.VerifyInputs(vi.workload, B, gamma, V, 1.0, vi.p.to(pd), vi.q.to(qd), vi.draft)
             check_verify(ctx, v2, label=f"{pd}/{qd}")
             # per-request lengths take the compacted row-statistics path
             vl = np.array([(3 * b + 1) % (gamma + 1) for b in range(B)], np.int32)
@@ -235,7 +235,7 @@ def test_data_errors_and_device_status(V):
     p[2, 1, 77] = float("nan")       # NaN in a verified row
     q[3, 0, :] = float("-inf")       # all -inf row
     p[4, 2, 5] = float("inf")        # +inf
-    bad = WL.VerifyInputs(3, B, gamma, V, 1.0, p, q, x)
+    bad = WL.VerifyInputs("data errors", B, gamma, V, 1.0, p, q, x)
     with make_ctx(B, gamma, V) as ctx:
         assert L.spec_verify_device_status(ctx) == 0
         for blk in (False, True):
@@ -272,6 +272,29 @@ def test_host_argument_errors():
                                torch.zeros(1000, 256, dtype=torch.bfloat16, device="cuda"),
                                torch.zeros(4, dtype=torch.int32, device="cuda"),
                                torch.empty(4, 3, dtype=torch.int32, device="cuda"))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_configurations(case):
+    """Seeded random shapes, dtypes, temperatures and recipes: B in [1, 40],
+    gamma in [0, 12], V from 3 to 70,000 (either side of one 2048-token
+    segment and of the split-tail threshold); token and block verification,
+    the latter also with random verify lengths."""
+    rng = np.random.default_rng(9100 + case)
+    B = int(rng.integers(1, 41))
+    gamma = int(rng.integers(0, 13))
+    V = int(rng.integers(3, 2049)) if case % 3 == 0 else int(rng.integers(2049, 70001))
+    recipe = "batched" if case % 2 else "headline"
+    T = float(rng.choice([0.5, 0.7, 1.0, 1.6]))
+    pd, qd = [torch.float32 if f else torch.bfloat16 for f in rng.integers(0, 2, size=2)]
+    _say(f"case: random {case}: B={B} gamma={gamma} V={V} {recipe} T={T} p={pd} q={qd}")
+    src = WL.make_verify_inputs(recipe, "cuda", B=B, gamma=gamma, V=V, seed=7000 + case)
+    vi = WL.VerifyInputs(recipe, B, gamma, V, T, src.p.to(pd), src.q.to(qd), src.draft)
+    with make_ctx(B, gamma, V) as ctx:
+        check_verify(ctx, vi, offset=case, label=f"random {case} token")
+        check_verify(ctx, vi, block=True, offset=case, label=f"random {case} block")
+        vl = rng.integers(0, gamma + 1, size=B).astype(np.int32)
+        check_verify(ctx, vi, block=True, verify_len=vl, offset=case, label=f"random {case} block verify_len")
 
 
 def test_determinism_run_to_run():
@@ -998,7 +1021,7 @@ def test_full_markov_then_verify_sampled():
     mi = WL.make_markov_inputs("cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
         d, ql, lse = gpu_markov(ctx, mi)
-        vi = WL.VerifyInputs(4, mi.B, mi.gamma, mi.V, mi.T, mi.p, ql, d)
+        vi = WL.VerifyInputs("markov then verify", mi.B, mi.gamma, mi.V, mi.T, mi.p, ql, d)
         res = gpu_verify(ctx, vi)
     req = _sample(mi.B, 3, 4)
     o = oracle_markov(mi, req)
