@@ -672,6 +672,32 @@ def test_tree_small(shape, V, dtype, noise):
             check_tree(ctx, ti, list(range(B)), f"tree {shape} off={off}", offset=off)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_tree_random_topologies(case):
+    """Seeded random trees: N from 1 to 40 nodes, each node's parent drawn
+    among the earlier nodes (deep, wide or mixed), B from 1 to 40, V from 100
+    to 50,000, bf16 or fp32, low to high acceptance."""
+    rng = np.random.default_rng(9300 + case)
+    N = int(rng.integers(1, 41))
+    style = case % 3   # 0: any earlier node, 1: one of the last two (deep), 2: the root or its children (wide)
+    parents = []
+    for i in range(N):
+        if style == 0 or i == 0:
+            parents.append(int(rng.integers(0, i + 1)))
+        elif style == 1:
+            parents.append(int(rng.integers(max(0, i - 1), i + 1)))
+        else:
+            parents.append(int(rng.integers(0, min(i, 3) + 1)))
+    B = int(rng.integers(1, 41))
+    V = int(rng.integers(100, 50001))
+    dtype = torch.float32 if rng.integers(0, 2) else torch.bfloat16
+    noise = float(rng.choice([0.35, 1.0, 2.0]))
+    _say(f"case: random tree {case}: N={N} parents={parents} B={B} V={V} {dtype} noise={noise}")
+    ti = WL.make_tree_inputs("cuda", B=B, V=V, parents=parents, dtype=dtype, noise=noise, seed=7300 + case)
+    with make_ctx(B, N, V) as ctx:
+        check_tree(ctx, ti, list(range(B)), f"random tree {case}", offset=case)
+
+
 def test_tree_chain_is_token_verification_on_gpu():
     """A chain-shaped tree through tree_verify_run gives spec_verify_run's
     outputs bit for bit (same rows, same uniforms)."""
