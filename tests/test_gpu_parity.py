@@ -989,14 +989,49 @@ def check_markov_verify(ctx, mi, req, label):
 
 @pytest.mark.parametrize("B,gamma,V,R,std,p32", [(16, 8, 20000, 256, 0.25, False), (130, 3, 4999, 256, 0.25, False),
                                                  (24, 5, 9001, 64, 0.25, False), (8, 4, 5000, 256, 0.02, False),
-                                                 (12, 6, 6007, 128, 0.25, True)])
+                                                 (12, 6, 6007, 128, 0.25, True), (16, 4, 40000, 128, 0.25, False)])
 def test_markov_verify_fused_small(B, gamma, V, R, std, p32):
+    """The last case (16 requests, 20 segments) takes the split tail."""
     _say(f"case: fused Markov -> verify B={B} gamma={gamma} V={V} R={R} std={std} p fp32={p32}")
     mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=std)
     if p32:
         mi.p = mi.p.float()
     with make_ctx(B, gamma, V, R) as ctx:
         check_markov_verify(ctx, mi, list(range(B)), f"fused B={B} V={V} R={R}")
+
+
+def _random_markov_case(case, base_seed):
+    rng = np.random.default_rng(base_seed + case)
+    return dict(B=int(rng.integers(1, 141)), gamma=int(rng.integers(1, 9)), V=int(rng.integers(200, 45001)),
+                R=int(rng.choice([32, 64, 128, 256])), std=float(rng.choice([0.02, 0.25, 0.5])),
+                astd=float(rng.choice([0.1, 0.3, 0.5])))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_markov_verify_fused_random(case):
+    """Seeded random B (1-140), gamma (1-8), V (200-45,000), rank (32-256) and
+    transition scale through the fused draft -> verification path (case 5
+    takes the split tail)."""
+    c = _random_markov_case(case, 9500)
+    _say(f"case: random fused Markov -> verify {case}: {c}")
+    mi = WL.make_markov_inputs("cuda", B=c["B"], gamma=c["gamma"], V=c["V"], R=c["R"], uw_std=c["std"])
+    with make_ctx(c["B"], c["gamma"], c["V"], c["R"]) as ctx:
+        check_markov_verify(ctx, mi, list(range(min(c["B"], 16))), f"random fused {case}")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_rnn_random(case):
+    """Seeded random shapes and recurrence scales through the RNN head, with
+    and without stored logit rows."""
+    c = _random_markov_case(case, 9700)
+    _say(f"case: random RNN {case}: {c}")
+    mi = WL.make_markov_inputs("cuda", B=c["B"], gamma=c["gamma"], V=c["V"], R=c["R"], uw_std=c["std"])
+    A = WL.make_rnn_recurrence(c["R"], "cuda", std=c["astd"])
+    req = list(range(min(c["B"], 12)))
+    with make_ctx(c["B"], c["gamma"], c["V"], c["R"]) as ctx:
+        d, lse, st = check_rnn(ctx, mi, A, req, f"random rnn {case}")
+        d2, lse2, st2 = check_rnn(ctx, mi, A, req, f"random rnn {case} no q", want_q=False)
+    assert torch.equal(d, d2) and torch.equal(lse, lse2) and torch.equal(st, st2)
 
 
 def test_markov_verify_fused_full_size_sampled():
