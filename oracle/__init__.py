@@ -89,7 +89,7 @@ def _load():
 class _Diag(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("lse_p", "lse_q", "ratio", "w", "h", "dec_margin", "resid_mass",
-                 "icdf_margin", "uniform")]
+                 "icdf_margin", "uniform", "m")]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -151,6 +151,7 @@ class VerifyResult:
     resid_mass: np.ndarray        # [B]
     icdf_margin: np.ndarray       # [B]
     uniform: np.ndarray           # [B, gamma+1]
+    m: np.ndarray                 # [B, gamma] block residual masses m_i, i < L (NaN elsewhere)
 
 
 def _verify(fn_name, p, q, draft, gamma, temperature=1.0, seed=1, offset=0,
@@ -173,7 +174,8 @@ def _verify(fn_name, p, q, draft, gamma, temperature=1.0, seed=1, offset=0,
     arrs = dict(lse_p=np.zeros((B, gamma + 1)), lse_q=np.zeros((B, gamma)),
                 ratio=np.zeros((B, gamma)), w=np.zeros((B, gamma)), h=np.zeros((B, gamma)),
                 dec_margin=np.zeros((B, gamma)), resid_mass=np.zeros(B),
-                icdf_margin=np.zeros(B), uniform=np.zeros((B, gamma + 1), np.float32))
+                icdf_margin=np.zeros(B), uniform=np.zeros((B, gamma + 1), np.float32),
+                m=np.full((B, gamma), np.nan))
     diag = _Diag(**{k: _ptr(v).value if v.size else None for k, v in arrs.items()})
     rc = getattr(_load(), fn_name)(_ptr(p), _ptr(q), _ptr(draft), _ptr(vl), _ptr(rid), B, gamma,
                                    V, temperature, seed, offset, _ptr(un), _ptr(acc), _ptr(out),

@@ -123,6 +123,7 @@ static void put_diag_nan(const orc_diag *d, int b, int gamma)
         if (d->ratio) d->ratio[(int64_t)b * gamma + i] = NAN;
         if (d->w) d->w[(int64_t)b * gamma + i] = NAN;
         if (d->h) d->h[(int64_t)b * gamma + i] = NAN;
+        if (d->m) d->m[(int64_t)b * gamma + i] = NAN;
         if (d->dec_margin) d->dec_margin[(int64_t)b * gamma + i] = NAN;
         if (d->lse_q) d->lse_q[(int64_t)b * gamma + i] = NAN;
     }
@@ -340,6 +341,7 @@ int orc_block_verify(const double *p, const double *q, const int32_t *draft,
             }
             double den = m + 1.0 - w[i];
             h[i] = den > 0.0 ? m / den : 1.0;
+            if (d && d->m) d->m[(int64_t)b * gamma + i - 1] = m;
         }
         if (L >= 1) h[L] = w[L];
 

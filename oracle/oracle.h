@@ -71,6 +71,8 @@ typedef struct {
     double *resid_mass;  /* [B]          mass Z of the correction/bonus weights */
     double *icdf_margin; /* [B]          min(t - C(y-1), C(y) - t) / Z          */
     float  *uniform;     /* [B, gamma+1] uniforms used (col gamma = u')         */
+    double *m;           /* [B, gamma]   block: residual mass m_i of position i < L
+                                         (NaN elsewhere)                           */
 } orc_diag;
 
 /* Philox4x32-10 block function [PH]: out = bijection(key, ctr). */

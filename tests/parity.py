@@ -39,15 +39,25 @@ class Report:
                 f"{self.failures[:5]}")
 
 
-def _close_threshold(rep, g, o, w, what, b):
-    """Block thresholds h = m / (m + 1 - w).  With D = m + 1 - w,
-    dh/dm = (1 - h)^2 / (1 - w) and dh/dw = h (1 - h) / (1 - w), so absolute
-    errors eps in m and w move h by at most eps (1 - h) / (1 - w) to first
-    order -- more than the flat probability tolerance when 1 - w is small.
-    The bound used is PROB_ATOL plus that propagated error."""
+def threshold_tol(w, m):
+    """Bound on the GPU's block thresholds h = m / D, D = m + 1 - w (oracle
+    values; m is NaN at i = L, where h_L = w_L).  dh/dm = (1 - h) / D and
+    dh/dw = h / D, so absolute errors eps in m and w move h by at most eps / D
+    to first order -- more than the flat probability tolerance when D is
+    small, and without bound at D = 0, where h is 1 by convention but the
+    GPU's rounding of w and m can put it anywhere in [0, 1]."""
+    w = np.asarray(w, np.float64)
+    m = np.asarray(m, np.float64)
+    den = m + 1.0 - w
+    with np.errstate(divide="ignore"):
+        extra = np.where(np.isnan(m), 0.0, np.where(den > 0.0, WM_ABS_EPS / np.maximum(den, 1e-300), np.inf))
+    return PROB_ATOL + WM_ABS_EPS * np.isnan(m) + extra
+
+
+def _close_threshold(rep, g, o, w, mres, what, b):
+    """Block thresholds within threshold_tol of the oracle's."""
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
-    w = np.asarray(w, np.float64)
     m = ~np.isnan(o)
     if not m.any():
         return
@@ -55,8 +65,7 @@ def _close_threshold(rep, g, o, w, what, b):
         rep.failures.append((b, what, "nan on the GPU"))
         return
     err = np.abs(g[m] - o[m])
-    # w = 1 exactly gives h = 1 whatever m is: the bound then vanishes
-    tol = PROB_ATOL + WM_ABS_EPS * np.abs(1.0 - o[m]) / np.maximum(1.0 - w[m], 1e-12)
+    tol = threshold_tol(np.asarray(w, np.float64)[m], np.asarray(mres, np.float64)[m])
     rep.max_prob_err = max(rep.max_prob_err, float(err.max()))
     if (err > tol).any():
         i = int(np.argmax(err - tol))
@@ -121,8 +130,11 @@ def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = Fa
                 if not o_acc:
                     break
         elif oa != ga:
+            # the decisions above the smaller tau: a flip where |eta_i - h_i|
+            # is within the margin or within h_i's own bound
             i = max(oa, ga)
-            if orc.dec_margin[b, i - 1] <= MARGIN:
+            htol = float(threshold_tol([orc.w[b, i - 1]], [orc.m[b, i - 1]])[0])
+            if orc.dec_margin[b, i - 1] <= max(MARGIN, htol):
                 rep.flips += 1
                 flipped = True
             else:
@@ -154,7 +166,7 @@ def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = Fa
         if block and "w" in gpu and L > 0:
             _close_prob(rep, gpu["w"][b, :L], orc.w[b, :L], "w", b)
         if block and "h" in gpu and L > 0:
-            _close_threshold(rep, gpu["h"][b, :L], orc.h[b, :L], orc.w[b, :L], "h", b)
+            _close_threshold(rep, gpu["h"][b, :L], orc.h[b, :L], orc.w[b, :L], orc.m[b, :L], "h", b)
         if "resid_mass" in gpu:
             _close_prob(rep, [gpu["resid_mass"][b]], [orc.resid_mass[b]], "resid_mass", b)
         if "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):

@@ -297,6 +297,22 @@ def test_random_configurations(case):
         check_verify(ctx, vi, block=True, verify_len=vl, offset=case, label=f"random {case} block verify_len")
 
 
+@pytest.mark.parametrize("B,gamma,V", [(3, 64, 3000), (5, 64, 40000), (4, 3, 1), (4, 3, 2), (2, 64, 1)])
+def test_edge_sizes(B, gamma, V):
+    """The largest draft (gamma = 64: the bonus position's p row is the 65th,
+    one past a wavefront's lanes), a one- and a two-token vocabulary; token
+    and block verification, and with q = p so that every token is accepted
+    and the 65th row is drawn from."""
+    _say(f"case: edge sizes B={B} gamma={gamma} V={V}")
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
+    same = WL.VerifyInputs("q equals p", B, gamma, V, vi.T, vi.p, vi.p[:, :gamma].contiguous(), vi.draft)
+    with make_ctx(B, gamma, V) as ctx:
+        for blk in (False, True):
+            check_verify(ctx, vi, block=blk, label=f"edge B={B} g={gamma} V={V} block={blk}")
+            g, _, _ = check_verify(ctx, same, block=blk, label=f"edge q=p B={B} g={gamma} V={V} block={blk}")
+            assert (g["accepted_len"] == gamma).all()
+
+
 def test_determinism_run_to_run():
     vi = WL.make_verify_inputs("headline", "cuda", B=32, V=50000)
     with make_ctx(32, 7, 50000) as ctx:
