@@ -1,5 +1,6 @@
 """The *_run entry points allocate nothing, clear nothing with a memset and
-never synchronise, so a caller can capture them in a HIP graph: each test
+never synchronise, so a caller can capture them in a HIP graph (every entry
+point that launches kernels is covered here): each test
 captures a call once, then for several input sets written in place runs the
 same call eagerly (fresh outputs, synchronised) and replays the graph, and
 requires every replay's outputs to equal the eager ones bit for bit."""
@@ -44,7 +45,10 @@ def _diag(o):
 
 def _equal(a, b, label):
     for k in a:
-        x, y = a[k].cpu().numpy(), b[k].cpu().numpy()
+        x, y = a[k], b[k]
+        if x.dtype == torch.bfloat16:   # compared bit for bit
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        x, y = x.cpu().numpy(), y.cpu().numpy()
         assert np.array_equal(x, y, equal_nan=x.dtype.kind == "f"), f"{label}: {k} differs after replay"
 
 
@@ -160,3 +164,77 @@ def test_tree_verification_rounds_replay_in_a_graph():
             torch.cuda.synchronize()
             _equal(ref, gout, f"tree verification, input set {k}")
             assert (gout["acc"] >= 0).all()
+
+
+def test_markov_and_rnn_drafts_replay_in_a_graph():
+    B, gamma, V, R = 16, 4, 5003, 64
+    mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=0.25)
+    A = WL.make_rnn_recurrence(R, "cuda", std=0.3)
+    base = mi.base.clone()
+    x0 = mi.x0.clone()
+    gen = torch.Generator(device="cuda").manual_seed(13)
+
+    def outs():
+        return dict(draft=torch.full((B, gamma), -7, dtype=torch.int32, device="cuda"),
+                    q=torch.full((B, gamma, V), -7.0, device="cuda"),
+                    lse=torch.full((B, gamma), -7.0, device="cuda"),
+                    states=torch.full((B, gamma, R), -7.0, device="cuda").to(torch.bfloat16))
+
+    with L.Context(DEV, B, gamma, V, R) as ctx:
+        def markov(o):
+            L.markov_draft_run(ctx, base, mi.U, mi.Wt, x0, o["draft"], q_logits=o["q"], lse_q=o["lse"],
+                               temperature=mi.T, seed=WL.DRAFT_SEED, offset=4)
+
+        def rnn(o):
+            L.rnn_draft_run(ctx, base, mi.U, mi.Wt, A, x0, o["draft"], lse_q=o["lse"], states=o["states"],
+                            temperature=mi.T, seed=WL.DRAFT_SEED, offset=4)
+
+        for name, fn in (("Markov draft", markov), ("RNN draft", rnn)):
+            gout = outs()
+            g = _capture(lambda: fn(gout))
+            for k in range(3):
+                if k:
+                    base.copy_((base.float() + 0.5 * torch.randn(base.shape, generator=gen, device="cuda"))
+                               .to(base.dtype))
+                    x0.copy_(torch.randint(0, V, (B,), generator=gen, device="cuda", dtype=torch.int32))
+                ref = outs()
+                fn(ref)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                _equal(ref, gout, f"{name}, input set {k}")
+                assert (gout["draft"] >= 0).all()
+
+
+def test_schedulers_replay_in_a_graph():
+    B, gamma = 64, 8
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    conf = torch.rand(B, gamma, generator=gen, device="cuda")
+    logits = torch.randn(B, gamma, generator=gen, device="cuda")
+    temps = [1.0 + 0.15 * i for i in range(gamma)]
+
+    def outs():
+        return dict(vl=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+                    ex=torch.full((1,), -7.0, dtype=torch.float64, device="cuda"))
+
+    with L.Context(DEV, B, gamma, 1000) as ctx:
+        def plain(o):
+            L.spec_schedule_run(ctx, conf, o["vl"], expected=o["ex"])
+
+        def sts(o):
+            L.spec_schedule_sts_run(ctx, logits, temps, o["vl"], expected=o["ex"])
+
+        for name, fn in (("scheduler", plain), ("temperature-scaled scheduler", sts)):
+            gout = outs()
+            g = _capture(lambda: fn(gout))
+            for k in range(3):
+                if k:
+                    conf.copy_(torch.rand(B, gamma, generator=gen, device="cuda"))
+                    logits.copy_(torch.randn(B, gamma, generator=gen, device="cuda"))
+                ref = outs()
+                fn(ref)
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                _equal(ref, gout, f"{name}, input set {k}")
+                assert (gout["vl"] >= 0).all() and (gout["vl"] <= gamma).all()
