@@ -604,155 +604,8 @@ __global__ __launch_bounds__(NT) void k_resid_sum(svh::VerifyArgs a, const ReqG 
 }
 
 // ---------------------------------------------------------------------------
-// Inverse-CDF selection, one workgroup per request.
+// Inverse-CDF selection.
 // ---------------------------------------------------------------------------
-struct SelectShared {
-    double scan[16];       // one entry per wavefront (up to 1024 threads)
-    double cbase;          // cumulative weight before the chosen segment
-    int cstar;             // chosen segment
-    int clast;             // last segment with positive weight
-    int ybest;             // chosen token (min over threads)
-    int ylast;             // last positive-weight token of the segment
-};
-
-template <int PES, int QES, int NTB = NT>
-__device__ int select_token(const svh::VerifyArgs &a, int mode, float wmul, float lp2, float lq2,
-                            const float *sums, int nseg, const char *prow, const char *qrow, float u,
-                            SelectShared &sh, double &Z_out)
-{
-    // segment sums -> fp64 prefix (each thread owns a contiguous run of segments)
-    const int per = (nseg + NTB - 1) / NTB;
-    const int k0 = threadIdx.x * per;
-    const int k1 = k0 + per < nseg ? k0 + per : nseg;
-    double loc = 0.0;
-    for (int k = k0; k < k1; ++k) loc += (double)sums[k];
-    if (threadIdx.x == 0) {
-        sh.cstar = 0x7FFFFFFF;
-        sh.clast = -1;
-        sh.ybest = 0x7FFFFFFF;
-        sh.ylast = -1;
-    }
-    double Z;
-    const double excl = svk::block_exclusive_scan_d<NTB>(loc, sh.scan, &Z);
-    Z_out = Z;
-    if (!(Z > 0.0)) return -1;
-    const float tf = __fmul_rn(u, (float)Z);
-    {
-        double run = excl;
-        for (int k = k0; k < k1; ++k) {
-            const float ck = sums[k];
-            run += (double)ck;
-            if (ck > 0.0f) {
-                atomicMax(&sh.clast, k);
-                if ((float)run > tf) {
-                    atomicMin(&sh.cstar, k);
-                    break;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    const bool fallback = sh.cstar == 0x7FFFFFFF;
-    const int cst = fallback ? sh.clast : sh.cstar;
-    if (k0 <= cst && cst < k1) {
-        double run = excl;
-        for (int k = k0; k < cst; ++k) run += (double)sums[k];
-        sh.cbase = run;
-    }
-    __syncthreads();
-
-    // inside the segment: thread t owns tokens [s0 + 8t, s0 + 8t + 8)
-    constexpr int PER = SEG / NTB;
-    static_assert(PER >= 1 && SEG % NTB == 0, "segment split over the block");
-    const int64_t s0 = (int64_t)cst * SEG;
-    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
-    const int64_t t0 = s0 + (int64_t)threadIdx.x * PER;
-    const bool aligned = (((uintptr_t)(prow + s0 * PES)) & 15) == 0 &&
-                         (mode || (((uintptr_t)(qrow + s0 * QES)) & 15) == 0);
-    float w[PER];
-    if (PER == 8 && aligned && t0 + PER <= s1) {
-        float xp[8], xq[8];
-        load8<PES>(prow, t0, xp);
-        if (!mode) load8<QES>(qrow, t0, xq);
-#pragma unroll
-        for (int k = 0; k < PER; ++k) w[k] = weight(xp[k], mode ? 0.0f : xq[k], mode, wmul, lp2, lq2, a.c);
-    } else {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int64_t e = t0 + k;
-            float wk = 0.0f;
-            if (e < s1) {
-                const float xp = svk::load_logit<PES>(prow, e);
-                const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
-                wk = weight(xp, xq, mode, wmul, lp2, lq2, a.c);
-            }
-            w[k] = wk;
-        }
-    }
-    double lsum = 0.0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) lsum += (double)w[k];
-    double dummy;
-    const double texcl = svk::block_exclusive_scan_d<NTB>(lsum, sh.scan, &dummy);
-    int last_pos = -1;
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-        if (w[k] > 0.0f) last_pos = (int)(t0 + k);
-    if (last_pos >= 0) atomicMax(&sh.ylast, last_pos);
-    if (!fallback) {
-        double C = sh.cbase + texcl;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            C += (double)w[k];
-            if (w[k] > 0.0f && (float)C > tf) {
-                atomicMin(&sh.ybest, (int)(t0 + k));
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    return sh.ybest != 0x7FFFFFFF ? sh.ybest : sh.ylast;
-}
-
-template <int PES, int QES>
-__global__ __launch_bounds__(NT) void k_select(svh::VerifyArgs a, const ReqG *__restrict__ req,
-                                               float *__restrict__ csum, const float *__restrict__ bm,
-                                               int nseg, uint32_t *__restrict__ errword)
-{
-    __shared__ SelectShared sh;
-    __shared__ int32_t xs[MAXG];
-    const int b = a.b0 + (int)blockIdx.x;
-    const ReqG r = req[b];
-    if (r.flags) return;   // k_accept wrote the request's error outputs
-    const int gamma = a.gamma;
-    const int G1 = gamma + 1;
-    if ((int)threadIdx.x < r.tau) xs[threadIdx.x] = a.draft[(int64_t)b * gamma + threadIdx.x];
-    const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
-    const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
-    float *own = csum + (int64_t)b * nseg;
-    const float *sums = sums_from_pass2(a, r) ? bm + ((int64_t)b * gamma + r.tau) * nseg : own;
-
-    uint32_t flags = 0;
-    double Z = 0.0;
-    int y = select_token<PES, QES>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, sh, Z);
-    if (y < 0 && r.mode == 0) {
-        // residual mass rounded to zero (in exact arithmetic a rejection
-        // implies p != q): draw from the p row instead
-        flags |= SV_FLAG_RESID_ZERO;
-        const int wid = threadIdx.x / svk::kWave;
-        for (int k = wid; k < nseg; k += SPW) {
-            const int64_t s0 = (int64_t)k * SEG;
-            const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
-            const float tot = segment_weight_sum<PES, QES>(prow, nullptr, s0, s1, 1, 1.0f, r.lp2, 0.0f, a.c);
-            if ((threadIdx.x & (svk::kWave - 1)) == 0) own[k] = tot;
-        }
-        __syncthreads();
-        y = select_token<PES, QES>(a, 1, 1.0f, r.lp2, 0.0f, own, nseg, prow, nullptr, r.u2, sh, Z);
-    }
-    if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
-    write_outputs(a, b, r.tau, y, xs, flags, Z, errword, blockDim.x);
-}
-
 // Inverse-CDF selection by one wavefront (no workgroup barrier): the segment
 // sums give an fp64 wavefront prefix that picks the segment holding u * Z;
 // lane l then owns tokens [32 l, 32 l + 32) of that segment and a second
@@ -886,6 +739,45 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
     return ybest != 0x7FFFFFFF ? ybest : ylast;
 }
 
+// Split tail, selection: one wavefront per request draws the correction /
+// bonus token from the segment sums (k_resid_sum's or block pass 2's) with
+// the fused tail's wavefront draw.
+template <int PES, int QES>
+__global__ __launch_bounds__(svk::kWave) void k_select(svh::VerifyArgs a, const ReqG *__restrict__ req,
+                                                       float *__restrict__ csum, const float *__restrict__ bm,
+                                                       int nseg, uint32_t *__restrict__ errword)
+{
+    __shared__ int32_t xs[MAXG];
+    const int b = a.b0 + (int)blockIdx.x;
+    const ReqG r = req[b];
+    if (r.flags) return;   // k_accept wrote the request's error outputs
+    const int gamma = a.gamma;
+    const int G1 = gamma + 1;
+    if ((int)threadIdx.x < r.tau) xs[threadIdx.x] = a.draft[(int64_t)b * gamma + threadIdx.x];
+    const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
+    const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
+    float *own = csum + (int64_t)b * nseg;
+    const float *sums = sums_from_pass2(a, r) ? bm + ((int64_t)b * gamma + r.tau) * nseg : own;
+
+    uint32_t flags = 0;
+    double Z = 0.0;
+    int y = select_token_wave<PES, QES>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, Z);
+    if (y < 0 && r.mode == 0) {
+        // residual mass rounded to zero (in exact arithmetic a rejection
+        // implies p != q): draw from the p row instead
+        flags |= SV_FLAG_RESID_ZERO;
+        segment_sums<PES, QES, 1>(a, prow, nullptr, 1, 1.0f, r.lp2, 0.0f, nseg, own);
+        // lane 0 wrote the sums the whole wavefront reads next
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        y = select_token_wave<PES, QES>(a, 1, 1.0f, r.lp2, 0.0f, own, nseg, prow, nullptr, r.u2, Z);
+    }
+    if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
+    __syncthreads();   // xs written above
+    write_outputs(a, b, r.tau, y, xs, flags, Z, errword, svk::kWave);
+}
+
 // ---------------------------------------------------------------------------
 // Fused tail: one workgroup of NTT threads per request evaluates the request
 // (wavefront 0), sums the correction / bonus weights of row tau+1 segment by
@@ -909,7 +801,7 @@ __global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, const float2
     __shared__ AcceptLDS as;
     __shared__ ReqG r;
     __shared__ float segsum[kTailMaxSeg];
-    __shared__ SelectShared sh;
+    __shared__ int ybest;   // the draw's token (wavefront 0)
     const int b = a.b0 + (int)blockIdx.x;
     if (stage == STAGE_FROM_REQ) {
         // k_accept already evaluated the request (and wrote the outputs of a
@@ -940,10 +832,10 @@ __global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, const float2
     int y = 0;
     if (wid == 0) {
         y = select_token_wave<PES, QES>(a, r.mode, r.wmul, r.lp2, r.lq2, sums, nseg, prow, qrow, r.u2, Z);
-        if (lane == 0) sh.ybest = y;
+        if (lane == 0) ybest = y;
     }
     __syncthreads();
-    if (sh.ybest < 0 && r.mode == 0) {
+    if (ybest < 0 && r.mode == 0) {
         // residual mass rounded to zero (in exact arithmetic a rejection
         // implies p != q): draw from the p row instead
         flags |= SV_FLAG_RESID_ZERO;
@@ -985,7 +877,7 @@ void launch_sum_and_select(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
                        ctx->ws.csum, nseg);
     svh::prof_end(ctx, s, slot);
     slot = svh::prof_begin(ctx, s, SV_KERNEL_SELECT);
-    hipLaunchKernelGGL((k_select<PES, QES>), dim3(a.nb), dim3(NT), 0, s, a, req, ctx->ws.csum,
+    hipLaunchKernelGGL((k_select<PES, QES>), dim3(a.nb), dim3(svk::kWave), 0, s, a, req, ctx->ws.csum,
                        (const float *)ctx->ws.bm, nseg, ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
 }
