@@ -706,16 +706,32 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
             for (int j = 0; j < 8; ++j) w[8 * g + j] = weight(xp[j], mode ? 0.0f : xq[j], mode, wmul, lp2, lq2, a.c);
         }
     } else {
+        // a partial or unaligned segment: DB elements at a time, each batch
+        // requested before it is weighed (past the segment's end, an in-row
+        // index whose weight is discarded), addressed by 32-bit offsets from
+        // the segment start
+        constexpr int DB = 4;
+        const int ts = (int)(t0 - s0), ns = (int)(s1 - s0);   // within the segment (< SEG)
 #pragma unroll
-        for (int j = 0; j < TPL; ++j) {
-            const int64_t e = t0 + j;
-            float wj = 0.0f;
-            if (e < s1) {
-                const float xp = svk::load_logit<PES>(prow, e);
-                const float xq = mode ? 0.0f : svk::load_logit<QES>(qrow, e);
-                wj = weight(xp, xq, mode, wmul, lp2, lq2, a.c);
+        for (int g = 0; g < TPL / DB; ++g) {
+            float xp[DB], xq[DB];
+#pragma unroll
+            for (int j = 0; j < DB; ++j) {
+                const int o = ts + DB * g + j;
+                xp[j] = svk::load_logit<PES>(prow, s0 + (o < ns ? o : 0));
             }
-            w[j] = wj;
+            if (!mode) {
+#pragma unroll
+                for (int j = 0; j < DB; ++j) {
+                    const int o = ts + DB * g + j;
+                    xq[j] = svk::load_logit<QES>(qrow, s0 + (o < ns ? o : 0));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < DB; ++j)
+                w[DB * g + j] = ts + DB * g + j < ns ? weight(xp[j], mode ? 0.0f : xq[j], mode, wmul, lp2, lq2, a.c)
+                                                     : 0.0f;
+            __builtin_amdgcn_sched_barrier(0);   // one batch of loads live at a time
         }
     }
     double lsum = 0.0;
