@@ -863,3 +863,27 @@ def test_oracle_tree_output_distribution_equals_target(orc, parents):
     assert set(counts) <= set(tj)
     chi2 = sum((counts.get(k, 0) - Nr * v) ** 2 / (Nr * v) for k, v in tj.items())
     assert chi2 < stats.chi2.ppf(1 - 1e-6, len(tj) - 1), chi2
+
+
+def test_block_residual_masses_are_the_thresholds_numerators(orc):
+    """The residual masses the oracle reports are the m_i of its thresholds:
+    h_i = m_i / (m_i + 1 - w_i) (1 where that denominator is 0) for i < L,
+    m_i >= 0, and each m_i is at most w_i (it sums w_i p - q over the tokens
+    where that is positive, and p sums to 1); NaN at i = L and beyond."""
+    rng = np.random.default_rng(31)
+    B, gamma, V = 24, 6, 97
+    p = rng.normal(size=(B, gamma + 1, V)) * 2.0
+    q = p[:, :gamma] + rng.normal(size=(B, gamma, V)) * rng.choice([0.2, 1.0, 3.0], size=(B, 1, 1))
+    draft = rng.integers(0, V, size=(B, gamma)).astype(np.int32)
+    vl = rng.integers(0, gamma + 1, size=B).astype(np.int32)
+    r = orc.block_verify(p, q, draft, gamma, verify_len=vl, seed=5)
+    for b in range(B):
+        L = int(vl[b])
+        for i in range(gamma):
+            m, w, h = r.m[b, i], r.w[b, i], r.h[b, i]
+            if i + 1 >= L:
+                assert np.isnan(m)
+                continue
+            assert 0.0 <= m <= w + 1e-12
+            den = m + 1.0 - w
+            assert h == (m / den if den > 0.0 else 1.0)
