@@ -30,6 +30,13 @@ template <int ESIZE, int NB, int NT>
 __device__ __forceinline__ MS thread_stats(const char *__restrict__ rowptr, int64_t e0, int64_t e1, float c,
                                            bool nontemporal, int tid)
 {
+    // The reference ref = round(max * c) must be the same rounded value in
+    // every use: the terms are exp2(x * c - ref) (one fused multiply-add) and
+    // an earlier partial sum is rescaled by exp2(ref_old - ref).  Contracting
+    // the product into the rescale's subtraction would use the unrounded
+    // max * c there and scale the whole partial sum by the product's rounding
+    // error; no contraction here.
+#pragma clang fp contract(off)
     constexpr int EPV = 16 / ESIZE;   // elements per 16-byte vector
 
     // 16-byte aligned body [a0, a1) inside [e0, e1)
