@@ -77,6 +77,9 @@ typedef struct {
     float *h;            /* [B, gamma]   block: acceptance threshold h_i              */
     float *resid_mass;   /* [B]          mass Z of the correction / bonus weights     */
     uint32_t *flags;     /* [B]          SV_FLAG_* bits of the request                */
+    float *uniform;      /* [B, gamma+1] the uniforms the decisions used: column i-1  */
+                         /* u_i (block: eta_i) for i <= L, column gamma the          */
+                         /* correction / bonus draw's (not written by tree calls)    */
 } sv_diag;
 
 /* Creates a context on `device` for calls with B <= max_batch,

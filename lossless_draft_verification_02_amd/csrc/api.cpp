@@ -177,6 +177,25 @@ svh::MarkovArgs make_markov_args(const void *base_logits, const void *U, const v
 
 }  // namespace
 
+namespace svh {
+
+void set_geometry(sv_ctx *ctx, int64_t vocab, int64_t rows_max)
+{
+    (void)rows_max;
+    // row-statistics chunks: about kTargetChunk1 elements, rounded to 8
+    int64_t nch1 = (vocab + kTargetChunk1 / 2) / kTargetChunk1;
+    if (nch1 < 1) nch1 = 1;
+    int64_t chunk1 = (vocab + nch1 - 1) / nch1;
+    chunk1 = (chunk1 + 7) / 8 * 8;
+    nch1 = (vocab + chunk1 - 1) / chunk1;
+    ctx->nch1 = (int)nch1;
+    ctx->chunk1 = chunk1;
+    ctx->nseg = (int)((vocab + kSegR - 1) / kSegR);
+    ctx->ntile = (int)((vocab + kMarkovTileN - 1) / kMarkovTileN);
+}
+
+}  // namespace svh
+
 extern "C" {
 
 const char *spec_verify_last_error(void) { return g_err; }
@@ -209,16 +228,7 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || ncu <= 0)
         ncu = 256;
     ctx->num_cu = ncu;
-    // row-statistics chunks: about kTargetChunk1 elements, rounded to 8
-    int64_t nch1 = (vocab + svh::kTargetChunk1 / 2) / svh::kTargetChunk1;
-    if (nch1 < 1) nch1 = 1;
-    int64_t chunk1 = (vocab + nch1 - 1) / nch1;
-    chunk1 = (chunk1 + 7) / 8 * 8;
-    nch1 = (vocab + chunk1 - 1) / chunk1;
-    ctx->nch1 = (int)nch1;
-    ctx->chunk1 = chunk1;
-    ctx->nseg = (int)((vocab + svh::kSegR - 1) / svh::kSegR);
-    ctx->ntile = (int)((vocab + svh::kMarkovTileN - 1) / svh::kMarkovTileN);
+    svh::set_geometry(ctx, vocab, (int64_t)max_batch * (2 * (int64_t)max_gamma + 1));
 
     const size_t rows_max = (size_t)max_batch * (2 * (size_t)max_gamma + 1);
     size_t off = 0;
@@ -233,7 +243,7 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_req = carve((size_t)max_batch * svh::kReqStateBytes);
     const size_t o_lp2 = carve((size_t)max_batch * (max_gamma + 1) * sizeof(float));
     const size_t o_lq2 = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
-    const size_t o_wrun = carve((size_t)max_batch * (max_gamma + 1) * sizeof(float));
+    const size_t o_wrun = carve((size_t)max_batch * (max_gamma + 1) * sizeof(double));
     const size_t o_err = carve(sizeof(uint32_t));
     const size_t o_sched = carve((size_t)max_batch * sizeof(int32_t));
     const size_t o_srank = carve((size_t)svh::kSchedMax * sizeof(int32_t));
@@ -268,7 +278,7 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.req = (void *)(b + o_req);
     ctx->ws.lp2 = (float *)(b + o_lp2);
     ctx->ws.lq2 = (float *)(b + o_lq2);
-    ctx->ws.wrun = (float *)(b + o_wrun);
+    ctx->ws.wrun = (double *)(b + o_wrun);
     ctx->ws.errword = (uint32_t *)(b + o_err);
     ctx->ws.sched_len = (int32_t *)(b + o_sched);
     ctx->ws.sched_rank = (int32_t *)(b + o_srank);

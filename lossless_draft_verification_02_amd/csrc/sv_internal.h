@@ -61,7 +61,7 @@ struct Workspace {
     void *req;           // [max_batch] per-request state (ReqG, verify.hip)
     float *lp2;          // [max_batch * (max_gamma + 1)] log2-sum-exp2 of verified p rows
     float *lq2;          // [max_batch * max_gamma]       ... and q rows
-    float *wrun;         // [max_batch * (max_gamma + 1)] block running ratios w_0..w_L
+    double *wrun;        // [max_batch * (max_gamma + 1)] block running ratios w_0..w_L
     uint32_t *errword;   // [1] OR of SV_FLAG_* bits
     int32_t *sched_len;  // [max_batch] scheduler output when the caller gives none
     int32_t *sched_rank; // [kSchedMax] candidate ranks, zero between calls
@@ -165,6 +165,10 @@ struct ReqG {
     float lp2, lq2;    // log2-sum-exp2 of p row tau+1 and q row tau+1
     float u2;          // correction / bonus uniform
 };
+
+// Row-chunk and segment geometry of a context for vocabulary `vocab` and at
+// most `rows_max` verified rows per call (nch1, chunk1, nseg, ntile).
+void set_geometry(sv_ctx *ctx, int64_t vocab, int64_t rows_max);
 
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 // Token verification after the row statistics: accept -> chunk sums -> select.

@@ -146,7 +146,7 @@ __device__ double residual_masses(const float *__restrict__ bmr, int L, int nseg
 struct AcceptLDS {
     double lp2[MAXG + 1];   // log2-sum-exp2 of the verified p rows
     double lq2[MAXG];       // ... and q rows
-    float rr[MAXG];         // uncapped p/q ratio of each draft token
+    double rr[MAXG];        // uncapped p/q ratio of each draft token
     int32_t x[MAXG];        // the draft tokens
 };
 
@@ -160,12 +160,12 @@ struct AcceptLDS {
 template <int PES, int QES>
 __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__ part, int nch1,
                             const float *__restrict__ bm, int nseg, int stage, int b, const ReqG *pre, ReqG *out,
-                            float *__restrict__ lp2g, float *__restrict__ lq2g, float *__restrict__ wrun,
+                            float *__restrict__ lp2g, float *__restrict__ lq2g, double *__restrict__ wrun,
                             uint32_t *__restrict__ errword, AcceptLDS &s)
 {
     double *lp2 = s.lp2;
     double *lq2 = s.lq2;
-    float *rr = s.rr;
+    double *rr = s.rr;
     const int lane = threadIdx.x;
     const int gamma = a.gamma;
     const int G1 = gamma + 1;
@@ -207,7 +207,7 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
     // block thresholds: running ratio and residual mass of position lane + 1
     // (not needed when the pre stage already decided tau = L)
     const int tau_pre = stage == STAGE_BLOCK_FINAL ? pre->tau : -1;
-    float wi = 1.0f;
+    double wi = 1.0;
     double mi = 0.0;
     if (stage == STAGE_BLOCK_FINAL) {
         if (lane + 1 <= gamma) wi = wrun[(int64_t)b * G1 + lane + 1];
@@ -232,6 +232,8 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
             a.out_tokens[(int64_t)b * G1 + j] = -1;
             if (a.diag.lse_p) a.diag.lse_p[(int64_t)b * G1 + j] = nan;
         }
+        for (int j = lane; j < G1; j += svk::kWave)
+            if (a.diag.uniform) a.diag.uniform[(int64_t)b * G1 + j] = nan;
         for (int j = lane; j < gamma; j += svk::kWave) {
             if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * gamma + j] = nan;
             if (a.diag.ratio) a.diag.ratio[(int64_t)b * gamma + j] = nan;
@@ -255,8 +257,8 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
         lq2[lane] = lq;
         const double dp = (double)gp * (double)a.c - lp;
         const double dq = (double)gq * (double)a.c - lq;
-        const float r = (float)exp2(dp - dq);
-        rr[lane] = (lane < L && r == r) ? r : 0.0f;
+        const double r = exp2(dp - dq);
+        rr[lane] = (lane < L && r == r) ? r : 0.0;
     }
     // only this wavefront runs: order its LDS writes before other lanes read them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -267,11 +269,13 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
         for (int j = lane; j <= L; j += svk::kWave) lp2g[(int64_t)b * G1 + j] = (float)lp2[j];
         for (int j = lane; j < L; j += svk::kWave) lq2g[(int64_t)b * gamma + j] = (float)lq2[j];
         if (lane == 0) {
-            float w = 1.0f;
+            // binary64 running product, as the thresholds built from it
+            // are ill-conditioned where m_i + 1 - w_i is small
+            double w = 1.0;
             wrun[(int64_t)b * G1] = w;
             for (int i = 1; i <= L; ++i) {
-                const float prod = w == 0.0f ? 0.0f : w * rr[i - 1];   // 0 * inf := 0
-                w = fminf(prod, 1.0f);
+                const double prod = w == 0.0 ? 0.0 : w * rr[i - 1];   // 0 * inf := 0
+                w = fmin(prod, 1.0);
                 wrun[(int64_t)b * G1 + i] = w;
             }
             // tau is the largest passing prefix, so eta_L < h_L = w_L decides
@@ -281,7 +285,7 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
             if (L >= 1 && !a.diag.h) {
                 const float eta = a.uniforms ? a.uniforms[(int64_t)b * G1 + L - 1]
                                              : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, (uint32_t)L, 0u);
-                if (eta < w) tau_early = L;
+                if (eta < (float)w) tau_early = L;
             }
             ReqG r{};
             r.flags = 0;
@@ -297,8 +301,9 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
         if (a.diag.lse_p) a.diag.lse_p[(int64_t)b * G1 + j] = j <= L ? (float)(lp2[j] * kLn2d) : nan;
     if (has_tok) {
         if (a.diag.lse_q) a.diag.lse_q[(int64_t)b * gamma + lane] = lane < L ? (float)(lq * kLn2d) : nan;
-        if (a.diag.ratio) a.diag.ratio[(int64_t)b * gamma + lane] = lane < L ? fminf(rr[lane], 1.0f) : nan;
+        if (a.diag.ratio) a.diag.ratio[(int64_t)b * gamma + lane] = lane < L ? (float)fmin(rr[lane], 1.0) : nan;
     }
+    if (a.diag.uniform && has_tok) a.diag.uniform[(int64_t)b * G1 + lane] = lane < L ? u : nan;
 
     // lane j takes the decision at position j + 1
     const bool active = lane < L;
@@ -306,7 +311,7 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
     float wmul = 1.0f;
     if (stage == STAGE_TOKEN) {
         // accept x_{j+1} iff u < min(1, ratio); tau = first rejection
-        const uint64_t rej = __ballot(active && !(u < fminf(rr[lane], 1.0f)));
+        const uint64_t rej = __ballot(active && !(u < (float)fmin(rr[lane], 1.0)));
         tau = rej ? (int)__builtin_ctzll(rej) : L;
         if (has_tok) {
             if (a.diag.w) a.diag.w[(int64_t)b * gamma + lane] = nan;
@@ -318,20 +323,20 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
         float h = 0.0f;
         if (active) {
             if (i < L) {
-                const double den = mi + 1.0 - (double)wi;
+                const double den = mi + 1.0 - wi;
                 h = den > 0.0 ? (float)(mi / den) : 1.0f;
             } else {
-                h = wi;
+                h = (float)wi;
             }
         }
         const uint64_t pass = __ballot(active && u < h);    // eta_i < h_i
         tau = pass ? 64 - (int)__builtin_clzll(pass) : 0;   // largest passing i
         if (tau_pre >= 0) tau = tau_pre;                     // decided by the pre stage (= L)
         if (has_tok) {
-            if (a.diag.w) a.diag.w[(int64_t)b * gamma + lane] = active ? wi : nan;
+            if (a.diag.w) a.diag.w[(int64_t)b * gamma + lane] = active ? (float)wi : nan;
             if (a.diag.h) a.diag.h[(int64_t)b * gamma + lane] = active ? h : nan;
         }
-        wmul = tau == 0 ? 1.0f : __shfl(wi, tau - 1, svk::kWave);   // w_tau (w_0 = 1)
+        wmul = tau == 0 ? 1.0f : (float)__shfl(wi, tau - 1, svk::kWave);   // w_tau (w_0 = 1)
     }
     if (lane != 0) return;
     ReqG r;
@@ -344,6 +349,7 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
     r.lq2 = tau < L ? (float)lq2[tau] : 0.0f;
     r.u2 = a.uniforms ? a.uniforms[(int64_t)b * G1 + gamma]
                       : svk::philox_uniform(a.seed, a.offset, (uint32_t)b, 0u, 1u);
+    if (a.diag.uniform) a.diag.uniform[(int64_t)b * G1 + gamma] = r.u2;
     *out = r;
 }
 
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const 
                                                        int nch1, const float *__restrict__ bm, int nseg,
                                                        int stage, ReqG *__restrict__ req,
                                                        float *__restrict__ lp2g, float *__restrict__ lq2g,
-                                                       float *__restrict__ wrun,
+                                                       double *__restrict__ wrun,
                                                        uint32_t *__restrict__ errword)
 {
     __shared__ AcceptLDS s;
@@ -534,7 +540,7 @@ template <int PES, int QES>
 __global__ __launch_bounds__(NT) void k_block_pass2(svh::VerifyArgs a, const ReqG *__restrict__ req,
                                                     const float *__restrict__ lp2g,
                                                     const float *__restrict__ lq2g,
-                                                    const float *__restrict__ wrun, float *__restrict__ bm,
+                                                    const double *__restrict__ wrun, float *__restrict__ bm,
                                                     int nseg)
 {
     const int nwg = (nseg + SPW - 1) / SPW;
@@ -549,7 +555,7 @@ __global__ __launch_bounds__(NT) void k_block_pass2(svh::VerifyArgs a, const Req
     const ReqG r = req[b];
     if (r.flags || r.tau >= 0 || i >= r.L || sidx >= nseg) return;   // whole wavefronts leave together
     const int G1 = a.gamma + 1;
-    const float w = wrun[(int64_t)b * G1 + i];
+    const float w = (float)wrun[(int64_t)b * G1 + i];
     const int64_t s0 = (int64_t)sidx * SEG;
     const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + i) * a.V * PES;
@@ -812,7 +818,7 @@ __global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, const float2
                                               const float *__restrict__ bm, int nseg, int stage,
                                               const ReqG *__restrict__ pre,
                                               float *__restrict__ lp2g, float *__restrict__ lq2g,
-                                              float *__restrict__ wrun, uint32_t *__restrict__ errword)
+                                              double *__restrict__ wrun, uint32_t *__restrict__ errword)
 {
     __shared__ AcceptLDS as;
     __shared__ ReqG r;
@@ -944,7 +950,7 @@ hipError_t block_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
         const int64_t nwg = (ctx->nseg + SPW - 1) / SPW;
         hipLaunchKernelGGL((k_block_pass2<PES, QES>), dim3((unsigned)((int64_t)a.nb * (a.gamma - 1) * nwg)),
                            dim3(NT), 0, s, a, (const ReqG *)ctx->ws.req, (const float *)ctx->ws.lp2,
-                           (const float *)ctx->ws.lq2, (const float *)ctx->ws.wrun, ctx->ws.bm, ctx->nseg);
+                           (const float *)ctx->ws.lq2, (const double *)ctx->ws.wrun, ctx->ws.bm, ctx->nseg);
         svh::prof_end(ctx, s, slot);
     }
     if (fused_tail_fits(ctx, a)) {
