@@ -20,7 +20,8 @@ SV_F32, SV_BF16 = 0, 1
 SV_FLAG_BAD_TOKEN, SV_FLAG_BAD_ROW, SV_FLAG_RESID_ZERO, SV_FLAG_BAD_VERIFY_LEN = 1, 2, 4, 8
 
 EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error",
-            "spec_verify_device_status", "spec_verify_run", "spec_schedule_run", "spec_schedule_sts_run",
+            "spec_verify_device_status", "spec_verify_run", "spec_schedule_run",
+            "spec_schedule_sts_run",
             "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "rnn_draft_run", "tree_verify_run",
             "spec_verify_profile_enable",
             "spec_verify_profile_read")
@@ -37,7 +38,7 @@ class SpecVerifyError(RuntimeError):
 class SvDiag(ctypes.Structure):
     _fields_ = [("lse_p", ctypes.c_void_p), ("lse_q", ctypes.c_void_p), ("ratio", ctypes.c_void_p),
                 ("w", ctypes.c_void_p), ("h", ctypes.c_void_p), ("resid_mass", ctypes.c_void_p),
-                ("flags", ctypes.c_void_p)]
+                ("flags", ctypes.c_void_p), ("uniform", ctypes.c_void_p)]
 
 
 _lib = None
@@ -136,10 +137,35 @@ def _stream(device: int, stream=None) -> int:
     return s.cuda_stream
 
 
-def _diag_struct(diag: Optional[dict]):
+def _diag_struct(diag: Optional[dict], device: int, shapes: dict):
+    """sv_diag of the given tensors, each checked against `shapes` (entry name
+    -> accepted shape, or a tuple of accepted shapes) before any launch: the
+    kernels write every entry they are given."""
     if not diag:
         return None
+    torch = _torch()
+    unknown = sorted(set(diag) - set(shapes))
+    if unknown:
+        raise ValueError(f"unknown or unsupported diagnostics {unknown}; accepted: {sorted(shapes)}")
+    for k, v in diag.items():
+        if v is None:
+            continue
+        want = shapes[k]
+        opts = want if isinstance(want[0], tuple) else (want,)
+        dt = torch.int32 if k == "flags" else torch.float32
+        _need(v, f"diag[{k!r}]", dtype=dt, device=device)
+        if tuple(v.shape) not in [tuple(o) for o in opts]:
+            raise ValueError(f"diag[{k!r}] must have shape {' or '.join(str(tuple(o)) for o in opts)}, "
+                             f"got {tuple(v.shape)}")
     return SvDiag(**{k: _ptr(v) for k, v in diag.items()})
+
+
+def _verify_diag_shapes(B: int, gamma: int) -> dict:
+    """Diagnostic shapes of a draft verification call ([B, 0] or [B, 1] for
+    the per-position entries when gamma = 0)."""
+    g = ((B, gamma), (B, 1)) if gamma == 0 else (B, gamma)
+    return dict(lse_p=(B, gamma + 1), lse_q=g, ratio=g, w=g, h=g, resid_mass=(B,), flags=(B,),
+                uniform=(B, gamma + 1))
 
 
 # ----------------------------------------------------------- entry points --
@@ -194,20 +220,20 @@ def spec_verify_device_status(ctx: Context, stream=None) -> int:
     return flags.value
 
 
-def _verify_shapes(ctx, p, q, draft, accepted_len, out_tokens, verify_len, uniforms):
+def _verify_shapes(device: int, p, q, draft, accepted_len, out_tokens, verify_len, uniforms):
     torch = _torch()
     if p.dim() != 3:
         raise ValueError("p must be [B, gamma+1, V]")
     B, G1, V = p.shape
     gamma = G1 - 1
-    _need(p, "p", device=ctx.device)
+    _need(p, "p", device=device)
     if gamma > 0:
-        _need(q, "q", shape=(B, gamma, V), device=ctx.device)
-        _need(draft, "draft", dtype=torch.int32, shape=(B, gamma), device=ctx.device)
-    _need(accepted_len, "accepted_len", dtype=torch.int32, shape=(B,), device=ctx.device)
-    _need(out_tokens, "out_tokens", dtype=torch.int32, shape=(B, gamma + 1), device=ctx.device)
-    _need(verify_len, "verify_len", dtype=torch.int32, shape=(B,), device=ctx.device)
-    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, gamma + 1), device=ctx.device)
+        _need(q, "q", shape=(B, gamma, V), device=device)
+        _need(draft, "draft", dtype=torch.int32, shape=(B, gamma), device=device)
+    _need(accepted_len, "accepted_len", dtype=torch.int32, shape=(B,), device=device)
+    _need(out_tokens, "out_tokens", dtype=torch.int32, shape=(B, gamma + 1), device=device)
+    _need(verify_len, "verify_len", dtype=torch.int32, shape=(B,), device=device)
+    _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, gamma + 1), device=device)
     return B, gamma, V
 
 
@@ -215,8 +241,8 @@ def spec_verify_run(ctx: Context, p, q, draft, accepted_len, out_tokens, *, temp
                     seed: int = 1, offset: int = 0, verify_len=None, uniforms=None,
                     diag: Optional[dict] = None, stream=None):
     """Token-level verification into accepted_len [B] / out_tokens [B, gamma+1] (int32)."""
-    B, gamma, V = _verify_shapes(ctx, p, q, draft, accepted_len, out_tokens, verify_len, uniforms)
-    d = _diag_struct(diag)
+    B, gamma, V = _verify_shapes(ctx.device, p, q, draft, accepted_len, out_tokens, verify_len, uniforms)
+    d = _diag_struct(diag, ctx.device, _verify_diag_shapes(B, gamma))
     qd = _dtype_code(q) if gamma > 0 else SV_BF16
     _check("spec_verify_run", load_library().spec_verify_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(p), _dtype_code(p), _ptr(q) if gamma > 0 else None, qd,
@@ -262,10 +288,10 @@ def spec_blockverify_run(ctx: Context, p, q, draft, accepted_len, out_tokens, *,
                          diag: Optional[dict] = None, stream=None):
     """Block verification (optionally scheduled by conf) into accepted_len / out_tokens."""
     torch = _torch()
-    B, gamma, V = _verify_shapes(ctx, p, q, draft, accepted_len, out_tokens, verify_len, uniforms)
+    B, gamma, V = _verify_shapes(ctx.device, p, q, draft, accepted_len, out_tokens, verify_len, uniforms)
     _need(conf, "conf", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
     _need(verify_len_out, "verify_len_out", dtype=torch.int32, shape=(B,), device=ctx.device)
-    d = _diag_struct(diag)
+    d = _diag_struct(diag, ctx.device, _verify_diag_shapes(B, gamma))
     qd = _dtype_code(q) if gamma > 0 else SV_BF16
     _check("spec_blockverify_run", load_library().spec_blockverify_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(p), _dtype_code(p), _ptr(q) if gamma > 0 else None, qd,
@@ -322,7 +348,9 @@ def tree_verify_run(ctx: Context, p, q, tokens, parents, accepted_len, out_token
     _need(out_tokens, "out_tokens", dtype=torch.int32, shape=(B, D + 1), device=ctx.device)
     _need(accepted_nodes, "accepted_nodes", dtype=torch.int32, shape=(B, D), device=ctx.device)
     _need(uniforms, "uniforms", dtype=torch.float32, shape=(B, N + 1), device=ctx.device)
-    d = _diag_struct(diag)
+    nq = ((B, NQ), (B, 1)) if NQ == 0 else (B, NQ)
+    nn = ((B, N), (B, 1)) if N == 0 else (B, N)
+    d = _diag_struct(diag, ctx.device, dict(lse_p=(B, N + 1), lse_q=nq, ratio=nn, resid_mass=(B,), flags=(B,)))
     host = (ctypes.c_int32 * max(N, 1))(*par)
     _check("tree_verify_run", load_library().tree_verify_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(p), _dtype_code(p), _ptr(q) if N > 0 else None,
@@ -370,7 +398,7 @@ def markov_verify_run(ctx: Context, base, U, Wt, x0, p, draft_out, accepted_len,
     _need(accepted_len, "accepted_len", dtype=torch.int32, shape=(B,), device=ctx.device)
     _need(out_tokens, "out_tokens", dtype=torch.int32, shape=(B, gamma + 1), device=ctx.device)
     _need(lse_q, "lse_q", dtype=torch.float32, shape=(B, gamma), device=ctx.device)
-    d = _diag_struct(diag)
+    d = _diag_struct(diag, ctx.device, _verify_diag_shapes(B, gamma))
     _check("markov_verify_run", load_library().markov_verify_run(
         ctx.handle, _stream(ctx.device, stream), _ptr(base), _ptr(U), _ptr(Wt), R, _ptr(x0), _ptr(p),
         _dtype_code(p), B, gamma, V, temperature, draft_seed, verify_seed, offset, _ptr(draft_out),
