@@ -77,9 +77,24 @@ def declare(lib):
     return lib
 
 
+def build_sanitized(path: str) -> str:
+    """Compile the oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+    into `path` (same arithmetic flags; any undefined behaviour aborts).  A
+    process loads it through ORACLE_LIB, with libasan preloaded."""
+    cmd = ["gcc", "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-Wall", "-Wextra", "-o", path, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
+
+
 def _load():
     global _lib
     if _lib is None:
+        alt = os.environ.get("ORACLE_LIB")
+        if alt:   # a separately built oracle (the sanitizer build)
+            _lib = declare(ctypes.CDLL(alt))
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = declare(ctypes.CDLL(_LIB))

@@ -78,3 +78,18 @@ def test_binding_requires_built_library(tmp_path):
             binding.load_library(str(tmp_path / "missing.so"))
     finally:
         binding._lib = saved
+
+
+def test_binding_checks_diagnostics_before_any_launch():
+    """Diagnostic tensors are checked (device, dtype, shape, known names) on
+    the host; a bad one raises before the C ABI is called."""
+    import torch
+    shapes = binding._verify_diag_shapes(4, 3)
+    assert shapes["lse_p"] == (4, 4) and shapes["uniform"] == (4, 4) and shapes["ratio"] == (4, 3)
+    with pytest.raises(ValueError, match="unknown"):
+        binding._diag_struct({"margin": None}, 0, shapes)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        binding._diag_struct({"lse_p": torch.zeros(4, 4)}, 0, shapes)
+    assert binding._diag_struct(None, 0, shapes) is None
+    # gamma = 0: the per-position entries may be [B, 0] or [B, 1]
+    assert binding._verify_diag_shapes(2, 0)["lse_q"] == ((2, 0), (2, 1))
