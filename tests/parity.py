@@ -21,11 +21,17 @@ LSE_ATOL, LSE_RTOL = 1e-5, 1e-6
 # sums (~1e-7 of sum(w p + q) <= 2) plus its fp32 segment sums.  1e-6 bounds
 # both with room to spare.
 WM_ABS_EPS = 1e-6
+# A block tau disagreement beyond MARGIN is accepted (and counted apart, as a
+# widened flip) only where the threshold is that ill-conditioned:
+# D = m + 1 - w at most WIDEN_MAX_D.
+WIDEN_MAX_D = 1e-3
 
 @dataclass
 class Report:
     requests: int = 0
     flips: int = 0
+    widened_flips: int = 0   # block tau flips beyond MARGIN at D <= WIDEN_MAX_D (included in flips)
+    uniforms_checked: int = 0
     failures: list = field(default_factory=list)
     max_prob_err: float = 0.0
     max_lse_err: float = 0.0
@@ -34,28 +40,44 @@ class Report:
         return not self.failures
 
     def __str__(self):
-        return (f"requests={self.requests} flips={self.flips} failures={len(self.failures)} "
+        return (f"requests={self.requests} flips={self.flips} widened_flips={self.widened_flips} "
+                f"failures={len(self.failures)} uniforms_checked={self.uniforms_checked} "
                 f"max_prob_err={self.max_prob_err:.2e} max_lse_err={self.max_lse_err:.2e} "
                 f"{self.failures[:5]}")
 
+    def as_dict(self) -> dict:
+        return {"requests": self.requests, "flips": self.flips, "widened_flips": self.widened_flips,
+                "failures": len(self.failures), "uniforms_checked": self.uniforms_checked,
+                "max_prob_err": self.max_prob_err, "max_lse_err": self.max_lse_err}
 
-def threshold_tol(w, m):
+
+def threshold_tol(w, m, dw=None):
     """Bound on the GPU's block thresholds h = m / D, D = m + 1 - w (oracle
     values; m is NaN at i = L, where h_L = w_L).  dh/dm = (1 - h) / D and
-    dh/dw = h / D, so absolute errors eps in m and w move h by at most eps / D
-    to first order -- more than the flat probability tolerance when D is
-    small, and without bound at D = 0, where h is 1 by convention but the
-    GPU's rounding of w and m can put it anywhere in [0, 1]."""
+    dh/dw = h / D, so absolute errors eps_m in m and eps_w in w move h by at
+    most ((1 - h) eps_m + h eps_w) / D to first order -- more than the flat
+    probability tolerance when D is small, and without bound at D = 0, where
+    h is 1 by convention but the GPU's rounding of w and m can put it
+    anywhere in [0, 1].  eps_m = WM_ABS_EPS; eps_w is the GPU's own w
+    difference `dw` where it is known (w is a product of up to L ratios of
+    fp32-normalised probabilities, each off by about 1e-7 to 1e-6, and is
+    itself checked against PROB_ATOL), at least WM_ABS_EPS."""
     w = np.asarray(w, np.float64)
     m = np.asarray(m, np.float64)
+    eps_w = np.full_like(w, WM_ABS_EPS) if dw is None else np.maximum(np.abs(np.asarray(dw, np.float64)), WM_ABS_EPS)
     den = m + 1.0 - w
-    with np.errstate(divide="ignore"):
-        extra = np.where(np.isnan(m), 0.0, np.where(den > 0.0, WM_ABS_EPS / np.maximum(den, 1e-300), np.inf))
-    return PROB_ATOL + WM_ABS_EPS * np.isnan(m) + extra
+    h = np.where(den > 0.0, m / np.where(den > 0.0, den, 1.0), 1.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        extra = np.where(np.isnan(m), 0.0,
+                         np.where(den > 0.0, ((1.0 - h) * WM_ABS_EPS + h * eps_w) / np.maximum(den, 1e-300),
+                                  np.inf))
+    return PROB_ATOL + np.where(np.isnan(m), eps_w, 0.0) + extra
 
 
-def _close_threshold(rep, g, o, w, mres, what, b):
-    """Block thresholds within threshold_tol of the oracle's."""
+def _close_threshold(rep, g, o, w, mres, what, b, gw=None):
+    """Block thresholds within threshold_tol of the oracle's.  A failure
+    records the position, both thresholds, both running ratios (gw: the
+    GPU's), the oracle's residual mass and the one the GPU's h and w imply."""
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
     m = ~np.isnan(o)
@@ -65,11 +87,18 @@ def _close_threshold(rep, g, o, w, mres, what, b):
         rep.failures.append((b, what, "nan on the GPU"))
         return
     err = np.abs(g[m] - o[m])
-    tol = threshold_tol(np.asarray(w, np.float64)[m], np.asarray(mres, np.float64)[m])
+    dw = None if gw is None else (np.asarray(gw, np.float64) - np.asarray(w, np.float64))[m]
+    tol = threshold_tol(np.asarray(w, np.float64)[m], np.asarray(mres, np.float64)[m], dw)
     rep.max_prob_err = max(rep.max_prob_err, float(err.max()))
     if (err > tol).any():
-        i = int(np.argmax(err - tol))
-        rep.failures.append((b, what, float(err[i]), float(tol[i])))
+        k = int(np.argmax(err - tol))
+        i = int(np.flatnonzero(m)[k])
+        ow, om = float(np.asarray(w)[i]), float(np.asarray(mres)[i])
+        gwi = float(np.asarray(gw)[i]) if gw is not None else float("nan")
+        gm = g[i] * (1.0 - gwi) / (1.0 - g[i]) if g[i] < 1.0 else float("nan")
+        rep.failures.append((b, what, float(err[k]), float(tol[k]),
+                             dict(pos=i + 1, h_gpu=float(g[i]), h_orc=float(o[i]), w_gpu=gwi, w_orc=ow,
+                                  m_orc=om, m_gpu_implied=gm)))
 
 
 def _close_prob(rep, g, o, what, b):
@@ -97,17 +126,35 @@ def _close_lse(rep, g, o, what, b):
             rep.failures.append((b, what, float(np.nanmax(err))))
 
 
+def _same_uniforms(rep, g, o, b):
+    """Uniforms the oracle drew for request b (non-NaN entries) against the
+    GPU's, bit for bit: both sides evaluate the same Philox4x32-10 counters."""
+    g = np.asarray(g, np.float32)
+    o = np.asarray(o, np.float32)
+    m = ~np.isnan(o)
+    rep.uniforms_checked += int(m.sum())
+    if not np.array_equal(g[m].view(np.uint32), o[m].view(np.uint32)):
+        i = int(np.flatnonzero(m)[np.argmax(g[m] != o[m])])
+        rep.failures.append((b, "uniform", i, float(o[i]), float(g[i])))
+        return False
+    return True
+
+
 def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = False,
                    draft=None, rep: Report | None = None) -> Report:
     """gpu: dict of numpy arrays accepted_len, out_tokens and diag entries
-    (lse_p, lse_q, ratio, w, h, resid_mass, flags) for the same requests as
-    the oracle result `orc` (oracle.VerifyResult)."""
+    (lse_p, lse_q, ratio, w, h, resid_mass, flags, uniform) for the same
+    requests as the oracle result `orc` (oracle.VerifyResult)."""
     rep = rep or Report()
     B = len(orc.accepted_len)
     for b in range(B):
         rep.requests += 1
         L = gamma if verify_len is None else int(verify_len[b])
         oa, ga = int(orc.accepted_len[b]), int(gpu["accepted_len"][b])
+        if "uniform" in gpu and oa >= 0 and ga >= 0:
+            # the decisions below are only comparable on the same uniforms
+            if not _same_uniforms(rep, gpu["uniform"][b], orc.uniform[b], b):
+                continue
         if oa < 0 or ga < 0:
             if oa != ga:
                 rep.failures.append((b, "error status", oa, ga))
@@ -130,15 +177,24 @@ def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = Fa
                 if not o_acc:
                     break
         elif oa != ga:
-            # the decisions above the smaller tau: a flip where |eta_i - h_i|
-            # is within the margin or within h_i's own bound
+            # the decision at the larger tau: a flip where |eta_i - h_i| is
+            # within the margin, or, where h_i is ill-conditioned (D small),
+            # within h_i's own bound (counted apart)
             i = max(oa, ga)
-            htol = float(threshold_tol([orc.w[b, i - 1]], [orc.m[b, i - 1]])[0])
-            if orc.dec_margin[b, i - 1] <= max(MARGIN, htol):
+            mi, wi = float(orc.m[b, i - 1]), float(orc.w[b, i - 1])
+            marg = float(orc.dec_margin[b, i - 1])
+            den = mi + 1.0 - wi   # NaN at i = L, where h_L = w_L
+            dw = float(gpu["w"][b, i - 1]) - wi if "w" in gpu else None
+            htol = float(threshold_tol([wi], [mi], None if dw is None else [dw])[0])
+            if marg <= MARGIN:
                 rep.flips += 1
                 flipped = True
+            elif den == den and den <= WIDEN_MAX_D and marg <= htol:
+                rep.flips += 1
+                rep.widened_flips += 1
+                flipped = True
             else:
-                rep.failures.append((b, "block tau", oa, ga, float(orc.dec_margin[b, i - 1])))
+                rep.failures.append((b, "block tau", oa, ga, marg, den))
         if flipped or (rep.failures and rep.failures[-1][0] == b):
             continue
         # same tau: tokens x_1..x_tau, then the drawn token
@@ -166,7 +222,8 @@ def compare_verify(gpu: dict, orc, gamma: int, verify_len=None, block: bool = Fa
         if block and "w" in gpu and L > 0:
             _close_prob(rep, gpu["w"][b, :L], orc.w[b, :L], "w", b)
         if block and "h" in gpu and L > 0:
-            _close_threshold(rep, gpu["h"][b, :L], orc.h[b, :L], orc.w[b, :L], orc.m[b, :L], "h", b)
+            _close_threshold(rep, gpu["h"][b, :L], orc.h[b, :L], orc.w[b, :L], orc.m[b, :L], "h", b,
+                             gw=gpu["w"][b, :L] if "w" in gpu else None)
         if "resid_mass" in gpu:
             _close_prob(rep, [gpu["resid_mass"][b]], [orc.resid_mass[b]], "resid_mass", b)
         if "flags" in gpu and int(gpu["flags"][b]) != int(orc.flags[b]):

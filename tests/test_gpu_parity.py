@@ -17,6 +17,7 @@ import torch
 import oracle
 import lossless_draft_verification_02_amd as L
 from lossless_draft_verification_02_amd import workloads as WL
+from oracle_pool import map_requests
 from parity import Report, compare_markov, compare_rnn, compare_tree, compare_verify
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +52,7 @@ def gpu_verify(ctx, vi, *, block=False, verify_len=None, conf=None, uniforms=Non
     diag = dict(lse_p=torch.empty(B, gamma + 1, device=dev), lse_q=torch.empty(B, max(gamma, 1), device=dev),
                 ratio=torch.empty(B, max(gamma, 1), device=dev), w=torch.empty(B, max(gamma, 1), device=dev),
                 h=torch.empty(B, max(gamma, 1), device=dev), resid_mass=torch.empty(B, device=dev),
-                flags=torch.zeros(B, dtype=torch.int32, device=dev))
+                flags=torch.zeros(B, dtype=torch.int32, device=dev), uniform=torch.empty(B, gamma + 1, device=dev))
     for k in skip_diag:
         del diag[k]
     vlo = torch.full((B,), -7, dtype=torch.int32, device=dev) if conf is not None else None
@@ -78,6 +79,18 @@ def _np64(t):
 
 def oracle_verify(vi, req, *, block=False, verify_len=None, uniforms=None, seed=WL.VERIFY_SEED, offset=0,
                   p=None, q=None, draft=None, T=None):
+    """The oracle on requests `req` of vi (chunks of 8 on a thread pool for
+    larger sets)."""
+    req = list(req)
+    if len(req) > 8:
+        return map_requests(lambda r: _oracle_verify(vi, r, block=block, verify_len=verify_len, uniforms=uniforms,
+                                                     seed=seed, offset=offset, p=p, q=q, draft=draft, T=T), req)
+    return _oracle_verify(vi, req, block=block, verify_len=verify_len, uniforms=uniforms, seed=seed,
+                          offset=offset, p=p, q=q, draft=draft, T=T)
+
+
+def _oracle_verify(vi, req, *, block=False, verify_len=None, uniforms=None, seed=WL.VERIFY_SEED, offset=0,
+                   p=None, q=None, draft=None, T=None):
     p = vi.p if p is None else p
     q = vi.q if q is None else q
     draft = vi.draft if draft is None else draft
@@ -267,6 +280,18 @@ def test_host_argument_errors():
         out4 = torch.empty(4, 4, dtype=torch.int32, device="cuda")
         with pytest.raises(L.SpecVerifyError):
             L.spec_verify_run(ctx, vi.p, vi.q, vi.draft, acc4, out4, temperature=0.0)
+        # diagnostics are checked before anything is launched: the outputs
+        # stay untouched
+        acc4.fill_(-7)
+        for bad in (dict(lse_p=torch.empty(4, 3, device="cuda")),                 # too small
+                    dict(flags=torch.empty(4, device="cuda")),                     # float, not int32
+                    dict(ratio=torch.empty(4, 3)),                                 # host memory
+                    dict(uniform=torch.empty(4, 8, device="cuda")[:, ::2]),        # not contiguous
+                    dict(margin=torch.empty(4, 3, device="cuda"))):                # unknown entry
+            with pytest.raises((ValueError, TypeError)):
+                L.spec_verify_run(ctx, vi.p, vi.q, vi.draft, acc4, out4, diag=bad)
+        torch.cuda.synchronize()
+        assert (acc4 == -7).all()
         with pytest.raises(L.SpecVerifyError):
             L.markov_draft_run(ctx, vi.q, torch.zeros(1000, 256, dtype=torch.bfloat16, device="cuda"),
                                torch.zeros(1000, 256, dtype=torch.bfloat16, device="cuda"),
@@ -595,6 +620,15 @@ def gpu_markov(ctx, mi, uniforms=None, want_q=True, seed=WL.DRAFT_SEED):
 
 
 def oracle_markov(mi, req, uniforms=None, seed=WL.DRAFT_SEED, want_q=True):
+    """The oracle's Markov sampler on requests `req` (chunks of 4 on a thread
+    pool for larger sets)."""
+    req = list(req)
+    if len(req) > 4:
+        return map_requests(lambda r: _oracle_markov(mi, r, uniforms, seed, want_q), req, chunk=4)
+    return _oracle_markov(mi, req, uniforms, seed, want_q)
+
+
+def _oracle_markov(mi, req, uniforms=None, seed=WL.DRAFT_SEED, want_q=True):
     idx = torch.as_tensor(req, device=mi.base.device)
     return oracle.markov_draft(_np64(mi.base[idx]), _np64(mi.U), _np64(mi.W), mi.x0[idx].cpu().numpy(),
                                temperature=mi.T, seed=seed, req_ids=np.asarray(req, np.int32),
@@ -650,6 +684,13 @@ def gpu_tree(ctx, ti, uniforms=None, seed=WL.VERIFY_SEED, offset=0):
 
 
 def oracle_tree(ti, req, seed=WL.VERIFY_SEED, offset=0, uniforms=None):
+    req = list(req)
+    if len(req) > 8:
+        return map_requests(lambda r: _oracle_tree(ti, r, seed, offset, uniforms), req)
+    return _oracle_tree(ti, req, seed, offset, uniforms)
+
+
+def _oracle_tree(ti, req, seed=WL.VERIFY_SEED, offset=0, uniforms=None):
     idx = torch.as_tensor(req, device=ti.p.device)
     return oracle.tree_verify(_np64(ti.p[idx]), _np64(ti.q[idx]), ti.tokens[idx].cpu().numpy(), ti.parents,
                               temperature=ti.T, seed=seed, offset=offset, req_ids=np.asarray(req, np.int32),
@@ -813,13 +854,13 @@ def test_tree_largest_trees(shape):
             check_tree(ctx, ti, list(range(B)), "tree 64 children")
 
 
-def test_tree_workload_full_sampled():
+def test_tree_workload_full():
     """The tree workload at full size (B=64, 4 branches x 5, V=129,280, bf16);
-    the oracle on sampled requests."""
-    _say("case: tree workload full size")
+    every request against the oracle."""
+    _say("case: tree workload full size, all requests")
     ti = WL.make_tree_inputs("cuda")
     with make_ctx(ti.B, len(ti.parents), ti.V) as ctx:
-        check_tree(ctx, ti, [0, 17, 40, 63], "tree full")
+        check_tree(ctx, ti, list(range(ti.B)), "tree full")
 
 
 # ---------------------------------------------------------------- RNN ----
@@ -837,6 +878,13 @@ def gpu_rnn(ctx, mi, A, want_q=True, seed=WL.DRAFT_SEED, uniforms=None):
 
 
 def oracle_rnn(mi, A, req, seed=WL.DRAFT_SEED, want_q=True, uniforms=None):
+    req = list(req)
+    if len(req) > 4:
+        return map_requests(lambda r: _oracle_rnn(mi, A, r, seed, want_q, uniforms), req, chunk=4)
+    return _oracle_rnn(mi, A, req, seed, want_q, uniforms)
+
+
+def _oracle_rnn(mi, A, req, seed=WL.DRAFT_SEED, want_q=True, uniforms=None):
     idx = torch.as_tensor(req, device=mi.base.device)
     return oracle.rnn_draft(_np64(mi.base[idx]), _np64(mi.U), _np64(mi.W), _np64(A), mi.x0[idx].cpu().numpy(),
                             temperature=mi.T, seed=seed, req_ids=np.asarray(req, np.int32),
@@ -895,14 +943,14 @@ def test_rnn_zero_recurrence_is_markov_on_tanh_embeddings():
     assert torch.equal(d, dm) and torch.equal(ql, qm) and torch.equal(lse, lm)
 
 
-def test_rnn_markov_workload_sampled():
+def test_rnn_markov_workload_full():
     """The markov workload at full size (B=128, gamma=8, V=129,280, R=256) with the
-    recurrent matrix of the RNN variant; the oracle on sampled requests."""
-    _say("case: RNN head, markov workload at full size")
+    recurrent matrix of the RNN variant; every request against the oracle."""
+    _say("case: RNN head, markov workload at full size, all requests")
     mi = WL.make_markov_inputs("cuda")
     A = WL.make_rnn_recurrence(mi.R, "cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
-        check_rnn(ctx, mi, A, [0, 37, 127], "rnn w4 full", want_q=False)
+        check_rnn(ctx, mi, A, list(range(mi.B)), "rnn w4 full", want_q=False)
 
 
 # ------------------------------------------------------- the bare C ABI --
@@ -969,7 +1017,8 @@ def gpu_markov_verify(ctx, mi, seed_d=WL.DRAFT_SEED, seed_v=WL.VERIFY_SEED, offs
     lse = torch.empty(B, gamma, device="cuda")
     diag = dict(lse_p=torch.empty(B, gamma + 1, device="cuda"), lse_q=torch.empty(B, gamma, device="cuda"),
                 ratio=torch.empty(B, gamma, device="cuda"), resid_mass=torch.empty(B, device="cuda"),
-                flags=torch.zeros(B, dtype=torch.int32, device="cuda"))
+                flags=torch.zeros(B, dtype=torch.int32, device="cuda"),
+                uniform=torch.empty(B, gamma + 1, device="cuda"))
     L.markov_verify_run(ctx, mi.base, mi.U, mi.Wt, mi.x0, mi.p, d, acc, out, lse_q=lse, temperature=mi.T,
                         draft_seed=seed_d, verify_seed=seed_v, offset=offset, diag=diag)
     torch.cuda.synchronize()
@@ -1050,57 +1099,61 @@ def test_rnn_random(case):
     assert torch.equal(d, d2) and torch.equal(lse, lse2) and torch.equal(st, st2)
 
 
-def test_markov_verify_fused_full_size_sampled():
-    _say("case: markov workload at full size, fused Markov -> verify")
+def test_markov_verify_fused_full_size():
+    """The markov workload at full size through the fused path, every request
+    against the oracle."""
+    _say("case: markov workload at full size, fused Markov -> verify, all requests")
     mi = WL.make_markov_inputs("cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
-        check_markov_verify(ctx, mi, _sample(mi.B, 3, 14), "fused w4")
+        check_markov_verify(ctx, mi, list(range(mi.B)), "fused w4 full")
 
 
-# ------------------------------------------ full sizes, sampled requests --
+# ------------------------------ full sizes, every request against the oracle --
 
 def _sample(B, n, seed):
     rng = np.random.default_rng(seed)
     return sorted(set([0, B - 1] + rng.choice(B, size=min(n, B), replace=False).tolist()))
 
 
-def test_full_headline_sampled():
-    """B=256, gamma=7, V=129280 bf16, the benchmark's launch configuration."""
-    _say("case: headline workload at full size")
+def test_full_headline():
+    """B=256, gamma=7, V=129280 bf16, the benchmark's launch configuration;
+    all 256 requests."""
+    _say("case: headline workload at full size, all requests")
     vi = WL.make_verify_inputs("headline", "cuda")
     with make_ctx(vi.B, vi.gamma, vi.V) as ctx:
-        check_verify(ctx, vi, req=_sample(vi.B, 14, 3), label="w3 full")
+        check_verify(ctx, vi, label="w3 full")
 
 
-def test_full_batched_sampled():
-    _say("case: batched workload at full size")
+def test_full_batched():
+    _say("case: batched workload at full size, all requests")
     vi = WL.make_verify_inputs("batched", "cuda")
     with make_ctx(vi.B, vi.gamma, vi.V) as ctx:
-        check_verify(ctx, vi, req=_sample(vi.B, 10, 2), label="w2 full")
+        check_verify(ctx, vi, label="w2 full")
 
 
-def test_full_block_scheduled_sampled():
-    _say("case: block workload at full size (scheduler + block verification)")
+def test_full_block_scheduled():
+    _say("case: block workload at full size (scheduler + block verification), all requests")
     vi = WL.make_verify_inputs("block", "cuda")
     with make_ctx(vi.B, vi.gamma, vi.V) as ctx:
         res = gpu_verify(ctx, vi, block=True, conf=vi.conf)
     ovl, _, _ = _oracle_schedule(vi.conf)
     assert np.array_equal(res["verify_len_out"], ovl)
-    req = _sample(vi.B, 12, 5)
+    req = list(range(vi.B))
     o = oracle_verify(vi, req, block=True, verify_len=ovl)
     rep = compare_verify(_subset(res, req), o, vi.gamma, verify_len=ovl[req], block=True)
     _say(f"[w5 full] {rep} mean verify_len={ovl.mean():.3f}")
     assert rep.ok(), str(rep)
+    assert rep.flips <= max(1, 0.02 * rep.requests), str(rep)
 
 
-def test_full_markov_then_verify_sampled():
-    _say("case: markov workload at full size (Markov sampler, then verification)")
+def test_full_markov_then_verify():
+    _say("case: markov workload at full size (Markov sampler, then verification), all requests")
     mi = WL.make_markov_inputs("cuda")
     with make_ctx(mi.B, mi.gamma, mi.V, mi.R) as ctx:
         d, ql, lse = gpu_markov(ctx, mi)
         vi = WL.VerifyInputs("markov then verify", mi.B, mi.gamma, mi.V, mi.T, mi.p, ql, d)
         res = gpu_verify(ctx, vi)
-    req = _sample(mi.B, 3, 4)
+    req = list(range(mi.B))
     o = oracle_markov(mi, req)
     rep = compare_markov(d.cpu().numpy()[req], lse.cpu().numpy()[req], ql.cpu().numpy()[req], o)
     _say(f"[w4 markov full] {rep}")
