@@ -12,8 +12,16 @@ steps.  Prints ONE JSON line:
             events recorded inside the library on the launch stream, against
             8 TB/s; `traffic` from rocprofv3 FETCH_SIZE / WRITE_SIZE when the
             committed counter summary matches the current kernel source
-  cpu_baseline  the CPU oracle, single thread, on a bounded sample of the same
-            batch (rows of the first requests until ~10 s of oracle time)
+  call_roofline  the whole call (row statistics + tail): algorithmic bytes of
+            the timed steps (every verified logit once, plus the one or two
+            rows each request's correction / bonus draw reads) / step time
+  cpu_baseline  the CPU oracle on the same batch and round as the last timed
+            step: all 256 requests on a pool of host threads (`value`,
+            `cores`), and one thread on a bounded sample
+  parity    the last timed step's outputs (and, from one more call with the
+            same inputs and round, its diagnostics) against that oracle run,
+            walked decision by decision: requests, within-margin flips,
+            failures, largest probability / log-sum-exp differences
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
        [--copy-probe]   (accepted for the recorded profile commands; the copy probe always runs)
@@ -62,29 +70,67 @@ def measured_traffic(bytes_per_launch_alg):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(vi, budget_s=10.0, chunk=4):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_and_parity(vi, offset, gpu, single_budget_s=3.0, chunk=4):
+    """The CPU oracle on every request of `vi` at round `offset`: timed on one
+    host thread over a bounded sample, then on a pool of threads over the
+    whole batch (logits converted to float64 beforehand, outside the timed
+    region); that result is walked against the GPU's outputs `gpu`."""
+    import concurrent.futures
     import numpy as np
     import oracle
     from lossless_draft_verification_02_amd import workloads as WL
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_pool import merge, workers
+    from parity import compare_verify
 
     oracle.build(force=False)
-    spent = 0.0
-    done = 0
+    chunks = []
     for b0 in range(0, vi.B, chunk):
         b1 = min(vi.B, b0 + chunk)
-        p = vi.p[b0:b1].float().cpu().double().numpy()
-        q = vi.q[b0:b1].float().cpu().double().numpy()
-        x = vi.draft[b0:b1].cpu().numpy()
-        rid = np.arange(b0, b1, dtype=np.int32)
+        chunks.append((vi.p[b0:b1].float().cpu().double().numpy(), vi.q[b0:b1].float().cpu().double().numpy(),
+                       vi.draft[b0:b1].cpu().numpy(), np.arange(b0, b1, dtype=np.int32)))
+
+    def run(c):
+        p, q, x, rid = c
+        return oracle.token_verify(p, q, x, vi.gamma, temperature=vi.T, seed=WL.VERIFY_SEED, offset=offset,
+                                   req_ids=rid)
+
+    spent, done = 0.0, 0
+    for c in chunks:
         t0 = time.perf_counter()
-        oracle.token_verify(p, q, x, vi.gamma, temperature=vi.T, seed=WL.VERIFY_SEED, req_ids=rid)
+        run(c)
         spent += time.perf_counter() - t0
-        done = b1
-        if spent >= budget_s:
+        done += len(c[3])
+        if spent >= single_budget_s:
             break
-    return {"value": done * vi.gamma / spent, "unit": "verified positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {vi.B} requests of the same batch (gamma={vi.gamma}, V={vi.V}), "
-                      f"{spent:.1f} s of single-thread oracle time"}
+    n = workers()
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+        parts = list(ex.map(run, chunks))
+    wall = time.perf_counter() - t0
+    orc = merge(parts)
+    rep = compare_verify(gpu, orc, vi.gamma, draft=vi.draft.cpu().numpy())
+    base = {"value": round(vi.B * vi.gamma / wall, 1), "unit": "verified positions/s", "cores": n,
+            "kind": "oracle",
+            "sample": f"all {vi.B} requests of the last timed step's batch and round (gamma={vi.gamma}, "
+                      f"V={vi.V}) on {n} host threads, {wall:.2f} s wall; one thread: {done} requests in "
+                      f"{spent:.2f} s",
+            "single_thread_value": round(done * vi.gamma / spent, 1),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+    parity = rep.as_dict()
+    parity["failure_examples"] = [str(f) for f in rep.failures[:3]]
+    return base, parity
 
 
 def _time_steps(step, warmup, steps):
@@ -136,6 +182,7 @@ def _line(metric, value, unit, args, ms, config, roofline, **extra):
 
 
 def bench_headline(args, L, WL):
+    import numpy as np
     import torch
     cfg = WL.WORKLOADS["headline"]
     # two independent batches of the headline recipe (each above the 256 MB
@@ -152,11 +199,42 @@ def bench_headline(args, L, WL):
         L.spec_verify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k)
 
     ms, wall_ms = _time_steps(step, args.warmup, args.steps)
-    a = acc.cpu().numpy()
-    accepted = float(a[a >= 0].mean())
+    # the last timed step's outputs, then one more call on the same inputs and
+    # round with every diagnostic (its outputs must be the same)
+    k_last = args.warmup + args.steps - 1
+    gpu = {"accepted_len": acc.cpu().numpy().copy(), "out_tokens": out.cpu().numpy().copy()}
+    s_last = sets[k_last % len(sets)]
+    diag = dict(lse_p=torch.empty(B, gamma + 1, device="cuda"), lse_q=torch.empty(B, gamma, device="cuda"),
+                ratio=torch.empty(B, gamma, device="cuda"), resid_mass=torch.empty(B, device="cuda"),
+                flags=torch.zeros(B, dtype=torch.int32, device="cuda"),
+                uniform=torch.empty(B, gamma + 1, device="cuda"))
+    L.spec_verify_run(ctx, s_last.p, s_last.q, s_last.draft, acc, out, temperature=s_last.T, seed=WL.VERIFY_SEED,
+                      offset=k_last, diag=diag)
+    torch.cuda.synchronize()
+    same = bool((acc.cpu().numpy() == gpu["accepted_len"]).all() and (out.cpu().numpy() == gpu["out_tokens"]).all())
+    gpu.update({k: v.cpu().numpy() for k, v in diag.items()})
+    gpu["flags"] = gpu["flags"].astype("uint32")
+    # bytes of the timed steps: every verified row once, plus the rows each
+    # request's draw re-reads (p and q row tau+1 after a rejection, the bonus
+    # row alone otherwise)
+    row_bytes = V * vi.p.element_size()
+    reread = 0
+    a_all = []
+    for k in range(args.warmup, args.warmup + args.steps):
+        step(k)
+        a = acc.cpu().numpy()
+        a_all.append(a)
+        reread += int(((a >= 0) & (a < gamma)).sum()) * 2 * row_bytes + int((a == gamma).sum()) * row_bytes
+    a_all = np.concatenate(a_all)
+    accepted = float(a_all[a_all >= 0].mean())
+    call_bytes = WL.bytes_single_read(vi) + reread / args.steps + B * gamma * 4 + B * (gamma + 2) * 4
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     alg = WL.bytes_single_read(vi)
     roofline = _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats"), measured_traffic(alg))
+    call_gbps = call_bytes / (ms * 1e-3) / 1e9
+    call_roofline = {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(call_gbps / PEAK_HBM_GBPS, 4), "alg_bytes_per_call": int(call_bytes),
+                     "what": "whole verification call: every verified row once + the draw's re-read rows"}
     # a plain streaming kernel of known traffic (1 GiB read + 1 GiB written per
     # dispatch): a reference for what this part sustains on a copy, and the
     # kernel whose FETCH_SIZE / WRITE_SIZE readings scale the counters
@@ -175,12 +253,15 @@ def bench_headline(args, L, WL):
     copy_probe = {"kernel": "torch.bitwise_not over 1 GiB int32", "bytes_per_launch": 2 << 30,
                   "mean_us": round(copy_us, 2), "gbps": round((2 << 30) / (copy_us * 1e-6) / 1e9, 1)}
     del src, dst
-    cpu = None if args.no_cpu_baseline else cpu_baseline(vi)
     ctx.close()
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline_and_parity(s_last, k_last, gpu)
+        parity["diag_call_outputs_equal_timed"] = same
     return _line(METRIC, B * gamma / (ms / 1e3), "verified positions/s", args, ms,
                  {"workload": "token-level verification, headline batch", "B": B, "gamma": gamma, "V": V,
                   "logits": "bf16", "temperature": cfg["T"], "input_sets": len(sets)},
-                 roofline, cpu_baseline=cpu,
+                 roofline, cpu_baseline=cpu, parity=parity, call_roofline=call_roofline,
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  mean_accepted=round(accepted, 4), wall_ms_per_step=round(wall_ms, 5), copy_probe=copy_probe,
