@@ -127,6 +127,30 @@ sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream,
                           uint64_t seed, uint64_t offset, const float *uniforms,
                           int32_t *accepted_len, int32_t *out_tokens, const sv_diag *diag);
 
+/* Token-level verification without a context and without allocating: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results as spec_verify_run, on the CURRENT HIP device; the
+ * call's scratch (row-chunk statistics, request state, correction-weight
+ * segment sums) lives in a file-scope device array of the library, 8 MiB
+ * per GPU, held until the process ends, found with hipGetSymbolAddress on
+ * the first call on each device.  A call needs 256-byte-aligned space for
+ * B (2 gamma + 1) ceil(V / chunk) float2 (chunk about 16K tokens), B
+ * ceil(V / 2048) floats and B 32-byte request states (about 0.3 MiB at
+ * B = 256, gamma = 7, V = 129,280); a larger call returns
+ * SV_ERR_UNSUPPORTED and launches nothing.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (several streams, several host
+ * threads) race and must be serialised by the caller.  There is no device
+ * error word to read: data errors show per request (accepted_len = -1,
+ * diag->flags).  No hipMalloc, hipFree or hipMemset is issued. */
+sv_status spec_verify_run_noalloc(hipStream_t stream,
+                                  const void *p_logits, sv_dtype p_dtype,
+                                  const void *q_logits, sv_dtype q_dtype,
+                                  const int32_t *draft_tokens, const int32_t *verify_len,
+                                  int B, int gamma, int64_t V, float temperature,
+                                  uint64_t seed, uint64_t offset, const float *uniforms,
+                                  int32_t *accepted_len, int32_t *out_tokens, const sv_diag *diag);
+
 /* Hardware-aware prefix scheduler.  Survival S_{b,i} = prod_{j<=i} conf_{b,j}
  * (binary64); candidates are ranked by (S descending, b ascending, i
  * ascending) and admitted one by one while E * SPS(rows) strictly rises, with

@@ -20,7 +20,7 @@ SV_F32, SV_BF16 = 0, 1
 SV_FLAG_BAD_TOKEN, SV_FLAG_BAD_ROW, SV_FLAG_RESID_ZERO, SV_FLAG_BAD_VERIFY_LEN = 1, 2, 4, 8
 
 EXPORTED = ("spec_verify_create", "spec_verify_destroy", "spec_verify_last_error",
-            "spec_verify_device_status", "spec_verify_run", "spec_schedule_run",
+            "spec_verify_device_status", "spec_verify_run", "spec_verify_run_noalloc", "spec_schedule_run",
             "spec_schedule_sts_run",
             "spec_blockverify_run", "markov_draft_run", "markov_verify_run", "rnn_draft_run", "tree_verify_run",
             "spec_verify_profile_enable",
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.spec_verify_device_status.restype = I
     lib.spec_verify_run.argtypes = [P, P, P, I, P, I, P, P, I, I, I64, F, U64, U64, P, P, P, P]
     lib.spec_verify_run.restype = I
+    lib.spec_verify_run_noalloc.argtypes = [P, P, I, P, I, P, P, I, I, I64, F, U64, U64, P, P, P, P]
+    lib.spec_verify_run_noalloc.restype = I
     lib.spec_schedule_run.argtypes = [P, P, P, I, I, F, F, P, P]
     lib.spec_schedule_run.restype = I
     lib.spec_schedule_sts_run.argtypes = [P, P, P, P, I, I, F, F, P, P]
@@ -248,6 +250,26 @@ def spec_verify_run(ctx: Context, p, q, draft, accepted_len, out_tokens, *, temp
         ctx.handle, _stream(ctx.device, stream), _ptr(p), _dtype_code(p), _ptr(q) if gamma > 0 else None, qd,
         _ptr(draft) if gamma > 0 else None, _ptr(verify_len), B, gamma, V, temperature, seed, offset,
         _ptr(uniforms), _ptr(accepted_len), _ptr(out_tokens), ctypes.byref(d) if d else None))
+
+
+def spec_verify_run_noalloc(p, q, draft, accepted_len, out_tokens, *, temperature: float = 1.0, seed: int = 1,
+                            offset: int = 0, verify_len=None, uniforms=None, diag: Optional[dict] = None,
+                            stream=None):
+    """Token-level verification without a context or any allocation (the
+    library's per-GPU scratch array), on p's device; calls that overlap on one
+    GPU race."""
+    torch = _torch()
+    if p.dim() != 3 or not p.is_cuda:
+        raise ValueError("p must be a GPU tensor [B, gamma+1, V]")
+    dev = p.device.index
+    B, gamma, V = _verify_shapes(dev, p, q, draft, accepted_len, out_tokens, verify_len, uniforms)
+    d = _diag_struct(diag, dev, _verify_diag_shapes(B, gamma))
+    qd = _dtype_code(q) if gamma > 0 else SV_BF16
+    with torch.cuda.device(dev):
+        _check("spec_verify_run_noalloc", load_library().spec_verify_run_noalloc(
+            _stream(dev, stream), _ptr(p), _dtype_code(p), _ptr(q) if gamma > 0 else None, qd,
+            _ptr(draft) if gamma > 0 else None, _ptr(verify_len), B, gamma, V, temperature, seed, offset,
+            _ptr(uniforms), _ptr(accepted_len), _ptr(out_tokens), ctypes.byref(d) if d else None))
 
 
 def spec_schedule_run(ctx: Context, conf, verify_len, *, sps_a: float = 2000.0, sps_k: float = 4096.0,

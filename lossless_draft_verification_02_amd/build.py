@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 
-SOURCES = ["rowstats.hip", "verify.hip", "schedule.hip", "markov.hip", "api.cpp"]
+SOURCES = ["rowstats.hip", "verify.hip", "schedule.hip", "markov.hip", "noalloc.hip", "api.cpp"]
 
 ARCH = os.environ.get("SPECVERIFY_ARCH", "gfx950")
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

@@ -194,6 +194,28 @@ void set_geometry(sv_ctx *ctx, int64_t vocab, int64_t rows_max)
     ctx->ntile = (int)((vocab + kMarkovTileN - 1) / kMarkovTileN);
 }
 
+sv_status set_error(sv_status st, const char *msg)
+{
+    if (st == SV_OK) return ok();
+    return fail(st, "%s", msg);
+}
+
+sv_status verify_args_ok(const sv_ctx *ctx, const void *p, sv_dtype pd, const void *q, sv_dtype qd,
+                         const int32_t *draft, int B, int gamma, int64_t V, float T, const int32_t *accepted_len,
+                         const int32_t *out_tokens, const char *fn)
+{
+    return check_verify_args(ctx, p, pd, q, qd, draft, B, gamma, V, T, accepted_len, out_tokens, fn);
+}
+
+VerifyArgs verify_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd, const int32_t *draft,
+                       const int32_t *verify_len, int B, int gamma, int64_t V, float T, uint64_t seed,
+                       uint64_t offset, const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                       const sv_diag *diag)
+{
+    return make_args(p, pd, q, qd, draft, verify_len, B, gamma, V, T, seed, offset, uniforms, accepted_len,
+                     out_tokens, diag, false);
+}
+
 }  // namespace svh
 
 extern "C" {

@@ -52,6 +52,11 @@ constexpr int kSchedMax = 8192;
 constexpr int kMarkovTileN = 128;
 constexpr int kMarkovMaxTiles = 256 * 8;   // the draw keeps 8 tile pairs per thread: V <= 262,144
 constexpr int kMaxGamma = 64;
+// Scratch of the allocation-free token verification (a file-scope device
+// array, one per GPU): row-chunk statistics, request state and segment sums.
+#ifndef SV_NOALLOC_SCRATCH_BYTES
+#define SV_NOALLOC_SCRATCH_BYTES (8u << 20)
+#endif
 
 
 struct Workspace {
@@ -169,6 +174,17 @@ struct ReqG {
 // Row-chunk and segment geometry of a context for vocabulary `vocab` and at
 // most `rows_max` verified rows per call (nch1, chunk1, nseg, ntile).
 void set_geometry(sv_ctx *ctx, int64_t vocab, int64_t rows_max);
+// Argument checks and argument block of token verification (api.cpp), for
+// entry points defined in other files; set_error records a status and
+// message for spec_verify_last_error (SV_OK clears it).
+sv_status set_error(sv_status st, const char *msg);
+sv_status verify_args_ok(const sv_ctx *ctx, const void *p, sv_dtype pd, const void *q, sv_dtype qd,
+                         const int32_t *draft, int B, int gamma, int64_t V, float T, const int32_t *accepted_len,
+                         const int32_t *out_tokens, const char *fn);
+VerifyArgs verify_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd, const int32_t *draft,
+                       const int32_t *verify_len, int B, int gamma, int64_t V, float T, uint64_t seed,
+                       uint64_t offset, const float *uniforms, int32_t *accepted_len, int32_t *out_tokens,
+                       const sv_diag *diag);
 
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 // Token verification after the row statistics: accept -> chunk sums -> select.
