@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -181,9 +182,17 @@ namespace svh {
 
 void set_geometry(sv_ctx *ctx, int64_t vocab, int64_t rows_max)
 {
+    // Row-statistics chunks (a multiple of 8 elements) of about
+    // kTargetChunk1 elements, one batch of loads per thread of a workgroup.
+    // SPECVERIFY_ROWSTATS_CHUNK (an element count) overrides the length,
+    // for tuning.
     (void)rows_max;
-    // row-statistics chunks: about kTargetChunk1 elements, rounded to 8
-    int64_t nch1 = (vocab + kTargetChunk1 / 2) / kTargetChunk1;
+    int64_t target = kTargetChunk1;
+    if (const char *env = std::getenv("SPECVERIFY_ROWSTATS_CHUNK")) {
+        const long long e = std::atoll(env);
+        if (e >= 256 && e <= (1 << 22)) target = e;
+    }
+    int64_t nch1 = (vocab + target - 1) / target;
     if (nch1 < 1) nch1 = 1;
     int64_t chunk1 = (vocab + nch1 - 1) / nch1;
     chunk1 = (chunk1 + 7) / 8 * 8;
