@@ -24,7 +24,9 @@ steps.  Prints ONE JSON line:
             failures, largest probability / log-sum-exp differences
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
-       [--copy-probe]   (accepted for the recorded profile commands; the copy probe always runs)
+       [--copy-probe]   (other workloads: also run the copy probe, for the counter scale;
+                         the headline line always carries it)
+       [--fused-only]   (markov workload: time only the fused path)
        [--workload headline|tiny|batched|block|block_async|markov|rnn|tree|all]
 The other workloads (one JSON line each, same fields) measure the tiny and
 batched token-verification batches, scheduler + block verification
@@ -49,11 +51,14 @@ PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rowstats_headline_traffic.json")
 ROWSTATS_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
                     for f in ("rowstats.hip", "sv_device.h")]
+MARKOV_COUNTERS_FILE = os.path.join(ROOT, "profiles", "markov_gemm_counters.json")
+MARKOV_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
+                  for f in ("markov.hip", "sv_device.h")]
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=ROWSTATS_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in ROWSTATS_SOURCES:
+    for f in sources:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -68,6 +73,18 @@ def measured_traffic(bytes_per_launch_alg):
     if t.get("kernel_source_sha256") != kernel_source_digest():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def markov_counters():
+    """The Markov contraction's committed counter summary (HBM bytes, MFMA
+    busy fraction per launch), or None if absent or taken on other sources."""
+    if not os.path.exists(MARKOV_COUNTERS_FILE):
+        return None
+    with open(MARKOV_COUNTERS_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_digest(MARKOV_SOURCES):
+        return None
+    return t
 
 
 def cpu_model() -> str:
@@ -166,6 +183,28 @@ def _mean_us(prof, name):
     return ms / max(n, 1) * 1e3
 
 
+def _copy_probe():
+    """A plain streaming kernel of known traffic (1 GiB read + 1 GiB written
+    per dispatch): a reference for what this part sustains on a copy, and the
+    kernel whose FETCH_SIZE / WRITE_SIZE readings scale the counters."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.zeros(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        torch.bitwise_not(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_us = e0.elapsed_time(e1) / 5 * 1e3
+    del src, dst
+    return {"kernel": "torch.bitwise_not over 1 GiB int32", "bytes_per_launch": 2 << 30,
+            "mean_us": round(copy_us, 2), "gbps": round((2 << 30) / (copy_us * 1e-6) / 1e9, 1)}
+
+
 def _hbm_roofline(kernel, alg_bytes, mean_us, traffic=None):
     achieved = alg_bytes / (mean_us * 1e-6) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -235,24 +274,7 @@ def bench_headline(args, L, WL):
     call_roofline = {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / PEAK_HBM_GBPS, 4), "alg_bytes_per_call": int(call_bytes),
                      "what": "whole verification call: every verified row once + the draw's re-read rows"}
-    # a plain streaming kernel of known traffic (1 GiB read + 1 GiB written per
-    # dispatch): a reference for what this part sustains on a copy, and the
-    # kernel whose FETCH_SIZE / WRITE_SIZE readings scale the counters
-    n = (1 << 30) // 4
-    src = torch.zeros(n, dtype=torch.int32, device="cuda")
-    dst = torch.empty_like(src)
-    torch.bitwise_not(src, out=dst)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        torch.bitwise_not(src, out=dst)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_us = e0.elapsed_time(e1) / 5 * 1e3
-    copy_probe = {"kernel": "torch.bitwise_not over 1 GiB int32", "bytes_per_launch": 2 << 30,
-                  "mean_us": round(copy_us, 2), "gbps": round((2 << 30) / (copy_us * 1e-6) / 1e9, 1)}
-    del src, dst
+    copy_probe = _copy_probe()
     ctx.close()
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -358,14 +380,26 @@ def bench_markov(args, L, WL):
 
     ms, _ = _time_steps(step, args.warmup, args.steps)
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
-    ms2, _ = _time_steps(step_two_calls, args.warmup, args.steps)
+    ms2 = None
+    if not args.fused_only:
+        ms2, _ = _time_steps(step_two_calls, args.warmup, args.steps)
     ctx.close()
     gemm_us = _mean_us(prof, "markov_gemm")
-    bytes_gemm = B * V * 2 + R * V * 2 + B * R * 2   # base_k + W + U rows (no z row stored)
+    # algorithmic bytes of the draft per call: the base logits once, W once
+    # (its re-reads at every position are the kernel's, not the method's),
+    # the gathered U rows; per launch = per call / gamma
+    per_call = B * gamma * V * 2 + R * V * 2 + B * gamma * R * 2
     flops = 2.0 * B * R * V
-    roof = _hbm_roofline("k_markov_gemm", bytes_gemm, gemm_us)
+    roof = _hbm_roofline("k_markov_gemm", per_call / gamma, gemm_us, None)
+    roof["alg_bytes_what"] = "base logits + W once per call + U rows, per launch (per call / gamma)"
+    per_launch_w_each = B * V * 2 + R * V * 2 + B * R * 2
+    roof["frac_w_each_position"] = round(per_launch_w_each / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
     roof["mfma_tflops"] = round(flops / (gemm_us * 1e-6) / 1e12, 2)
     roof["mfma_frac_of_bf16_peak"] = round(flops / (gemm_us * 1e-6) / 2.5e15, 4)
+    cnt = markov_counters()
+    if cnt:
+        roof["traffic"] = cnt.get("hbm_bytes_per_launch")
+        roof["mfma_busy_frac_counters"] = cnt.get("mfma_busy_frac")
     return _line("verified positions/s, B=128 gamma=8 V=129,280, Markov-head draft + verification",
                  B * gamma / (ms / 1e3), "verified positions/s", args, ms,
                  {"workload": "Markov-head draft sampling (R=256), then token verification of that draft "
@@ -373,8 +407,8 @@ def bench_markov(args, L, WL):
                   "B": B, "gamma": gamma, "V": V, "R": R},
                  roof, kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  markov_ms_per_call=round((prof["markov_gemm"][0] + prof["markov_select"][0]) / args.steps, 4),
-                 two_call_ms_per_step=round(ms2, 5),
-                 two_call_verified_positions_per_s=round(B * gamma / (ms2 / 1e3), 1))
+                 two_call_ms_per_step=None if ms2 is None else round(ms2, 5),
+                 two_call_verified_positions_per_s=None if ms2 is None else round(B * gamma / (ms2 / 1e3), 1))
 
 
 def bench_tree(args, L, WL):
@@ -445,9 +479,14 @@ def bench_rnn(args, L, WL):
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     ctx.close()
     gemm_us = _mean_us(prof, "markov_gemm")
-    bytes_gemm = B * V * 2 + R * V * 2 + B * R * 2   # base_k + W + the state rows (no z row stored)
+    # per call: the base logits once, W once, A once, the state rows; per
+    # launch = per call / gamma (W's re-read at each position is the kernel's)
+    per_call = B * gamma * V * 2 + R * V * 2 + R * R * 2 + B * gamma * R * 2
     flops = 2.0 * B * R * V
-    roof = _hbm_roofline("k_markov_gemm", bytes_gemm, gemm_us)
+    roof = _hbm_roofline("k_markov_gemm", per_call / gamma, gemm_us)
+    roof["alg_bytes_what"] = "base logits + W + A once per call + state rows, per launch (per call / gamma)"
+    roof["frac_w_each_position"] = round((B * V * 2 + R * V * 2 + B * R * 2) / (gemm_us * 1e-6) / 1e9
+                                         / PEAK_HBM_GBPS, 4)
     roof["mfma_tflops"] = round(flops / (gemm_us * 1e-6) / 1e12, 2)
     roof["mfma_frac_of_bf16_peak"] = round(flops / (gemm_us * 1e-6) / 2.5e15, 4)
     return _line("drafted positions/s, B=128 gamma=8 V=129,280 R=256, RNN-head draft",
@@ -545,6 +584,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="markov workload: time only the fused path (for clean per-kernel profiles)")
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "tiny", "batched", "block", "block_async", "markov", "rnn", "tree",
                              "all"],
@@ -583,7 +624,10 @@ def main():
                 sys.exit(r.returncode)
             print(r.stdout.strip().splitlines()[-1], flush=True)
             continue
-        print(json.dumps(runs[n]()), flush=True)
+        line = runs[n]()
+        if args.copy_probe and "copy_probe" not in line:
+            line["copy_probe"] = _copy_probe()
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
