@@ -312,9 +312,20 @@ def bench_token(args, L, WL, name, nsets):
     return _line(f"verified positions/s, {WL.describe(name)}", B * gamma / (ms / 1e3), "verified positions/s",
                  args, ms, {"workload": f"token-level verification, {name} batch", "B": B, "gamma": gamma, "V": V,
                             "logits": str(vi.p.dtype).split(".")[-1], "temperature": vi.T, "input_sets": nsets},
-                 _hbm_roofline("k_rowstats", WL.bytes_single_read(vi), _mean_us(prof, "rowstats")),
+                 _token_roofline(prof, vi, WL),
                  us_per_call=round(ms * 1e3, 2),
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
+
+
+def _token_roofline(prof, vi, WL):
+    """Row statistics' roofline, or, when a small problem ran as one launch
+    (no separate row-statistics kernel), that launch's."""
+    if prof["rowstats"][1]:
+        return _hbm_roofline("k_rowstats", WL.bytes_single_read(vi), _mean_us(prof, "rowstats"))
+    r = _hbm_roofline("k_tail (row statistics + tail in one launch)", WL.bytes_single_read(vi),
+                      _mean_us(prof, "tail"))
+    r["bound"] = "latency"
+    return r
 
 
 def bench_block(args, L, WL):

@@ -437,8 +437,7 @@ sv_status spec_verify_run(sv_ctx *ctx, hipStream_t stream, const void *p_logits,
     const svh::VerifyArgs a = make_args(p_logits, p_dtype, q_logits, q_dtype, draft_tokens, verify_len, B,
                                         gamma, V, temperature, seed, offset, uniforms, accepted_len,
                                         out_tokens, diag, false);
-    if ((st = run_verify(ctx, a, stream, svh::launch_token_tail, "acceptance / residual sampler")) != SV_OK)
-        return st;
+    if ((st = check_launch(svh::launch_token_verify(ctx, a, stream), "token verification")) != SV_OK) return st;
     return ok();
 }
 

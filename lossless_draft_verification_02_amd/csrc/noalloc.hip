@@ -123,8 +123,7 @@ extern "C" sv_status spec_verify_run_noalloc(hipStream_t stream, const void *p_l
     const svh::VerifyArgs a = svh::verify_args(p_logits, p_dtype, q_logits, q_dtype, draft_tokens, verify_len, B,
                                                gamma, V, temperature, seed, offset, uniforms, accepted_len,
                                                out_tokens, diag);
-    e = svh::launch_rowstats(&ctx, a, stream);
-    if (e == hipSuccess) e = svh::launch_token_tail(&ctx, a, stream);
+    e = svh::launch_token_verify(&ctx, a, stream);
     if (e != hipSuccess) {
         std::snprintf(msg, sizeof msg, "%s: launch failed: %s", fn, hipGetErrorString(e));
         return svh::set_error(SV_ERR_HIP, msg);

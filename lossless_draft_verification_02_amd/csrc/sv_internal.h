@@ -189,6 +189,9 @@ VerifyArgs verify_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd, c
 hipError_t launch_rowstats(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 // Token verification after the row statistics: accept -> chunk sums -> select.
 hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
+// The whole token verification: row statistics then the tail, or, for a
+// small problem (one chunk per row, few rows), one launch doing both.
+hipError_t launch_token_verify(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);
 // Block verification after the row statistics: ratios -> residual masses ->
 // thresholds -> chunk sums -> select.
 hipError_t launch_block_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s);

@@ -36,6 +36,7 @@
 //                 in ascending token id order).
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_rowstats.h"
 
 namespace {
 
@@ -680,7 +681,18 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
     const bool aligned = (((uintptr_t)(prow + s0 * PES)) & 15) == 0 &&
                          (mode || (((uintptr_t)(qrow + s0 * QES)) & 15) == 0);
     float w[TPL];
-    if (aligned && t0 + TPL <= s1) {
+    const bool vec_path = aligned && t0 + TPL <= s1;
+    // the other lanes load DB tokens per batch; batches past every such
+    // lane's tokens (a short segment leaves later batches, or whole lanes,
+    // empty) are skipped by the whole wavefront
+    constexpr int DB = 4;
+    int nbatch;
+    {
+        const int64_t left = s1 - t0;
+        const int mine = vec_path || left <= 0 ? 0 : (left < TPL ? (int)left : TPL);
+        nbatch = wave_max_i((mine + DB - 1) / DB);
+    }
+    if (vec_path) {
         // every vector of the lane's 32 tokens is requested before any is
         // used: one memory round trip
         constexpr int U = TPL / 8;
@@ -716,10 +728,14 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
         // requested before it is weighed (past the segment's end, an in-row
         // index whose weight is discarded), addressed by 32-bit offsets from
         // the segment start
-        constexpr int DB = 4;
         const int ts = (int)(t0 - s0), ns = (int)(s1 - s0);   // within the segment (< SEG)
 #pragma unroll
         for (int g = 0; g < TPL / DB; ++g) {
+            if (g >= nbatch) {   // wavefront-uniform: no lane has tokens left
+#pragma unroll
+                for (int j = 0; j < DB; ++j) w[DB * g + j] = 0.0f;
+                continue;
+            }
             float xp[DB], xq[DB];
 #pragma unroll
             for (int j = 0; j < DB; ++j) {
@@ -813,18 +829,55 @@ constexpr int kTailMaxSeg = svh::kTailMaxSeg;   // LDS segment sums: V <= 8.4M t
 #define SV_FUSED_TAIL 1             // 0: always the accept / sum / select kernels
 #endif
 
+// Small problems (rows of one chunk, few rows per request): the request's
+// own workgroup computes the statistics of the rows it verifies before the
+// tail runs -- wavefront w takes rows w, w + NW, ... (p rows 0..L, then q rows
+// 0..L-1), each streamed once with the row-statistics pass's per-thread
+// arithmetic and merged across the wavefront -- so a call is one launch.
+// The pairs go to the same place the row-statistics pass puts them
+// (nch1 == 1); the barrier after makes them visible to wavefront 0.
+template <int PES, int QES, int NW>
+__device__ void small_rowstats(const svh::VerifyArgs &a, int b, float2 *__restrict__ part)
+{
+    const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
+    const int L = a.verify_len ? a.verify_len[b] : a.gamma;
+    if (L < 0 || L > a.gamma) return;   // flagged by the acceptance
+    const int np = a.gamma + 1, nq = a.gamma;
+    for (int r = wid; r < 2 * L + 1; r += NW) {
+        const bool is_p = r <= L;
+        const int i = is_p ? r : r - (L + 1);
+        svk::MS t;
+        int64_t grow;
+        if (is_p) {
+            grow = (int64_t)b * np + i;
+            t = svk::thread_stats<PES, 8, svk::kWave>((const char *)a.p + grow * a.V * PES, 0, a.V, a.c, true, lane);
+        } else {
+            const int64_t qr = (int64_t)b * nq + i;
+            grow = (int64_t)a.B * np + qr;
+            t = svk::thread_stats<QES, 8, svk::kWave>((const char *)a.q + qr * a.V * QES, 0, a.V, a.c, true, lane);
+        }
+        t = svk::wave_merge(t);
+        if (lane == 0) part[grow] = make_float2(t.m, t.s);
+    }
+}
+
 template <int PES, int QES, int NTT>
-__global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, const float2 *__restrict__ part, int nch1,
+__global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, float2 *__restrict__ part, int nch1,
                                               const float *__restrict__ bm, int nseg, int stage,
                                               const ReqG *__restrict__ pre,
                                               float *__restrict__ lp2g, float *__restrict__ lq2g,
-                                              double *__restrict__ wrun, uint32_t *__restrict__ errword)
+                                              double *__restrict__ wrun, uint32_t *__restrict__ errword,
+                                              int small)
 {
     __shared__ AcceptLDS as;
     __shared__ ReqG r;
     __shared__ float segsum[kTailMaxSeg];
     __shared__ int ybest;   // the draw's token (wavefront 0)
     const int b = a.b0 + (int)blockIdx.x;
+    if (small) {   // token verification of a small problem: its row statistics first
+        small_rowstats<PES, QES, NTT / svk::kWave>(a, b, part);
+        __syncthreads();
+    }
     if (stage == STAGE_FROM_REQ) {
         // k_accept already evaluated the request (and wrote the outputs of a
         // request with a data error)
@@ -905,18 +958,29 @@ void launch_sum_and_select(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
 }
 
 template <int PES, int QES>
-void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int stage)
+void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int stage, int small = 0)
 {
     const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
-    if (a.nb <= ctx->num_cu)
-        hipLaunchKernelGGL((k_tail<PES, QES, NTT_WIDE>), dim3(a.nb), dim3(NTT_WIDE), 0, s, a,
-                           (const float2 *)ctx->ws.part, ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage,
-                           (const ReqG *)ctx->ws.req, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
+    if (a.nb <= ctx->num_cu || small)
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_WIDE>), dim3(a.nb), dim3(NTT_WIDE), 0, s, a, ctx->ws.part, ctx->nch1,
+                           (const float *)ctx->ws.bm, ctx->nseg, stage, (const ReqG *)ctx->ws.req, ctx->ws.lp2,
+                           ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword, small);
     else
-        hipLaunchKernelGGL((k_tail<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a,
-                           (const float2 *)ctx->ws.part, ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage,
-                           (const ReqG *)ctx->ws.req, ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword);
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a, ctx->ws.part,
+                           ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage, (const ReqG *)ctx->ws.req,
+                           ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword, 0);
     svh::prof_end(ctx, s, slot);
+}
+
+// One launch for token verification of a small problem: rows of a single
+// row-statistics chunk, at most kSmallRowsPerWave rows per wavefront of the
+// 1024-thread tail, and not more requests than two per CU (beyond that the
+// row-statistics pass spreads the rows better).
+constexpr int kSmallRowsPerWave = 4;
+inline bool small_fits(const sv_ctx *ctx, const svh::VerifyArgs &a)
+{
+    return SV_FUSED_TAIL && ctx->nch1 == 1 && !a.q_lse2 && a.np_rows == 0 && !a.block &&
+           2 * a.gamma + 1 <= kSmallRowsPerWave * (NTT_WIDE / svk::kWave) && a.nb <= 2 * ctx->num_cu;
 }
 
 // The fused tail puts each request's segment sums on one CU, which streams
@@ -927,6 +991,13 @@ inline bool fused_tail_fits(const sv_ctx *ctx, const svh::VerifyArgs &a)
 {
     if (!SV_FUSED_TAIL || ctx->nseg > kTailMaxSeg) return false;
     return !(4 * (int64_t)a.nb <= ctx->num_cu && ctx->nseg >= 16);
+}
+
+template <int PES, int QES>
+hipError_t token_single(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
+{
+    launch_fused_tail<PES, QES>(ctx, a, s, STAGE_TOKEN, 1);
+    return hipGetLastError();
 }
 
 template <int PES, int QES>
@@ -1370,6 +1441,20 @@ hipError_t launch_markov_verify_tail(sv_ctx *ctx, const VerifyArgs &a, const Mar
 {
     if (a.nb <= 0) return hipSuccess;
     return a.p_esize == 2 ? markov_verify_tail<2>(ctx, a, m, s) : markov_verify_tail<4>(ctx, a, m, s);
+}
+
+hipError_t launch_token_verify(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
+{
+    if (a.nb <= 0) return hipSuccess;
+    if (small_fits(ctx, a)) {
+        if (a.p_esize == 2 && a.q_esize == 2) return token_single<2, 2>(ctx, a, s);
+        if (a.p_esize == 2) return token_single<2, 4>(ctx, a, s);
+        if (a.q_esize == 2) return token_single<4, 2>(ctx, a, s);
+        return token_single<4, 4>(ctx, a, s);
+    }
+    const hipError_t e = launch_rowstats(ctx, a, s);
+    if (e != hipSuccess) return e;
+    return launch_token_tail(ctx, a, s);
 }
 
 hipError_t launch_token_tail(sv_ctx *ctx, const VerifyArgs &a, hipStream_t s)
