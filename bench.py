@@ -50,7 +50,7 @@ METRIC = "verified positions/s + HBM GB/s vs peak, B=256 gamma=7 V=129,280 bf16"
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rowstats_headline_traffic.json")
 ROWSTATS_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
-                    for f in ("rowstats.hip", "sv_device.h")]
+                    for f in ("rowstats.hip", "sv_rowstats.h", "sv_device.h")]
 MARKOV_COUNTERS_FILE = os.path.join(ROOT, "profiles", "markov_gemm_counters.json")
 MARKOV_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
                   for f in ("markov.hip", "sv_device.h")]
@@ -507,7 +507,7 @@ def bench_rnn(args, L, WL):
                  roof, kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
 
 
-def bench_block_async(args, L, WL):
+def bench_block_async(args, L, WL, side=None):
     """The block workload with temperature-scaled confidences and the scheduler run
     two steps ahead: at step k a second stream (own context) schedules from
     step k's head estimates the verify lengths that step k + 2 uses, while
@@ -529,7 +529,7 @@ def bench_block_async(args, L, WL):
     ctx = L.Context(0, B, gamma, V)
     sctx = L.Context(0, B, gamma, 1)         # the scheduler needs no vocabulary workspace
     main_s = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream() if side is None else side
 
     def schedule(k):                          # lengths for step k + 2 from step k's estimates
         side.wait_event(slot_free[k % 3])
@@ -622,19 +622,6 @@ def main():
             "tree": lambda: bench_tree(args, L, WL)}
     names = list(runs) if args.workload == "all" else [args.workload]
     for n in names:
-        if n == "block_async" and len(names) > 1:
-            # its cross-stream handoffs stall when earlier work in the same
-            # process has taken the hardware queues (measured 4x slower):
-            # it runs in a fresh child process
-            import subprocess
-            cmd = [sys.executable, os.path.abspath(__file__), "--workload", n, "--steps", str(args.steps),
-                   "--warmup", str(args.warmup), "--no-cpu-baseline"]
-            r = subprocess.run(cmd, capture_output=True, text=True)
-            if r.returncode != 0:
-                print(r.stderr, file=sys.stderr)
-                sys.exit(r.returncode)
-            print(r.stdout.strip().splitlines()[-1], flush=True)
-            continue
         line = runs[n]()
         if args.copy_probe and "copy_probe" not in line:
             line["copy_probe"] = _copy_probe()

@@ -181,7 +181,9 @@ sv_status spec_schedule_run(sv_ctx *ctx, hipStream_t stream, const float *conf,
  * takes it off the verification stream's critical path (the two-step-delayed
  * schedule of "DeepSeek Boosts Inference Speed by 85%", section "The Third
  * Ace", and "DSpark: DeepSeek's bet on speed that doesn't betray quality",
- * section "Verifying only what matters"). */
+ * section "Verifying only what matters").  Make that second stream
+ * non-blocking (hipStreamNonBlocking): a blocking stream also orders itself
+ * against the null stream, which serialises the handover. */
 sv_status spec_schedule_sts_run(sv_ctx *ctx, hipStream_t stream, const float *conf_logits,
                                 const float *temperatures, int B, int gamma, float sps_a, float sps_k,
                                 int32_t *verify_len, double *expected);
