@@ -98,56 +98,147 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline_and_parity(vi, offset, gpu, single_budget_s=3.0, chunk=4):
-    """The CPU oracle on every request of `vi` at round `offset`: timed on one
-    host thread over a bounded sample, then on a pool of threads over the
-    whole batch (logits converted to float64 beforehand, outside the timed
-    region); that result is walked against the GPU's outputs `gpu`."""
+def _oracle_pool(chunks, run, units_of, single_budget_s):
+    """Times `run` over `chunks`: on one thread over a bounded sample (until
+    `single_budget_s` of oracle time), then on a pool of host threads over
+    all of them.  Returns (results in order, pool wall s, threads, units done
+    by one thread, its seconds)."""
     import concurrent.futures
-    import numpy as np
-    import oracle
-    from lossless_draft_verification_02_amd import workloads as WL
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from oracle_pool import merge, workers
-    from parity import compare_verify
-
-    oracle.build(force=False)
-    chunks = []
-    for b0 in range(0, vi.B, chunk):
-        b1 = min(vi.B, b0 + chunk)
-        chunks.append((vi.p[b0:b1].float().cpu().double().numpy(), vi.q[b0:b1].float().cpu().double().numpy(),
-                       vi.draft[b0:b1].cpu().numpy(), np.arange(b0, b1, dtype=np.int32)))
-
-    def run(c):
-        p, q, x, rid = c
-        return oracle.token_verify(p, q, x, vi.gamma, temperature=vi.T, seed=WL.VERIFY_SEED, offset=offset,
-                                   req_ids=rid)
+    from oracle_pool import workers
 
     spent, done = 0.0, 0
     for c in chunks:
         t0 = time.perf_counter()
         run(c)
         spent += time.perf_counter() - t0
-        done += len(c[3])
+        done += units_of(c)
         if spent >= single_budget_s:
             break
-    n = workers()
+    n = min(workers(), len(chunks))   # a single chunk runs on one thread
     t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
-        parts = list(ex.map(run, chunks))
-    wall = time.perf_counter() - t0
+    if n == 1:
+        parts = [run(c) for c in chunks]
+    else:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+            parts = list(ex.map(run, chunks))
+    return parts, time.perf_counter() - t0, n, done, spent
+
+
+def _baseline_dict(units, wall, n, done, spent, unit, what):
+    return {"value": round(units / wall, 1), "unit": unit, "cores": n, "kind": "oracle",
+            "sample": f"{what} on {n} host threads, {wall:.2f} s wall; one thread: {done} positions in {spent:.2f} s",
+            "single_thread_value": round(done / spent, 1), "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_baseline_and_parity(vi, offset, gpu, single_budget_s=3.0, chunk=4, block=False, verify_len=None):
+    """The CPU oracle on every request of `vi` at round `offset` (token
+    verification, or block verification with `verify_len`): timed on one host
+    thread over a bounded sample, then on a pool of threads over the whole
+    batch (logits converted to float64 beforehand, outside the timed region);
+    that result is walked against the GPU's outputs `gpu`."""
+    import numpy as np
+    import oracle
+    from lossless_draft_verification_02_amd import workloads as WL
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_pool import merge
+    from parity import compare_verify
+
+    oracle.build(force=False)
+    vl = None if verify_len is None else np.asarray(verify_len, np.int32)
+    chunks = []
+    for b0 in range(0, vi.B, chunk):
+        b1 = min(vi.B, b0 + chunk)
+        chunks.append((vi.p[b0:b1].float().cpu().double().numpy(), vi.q[b0:b1].float().cpu().double().numpy(),
+                       vi.draft[b0:b1].cpu().numpy(), np.arange(b0, b1, dtype=np.int32),
+                       None if vl is None else vl[b0:b1]))
+    fn = oracle.block_verify if block else oracle.token_verify
+
+    def run(c):
+        p, q, x, rid, v = c
+        return fn(p, q, x, vi.gamma, temperature=vi.T, seed=WL.VERIFY_SEED, offset=offset, req_ids=rid,
+                  verify_len=v)
+
+    def units(c):
+        return int(c[4].sum()) if c[4] is not None else len(c[3]) * vi.gamma
+
+    parts, wall, n, done, spent = _oracle_pool(chunks, run, units, single_budget_s)
     orc = merge(parts)
-    rep = compare_verify(gpu, orc, vi.gamma, draft=vi.draft.cpu().numpy())
-    base = {"value": round(vi.B * vi.gamma / wall, 1), "unit": "verified positions/s", "cores": n,
-            "kind": "oracle",
-            "sample": f"all {vi.B} requests of the last timed step's batch and round (gamma={vi.gamma}, "
-                      f"V={vi.V}) on {n} host threads, {wall:.2f} s wall; one thread: {done} requests in "
-                      f"{spent:.2f} s",
-            "single_thread_value": round(done * vi.gamma / spent, 1),
-            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+    rep = compare_verify(gpu, orc, vi.gamma, verify_len=vl, block=block, draft=vi.draft.cpu().numpy())
+    total = int(vl.sum()) if vl is not None else vi.B * vi.gamma
+    base = _baseline_dict(total, wall, n, done, spent, "verified positions/s",
+                          f"all {vi.B} requests of the last timed step's batch and round "
+                          f"(gamma={vi.gamma}, V={vi.V}{', block verification' if block else ''})")
     parity = rep.as_dict()
     parity["failure_examples"] = [str(f) for f in rep.failures[:3]]
     return base, parity
+
+
+def cpu_baseline_and_parity_markov(mi, offset, draft, gpu, single_budget_s=3.0, chunk=2):
+    """The CPU oracle on every request of the markov workload at round
+    `offset`: the Markov-head draft (oracle sampler), then token verification
+    of the oracle's own draft against p with the oracle's fp64 draft logits;
+    timed as cpu_baseline_and_parity.  The GPU's drafts are walked against the
+    oracle's; its verification outputs against the oracle's on the requests
+    whose drafts agree."""
+    import numpy as np
+    import oracle
+    from lossless_draft_verification_02_amd import workloads as WL
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_pool import merge
+    from parity import compare_markov, compare_verify
+
+    oracle.build(force=False)
+    U = mi.U.float().cpu().double().numpy()
+    W = mi.W.float().cpu().double().numpy()
+    chunks = []
+    for b0 in range(0, mi.B, chunk):
+        b1 = min(mi.B, b0 + chunk)
+        chunks.append((mi.base[b0:b1].float().cpu().double().numpy(), mi.x0[b0:b1].cpu().numpy(),
+                       mi.p[b0:b1].float().cpu().double().numpy(), np.arange(b0, b1, dtype=np.int32)))
+
+    def run(c):
+        base, x0, p, rid = c
+        d = oracle.markov_draft(base, U, W, x0, temperature=mi.T, seed=WL.DRAFT_SEED, offset=offset, req_ids=rid)
+        v = oracle.token_verify(p, d.q_logits, d.draft, mi.gamma, temperature=mi.T, seed=WL.VERIFY_SEED,
+                                offset=offset, req_ids=rid)
+        d.q_logits = None   # the logits were only needed for the verification
+        return d, v
+
+    parts, wall, n, done, spent = _oracle_pool(chunks, run, lambda c: len(c[3]) * mi.gamma, single_budget_s)
+    od = merge([d for d, _ in parts])
+    ov = merge([v for _, v in parts])
+    rep = compare_markov(draft, None, None, od)
+    same = np.array([np.array_equal(od.draft[b], draft[b]) for b in range(mi.B)])
+    keep = np.flatnonzero(same)
+    rep2 = compare_verify({k: v[keep] for k, v in gpu.items()},
+                          type(ov)(*[getattr(ov, f)[keep] for f in ov.__dataclass_fields__]), mi.gamma)
+    base = _baseline_dict(mi.B * mi.gamma, wall, n, done, spent, "verified positions/s",
+                          f"all {mi.B} requests of the last timed step's round: Markov draft then verification "
+                          f"(gamma={mi.gamma}, V={mi.V}, R={mi.R})")
+    parity = {"draft": rep.as_dict(), "verify": rep2.as_dict(), "requests_with_equal_drafts": int(len(keep)),
+              "failure_examples": [str(f) for f in (rep.failures + rep2.failures)[:3]]}
+    return base, parity
+
+
+def _gpu_outputs(acc, out):
+    return {"accepted_len": acc.cpu().numpy().copy(), "out_tokens": out.cpu().numpy().copy()}
+
+
+def _diag_call(L, call, B, gamma, acc, out, gpu):
+    """One more call on the last timed step's inputs and round with every
+    diagnostic; returns whether its outputs equal the timed step's."""
+    import torch
+    diag = dict(lse_p=torch.empty(B, gamma + 1, device="cuda"), lse_q=torch.empty(B, max(gamma, 1), device="cuda"),
+                ratio=torch.empty(B, max(gamma, 1), device="cuda"), resid_mass=torch.empty(B, device="cuda"),
+                flags=torch.zeros(B, dtype=torch.int32, device="cuda"),
+                uniform=torch.empty(B, gamma + 1, device="cuda"))
+    call(diag)
+    torch.cuda.synchronize()
+    same = bool((acc.cpu().numpy() == gpu["accepted_len"]).all() and (out.cpu().numpy() == gpu["out_tokens"]).all())
+    gpu.update({k: v.cpu().numpy() for k, v in diag.items()})
+    gpu["flags"] = gpu["flags"].astype("uint32")
+    return same
 
 
 def _time_steps(step, warmup, steps):
@@ -241,18 +332,11 @@ def bench_headline(args, L, WL):
     # the last timed step's outputs, then one more call on the same inputs and
     # round with every diagnostic (its outputs must be the same)
     k_last = args.warmup + args.steps - 1
-    gpu = {"accepted_len": acc.cpu().numpy().copy(), "out_tokens": out.cpu().numpy().copy()}
+    gpu = _gpu_outputs(acc, out)
     s_last = sets[k_last % len(sets)]
-    diag = dict(lse_p=torch.empty(B, gamma + 1, device="cuda"), lse_q=torch.empty(B, gamma, device="cuda"),
-                ratio=torch.empty(B, gamma, device="cuda"), resid_mass=torch.empty(B, device="cuda"),
-                flags=torch.zeros(B, dtype=torch.int32, device="cuda"),
-                uniform=torch.empty(B, gamma + 1, device="cuda"))
-    L.spec_verify_run(ctx, s_last.p, s_last.q, s_last.draft, acc, out, temperature=s_last.T, seed=WL.VERIFY_SEED,
-                      offset=k_last, diag=diag)
-    torch.cuda.synchronize()
-    same = bool((acc.cpu().numpy() == gpu["accepted_len"]).all() and (out.cpu().numpy() == gpu["out_tokens"]).all())
-    gpu.update({k: v.cpu().numpy() for k, v in diag.items()})
-    gpu["flags"] = gpu["flags"].astype("uint32")
+    same = _diag_call(L, lambda d: L.spec_verify_run(ctx, s_last.p, s_last.q, s_last.draft, acc, out,
+                                                     temperature=s_last.T, seed=WL.VERIFY_SEED, offset=k_last,
+                                                     diag=d), B, gamma, acc, out, gpu)
     # bytes of the timed steps: every verified row once, plus the rows each
     # request's draw re-reads (p and q row tau+1 after a rejection, the bonus
     # row alone otherwise)
@@ -307,12 +391,25 @@ def bench_token(args, L, WL, name, nsets):
         L.spec_verify_run(ctx, s.p, s.q, s.draft, acc, out, temperature=s.T, seed=WL.VERIFY_SEED, offset=k)
 
     ms, _ = _time_steps(step, args.warmup, args.steps)
+    k_last = args.warmup + args.steps - 1
+    gpu = _gpu_outputs(acc, out)
+    s_last = sets[k_last % len(sets)]
+    same = _diag_call(L, lambda d: L.spec_verify_run(ctx, s_last.p, s_last.q, s_last.draft, acc, out,
+                                                     temperature=s_last.T, seed=WL.VERIFY_SEED, offset=k_last,
+                                                     diag=d), B, gamma, acc, out, gpu)
+    accepted = float(gpu["accepted_len"][gpu["accepted_len"] >= 0].mean())
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     ctx.close()
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline_and_parity(s_last, k_last, gpu)
+        parity["diag_call_outputs_equal_timed"] = same
     return _line(f"verified positions/s, {WL.describe(name)}", B * gamma / (ms / 1e3), "verified positions/s",
                  args, ms, {"workload": f"token-level verification, {name} batch", "B": B, "gamma": gamma, "V": V,
                             "logits": str(vi.p.dtype).split(".")[-1], "temperature": vi.T, "input_sets": nsets},
-                 _token_roofline(prof, vi, WL),
+                 _token_roofline(prof, vi, WL), cpu_baseline=cpu, parity=parity,
+                 mean_accepted_last_step=round(accepted, 4),
+                 emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  us_per_call=round(ms * 1e3, 2),
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
 
@@ -345,6 +442,14 @@ def bench_block(args, L, WL):
                                conf=s.conf, sps_a=2000.0, sps_k=4096.0, verify_len_out=vlen)
 
     ms, _ = _time_steps(step, args.warmup, args.steps)
+    k_last = args.warmup + args.steps - 1
+    gpu = _gpu_outputs(acc, out)
+    vl_last = vlen.cpu().numpy().copy()
+    s_last = sets[k_last % len(sets)]
+    same = _diag_call(L, lambda d: L.spec_blockverify_run(ctx, s_last.p, s_last.q, s_last.draft, acc, out,
+                                                          temperature=s_last.T, seed=WL.VERIFY_SEED, offset=k_last,
+                                                          verify_len=vlen, diag=d), B, gamma, acc, out, gpu)
+    accepted = float(gpu["accepted_len"][gpu["accepted_len"] >= 0].mean())
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     # verified positions: what the scheduler admitted (the same for every step of a set)
     admitted = []
@@ -353,6 +458,13 @@ def bench_block(args, L, WL):
         torch.cuda.synchronize()
         admitted.append(vlen.cpu().numpy().astype("int64"))
     ctx.close()
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        import oracle
+        ovl, _, _ = oracle.schedule(s_last.conf.double().cpu().numpy(), 2000.0, 4096.0)
+        cpu, parity = cpu_baseline_and_parity(s_last, k_last, gpu, block=True, verify_len=ovl)
+        parity["scheduler_lengths_equal_oracle"] = bool((ovl == vl_last).all())
+        parity["diag_call_outputs_equal_timed"] = same
     positions = sum(float(x.sum()) for x in admitted) / len(admitted)
     rows = sum(float((2 * x + 1).sum()) for x in admitted) / len(admitted)
     alg = rows * V * vi.p.element_size()
@@ -360,8 +472,9 @@ def bench_block(args, L, WL):
                  positions / (ms / 1e3), "verified positions/s", args, ms,
                  {"workload": "block verification driven by the confidence scheduler", "B": B, "gamma": gamma,
                   "V": V, "logits": "bf16", "sps": "2000/(1+n/4096)", "input_sets": len(sets)},
-                 _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats")),
-                 mean_verify_len=round(positions / B, 4),
+                 _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats")), cpu_baseline=cpu, parity=parity,
+                 mean_verify_len=round(positions / B, 4), mean_accepted_last_step=round(accepted, 4),
+                 emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
 
 
@@ -390,6 +503,15 @@ def bench_markov(args, L, WL):
         L.spec_verify_run(ctx, mi.p, ql, draft, acc, out, temperature=mi.T, seed=WL.VERIFY_SEED, offset=k)
 
     ms, _ = _time_steps(step, args.warmup, args.steps)
+    k_last = args.warmup + args.steps - 1
+    gpu = _gpu_outputs(acc, out)
+    draft_last = draft.cpu().numpy().copy()
+    same = _diag_call(L, lambda d: L.markov_verify_run(ctx, mi.base, mi.U, mi.Wt, mi.x0, mi.p, draft, acc, out,
+                                                       lse_q=lse, temperature=mi.T, draft_seed=WL.DRAFT_SEED,
+                                                       verify_seed=WL.VERIFY_SEED, offset=k_last, diag=d),
+                      B, gamma, acc, out, gpu)
+    same = same and bool((draft.cpu().numpy() == draft_last).all())
+    accepted = float(gpu["accepted_len"][gpu["accepted_len"] >= 0].mean())
     prof = _profile_steps(L, ctx, step, args.warmup + args.steps, args.steps)
     ms2 = None
     if not args.fused_only:
@@ -411,12 +533,18 @@ def bench_markov(args, L, WL):
     if cnt:
         roof["traffic"] = cnt.get("hbm_bytes_per_launch")
         roof["mfma_busy_frac_counters"] = cnt.get("mfma_busy_frac")
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline_and_parity_markov(mi, k_last, draft_last, gpu)
+        parity["diag_call_outputs_equal_timed"] = same
     return _line("verified positions/s, B=128 gamma=8 V=129,280, Markov-head draft + verification",
                  B * gamma / (ms / 1e3), "verified positions/s", args, ms,
                  {"workload": "Markov-head draft sampling (R=256), then token verification of that draft "
                               "(p bf16; fused: no fp32 draft logits stored)",
                   "B": B, "gamma": gamma, "V": V, "R": R},
-                 roof, kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
+                 roof, cpu_baseline=cpu, parity=parity, mean_accepted_last_step=round(accepted, 4),
+                 emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
+                 kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  markov_ms_per_call=round((prof["markov_gemm"][0] + prof["markov_select"][0]) / args.steps, 4),
                  two_call_ms_per_step=None if ms2 is None else round(ms2, 5),
                  two_call_verified_positions_per_s=None if ms2 is None else round(B * gamma / (ms2 / 1e3), 1))
