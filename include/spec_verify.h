@@ -279,7 +279,10 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream,
  * each draft row's normaliser and the drafted tokens' logits; the one draft
  * row per request that the residual max(p - q, 0) needs (position tau + 1) is
  * rebuilt after the acceptance scan with the sampler's own arithmetic, so it
- * equals the row the token was drawn from.  Decisions equal those of
+ * equals the row the token was drawn from, and weighed as it is built: the
+ * correction / bonus weights are summed per 128-token tile and the token is
+ * drawn from those sums and the chosen tile's weights (rebuilt again the same
+ * way), so no draft row is ever stored.  Decisions equal those of
  * markov_draft_run then spec_verify_run up to the fp32 rounding of the draft
  * normalisers (the two paths sum them in different orders).
  *   base_logits [B, gamma, V] bf16; U, Wt [V, R] bf16 (16-byte aligned);
@@ -337,7 +340,7 @@ typedef enum {
     SV_KERNEL_SCHEDULE = 6,      /* prefix scheduler                                     */
     SV_KERNEL_MARKOV_GEMM = 7,   /* Markov / RNN head contraction + epilogue (per position) */
     SV_KERNEL_MARKOV_SELECT = 8, /* Markov / RNN head draw (+ RNN state update), per position */
-    SV_KERNEL_MARKOV_REBUILD = 9,/* fused path: correction rows rebuilt after the scan   */
+    SV_KERNEL_MARKOV_REBUILD = 9,/* fused path: correction rows rebuilt and weighed per tile */
     SV_KERNEL_COUNT = 10
 } sv_kernel;
 

@@ -110,7 +110,6 @@ svh::VerifyArgs make_args(const void *p, sv_dtype pd, const void *q, sv_dtype qd
     a.block = block;
     a.q_lse2 = nullptr;
     a.q_zx = nullptr;
-    a.qrec = nullptr;
     a.np_rows = 0;
     a.nq_rows = 0;
     return a;
@@ -653,13 +652,13 @@ sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream, const void *base_lo
     m.zx_out = ctx->ws.mk_zx;
     if ((st = check_launch(svh::launch_markov(ctx, m, stream), "Markov sampler")) != SV_OK) return st;
     // 2. verification of that draft: row statistics of p only, the scan with
-    //    the sampler's q statistics, the correction rows rebuilt, the draw
+    //    the sampler's q statistics, the correction / bonus weights of the
+    //    rebuilt correction rows summed per tile, the draw
     svh::VerifyArgs a = make_args(p_logits, p_dtype, nullptr, SV_F32, draft_tokens, nullptr, B, gamma, V,
                                   temperature, verify_seed, offset, nullptr, accepted_len, out_tokens, diag, false);
     a.q_esize = 4;
     a.q_lse2 = ctx->ws.mk_lse2;
     a.q_zx = ctx->ws.mk_zx;
-    a.qrec = ctx->ws.mk_q;
     if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
     if ((st = check_launch(svh::launch_markov_verify_tail(ctx, a, m, stream), "fused verification")) != SV_OK)
         return st;

@@ -279,20 +279,106 @@ __device__ __forceinline__ uint2 base_quad(const uint16_t *brow, int n, int Vi, 
     return r;
 }
 
-// Position k of every request (req == null), or position tau + 1 of each
-// request whose scan ended in a rejection (req != null: the correction rows of
-// the fused draft -> verification path; other requests are skipped).  zout
-// may be null (no z rows stored) and tile_part may be null (no softmax pairs).
+// Weight of one token in the correction / bonus draw of the fused
+// verification ("Speculative Decoding: The Same Distribution, Twice as Fast",
+// section 4: after a rejection the token comes from max(p - q, 0)
+// normalised, after a full pass from p): with xp the target logit, z the
+// draft logit and lp2, lq2 the rows' log2-sum-exp2 of x * c,
+// w = max(wmul * 2^(xp c - lp2) - 2^(z c - lq2), 0), or 2^(xp c - lp2) for
+// the bonus (mode 1).  The contraction's residual epilogue and the draw
+// weigh a token through this one function, so their weights agree bit for
+// bit.
+__device__ __forceinline__ float resid_weight(float xp, float z, int mode, float wmul, float lp2, float lq2,
+                                              float c)
+{
+    const float pw = svk::fast_exp2(__builtin_fmaf(xp, c, -lp2));
+    if (mode) return pw;
+    const float qw = svk::fast_exp2(__builtin_fmaf(z, c, -lq2));
+    const float d = wmul * pw - qw;
+    return d > 0.0f ? d : 0.0f;
+}
+
+// Four consecutive target logits n .. n + 3 of a p row (bf16 or fp32), as
+// floats; -inf past V or for a null row.
+template <int PES>
+struct PQuad {
+    typedef typename std::conditional<PES == 2, uint2, uint4>::type T;
+};
+template <int PES>
+__device__ __forceinline__ typename PQuad<PES>::T p_quad(const char *prow, int n, int Vi, int vec)
+{
+    typename PQuad<PES>::T r;
+    if constexpr (PES == 2) {
+        r = make_uint2(0xFF80FF80u, 0xFF80FF80u);
+        if (prow) {
+            const uint16_t *row = (const uint16_t *)prow;
+            if (vec) {
+                if (n < Vi) r = *(const uint2 *)(row + n);
+            } else {
+                uint16_t e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) e[q] = n + q < Vi ? row[n + q] : (uint16_t)0xFF80u;
+                r = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
+            }
+        }
+    } else {
+        const uint32_t ninf = 0xFF800000u;
+        r = make_uint4(ninf, ninf, ninf, ninf);
+        if (prow) {
+            const uint32_t *row = (const uint32_t *)prow;
+            if (vec) {
+                if (n < Vi) r = *(const uint4 *)(row + n);
+            } else {
+                uint32_t e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) e[q] = n + q < Vi ? row[n + q] : ninf;
+                r = make_uint4(e[0], e[1], e[2], e[3]);
+            }
+        }
+    }
+    return r;
+}
+template <int PES>
+__device__ __forceinline__ void p_quad_floats(const typename PQuad<PES>::T &v, float (&x)[4])
+{
+    if constexpr (PES == 2) {
+        x[0] = __uint_as_float(v.x << 16);
+        x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(v.y << 16);
+        x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    } else {
+        x[0] = __uint_as_float(v.x);
+        x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z);
+        x[3] = __uint_as_float(v.w);
+    }
+}
+
+// Residual mode of the contraction (the fused verification's correction /
+// bonus rows): the target rows and the per-(request, tile) weight sums.
+struct ResidArgs {
+    const void *p;   // [B, gamma + 1, V] target logits
+    float *tsum;     // [B, ntile] sums of resid_weight over each tile
+};
+
+// Draft mode (RES = 0): position k of every request; zout may be null (no z
+// rows stored) and tile_part may be null (no softmax pairs).
+// Residual mode (RES = the target logits' element size, 2 or 4): position
+// tau + 1 of each request in req, the acceptance scan's results; every
+// request it left without an error flag contributes its correction / bonus
+// weights resid_weight over row tau + 1, summed per 128-token tile into
+// ra.tsum; the contraction runs only for the requests that rejected (a bonus
+// row needs p alone), and no z is stored.
 //
 // Per tile: wait for the tile's copy, barrier, request the next tile's copy
 // and base logits, then the MFMAs with the next k-step's A fragments read
 // from LDS while the current k-step's run; per output the k-steps accumulate
 // in ascending order (the draw rebuilds its chosen tile the same way).
-template <int R>
+template <int R, int RES>
 __global__ __launch_bounds__(NT, GemmShape<R>::MINB)
 void k_markov_gemm(
     svh::MarkovArgs a, int k, const svh::ReqG *__restrict__ req, float *__restrict__ zout, int64_t zstride,
-    float2 *__restrict__ tile_part, int ntile, int vec)
+    float2 *__restrict__ tile_part, int ntile, int vec, ResidArgs ra, int pvec)
 {
     using TL = TileLayout<R>;
     using GS = GemmShape<R>;
@@ -313,15 +399,33 @@ void k_markov_gemm(
     int m[G], km[G];
     bool act[G];
     const uint16_t *brow[G];   // base row of (request, position); null reads -inf
+    // residual mode: the request's target row tau + 1 (null: no weights) and
+    // its weight parameters
+    [[maybe_unused]] const char *prow[G];
+    [[maybe_unused]] float rmul[G], rlp2[G], rlq2[G];
+    [[maybe_unused]] int rmode[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
         m[g] = blockIdx.y * MC + q0 + 16 * g + li;     // the lane's requests (B operand columns)
         km[g] = k;                                      // and their positions
         act[g] = m[g] < a.B;
-        if (req && act[g]) {
-            const svh::ReqG r = req[m[g]];
-            act[g] = r.flags == 0 && r.mode == 0;
-            km[g] = r.tau + 1;
+        if constexpr (RES != 0) {
+            prow[g] = nullptr;
+            rmode[g] = 1;
+            rmul[g] = 1.0f;
+            rlp2[g] = rlq2[g] = 0.0f;
+            if (act[g]) {
+                const svh::ReqG r = req[m[g]];
+                act[g] = r.flags == 0 && r.mode == 0;
+                km[g] = r.tau + 1;
+                if (r.flags == 0) {
+                    prow[g] = (const char *)ra.p + ((int64_t)m[g] * (a.gamma + 1) + r.tau) * a.V * RES;
+                    rmode[g] = r.mode;
+                    rmul[g] = r.wmul;
+                    rlp2[g] = r.lp2;
+                    rlq2[g] = r.lq2;
+                }
+            }
         }
         brow[g] = act[g] ? base_row(a, km[g], m[g]) : nullptr;
     }
@@ -341,13 +445,20 @@ void k_markov_gemm(
     // G > 1: the softmax pair of (request, tile) from the row parts' partials,
     // written by the row-part-0 wavefronts once a barrier has passed
     auto merge_parts = [&](int par, int t) {
-        if (G > 1 && tile_part && rp == 0 && lane < 16 * G) {
+        if (G > 1 && (RES != 0 || tile_part) && rp == 0 && lane < 16 * G) {
             const int mm = blockIdx.y * MC + q0 + lane;
             if (mm < a.B) {
-                svk::MS v = parts[(par * G + 0) * MC + q0 + lane];
+                if constexpr (RES != 0) {
+                    float v = parts[(par * G + 0) * MC + q0 + lane].s;
 #pragma unroll
-                for (int r = 1; r < G; ++r) v = svk::ms_merge(v, parts[(par * G + r) * MC + q0 + lane]);
-                tile_part[(int64_t)mm * ntile + t] = make_float2(v.m, v.s);
+                    for (int r = 1; r < G; ++r) v += parts[(par * G + r) * MC + q0 + lane].s;
+                    ra.tsum[(int64_t)mm * ntile + t] = v;
+                } else {
+                    svk::MS v = parts[(par * G + 0) * MC + q0 + lane];
+#pragma unroll
+                    for (int r = 1; r < G; ++r) v = svk::ms_merge(v, parts[(par * G + r) * MC + q0 + lane]);
+                    tile_part[(int64_t)mm * ntile + t] = make_float2(v.m, v.s);
+                }
             }
         }
     };
@@ -393,6 +504,15 @@ void k_markov_gemm(
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int j = 0; j < VBW; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // residual mode: this tile's target logits, consumed by the epilogue
+        typename PQuad<RES == 4 ? 4 : 2>::T pq[G][VBW];
+        if constexpr (RES != 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int j = 0; j < VBW; ++j)
+                    pq[g][j] = p_quad<RES>(prow[g], tile * TN + 16 * (vb0 + j) + 4 * lg, Vi, pvec);
+        }
         // A fragments: with G > 1 the next k-step's are read while the
         // current k-step's MFMAs run (registers allow it at one workgroup per
         // CU); with G = 1 each k-step reads its own
@@ -511,7 +631,48 @@ void k_markov_gemm(
                 }
             }
         };
-        if (G > 1 && n0 + TN <= Vi && !zout)
+        // residual mode: the weights of the lane's tokens, summed per request
+        // over the wavefront's rows of the tile
+        auto resid_epilogue = [&]() {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float sm = 0.0f;
+#pragma unroll
+                for (int j = 0; j < VBW; ++j) {
+                    const int n = n0 + 16 * (vb0 + j) + 4 * lg;
+                    float xp[4];
+                    p_quad_floats<RES == 4 ? 4 : 2>(pq[g][j], xp);
+                    const uint32_t b01 = bv[g][j].x, b23 = bv[g][j].y;
+                    float z[4];
+                    z[0] = acc[g][j][0] + __uint_as_float(b01 << 16);
+                    z[1] = acc[g][j][1] + __uint_as_float(b01 & 0xFFFF0000u);
+                    z[2] = acc[g][j][2] + __uint_as_float(b23 << 16);
+                    z[3] = acc[g][j][3] + __uint_as_float(b23 & 0xFFFF0000u);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < Vi) sm += resid_weight(xp[r], z[r], rmode[g], rmul[g], rlp2[g], rlq2[g], a.c);
+                }
+                if (G > 1) {
+                    // the next tile's loads, as in the softmax epilogue
+#pragma unroll
+                    for (int pt = 0; pt < 4; ++pt) {
+                        const int e = 4 * g + pt;
+                        if ((e * 8) % (4 * G) == 0) issue(8 + e * 8 / (4 * G));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                sm = rows4_sum(sm);
+                if (lg == 0) {
+                    if (G > 1)
+                        parts[((it & 1) * G + rp) * MC + q0 + 16 * g + li] = svk::MS{0.0f, sm};
+                    else if (m[g] < a.B)
+                        ra.tsum[(int64_t)m[g] * ntile + tile] = sm;
+                }
+            }
+        };
+        if constexpr (RES != 0)
+            resid_epilogue();
+        else if (G > 1 && n0 + TN <= Vi && !zout)
             epilogue(std::true_type{});
         else
             epilogue(std::false_type{});
@@ -522,7 +683,7 @@ void k_markov_gemm(
                 for (int j = 0; j < VBW; ++j) bv[g][j] = bn[g][j];
         }
     }
-    if (G > 1 && tile_part) {
+    if (G > 1 && (RES != 0 || tile_part)) {
         // the last tile's partials
         const int it = (ntile - 1 - (int)blockIdx.x) / (int)gridDim.x;   // index of the workgroup's last tile
         svk::lds_barrier();
@@ -837,6 +998,247 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Correction / bonus draw of the fused draft -> verification path, from the
+// residual mode's tile sums.  One workgroup of four wavefronts per request
+// the acceptance scan left without an error flag (a flagged request's outputs
+// are already written):
+//   tile choice   thread t holds tile sums [t per, (t + 1) per); fp64 prefix
+//                 (thread runs, then a deterministic block scan) and total Z;
+//                 the first tile whose cumulative sum, rounded to binary32,
+//                 exceeds fp32(u' * fp32(Z)), else the last tile with weight
+//                 (inverse CDF in ascending token order, as the oracle's);
+//   the tile      its 128 weights with the residual epilogue's arithmetic:
+//                 the draft logits rebuilt by MFMA as the Markov draw does
+//                 (same Wt rows, same k order, same base add), the target
+//                 logits read back, both weighed by resid_weight;
+//   the token     wavefront 0: fp64 prefix of the weights from the mass
+//                 before the tile, the first token past the threshold, else
+//                 the tile's last token with weight.
+// A residual whose mass rounds to zero (Z <= 0 after a rejection; in exact
+// arithmetic a rejection implies p != q) falls back to the p row: the
+// workgroup sums p's tile weights itself (rare; one pass over the row) and
+// draws from them, flagging SV_FLAG_RESID_ZERO.
+// ---------------------------------------------------------------------------
+struct ResidSel {
+    double Z;       // total weight
+    float tf;       // fp32(u * fp32(Z))
+    double tbase;   // cumulative weight before the chosen tile
+    int ts;         // chosen tile
+    int fallback;   // no cumulative weight exceeded tf: the last token with weight
+};
+
+// Tile choice over the tile sums ts[0 .. ntile) (global or LDS) by the whole
+// workgroup; every thread returns the same result, false when no tile has
+// weight.
+__device__ bool choose_resid_tile(const float *ts_sum, int ntile, float u, DrawLDS &L, ResidSel &st)
+{
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int per = (ntile + kDrawThreads - 1) / kDrawThreads;
+    const int t0 = t * per;
+    float wt[kDrawTilesPerThread];
+    double loc = 0.0;
+#pragma unroll
+    for (int q = 0; q < kDrawTilesPerThread; ++q) {
+        wt[q] = (q < per && t0 + q < ntile) ? ts_sum[t0 + q] : 0.0f;
+        loc += (double)wt[q];
+    }
+    double Z;
+    const double excl = svk::block_exclusive_scan_d<kDrawThreads>(loc, L.scan, &Z);
+    const float tf = __fmul_rn(u, (float)Z);
+    int first = 0x7FFFFFFF, last = -1;
+    double firstb = 0.0, lastb = 0.0;
+    {
+        double run = excl;
+#pragma unroll
+        for (int q = 0; q < kDrawTilesPerThread; ++q) {
+            if (wt[q] > 0.0f) {
+                const double before = run;
+                run += (double)wt[q];
+                last = t0 + q;
+                lastb = before;
+                if (first == 0x7FFFFFFF && (float)run > tf) {
+                    first = t0 + q;
+                    firstb = before;
+                }
+            }
+        }
+    }
+    {
+        const uint64_t hasf = __ballot(first != 0x7FFFFFFF), hasl = __ballot(last >= 0);
+        const int lf = hasf ? __builtin_ctzll(hasf) : 0;
+        const int ll = hasl ? 63 - __builtin_clzll(hasl) : 0;
+        const int fw = __shfl(first, lf, 64), lw = __shfl(last, ll, 64);
+        const double fbw = __shfl(firstb, lf, 64), lbw = __shfl(lastb, ll, 64);
+        if (lane == 0) {
+            L.wfirst[wid] = hasf ? fw : 0x7FFFFFFF;
+            L.wfirstb[wid] = fbw;
+            L.wlast[wid] = hasl ? lw : -1;
+            L.wlastb[wid] = lbw;
+        }
+    }
+    __syncthreads();
+    int ts = 0x7FFFFFFF, tl = -1;
+    double tb = 0.0, tlb = 0.0;
+#pragma unroll
+    for (int w = 0; w < kDrawWaves; ++w) {
+        if (ts == 0x7FFFFFFF && L.wfirst[w] != 0x7FFFFFFF) {
+            ts = L.wfirst[w];
+            tb = L.wfirstb[w];
+        }
+        if (L.wlast[w] >= 0) {
+            tl = L.wlast[w];
+            tlb = L.wlastb[w];
+        }
+    }
+    __syncthreads();   // L is reused by a second choice
+    const bool fallback = ts == 0x7FFFFFFF;
+    st.Z = Z;
+    st.tf = tf;
+    st.tbase = fallback ? tlb : tb;
+    st.ts = fallback ? tl : ts;
+    st.fallback = fallback;
+    return tl >= 0 && Z > 0.0;
+}
+
+// The sum of p's tile weights 2^(xp c - lp2) of every tile into out[] (LDS),
+// by the whole workgroup: wavefront w takes tiles w, w + 4, ...; lane l
+// weighs tokens 2 l and 2 l + 1 of the tile.
+template <int PES>
+__device__ void p_tile_sums(const char *prow, float lp2, float c, int64_t V, int ntile, float *out)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int tl = wid; tl < ntile; tl += kDrawWaves) {
+        const int64_t c0 = (int64_t)tl * TN;
+        float w = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t n = c0 + 2 * lane + h;
+            if (n < V) w += resid_weight(svk::load_logit<PES>(prow, n), 0.0f, 1, 1.0f, lp2, 0.0f, c);
+        }
+        w = svk::wave_sum(w);
+        if (lane == 0) out[tl] = w;
+    }
+}
+
+template <int R, int PES>
+__global__ __launch_bounds__(kDrawThreads) void k_markov_resid_draw(svh::MarkovArgs a, svh::VerifyArgs v,
+                                                                    const svh::ReqG *__restrict__ req,
+                                                                    const float *__restrict__ tsum, int ntile,
+                                                                    uint32_t *__restrict__ errword)
+{
+    constexpr int KS = R / 32;
+    constexpr int VBW = NVB / kDrawWaves;   // 16-row blocks per wavefront
+    __shared__ DrawLDS L;
+    __shared__ float wtile[TN];                  // the chosen tile's weights
+    __shared__ float alt[svh::kMarkovMaxTiles];  // p's tile sums (zero-residual fallback)
+    const int b = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const svh::ReqG r = req[b];
+    if (r.flags) return;   // the acceptance scan wrote the request's outputs
+    const int G1 = a.gamma + 1;
+    const int k = r.tau + 1;   // the draft position of the correction row
+    const char *prow = (const char *)v.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
+    bf16x8 ufr[KS];
+    head_fragments<R>(a, k, b, lg, r.mode == 0, ufr);   // requested before the tile choice
+
+    int mode = r.mode;
+    float wmul = r.wmul;
+    uint32_t flags = 0;
+    ResidSel st;
+    bool ok = choose_resid_tile(tsum + (int64_t)b * ntile, ntile, r.u2, L, st);
+    if (!ok && mode == 0) {
+        flags |= SV_FLAG_RESID_ZERO;
+        mode = 1;
+        wmul = 1.0f;
+        p_tile_sums<PES>(prow, r.lp2, a.c, a.V, ntile, alt);
+        __syncthreads();
+        ok = choose_resid_tile(alt, ntile, r.u2, L, st);
+    }
+    int32_t y = -1;
+    if (ok) {
+        const int64_t c0 = (int64_t)st.ts * TN;
+        const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
+        if (mode == 0) {
+            bf16x8 afr[VBW][KS];
+#pragma unroll
+            for (int vb = 0; vb < VBW; ++vb) {
+                const int64_t n = c0 + 16 * (VBW * wid + vb) + li;
+                const uint16_t *wrow = a.W + (n < a.V ? n : a.V - 1) * R + 8 * lg;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) afr[vb][s] = *(const bf16x8 *)(wrow + 32 * s);
+            }
+            // base and target logits of the lane's outputs, requested with
+            // the A rows (an in-row address for every column)
+            const uint16_t *brow = a.base + ((int64_t)b * a.gamma + (k - 1)) * a.V + c0;
+            uint32_t bbits[VBW][4];
+            float xp[VBW][4];
+#pragma unroll
+            for (int vb = 0; vb < VBW; ++vb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = 16 * (VBW * wid + vb) + 4 * lg + q;
+                    const int cc = col < ncols ? col : 0;
+                    bbits[vb][q] = brow[cc];
+                    xp[vb][q] = svk::load_logit<PES>(prow, c0 + cc);
+                }
+#pragma unroll
+            for (int vb = 0; vb < VBW; ++vb) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[vb][s], ufr[s], acc, 0, 0, 0);
+                if (li == 0) {   // D[4 lg + q][0]: vocabulary row 16 vb + 4 lg + q of the tile
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = 16 * (VBW * wid + vb) + 4 * lg + q;
+                        const float z = acc[q] + __uint_as_float(bbits[vb][q] << 16);
+                        wtile[col] = col < ncols ? resid_weight(xp[vb][q], z, 0, wmul, r.lp2, r.lq2, a.c) : 0.0f;
+                    }
+                }
+            }
+        } else if (t < TN) {
+            wtile[t] = t < ncols ? resid_weight(svk::load_logit<PES>(prow, c0 + t), 0.0f, 1, wmul, r.lp2, r.lq2, a.c)
+                                 : 0.0f;
+        }
+        svk::lds_barrier();
+        if (wid == 0) {
+            const int j0 = 2 * lane, j1 = 2 * lane + 1;
+            const float w0 = wtile[j0], w1 = wtile[j1];
+            const double pair = (double)w0 + (double)w1;
+            const double pincl = svk::wave_inclusive_scan_d(pair);
+            const double pexcl = pincl - pair;
+            int yb = 0x7FFFFFFF, yl = -1;
+            if (w1 > 0.0f) {
+                yl = j1;
+                if (!st.fallback && (float)(st.tbase + pexcl + (double)w0 + (double)w1) > st.tf) yb = j1;
+            }
+            if (w0 > 0.0f) {
+                if (yl < 0) yl = j0;
+                if (!st.fallback && (float)(st.tbase + pexcl + (double)w0) > st.tf) yb = j0;
+            }
+            const int ybest = wave_min_i(yb);
+            const int ylast = wave_max_i(yl);
+            const int j = ybest != 0x7FFFFFFF ? ybest : ylast;
+            y = j >= 0 ? (int32_t)(c0 + j) : -1;
+        }
+    }
+    if (wid != 0) return;
+    if (y < 0) flags |= SV_FLAG_BAD_ROW;   // unreachable for a valid row: p sums to 1
+    // x_1 .. x_tau, the drawn token, then -1 (all -1 and length -1 if none)
+    const int64_t ob = (int64_t)b * G1;
+    for (int j = lane; j < G1; j += 64)
+        v.out_tokens[ob + j] =
+            y < 0 ? -1 : (j < r.tau ? a.draft[(int64_t)b * a.gamma + j] : (j == r.tau ? y : -1));
+    if (lane == 0) {
+        v.accepted_len[b] = y < 0 ? -1 : r.tau;
+        if (v.diag.flags) v.diag.flags[b] = flags;
+        if (v.diag.resid_mass) v.diag.resid_mass[b] = (float)st.Z;
+        if (flags) atomicOr(errword, flags);
+    }
+}
+
 template <int R>
 hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s)
 {
@@ -854,8 +1256,8 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
     for (int k = 1; k <= a.gamma; ++k) {
         float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        hipLaunchKernelGGL((k_markov_gemm<R>), dim3(gx, gy), dim3(NT), 0, s, a, k, (const svh::ReqG *)nullptr, zk,
-                           zstride, ctx->ws.mk_part, ntile, vec);
+        hipLaunchKernelGGL((k_markov_gemm<R, 0>), dim3(gx, gy), dim3(NT), 0, s, a, k, (const svh::ReqG *)nullptr,
+                           zk, zstride, ctx->ws.mk_part, ntile, vec, ResidArgs{nullptr, nullptr}, 0);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
         hipLaunchKernelGGL((k_markov_draw<R>), dim3(a.B), dim3(kDrawThreads), 0, s, a, k, (const float *)zk, zstride,
@@ -865,8 +1267,9 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
     return hipGetLastError();
 }
 
-template <int R>
-hipError_t launch_rebuild(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::ReqG *req, float *qrec, hipStream_t s)
+template <int R, int PES>
+hipError_t launch_resid(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::VerifyArgs &v, const svh::ReqG *req,
+                        hipStream_t s)
 {
     const int ntile = ctx->ntile;
     const int gy = (a.B + MC - 1) / MC;
@@ -874,28 +1277,43 @@ hipError_t launch_rebuild(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::ReqG
     const int per_cu = lds <= 80 * 1024 ? 2 : 1;
     int gx = ctx->num_cu * per_cu / gy;
     gx = gx < 1 ? 1 : (gx > ntile ? ntile : gx);
-    const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0) && ((((uintptr_t)qrec) & 15) == 0);
-    const int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_REBUILD);
-    hipLaunchKernelGGL((k_markov_gemm<R>), dim3(gx, gy), dim3(NT), 0, s, a, 0, req, qrec, a.V, (float2 *)nullptr,
-                       ntile, vec);
+    const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0);
+    const int pvec = (a.V % 4 == 0) && ((((uintptr_t)v.p) & (4 * PES - 1)) == 0);
+    // the draft's tile pairs are consumed: their buffer holds the tile sums
+    float *tsum = (float *)ctx->ws.mk_part;
+    int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_REBUILD);
+    hipLaunchKernelGGL((k_markov_gemm<R, PES>), dim3(gx, gy), dim3(NT), 0, s, a, 0, req, (float *)nullptr, a.V,
+                       (float2 *)nullptr, ntile, vec, ResidArgs{v.p, tsum}, pvec);
+    svh::prof_end(ctx, s, slot);
+    slot = svh::prof_begin(ctx, s, SV_KERNEL_SELECT);
+    hipLaunchKernelGGL((k_markov_resid_draw<R, PES>), dim3(a.B), dim3(kDrawThreads), 0, s, a, v, req,
+                       (const float *)tsum, ntile, ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
     return hipGetLastError();
+}
+
+template <int PES>
+hipError_t launch_resid_rank(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::VerifyArgs &v, const svh::ReqG *req,
+                             hipStream_t s)
+{
+    switch (a.R) {
+    case 32: return launch_resid<32, PES>(ctx, a, v, req, s);
+    case 64: return launch_resid<64, PES>(ctx, a, v, req, s);
+    case 128: return launch_resid<128, PES>(ctx, a, v, req, s);
+    case 256: return launch_resid<256, PES>(ctx, a, v, req, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 namespace svh {
 
-hipError_t launch_markov_recompute(sv_ctx *ctx, const MarkovArgs &a, const ReqG *req, float *qrec, hipStream_t s)
+hipError_t launch_markov_resid(sv_ctx *ctx, const MarkovArgs &a, const VerifyArgs &v, const ReqG *req,
+                               hipStream_t s)
 {
-    if (a.B <= 0 || a.gamma <= 0) return hipSuccess;
-    switch (a.R) {
-    case 32: return launch_rebuild<32>(ctx, a, req, qrec, s);
-    case 64: return launch_rebuild<64>(ctx, a, req, qrec, s);
-    case 128: return launch_rebuild<128>(ctx, a, req, qrec, s);
-    case 256: return launch_rebuild<256>(ctx, a, req, qrec, s);
-    default: return hipErrorInvalidValue;
-    }
+    if (a.B <= 0) return hipSuccess;
+    return v.p_esize == 2 ? launch_resid_rank<2>(ctx, a, v, req, s) : launch_resid_rank<4>(ctx, a, v, req, s);
 }
 
 hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s)

@@ -72,10 +72,11 @@ struct Workspace {
     int32_t *sched_rank; // [kSchedMax] candidate ranks, zero between calls
     double *sched_surv;  // [kSchedMax] candidate survival products
     uint16_t *rnn_h;     // [max_batch, max_rank] bf16 RNN-head state
-    float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials
+    float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials; after the
+                         // fused path's draft, its correction / bonus tile sums (floats)
     int32_t *mk_prev;    // [max_batch] Markov: token sampled at the previous position
     float *mk_q;         // [max_batch * V] Markov logits of the current position when
-                         // the caller does not keep them; fused path: rebuilt correction rows
+                         // the caller does not keep them
     float *mk_lse2;      // [max_batch * max_gamma] fused path: draft row log2-sum-exp2
     float *mk_zx;        // [max_batch * max_gamma] fused path: drafted tokens' logits
     void *tree_state;    // [2][max_batch] kTreeStateBytes: tree walk state by round parity
@@ -148,12 +149,9 @@ struct VerifyArgs {
     bool block;           // block verification
     // Draft rows that were never materialised (the fused Markov path): the
     // sampler's per-row log2-sum-exp2 of z * c and the drafted tokens' raw
-    // logits replace the q row statistics, and qrec [B, V] fp32 holds the one
-    // correction row per request that the residual needs (row b, rebuilt
-    // after the acceptance scan).  All null otherwise.
+    // logits replace the q row statistics.  Null otherwise.
     const float *q_lse2;  // [B, gamma]
     const float *q_zx;    // [B, gamma]
-    const float *qrec;    // [B, V]
     // Row counts per request when they are not gamma + 1 and gamma (tree
     // verification: N + 1 node rows of p, one q row per node with children);
     // 0 for a draft.
@@ -253,9 +251,12 @@ struct MarkovArgs {
 };
 
 hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s);
-// Rebuilds, for every request whose scan ended in a rejection (req[b].mode ==
-// 0, no flags), the draft logits z of position tau + 1 into qrec + b * V.
-hipError_t launch_markov_recompute(sv_ctx *ctx, const MarkovArgs &a, const ReqG *req, float *qrec, hipStream_t s);
+// Fused verification's correction / bonus draw after the acceptance scan
+// (req): the contraction's residual mode sums every request's correction /
+// bonus weights per vocabulary tile, then one workgroup per request draws
+// the token from those sums and writes its outputs.
+hipError_t launch_markov_resid(sv_ctx *ctx, const MarkovArgs &a, const VerifyArgs &v, const ReqG *req,
+                               hipStream_t s);
 // Fused Markov draft -> verification after the p row statistics: the
 // acceptance scan (token rule, q statistics from the sampler), the correction
 // rows rebuilt, then the correction / bonus draw.

@@ -47,16 +47,12 @@ constexpr int SEG = svh::kSegR;
 constexpr int MAXG = svh::kMaxGamma;
 constexpr double kLn2d = 0.69314718055994530942;
 
-// STAGE_FROM_REQ: the fused tail starts from the request state k_accept
-// stored (the fused Markov path rebuilds the correction rows in between).
-enum Stage { STAGE_TOKEN = 0, STAGE_BLOCK_PRE = 1, STAGE_BLOCK_FINAL = 2, STAGE_FROM_REQ = 3 };
+enum Stage { STAGE_TOKEN = 0, STAGE_BLOCK_PRE = 1, STAGE_BLOCK_FINAL = 2 };
 
-// The q row of request b's correction draw (position tau + 1): a row of the
-// caller's q, or the rebuilt row b of qrec on the fused Markov path.
+// The q row of request b's correction draw (position tau + 1).
 template <int QES>
 __device__ __forceinline__ const char *correction_qrow(const svh::VerifyArgs &a, int b, int tau)
 {
-    if (a.qrec) return (const char *)(a.qrec + (int64_t)b * a.V);
     return (const char *)a.q + ((int64_t)b * a.gamma + tau) * a.V * QES;
 }
 
@@ -878,12 +874,7 @@ __global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, float2 *__re
         small_rowstats<PES, QES, NTT / svk::kWave>(a, b, part);
         __syncthreads();
     }
-    if (stage == STAGE_FROM_REQ) {
-        // k_accept already evaluated the request (and wrote the outputs of a
-        // request with a data error)
-        if (threadIdx.x == 0) r = pre[b];
-        if ((int)threadIdx.x < a.gamma) as.x[threadIdx.x] = a.draft[(int64_t)b * a.gamma + threadIdx.x];
-    } else if (threadIdx.x < svk::kWave) {
+    if (threadIdx.x < svk::kWave) {
         accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, pre + b, &r, lp2g, lq2g, wrun, errword, as);
     }
     __syncthreads();
@@ -1037,13 +1028,7 @@ template <int PES>
 hipError_t markov_verify_tail(sv_ctx *ctx, const svh::VerifyArgs &a, const svh::MarkovArgs &m, hipStream_t s)
 {
     launch_accept<PES, 4>(ctx, a, s, STAGE_TOKEN);
-    hipError_t e = svh::launch_markov_recompute(ctx, m, (const ReqG *)ctx->ws.req, ctx->ws.mk_q, s);
-    if (e != hipSuccess) return e;
-    if (fused_tail_fits(ctx, a))
-        launch_fused_tail<PES, 4>(ctx, a, s, STAGE_FROM_REQ);
-    else
-        launch_sum_and_select<PES, 4>(ctx, a, s);
-    return hipGetLastError();
+    return svh::launch_markov_resid(ctx, m, a, (const ReqG *)ctx->ws.req, s);
 }
 
 // ---------------------------------------------------------------------------

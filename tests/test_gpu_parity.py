@@ -1056,7 +1056,8 @@ def check_markov_verify(ctx, mi, req, label):
                                                  (24, 5, 9001, 64, 0.25, False), (8, 4, 5000, 256, 0.02, False),
                                                  (12, 6, 6007, 128, 0.25, True), (16, 4, 40000, 128, 0.25, False)])
 def test_markov_verify_fused_small(B, gamma, V, R, std, p32):
-    """The last case (16 requests, 20 segments) takes the split tail."""
+    """Ranks 64-256, bf16 and fp32 target rows, vocabularies that are not a
+    multiple of four (scalar loads and a partial last tile)."""
     _say(f"case: fused Markov -> verify B={B} gamma={gamma} V={V} R={R} std={std} p fp32={p32}")
     mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=std)
     if p32:
@@ -1075,8 +1076,7 @@ def _random_markov_case(case, base_seed):
 @pytest.mark.parametrize("case", range(6))
 def test_markov_verify_fused_random(case):
     """Seeded random B (1-140), gamma (1-8), V (200-45,000), rank (32-256) and
-    transition scale through the fused draft -> verification path (case 5
-    takes the split tail)."""
+    transition scale through the fused draft -> verification path."""
     c = _random_markov_case(case, 9500)
     _say(f"case: random fused Markov -> verify {case}: {c}")
     mi = WL.make_markov_inputs("cuda", B=c["B"], gamma=c["gamma"], V=c["V"], R=c["R"], uw_std=c["std"])
