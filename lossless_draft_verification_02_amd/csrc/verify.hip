@@ -606,6 +606,45 @@ __global__ __launch_bounds__(NT) void k_resid_sum(svh::VerifyArgs a, const ReqG 
     if ((threadIdx.x & (svk::kWave - 1)) == 0) csum[(int64_t)b * nseg + sidx] = tot;
 }
 
+// Token rule, split tail, acceptance and sums in one launch: grid (request,
+// segment group); wavefront 0 of every workgroup evaluates its request (the
+// same loads and arithmetic in each, so every workgroup reaches the same
+// tau), then the workgroup's wavefronts sum their segments of the correction
+// / bonus row.  The first workgroup of a request stores its state for the
+// selection and writes its diagnostics; an error output is the same from
+// every workgroup.
+template <int PES, int QES>
+__global__ __launch_bounds__(NT) void k_accept_sum(svh::VerifyArgs a, const float2 *__restrict__ part, int nch1,
+                                                   ReqG *__restrict__ req, float *__restrict__ csum, int nseg,
+                                                   uint32_t *__restrict__ errword)
+{
+    __shared__ AcceptLDS as;
+    __shared__ ReqG r;
+    const int nwg = (nseg + SPW - 1) / SPW;
+    const int64_t wg = blockIdx.x;
+    const int bl = (int)(wg / nwg);
+    const int g = (int)(wg - (int64_t)bl * nwg);
+    const int b = a.b0 + bl;
+    if (threadIdx.x < svk::kWave) {
+        svh::VerifyArgs av = a;
+        if (g != 0) av.diag = sv_diag{};   // diagnostics once per request
+        accept_eval<PES, QES>(av, part, nch1, nullptr, nseg, STAGE_TOKEN, b, nullptr, &r, nullptr, nullptr, nullptr,
+                              errword, as);
+    }
+    __syncthreads();
+    if (g == 0 && threadIdx.x == 0) req[b] = r;
+    if (r.flags) return;
+    const int sidx = g * SPW + (int)(threadIdx.x / svk::kWave);
+    if (sidx >= nseg) return;
+    const int G1 = a.gamma + 1;
+    const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
+    const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
+    const int64_t s0 = (int64_t)sidx * SEG;
+    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
+    const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
+    if ((threadIdx.x & (svk::kWave - 1)) == 0) csum[(int64_t)b * nseg + sidx] = tot;
+}
+
 // ---------------------------------------------------------------------------
 // Inverse-CDF selection.
 // ---------------------------------------------------------------------------
@@ -997,8 +1036,17 @@ hipError_t token_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
     if (fused_tail_fits(ctx, a)) {
         launch_fused_tail<PES, QES>(ctx, a, s, STAGE_TOKEN);
     } else {
-        launch_accept<PES, QES>(ctx, a, s, STAGE_TOKEN);
-        launch_sum_and_select<PES, QES>(ctx, a, s);
+        const int nseg = ctx->nseg;
+        const int64_t nwg = (nseg + SPW - 1) / SPW;
+        int slot = svh::prof_begin(ctx, s, SV_KERNEL_RESID);
+        hipLaunchKernelGGL((k_accept_sum<PES, QES>), dim3((unsigned)((int64_t)a.nb * nwg)), dim3(NT), 0, s, a,
+                           (const float2 *)ctx->ws.part, ctx->nch1, (ReqG *)ctx->ws.req, ctx->ws.csum, nseg,
+                           ctx->ws.errword);
+        svh::prof_end(ctx, s, slot);
+        slot = svh::prof_begin(ctx, s, SV_KERNEL_SELECT);
+        hipLaunchKernelGGL((k_select<PES, QES>), dim3(a.nb), dim3(svk::kWave), 0, s, a, (const ReqG *)ctx->ws.req,
+                           ctx->ws.csum, (const float *)ctx->ws.bm, nseg, ctx->ws.errword);
+        svh::prof_end(ctx, s, slot);
     }
     return hipGetLastError();
 }
