@@ -56,11 +56,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 512;                 // 8 wavefronts
-constexpr int NWAVE = NT / 64;
-constexpr int TN = svh::kMarkovTileN;   // 128 vocabulary rows per tile (= the draw's tile)
-constexpr int MC = 16 * NWAVE;          // 128 requests per workgroup: wavefront w owns 16 w .. 16 w + 15
+constexpr int TN = svh::kMarkovTileN;   // vocabulary rows per tile (= the draw's tile)
 constexpr int NVB = TN / 16;            // 16-row vocabulary blocks per tile
+constexpr int NCW = 8;                  // contraction: compute wavefronts per workgroup
+constexpr int NLW = 4;                  // contraction: loader wavefronts per workgroup
+constexpr int NTG = (NCW + NLW) * 64;   // contraction workgroup
+constexpr int MC = 128;                 // requests per contraction workgroup
+constexpr int BASE_BYTES = MC * TN * 2; // base-logit tile: MC requests x TN tokens, bf16
+static_assert(TN == 64, "one draw column per lane");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -192,34 +195,90 @@ struct TileLayout {
     static constexpr int CH = R / 8;                        // 16-byte chunks per row
     static constexpr int SW = CH < 16 ? CH : 16;            // swizzle period
     static constexpr int BYTES = TN * R * 2;
-    static constexpr int PER_WAVE = TN * CH / (NWAVE * 64); // copy instructions per wavefront
-    static_assert(TN * CH % (NWAVE * 64) == 0, "whole copy instructions");
+    static constexpr int INSTR = TN * CH / 64;              // copy instructions (64 slots each)
     __device__ static __forceinline__ int slot(int row, int c) { return row * CH + (c ^ (row & (SW - 1))); }
 };
 
-// Direct global -> LDS copy of Wt rows [n0, n0 + TN) into `dst`: each
-// wavefront instruction fills 64 consecutive 16-byte slots (lane i -> slot
-// base + i), fetching whichever global chunk the swizzle puts there.  Rows
-// past V copy row V - 1; their outputs are never stored.
+// Copy instruction i of a Wt tile, rows [n0, n0 + TN) into `dst` (direct
+// global -> LDS): lane l fills slot 64 i + l, fetching whichever global chunk
+// the swizzle puts there.  Rows past V copy row V - 1; their outputs are
+// never stored.
 template <int R>
-__device__ __forceinline__ void copy_chunk(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int wid, int lane,
-                                           int j)
+__device__ __forceinline__ void copy_w(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int i, int lane)
 {
     using TL = TileLayout<R>;
-    const int base = (j * NWAVE + wid) * 64;
-    const int S = base + lane;
+    const int S = 64 * i + lane;
     const int row = S / TL::CH, p = S % TL::CH;
     const int c = p ^ (row & (TL::SW - 1));
     int64_t n = n0 + row;
     n = n < a.V ? n : a.V - 1;
-    __builtin_amdgcn_global_load_lds((const void *)(a.W + n * R + 8 * c), (lds_void *)(dst + base * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)(a.W + n * R + 8 * c), (lds_void *)(dst + 64 * i * 16), 16, 0, 0);
 }
 
-template <int R>
-__device__ __forceinline__ void copy_tile(const svh::MarkovArgs &a, int64_t n0, unsigned char *dst, int wid, int lane)
+// The base-logit tile in LDS: request m's TN tokens are 8 chunks of 16 bytes,
+// chunk c at slot 8 m + (c ^ (m & 7)).  Copy instruction i fills slots
+// [64 i, 64 i + 64): requests 8 i .. 8 i + 7.  brow is lane's request row
+// (the base row of its request and position); chunks past V fetch chunk 0.
+__device__ __forceinline__ void copy_base(const uint16_t *brow, int64_t n0, int64_t V, unsigned char *dst, int i,
+                                          int lane)
 {
+    const int S = 64 * i + lane;
+    const int m = S >> 3, p = S & 7;
+    int c = p ^ (m & 7);
+    if (n0 + 8 * c >= V) c = 0;
+    __builtin_amdgcn_global_load_lds((const void *)(brow + n0 + 8 * c), (lds_void *)(dst + 64 * i * 16), 16, 0, 0);
+}
+
+// The same tile from rows that are not 16-byte aligned: element loads,
+// -inf past V, one 16-byte LDS store per lane.
+__device__ __forceinline__ void copy_base_unaligned(const uint16_t *brow, int64_t n0, int64_t V, unsigned char *dst,
+                                                    int i, int lane)
+{
+    const int S = 64 * i + lane;
+    const int m = S >> 3, p = S & 7;
+    const int c = p ^ (m & 7);
+    uint16_t e[8];
 #pragma unroll
-    for (int j = 0; j < TileLayout<R>::PER_WAVE; ++j) copy_chunk<R>(a, n0, dst, wid, lane, j);
+    for (int q = 0; q < 8; ++q) {
+        const int64_t n = n0 + 8 * c + q;
+        e[q] = n < V ? brow[n] : (uint16_t)0xFF80u;
+    }
+    uint4 v;
+    v.x = e[0] | ((uint32_t)e[1] << 16);
+    v.y = e[2] | ((uint32_t)e[3] << 16);
+    v.z = e[4] | ((uint32_t)e[5] << 16);
+    v.w = e[6] | ((uint32_t)e[7] << 16);
+    *(uint4 *)(dst + (size_t)S * 16) = v;
+}
+
+// Base logits n .. n + 3 (n = 16 vb + 4 lg, a multiple of 4) of request ml
+// of the workgroup, from the LDS tile, as packed bf16 pairs.
+__device__ __forceinline__ uint2 base_from_lds(const unsigned char *tile, int ml, int n)
+{
+    const int c = n >> 3, half = (n >> 2) & 1;
+    return *(const uint2 *)(tile + (8 * ml + (c ^ (ml & 7))) * 16 + 8 * half);
+}
+
+// The loader wavefronts' side of the per-tile workgroup barrier.  Their
+// copies write LDS behind the compiler's back: completion is their own
+// explicit vmcnt wait before it, and the wavefront-scope fences only keep the
+// compiler from moving a copy across the barrier (a workgroup-scope LDS
+// fence here would make the compiler wait for every copy in flight, the next
+// tile's included).
+__device__ __forceinline__ void loader_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Waits until at most n of the calling wavefront's vector memory loads are
+// outstanding (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Max and sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48):
@@ -240,44 +299,30 @@ __device__ __forceinline__ float rows4_sum(float v)
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// How a workgroup's eight wavefronts share one tile x 128 requests.  A
-// wavefront holds the B fragments of G request groups of 16 in registers for
-// the whole launch and covers NVB / G of the tile's 16-row blocks, so every A
-// fragment it reads from LDS feeds G MFMAs; the G wavefronts of one request
-// set split the tile's rows and combine their softmax pairs through LDS.
-// G = 2 halves the LDS reads per MFMA; it needs the register room of one
-// workgroup per CU, which the largest rank has anyway (its tile ring fills
-// the LDS).
+// How a contraction workgroup shares its work.  Compute wavefronts: each
+// holds the B fragments of G request groups of 16 in registers for the whole
+// launch and covers VBW of a tile's 16-row blocks, so every A fragment it
+// reads from LDS feeds G MFMAs; the RP wavefronts of one request set split
+// the tile's rows and combine their partial results through LDS.  Loader
+// wavefronts only move data: each tile's Wt rows and base logits go straight
+// from global memory into a three-slot LDS ring, two tiles ahead of the
+// compute wavefronts, so no compute wavefront ever waits behind a memory
+// instruction of its own.
 template <int R>
 struct GemmShape {
-    static constexpr int G = R == 256 ? 2 : 1;   // request groups per wavefront
-    static constexpr int NSET = NWAVE / G;       // request sets of 16 G
-    static constexpr int VBW = NVB / G;          // 16-row blocks per wavefront
-    static constexpr int MINB = G == 1 ? 2 : 1;  // workgroups per CU the registers are sized for
+    static constexpr int G = R == 256 ? 2 : 1;      // request groups per compute wavefront
+    static constexpr int NSET = MC / (16 * G);      // request sets
+    static constexpr int RP = NCW / NSET;           // row parts of a tile
+    static constexpr int VBW = NVB / RP;            // 16-row blocks per compute wavefront
+    static constexpr int KS = R / 32;               // k-steps
+    static constexpr int SLOT = TileLayout<R>::BYTES + BASE_BYTES;
+    static constexpr int NSLOT = 3;
+    static constexpr int W_PER = TileLayout<R>::INSTR / NLW;   // copy instructions per loader, per tile
+    static constexpr int B_PER = BASE_BYTES / 1024 / NLW;
+    static constexpr int PER = W_PER + B_PER;
+    static_assert(NSET * RP == NCW && RP * VBW == NVB, "work split");
+    static_assert(TileLayout<R>::INSTR % NLW == 0 && (BASE_BYTES / 1024) % NLW == 0, "whole copy instructions");
 };
-
-// Base logits of the lane's outputs in one tile: request m, vocabulary
-// entries n0 + 16 (vb0 + j) + 4 lg + r, as packed bf16 pairs; -inf past V or B.
-__device__ __forceinline__ const uint16_t *base_row(const svh::MarkovArgs &a, int k, int m)
-{
-    return m < a.B ? a.base + ((int64_t)m * a.gamma + (k - 1)) * a.V : nullptr;
-}
-
-__device__ __forceinline__ uint2 base_quad(const uint16_t *brow, int n, int Vi, int vec)
-{
-    uint2 r = make_uint2(0xFF80FF80u, 0xFF80FF80u);
-    if (brow) {
-        if (vec) {
-            if (n < Vi) r = *(const uint2 *)(brow + n);
-        } else {
-            uint16_t e[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) e[q] = n + q < Vi ? brow[n + q] : (uint16_t)0xFF80u;
-            r = make_uint2(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16));
-        }
-    }
-    return r;
-}
 
 // Weight of one token in the correction / bonus draw of the fused
 // verification ("Speculative Decoding: The Same Distribution, Twice as Fast",
@@ -366,39 +411,96 @@ struct ResidArgs {
 // Residual mode (RES = the target logits' element size, 2 or 4): position
 // tau + 1 of each request in req, the acceptance scan's results; every
 // request it left without an error flag contributes its correction / bonus
-// weights resid_weight over row tau + 1, summed per 128-token tile into
-// ra.tsum; the contraction runs only for the requests that rejected (a bonus
-// row needs p alone), and no z is stored.
+// weights resid_weight over row tau + 1, summed per tile into ra.tsum; the
+// contraction runs only for the requests that rejected (a bonus row needs p
+// alone), and no z is stored.
 //
-// Per tile: wait for the tile's copy, barrier, request the next tile's copy
-// and base logits, then the MFMAs with the next k-step's A fragments read
-// from LDS while the current k-step's run; per output the k-steps accumulate
-// in ascending order (the draw rebuilds its chosen tile the same way).
+// Per tile j of the workgroup (tiles blockIdx.x + j gridDim.x): the loader
+// wavefronts request tile j + 2 into ring slot (j + 2) % 3 (the slot the
+// compute wavefronts finished in iteration j - 1), then wait for tile
+// j + 1's copies; the compute wavefronts multiply tile j out of slot j % 3
+// (copied before the previous barrier), with the next k-step's A fragments
+// read while the current k-step's MFMAs run, and reduce it.  One workgroup
+// barrier per tile.  Per output the k-steps accumulate in ascending order
+// (the draws rebuild their tiles the same way).
 template <int R, int RES>
-__global__ __launch_bounds__(NT, GemmShape<R>::MINB)
+__global__ __launch_bounds__(NTG, 1)
 void k_markov_gemm(
     svh::MarkovArgs a, int k, const svh::ReqG *__restrict__ req, float *__restrict__ zout, int64_t zstride,
-    float2 *__restrict__ tile_part, int ntile, int vec, ResidArgs ra, int pvec)
+    float2 *__restrict__ tile_part, int ntile, int vec, int zvec, ResidArgs ra, int pvec)
 {
     using TL = TileLayout<R>;
     using GS = GemmShape<R>;
-    constexpr int G = GS::G, VBW = GS::VBW;
-    constexpr int KS = R / 32;
-    __shared__ __attribute__((aligned(16))) unsigned char wtile[2 * TL::BYTES];   // double-buffered tile ring
-    __shared__ svk::MS parts[G > 1 ? 2 * G * MC : 1];  // [tile parity][row part][request]: partial pairs
+    constexpr int G = GS::G, VBW = GS::VBW, KS = GS::KS, RP = GS::RP;
+    __shared__ __attribute__((aligned(16))) unsigned char ring[GS::NSLOT * GS::SLOT];
+    __shared__ svk::MS parts[RP > 1 ? 2 * RP * MC : 1];   // [tile parity][row part][request]: partials
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool loader = wid >= NCW;
+    const int Vi = (int)a.V;
+    const int mbase = blockIdx.y * MC;   // first request of the workgroup
+    int nt = 0;                          // tiles of the workgroup
+    if ((int)blockIdx.x < ntile) nt = (ntile - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+    auto tile_of = [&](int j) { return (int)blockIdx.x + j * (int)gridDim.x; };
+    auto slot_of = [&](int j) { return ring + (j % GS::NSLOT) * GS::SLOT; };
+
+    if (loader) {
+        // ---------------------------------------------------------------
+        // loader wavefronts: Wt copy instructions lw, lw + NLW, ...; base
+        // copy instructions likewise, each lane for one request row
+        const int lw = wid - NCW;
+        const uint16_t *brow[GS::B_PER];
+#pragma unroll
+        for (int q = 0; q < GS::B_PER; ++q) {
+            const int i = lw + NLW * q;
+            int m = mbase + ((64 * i + lane) >> 3);
+            m = m < a.B ? m : a.B - 1;
+            int km = k;
+            if constexpr (RES != 0) {
+                const svh::ReqG r = req[m];
+                km = (r.flags == 0 && r.mode == 0) ? r.tau + 1 : 1;
+            }
+            brow[q] = a.base + ((int64_t)m * a.gamma + (km - 1)) * a.V;
+        }
+        auto issue = [&](int j) {
+            const int64_t n0 = (int64_t)tile_of(j) * TN;
+            unsigned char *sl = slot_of(j);
+#pragma unroll
+            for (int q = 0; q < GS::W_PER; ++q) copy_w<R>(a, n0, sl, lw + NLW * q, lane);
+#pragma unroll
+            for (int q = 0; q < GS::B_PER; ++q) {
+                if (vec)
+                    copy_base(brow[q], n0, a.V, sl + TL::BYTES, lw + NLW * q, lane);
+                else
+                    copy_base_unaligned(brow[q], n0, a.V, sl + TL::BYTES, lw + NLW * q, lane);
+            }
+        };
+        if (nt > 0) issue(0);
+        if (nt > 1) issue(1);
+        if (nt > 1 && vec) wait_vm<GS::PER>();   // tile 0 landed
+        else __builtin_amdgcn_s_waitcnt(0);     // (element copies: their LDS stores too)
+        loader_barrier();
+        for (int j = 0; j < nt; ++j) {
+            const bool more = j + 2 < nt;
+            if (more) issue(j + 2);
+            if (more && vec) wait_vm<GS::PER>();   // tile j + 1 landed
+            else __builtin_amdgcn_s_waitcnt(0);
+            loader_barrier();
+        }
+        return;
+    }
+
+    // -------------------------------------------------------------------
+    // compute wavefronts
     const int li = lane & 15, lg = lane >> 4;
     const int set = wid % GS::NSET, rp = wid / GS::NSET;   // request set, row part
     const int vb0 = rp * VBW;                              // first 16-row block of the wavefront
     const int q0 = 16 * G * set;                           // first request of the set within the workgroup
-    const bool wave_on = blockIdx.y * MC + q0 < a.B;
-    const int Vi = (int)a.V;
+    const bool wave_on = mbase + q0 < a.B;
 
     int m[G], km[G];
     bool act[G];
-    const uint16_t *brow[G];   // base row of (request, position); null reads -inf
     // residual mode: the request's target row tau + 1 (null: no weights) and
     // its weight parameters
     [[maybe_unused]] const char *prow[G];
@@ -406,8 +508,8 @@ void k_markov_gemm(
     [[maybe_unused]] int rmode[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        m[g] = blockIdx.y * MC + q0 + 16 * g + li;     // the lane's requests (B operand columns)
-        km[g] = k;                                      // and their positions
+        m[g] = mbase + q0 + 16 * g + li;   // the lane's requests (B operand columns)
+        km[g] = k;                         // and their positions
         act[g] = m[g] < a.B;
         if constexpr (RES != 0) {
             prow[g] = nullptr;
@@ -427,268 +529,161 @@ void k_markov_gemm(
                 }
             }
         }
-        brow[g] = act[g] ? base_row(a, km[g], m[g]) : nullptr;
     }
-
-    // prologue: first tile's copy, the lane's B fragments, first base logits
-    int tile = blockIdx.x;
-    copy_tile<R>(a, (int64_t)tile * TN, wtile, wid, lane);
     bf16x8 ufr[G][KS];
-    uint2 bv[G][VBW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        head_fragments<R>(a, km[g], m[g], lg, act[g], ufr[g]);
-#pragma unroll
-        for (int j = 0; j < VBW; ++j) bv[g][j] = base_quad(brow[g], tile * TN + 16 * (vb0 + j) + 4 * lg, Vi, vec);
-    }
+    for (int g = 0; g < G; ++g) head_fragments<R>(a, km[g], m[g], lg, act[g], ufr[g]);
 
-    // G > 1: the softmax pair of (request, tile) from the row parts' partials,
-    // written by the row-part-0 wavefronts once a barrier has passed
+    // RP > 1: the pair (or weight sum) of (request, tile) from the row parts'
+    // partials, written by the row-part-0 wavefronts once a barrier has passed
     auto merge_parts = [&](int par, int t) {
-        if (G > 1 && (RES != 0 || tile_part) && rp == 0 && lane < 16 * G) {
-            const int mm = blockIdx.y * MC + q0 + lane;
+        if (RP > 1 && (RES != 0 || tile_part) && rp == 0 && lane < 16 * G) {
+            const int mm = mbase + q0 + lane;
             if (mm < a.B) {
                 if constexpr (RES != 0) {
-                    float v = parts[(par * G + 0) * MC + q0 + lane].s;
+                    float v = parts[(par * RP + 0) * MC + q0 + lane].s;
 #pragma unroll
-                    for (int r = 1; r < G; ++r) v += parts[(par * G + r) * MC + q0 + lane].s;
+                    for (int r = 1; r < RP; ++r) v += parts[(par * RP + r) * MC + q0 + lane].s;
                     ra.tsum[(int64_t)mm * ntile + t] = v;
                 } else {
-                    svk::MS v = parts[(par * G + 0) * MC + q0 + lane];
+                    svk::MS v = parts[(par * RP + 0) * MC + q0 + lane];
 #pragma unroll
-                    for (int r = 1; r < G; ++r) v = svk::ms_merge(v, parts[(par * G + r) * MC + q0 + lane]);
+                    for (int r = 1; r < RP; ++r) v = svk::ms_merge(v, parts[(par * RP + r) * MC + q0 + lane]);
                     tile_part[(int64_t)mm * ntile + t] = make_float2(v.m, v.s);
                 }
             }
         }
     };
 
-    // The next tile's loads (PER_WAVE = KS copy instructions and NVB base
-    // quads per wavefront) are spread over the tile's work so that the
-    // memory queue drains as fast as it fills and no issue stalls the
-    // VALU/MFMA stream behind it.  G = 1: over the k-steps (one copy
-    // instruction and NVB / KS base quads per k-step).  G > 1 (KS = NVB = 8):
-    // sixteen issue points, op i a copy instruction (i even) or a base quad
-    // (i odd), ops 0..7 at the k-steps and 8..15 through the epilogue.
-    constexpr int BPS = (NVB + KS - 1) / KS;   // base quads per k-step (G = 1)
-    static_assert(TL::PER_WAVE == KS, "one copy instruction per k-step");
-    static_assert(G == 1 || (KS == 8 && NVB == 8), "sixteen issue points");
-
-    for (int it = 0; tile < ntile; ++it, tile += gridDim.x) {
-        unsigned char *buf = wtile + (it & 1) * TL::BYTES;
-        unsigned char *nbuf = wtile + ((it + 1) & 1) * TL::BYTES;
-        // this tile's copy (and base loads) landed for every wavefront, every
-        // wavefront finished reading the other buffer and wrote its partials
-        __builtin_amdgcn_s_waitcnt(0);
-        svk::lds_barrier();
-        if (it > 0) merge_parts((it - 1) & 1, tile - (int)gridDim.x);
-        const int next = tile + (int)gridDim.x;
-        const bool has_next = next < ntile;
-        const int64_t nn0 = (int64_t)next * TN;
-        uint2 bn[G][VBW];
-        auto issue = [&](int i) {   // G > 1: op i of the next tile's loads
-            if (!has_next) return;
-            if ((i & 1) == 0) {
-                copy_chunk<R>(a, nn0, nbuf, wid, lane, i >> 1);
-            } else {
-                const int f = i >> 1;
-                bn[f / VBW][f % VBW] = base_quad(brow[f / VBW], next * TN + 16 * (vb0 + f % VBW) + 4 * lg, Vi, vec);
+    svk::lds_barrier();   // tile 0 landed
+    for (int j = 0; j < nt; ++j) {
+        const int tile = tile_of(j);
+        const unsigned char *sl = slot_of(j);
+        const unsigned char *bt = sl + TL::BYTES;   // base-logit tile
+        if (j > 0) merge_parts((j - 1) & 1, tile_of(j - 1));
+        if (wave_on) {
+            const int n0 = tile * TN;
+            // residual mode: this tile's target logits, consumed by the epilogue
+            typename PQuad<RES == 4 ? 4 : 2>::T pq[G][VBW];
+            if constexpr (RES != 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int v = 0; v < VBW; ++v)
+                        pq[g][v] = p_quad<RES>(prow[g], n0 + 16 * (vb0 + v) + 4 * lg, Vi, pvec);
             }
-        };
-        if (!wave_on) {
-            if (has_next) copy_tile<R>(a, nn0, nbuf, wid, lane);
-            continue;
-        }
-        f32x4 acc[G][VBW];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int j = 0; j < VBW; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // residual mode: this tile's target logits, consumed by the epilogue
-        typename PQuad<RES == 4 ? 4 : 2>::T pq[G][VBW];
-        if constexpr (RES != 0) {
+            f32x4 acc[G][VBW];
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int j = 0; j < VBW; ++j)
-                    pq[g][j] = p_quad<RES>(prow[g], tile * TN + 16 * (vb0 + j) + 4 * lg, Vi, pvec);
-        }
-        // A fragments: with G > 1 the next k-step's are read while the
-        // current k-step's MFMAs run (registers allow it at one workgroup per
-        // CU); with G = 1 each k-step reads its own
-        constexpr int NBUF = G > 1 ? 2 : 1;
-        bf16x8 af[NBUF][VBW];
-        if (NBUF == 2) {
+                for (int v = 0; v < VBW; ++v) acc[g][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            bf16x8 af[2][VBW];
 #pragma unroll
-            for (int j = 0; j < VBW; ++j) af[0][j] = *(const bf16x8 *)(buf + 16 * TL::slot(16 * (vb0 + j) + li, lg));
-        }
+            for (int v = 0; v < VBW; ++v) af[0][v] = *(const bf16x8 *)(sl + 16 * TL::slot(16 * (vb0 + v) + li, lg));
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            if (G > 1) {
-                issue(s);
-            } else if (has_next) {
-                copy_chunk<R>(a, nn0, nbuf, wid, lane, s);
+            for (int s = 0; s < KS; ++s) {
+                const int cur = s & 1;
+                if (s + 1 < KS) {
 #pragma unroll
-                for (int f = s * BPS; f < (s + 1) * BPS && f < NVB; ++f)
-                    bn[f / VBW][f % VBW] =
-                        base_quad(brow[f / VBW], next * TN + 16 * (vb0 + f % VBW) + 4 * lg, Vi, vec);
+                    for (int v = 0; v < VBW; ++v)
+                        af[cur ^ 1][v] = *(const bf16x8 *)(sl + 16 * TL::slot(16 * (vb0 + v) + li, 4 * (s + 1) + lg));
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int v = 0; v < VBW; ++v)
+                        acc[g][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cur][v], ufr[g][s], acc[g][v], 0, 0, 0);
             }
-            const int cur = NBUF == 2 ? (s & 1) : 0;
-            if (NBUF == 2 && s + 1 < KS) {
-#pragma unroll
-                for (int j = 0; j < VBW; ++j)
-                    af[(s + 1) % NBUF][j] =
-                        *(const bf16x8 *)(buf + 16 * TL::slot(16 * (vb0 + j) + li, 4 * (s + 1) + lg));
-            } else if (NBUF == 1) {
-#pragma unroll
-                for (int j = 0; j < VBW; ++j)
-                    af[0][j] = *(const bf16x8 *)(buf + 16 * TL::slot(16 * (vb0 + j) + li, 4 * s + lg));
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int j = 0; j < VBW; ++j)
-                    acc[g][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[cur][j], ufr[g][s], acc[g][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // epilogue: lane holds z^T[n0 + 16 (vb0 + j) + 4 lg + r][m[g]]; at the
-        // largest rank the common case (a full tile, no z rows stored) runs
-        // without per-entry checks
-        const int n0 = tile * TN;
-        auto epilogue = [&](auto fast_c) {
-            constexpr bool FAST = decltype(fast_c)::value;
-            constexpr bool FULL = FAST;
+            // epilogue: lane holds z^T[n0 + 16 (vb0 + v) + 4 lg + r][m[g]]
+            const bool full = n0 + TN <= Vi;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const bool STORE = !FAST && zout != nullptr;
-                float *zrow = STORE ? zout + (int64_t)(act[g] ? m[g] : 0) * zstride : nullptr;
-                float mx = svk::neg_inf();
-                float zc[VBW][4];
+                const int ml = q0 + 16 * g + li;   // request within the workgroup
+                float z[VBW][4];
 #pragma unroll
-                for (int j = 0; j < VBW; ++j) {
-                    const int n = n0 + 16 * (vb0 + j) + 4 * lg;
-                    const uint32_t b01 = bv[g][j].x, b23 = bv[g][j].y;
-                    float z[4];
-                    z[0] = acc[g][j][0] + __uint_as_float(b01 << 16);
-                    z[1] = acc[g][j][1] + __uint_as_float(b01 & 0xFFFF0000u);
-                    z[2] = acc[g][j][2] + __uint_as_float(b23 << 16);
-                    z[3] = acc[g][j][3] + __uint_as_float(b23 & 0xFFFF0000u);
-                    if (STORE && act[g]) {
-                        if (FULL && vec) {
-                            *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
-                        } else if (vec) {
-                            if (n < Vi) *(float4 *)(zrow + n) = make_float4(z[0], z[1], z[2], z[3]);
-                        } else {
+                for (int v = 0; v < VBW; ++v) {
+                    const uint2 bq = base_from_lds(bt, ml, 16 * (vb0 + v) + 4 * lg);
+                    z[v][0] = acc[g][v][0] + __uint_as_float(bq.x << 16);
+                    z[v][1] = acc[g][v][1] + __uint_as_float(bq.x & 0xFFFF0000u);
+                    z[v][2] = acc[g][v][2] + __uint_as_float(bq.y << 16);
+                    z[v][3] = acc[g][v][3] + __uint_as_float(bq.y & 0xFFFF0000u);
+                }
+                if constexpr (RES != 0) {
+                    float sm = 0.0f;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (FULL || n + r < Vi) zrow[n + r] = z[r];
+                    for (int v = 0; v < VBW; ++v) {
+                        const int n = n0 + 16 * (vb0 + v) + 4 * lg;
+                        float xp[4];
+                        p_quad_floats<RES == 4 ? 4 : 2>(pq[g][v], xp);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (full || n + r < Vi)
+                                sm += resid_weight(xp[r], z[v][r], rmode[g], rmul[g], rlp2[g], rlq2[g], a.c);
+                    }
+                    sm = rows4_sum(sm);
+                    if (lg == 0) {
+                        if (RP > 1)
+                            parts[((j & 1) * RP + rp) * MC + ml] = svk::MS{0.0f, sm};
+                        else if (m[g] < a.B)
+                            ra.tsum[(int64_t)m[g] * ntile + tile] = sm;
+                    }
+                } else {
+                    if (zout && act[g]) {
+                        float *zrow = zout + (int64_t)m[g] * zstride;
+#pragma unroll
+                        for (int v = 0; v < VBW; ++v) {
+                            const int n = n0 + 16 * (vb0 + v) + 4 * lg;
+                            if (zvec && (full || n < Vi)) {
+                                *(float4 *)(zrow + n) = make_float4(z[v][0], z[v][1], z[v][2], z[v][3]);
+                            } else if (!zvec) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (n + r < Vi) zrow[n + r] = z[v][r];
+                            }
                         }
                     }
+                    if (!tile_part) continue;
+                    float mx = svk::neg_inf();
+                    float zc[VBW][4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        zc[j][r] = (FULL || n + r < Vi) ? z[r] * a.c : svk::neg_inf();
-                        mx = fmaxf(mx, zc[j][r]);
+                    for (int v = 0; v < VBW; ++v) {
+                        const int n = n0 + 16 * (vb0 + v) + 4 * lg;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            zc[v][r] = (full || n + r < Vi) ? z[v][r] * a.c : svk::neg_inf();
+                            mx = fmaxf(mx, zc[v][r]);
+                        }
                     }
-                }
-                auto point = [&](int pt) {   // issue points 8 + 4 g + pt
-                    if (G > 1) {
-                        issue(8 + 4 * g + pt);
-                        __builtin_amdgcn_sched_barrier(0);
+                    mx = rows4_max(mx);   // over the request's 4 lanes: the wavefront's rows of the tile
+                    // a NaN entry poisons the row (the draw flags it): through the
+                    // exponentials when the maximum is finite, explicitly otherwise
+                    float sm = 0.0f;
+                    if (mx != svk::neg_inf()) {
+#pragma unroll
+                        for (int v = 0; v < VBW; ++v)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[v][r] - mx);
+                    } else {
+                        bool bad = false;
+#pragma unroll
+                        for (int v = 0; v < VBW; ++v)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) bad |= zc[v][r] != zc[v][r];
+                        if (bad) sm = __builtin_nanf("");
                     }
-                };
-                if (!tile_part) {
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) point(pt);
-                    continue;
-                }
-                point(0);
-                mx = rows4_max(mx);   // over the request's 4 lanes: the wavefront's rows of the tile
-                point(1);
-                // a NaN entry poisons the row (the draw flags it): through the
-                // exponentials when the maximum is finite, explicitly otherwise
-                float sm = 0.0f;
-                if (mx != svk::neg_inf()) {
-#pragma unroll
-                    for (int j = 0; j < VBW; ++j)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sm += svk::fast_exp2(zc[j][r] - mx);
-                } else {
-                    bool bad = false;
-#pragma unroll
-                    for (int j = 0; j < VBW; ++j)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) bad |= zc[j][r] != zc[j][r];
-                    if (bad) sm = __builtin_nanf("");
-                }
-                point(2);
-                sm = rows4_sum(sm);
-                point(3);
-                if (lg == 0) {
-                    if (G > 1)
-                        parts[((it & 1) * G + rp) * MC + q0 + 16 * g + li] = svk::MS{mx, sm};
-                    else if (m[g] < a.B)
-                        tile_part[(int64_t)m[g] * ntile + tile] = make_float2(mx, sm);
+                    sm = rows4_sum(sm);
+                    if (lg == 0) {
+                        if (RP > 1)
+                            parts[((j & 1) * RP + rp) * MC + ml] = svk::MS{mx, sm};
+                        else if (m[g] < a.B)
+                            tile_part[(int64_t)m[g] * ntile + tile] = make_float2(mx, sm);
+                    }
                 }
             }
-        };
-        // residual mode: the weights of the lane's tokens, summed per request
-        // over the wavefront's rows of the tile
-        auto resid_epilogue = [&]() {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float sm = 0.0f;
-#pragma unroll
-                for (int j = 0; j < VBW; ++j) {
-                    const int n = n0 + 16 * (vb0 + j) + 4 * lg;
-                    float xp[4];
-                    p_quad_floats<RES == 4 ? 4 : 2>(pq[g][j], xp);
-                    const uint32_t b01 = bv[g][j].x, b23 = bv[g][j].y;
-                    float z[4];
-                    z[0] = acc[g][j][0] + __uint_as_float(b01 << 16);
-                    z[1] = acc[g][j][1] + __uint_as_float(b01 & 0xFFFF0000u);
-                    z[2] = acc[g][j][2] + __uint_as_float(b23 << 16);
-                    z[3] = acc[g][j][3] + __uint_as_float(b23 & 0xFFFF0000u);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < Vi) sm += resid_weight(xp[r], z[r], rmode[g], rmul[g], rlp2[g], rlq2[g], a.c);
-                }
-                if (G > 1) {
-                    // the next tile's loads, as in the softmax epilogue
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) {
-                        const int e = 4 * g + pt;
-                        if ((e * 8) % (4 * G) == 0) issue(8 + e * 8 / (4 * G));
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                sm = rows4_sum(sm);
-                if (lg == 0) {
-                    if (G > 1)
-                        parts[((it & 1) * G + rp) * MC + q0 + 16 * g + li] = svk::MS{0.0f, sm};
-                    else if (m[g] < a.B)
-                        ra.tsum[(int64_t)m[g] * ntile + tile] = sm;
-                }
-            }
-        };
-        if constexpr (RES != 0)
-            resid_epilogue();
-        else if (G > 1 && n0 + TN <= Vi && !zout)
-            epilogue(std::true_type{});
-        else
-            epilogue(std::false_type{});
-        if (has_next) {
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int j = 0; j < VBW; ++j) bv[g][j] = bn[g][j];
         }
+        svk::lds_barrier();   // slot j % 3 is free again; tile j + 1 landed
     }
-    if (G > 1 && (RES != 0 || tile_part)) {
-        // the last tile's partials
-        const int it = (ntile - 1 - (int)blockIdx.x) / (int)gridDim.x;   // index of the workgroup's last tile
-        svk::lds_barrier();
-        merge_parts(it & 1, tile - (int)gridDim.x);
-    }
+    if (nt > 0) merge_parts((nt - 1) & 1, tile_of(nt - 1));
 }
 
 constexpr int kDrawThreads = 256;                                        // one workgroup per request
@@ -878,10 +873,9 @@ __device__ bool select_tile_wg(const svh::MarkovArgs &a, int k, const float2 *__
     return true;
 }
 
-// Token of the chosen tile (z values zr[0 .. 128)) by one wavefront: lane
-// owns columns 2 lane, 2 lane + 1; masses exp2(z c - ref) as the tile
-// choice's; fp64 prefix; outputs.  Returns the token (the same on every
-// lane), -1 if none.
+// Token of the chosen tile (z values zr[0 .. TN)) by one wavefront: lane
+// owns column lane; masses exp2(z c - ref) as the tile choice's; fp64
+// prefix; outputs.  Returns the token (the same on every lane), -1 if none.
 __device__ int32_t select_token_in_tile(const svh::MarkovArgs &a, int k, int b, const SelState &st,
                                         const float *zr, uint32_t *__restrict__ errword)
 {
@@ -889,19 +883,13 @@ __device__ int32_t select_token_in_tile(const svh::MarkovArgs &a, int k, int b, 
     const int64_t out = (int64_t)b * a.gamma + (k - 1);
     const int64_t c0 = (int64_t)st.ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
-    const int j0 = 2 * lane, j1 = 2 * lane + 1;
+    const int j0 = lane;
     const float w0 = j0 < ncols ? svk::fast_exp2(zr[j0] * a.c - st.ref) : 0.0f;
-    const float w1 = j1 < ncols ? svk::fast_exp2(zr[j1] * a.c - st.ref) : 0.0f;
-    const double pair = (double)w0 + (double)w1;
-    const double pincl = svk::wave_inclusive_scan_d(pair);
-    const double pexcl = pincl - pair;
+    const double pincl = svk::wave_inclusive_scan_d((double)w0);
+    const double pexcl = pincl - (double)w0;
     int yb = 0x7FFFFFFF, yl = -1;
-    if (w1 > 0.0f) {
-        yl = j1;
-        if (!st.fallback && (float)(st.tbase + pexcl + (double)w0 + (double)w1) > st.tf) yb = j1;
-    }
     if (w0 > 0.0f) {
-        if (yl < 0) yl = j0;
+        yl = j0;
         if (!st.fallback && (float)(st.tbase + pexcl + (double)w0) > st.tf) yb = j0;
     }
     const int ybest = wave_min_i(yb);
@@ -1103,19 +1091,15 @@ __device__ bool choose_resid_tile(const float *ts_sum, int ntile, float u, DrawL
 
 // The sum of p's tile weights 2^(xp c - lp2) of every tile into out[] (LDS),
 // by the whole workgroup: wavefront w takes tiles w, w + 4, ...; lane l
-// weighs tokens 2 l and 2 l + 1 of the tile.
+// weighs token l of the tile.
 template <int PES>
 __device__ void p_tile_sums(const char *prow, float lp2, float c, int64_t V, int ntile, float *out)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int tl = wid; tl < ntile; tl += kDrawWaves) {
         const int64_t c0 = (int64_t)tl * TN;
-        float w = 0.0f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t n = c0 + 2 * lane + h;
-            if (n < V) w += resid_weight(svk::load_logit<PES>(prow, n), 0.0f, 1, 1.0f, lp2, 0.0f, c);
-        }
+        const int64_t n = c0 + lane;
+        float w = n < V ? resid_weight(svk::load_logit<PES>(prow, n), 0.0f, 1, 1.0f, lp2, 0.0f, c) : 0.0f;
         w = svk::wave_sum(w);
         if (lane == 0) out[tl] = w;
     }
@@ -1204,18 +1188,13 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_resid_draw(svh::MarkovA
         }
         svk::lds_barrier();
         if (wid == 0) {
-            const int j0 = 2 * lane, j1 = 2 * lane + 1;
-            const float w0 = wtile[j0], w1 = wtile[j1];
-            const double pair = (double)w0 + (double)w1;
-            const double pincl = svk::wave_inclusive_scan_d(pair);
-            const double pexcl = pincl - pair;
+            const int j0 = lane;
+            const float w0 = wtile[j0];
+            const double pincl = svk::wave_inclusive_scan_d((double)w0);
+            const double pexcl = pincl - (double)w0;
             int yb = 0x7FFFFFFF, yl = -1;
-            if (w1 > 0.0f) {
-                yl = j1;
-                if (!st.fallback && (float)(st.tbase + pexcl + (double)w0 + (double)w1) > st.tf) yb = j1;
-            }
             if (w0 > 0.0f) {
-                if (yl < 0) yl = j0;
+                yl = j0;
                 if (!st.fallback && (float)(st.tbase + pexcl + (double)w0) > st.tf) yb = j0;
             }
             const int ybest = wave_min_i(yb);
@@ -1239,25 +1218,30 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_resid_draw(svh::MarkovA
     }
 }
 
+// Every base-logit row starts on a 16-byte boundary (the loaders copy it with
+// 16-byte direct loads); otherwise they copy element by element.
+inline int base_rows_aligned(const svh::MarkovArgs &a)
+{
+    return (a.V % 8 == 0) && ((((uintptr_t)a.base) & 15) == 0);
+}
+
 template <int R>
 hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s)
 {
     const int ntile = ctx->ntile;
     const int gy = (a.B + MC - 1) / MC;
-    const size_t lds = 2 * (size_t)TileLayout<R>::BYTES;
-    const int per_cu = lds <= 80 * 1024 ? 2 : 1;   // 160 KB of LDS per CU
-    int gx = ctx->num_cu * per_cu / gy;
+    int gx = ctx->num_cu / gy;   // one workgroup per CU (its tile ring fills most of the LDS)
     gx = gx < 1 ? 1 : (gx > ntile ? ntile : gx);
     // z rows of position k: the caller's q_logits [B, gamma, V], else a
     // workspace row per request
     const int64_t zstride = a.q_logits ? (int64_t)a.gamma * a.V : a.V;
-    const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0) &&
-                    ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
+    const int vec = base_rows_aligned(a);
+    const int zvec = (a.V % 4 == 0) && ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
     for (int k = 1; k <= a.gamma; ++k) {
         float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        hipLaunchKernelGGL((k_markov_gemm<R, 0>), dim3(gx, gy), dim3(NT), 0, s, a, k, (const svh::ReqG *)nullptr,
-                           zk, zstride, ctx->ws.mk_part, ntile, vec, ResidArgs{nullptr, nullptr}, 0);
+        hipLaunchKernelGGL((k_markov_gemm<R, 0>), dim3(gx, gy), dim3(NTG), 0, s, a, k, (const svh::ReqG *)nullptr,
+                           zk, zstride, ctx->ws.mk_part, ntile, vec, zvec, ResidArgs{nullptr, nullptr}, 0);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
         hipLaunchKernelGGL((k_markov_draw<R>), dim3(a.B), dim3(kDrawThreads), 0, s, a, k, (const float *)zk, zstride,
@@ -1273,17 +1257,15 @@ hipError_t launch_resid(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::Verify
 {
     const int ntile = ctx->ntile;
     const int gy = (a.B + MC - 1) / MC;
-    const size_t lds = 2 * (size_t)TileLayout<R>::BYTES;
-    const int per_cu = lds <= 80 * 1024 ? 2 : 1;
-    int gx = ctx->num_cu * per_cu / gy;
+    int gx = ctx->num_cu / gy;
     gx = gx < 1 ? 1 : (gx > ntile ? ntile : gx);
-    const int vec = (a.V % 4 == 0) && ((((uintptr_t)a.base) & 7) == 0);
+    const int vec = base_rows_aligned(a);
     const int pvec = (a.V % 4 == 0) && ((((uintptr_t)v.p) & (4 * PES - 1)) == 0);
     // the draft's tile pairs are consumed: their buffer holds the tile sums
     float *tsum = (float *)ctx->ws.mk_part;
     int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_REBUILD);
-    hipLaunchKernelGGL((k_markov_gemm<R, PES>), dim3(gx, gy), dim3(NT), 0, s, a, 0, req, (float *)nullptr, a.V,
-                       (float2 *)nullptr, ntile, vec, ResidArgs{v.p, tsum}, pvec);
+    hipLaunchKernelGGL((k_markov_gemm<R, PES>), dim3(gx, gy), dim3(NTG), 0, s, a, 0, req, (float *)nullptr, a.V,
+                       (float2 *)nullptr, ntile, vec, 0, ResidArgs{v.p, tsum}, pvec);
     svh::prof_end(ctx, s, slot);
     slot = svh::prof_begin(ctx, s, SV_KERNEL_SELECT);
     hipLaunchKernelGGL((k_markov_resid_draw<R, PES>), dim3(a.B), dim3(kDrawThreads), 0, s, a, v, req,

@@ -49,8 +49,8 @@ constexpr int kTailMaxSeg = 4096;
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedMax = 8192;
 // Markov head: output tiles of kMarkovTileN vocabulary columns.
-constexpr int kMarkovTileN = 128;
-constexpr int kMarkovMaxTiles = 256 * 8;   // the draw keeps 8 tile pairs per thread: V <= 262,144
+constexpr int kMarkovTileN = 64;
+constexpr int kMarkovMaxTiles = 256 * 16;  // the draw keeps 16 tile pairs per thread: V <= 262,144
 constexpr int kMaxGamma = 64;
 // Scratch of the allocation-free token verification (a file-scope device
 // array, one per GPU): row-chunk statistics, request state and segment sums.
