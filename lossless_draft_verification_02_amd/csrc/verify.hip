@@ -1063,12 +1063,12 @@ hipError_t block_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
                            (const float *)ctx->ws.lq2, (const double *)ctx->ws.wrun, ctx->ws.bm, ctx->nseg);
         svh::prof_end(ctx, s, slot);
     }
-    if (fused_tail_fits(ctx, a)) {
-        launch_fused_tail<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
-    } else {
-        launch_accept<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
-        launch_sum_and_select<PES, QES>(ctx, a, s);
-    }
+    // the final stage, then the correction / bonus sums over many workgroups
+    // per request (most requests' sums come from pass 2; the rest stream a
+    // row or two, which one workgroup per request would do at one CU's
+    // rate), then the selection
+    launch_accept<PES, QES>(ctx, a, s, STAGE_BLOCK_FINAL);
+    launch_sum_and_select<PES, QES>(ctx, a, s);
     return hipGetLastError();
 }
 
