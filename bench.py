@@ -52,6 +52,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rowstats_headline_traffic.json")
 ROWSTATS_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
                     for f in ("rowstats.hip", "sv_rowstats.h", "sv_device.h")]
 MARKOV_COUNTERS_FILE = os.path.join(ROOT, "profiles", "markov_gemm_counters.json")
+TAIL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tail_headline_traffic.json")
+TAIL_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
+                for f in ("verify.hip", "sv_rowstats.h", "sv_device.h")]
 MARKOV_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_02_amd", "csrc", f)
                   for f in ("markov.hip", "sv_device.h")]
 
@@ -71,6 +74,18 @@ def measured_traffic(bytes_per_launch_alg):
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def tail_traffic():
+    """The headline tail's committed counter bytes per launch, or None if
+    absent or taken on other sources."""
+    if not os.path.exists(TAIL_TRAFFIC_FILE):
+        return None
+    with open(TAIL_TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_digest(TAIL_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -355,6 +370,18 @@ def bench_headline(args, L, WL):
     alg = WL.bytes_single_read(vi)
     roofline = _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats"), measured_traffic(alg))
     call_gbps = call_bytes / (ms * 1e-3) / 1e9
+    # the tail (acceptance, correction / bonus sums, draw): the rows the draws
+    # re-read per call, over the tail's own time; with the committed counter
+    # bytes when they were taken on the current sources
+    tail_us = _mean_us(prof, "tail")
+    tail_alg = reread / args.steps
+    tail_hbm = tail_traffic()
+    tail_roofline = {"bound": "hbm (re-read) + latency", "achieved": round(tail_alg / (tail_us * 1e-6) / 1e9, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(tail_alg / (tail_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "alg_bytes_per_launch": int(tail_alg), "mean_us": tail_us, "traffic": tail_hbm,
+                     "traffic_gbps": (round(tail_hbm / (tail_us * 1e-6) / 1e9, 1) if tail_hbm else None),
+                     "what": "k_tail: the rows each request's draw re-reads (2 after a rejection, 1 for a bonus)"}
     call_roofline = {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / PEAK_HBM_GBPS, 4), "alg_bytes_per_call": int(call_bytes),
                      "what": "whole verification call: every verified row once + the draw's re-read rows"}
@@ -367,7 +394,7 @@ def bench_headline(args, L, WL):
     return _line(METRIC, B * gamma / (ms / 1e3), "verified positions/s", args, ms,
                  {"workload": "token-level verification, headline batch", "B": B, "gamma": gamma, "V": V,
                   "logits": "bf16", "temperature": cfg["T"], "input_sets": len(sets)},
-                 roofline, cpu_baseline=cpu, parity=parity, call_roofline=call_roofline,
+                 roofline, cpu_baseline=cpu, parity=parity, call_roofline=call_roofline, tail_roofline=tail_roofline,
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  mean_accepted=round(accepted, 4), wall_ms_per_step=round(wall_ms, 5), copy_probe=copy_probe,
