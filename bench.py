@@ -382,9 +382,13 @@ def bench_headline(args, L, WL):
                      "alg_bytes_per_launch": int(tail_alg), "mean_us": tail_us, "traffic": tail_hbm,
                      "traffic_gbps": (round(tail_hbm / (tail_us * 1e-6) / 1e9, 1) if tail_hbm else None),
                      "what": "k_tail: the rows each request's draw re-reads (2 after a rejection, 1 for a bonus)"}
+    single_gbps = alg / (ms * 1e-3) / 1e9
     call_roofline = {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(call_gbps / PEAK_HBM_GBPS, 4), "alg_bytes_per_call": int(call_bytes),
-                     "what": "whole verification call: every verified row once + the draw's re-read rows"}
+                     "what": "whole verification call: every verified row once + the draw's re-read rows",
+                     "single_read_achieved": round(single_gbps, 1),
+                     "single_read_frac": round(single_gbps / PEAK_HBM_GBPS, 4),
+                     "single_read_what": "the same call counting every verified row once and nothing else"}
     copy_probe = _copy_probe()
     ctx.close()
     cpu, parity = None, None

@@ -133,6 +133,35 @@ def make_ctx(B, gamma, V, R=0):
 
 # ------------------------------------------------- token verification ----
 
+@pytest.mark.parametrize("block", [False, True])
+@pytest.mark.parametrize("V", [6008, 40000])
+def test_zero_residual_falls_back_to_p(V, block):
+    """q equal to p at every draft position and acceptance uniforms forced to
+    1: every request rejects its first position, the residual max(p - q, 0)
+    is zero everywhere, so the correction is drawn from p instead and flagged
+    SV_FLAG_RESID_ZERO, as the oracle does ("Speculative Decoding: The Same
+    Distribution, Twice as Fast", section 4: in exact arithmetic a rejection
+    implies p != q).  V = 6008 takes the single launch, 40,000 the split tail
+    (token rule) or the block stages.  Both keep every bf16 row 16-byte
+    aligned: a p row and an equal q row at different alignments are summed in
+    different orders, so their normalisers can differ in the last place and
+    leave a residual of rounding noise, which the kernels draw from (the
+    oracle, in fp64, gets exactly zero)."""
+    import dataclasses
+    B, gamma = 12, 4
+    _say(f"case: zero residual V={V} block={block}")
+    vi = WL.make_verify_inputs("headline", "cuda", B=B, gamma=gamma, V=V)
+    vi = dataclasses.replace(vi, q=vi.p[:, :gamma].contiguous())
+    u = torch.ones(B, gamma + 1, device="cuda")
+    u[:, gamma] = torch.rand(B, generator=torch.Generator().manual_seed(77)).to("cuda")
+    with make_ctx(B, gamma, V) as ctx:
+        g, o, rep = check_verify(ctx, vi, block=block, uniforms=u,
+                                 verify_len=np.full(B, gamma, np.int32) if block else None,
+                                 label=f"zero residual V={V} block={block}")
+    assert (g["accepted_len"] == 0).all()
+    assert (g["flags"] == L.binding.SV_FLAG_RESID_ZERO).all()
+
+
 def test_tiny_config_many_rounds():
     """The tiny workload (B=1, gamma=4, V=1000, fp32) over 300 offsets."""
     _say("case: tiny workload, 300 offsets")
