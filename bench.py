@@ -373,7 +373,10 @@ def bench_headline(args, L, WL):
     # the tail (acceptance, correction / bonus sums, draw): the rows the draws
     # re-read per call, over the tail's own time; with the committed counter
     # bytes when they were taken on the current sources
-    tail_us = _mean_us(prof, "tail")
+    # (the fused k_tail, or the split accept+sums / select pair where the
+    # library routes the batch that way)
+    tail_us = (_mean_us(prof, "tail") if prof["tail"][1]
+               else sum(_mean_us(prof, k) for k in ("resid", "select") if prof[k][1]))
     tail_alg = reread / args.steps
     tail_hbm = tail_traffic()
     tail_roofline = {"bound": "hbm (re-read) + latency", "achieved": round(tail_alg / (tail_us * 1e-6) / 1e9, 1),

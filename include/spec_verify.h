@@ -280,7 +280,7 @@ sv_status markov_draft_run(sv_ctx *ctx, hipStream_t stream,
  * row per request that the residual max(p - q, 0) needs (position tau + 1) is
  * rebuilt after the acceptance scan with the sampler's own arithmetic, so it
  * equals the row the token was drawn from, and weighed as it is built: the
- * correction / bonus weights are summed per 128-token tile and the token is
+ * correction / bonus weights are summed per 64-token tile and the token is
  * drawn from those sums and the chosen tile's weights (rebuilt again the same
  * way), so no draft row is ever stored.  Decisions equal those of
  * markov_draft_run then spec_verify_run up to the fp32 rounding of the draft
@@ -317,7 +317,7 @@ sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream,
  *   states        [B, gamma, R] bf16 out or NULL: hb_k, the state position k
  *                 used (not written for a request whose draw failed)
  *   other arguments as markov_draft_run.  With q_logits NULL no logit row is
- *   stored (the draw rebuilds the 128 logits of its chosen tile); the
+ *   stored (the draw rebuilds the 64 logits of its chosen tile); the
  *   context's workspace holds the state between positions, so calls on one
  *   context must not overlap. */
 sv_status rnn_draft_run(sv_ctx *ctx, hipStream_t stream,

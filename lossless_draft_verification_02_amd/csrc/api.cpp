@@ -172,6 +172,7 @@ svh::MarkovArgs make_markov_args(const void *base_logits, const void *U, const v
     a.A = nullptr;
     a.hstate = nullptr;
     a.states_out = nullptr;
+    a.ride = svh::RowRide{nullptr, 0, 0, 0, 0.0f, nullptr, 0};
     return a;
 }
 
@@ -643,23 +644,27 @@ sv_status markov_verify_run(sv_ctx *ctx, hipStream_t stream, const void *base_lo
     if (!aligned(p_logits, esize_of(p_dtype)))
         return fail(SV_ERR_INVALID, "markov_verify_run: p_logits must be aligned to its element size");
     DeviceGuard guard(ctx->device);
-    // 1. the draft: no z rows stored; the sampler records each row's
-    //    log2-sum-exp2 and the drafted tokens' logits
-    svh::MarkovArgs m = make_markov_args(base_logits, U, W, R, x0, B, gamma, V, temperature, draft_seed, offset,
-                                         nullptr, draft_tokens, nullptr, lse_q);
-    m.fused = true;
-    m.lse2_out = ctx->ws.mk_lse2;
-    m.zx_out = ctx->ws.mk_zx;
-    if ((st = check_launch(svh::launch_markov(ctx, m, stream), "Markov sampler")) != SV_OK) return st;
-    // 2. verification of that draft: row statistics of p only, the scan with
-    //    the sampler's q statistics, the correction / bonus weights of the
-    //    rebuilt correction rows summed per tile, the draw
     svh::VerifyArgs a = make_args(p_logits, p_dtype, nullptr, SV_F32, draft_tokens, nullptr, B, gamma, V,
                                   temperature, verify_seed, offset, nullptr, accepted_len, out_tokens, diag, false);
     a.q_esize = 4;
     a.q_lse2 = ctx->ws.mk_lse2;
     a.q_zx = ctx->ws.mk_zx;
-    if ((st = check_launch(svh::launch_rowstats(ctx, a, stream), "row statistics")) != SV_OK) return st;
+    // 1. the draft: no z rows stored; the sampler records each row's
+    //    log2-sum-exp2 and the drafted tokens' logits.  The chunk
+    //    statistics of the p rows (they do not depend on the draft) ride in
+    //    the draws' launches, whose few dependent round trips leave the
+    //    memory system idle.
+    svh::MarkovArgs m = make_markov_args(base_logits, U, W, R, x0, B, gamma, V, temperature, draft_seed, offset,
+                                         nullptr, draft_tokens, nullptr, lse_q);
+    m.fused = true;
+    m.lse2_out = ctx->ws.mk_lse2;
+    m.zx_out = ctx->ws.mk_zx;
+    m.ride = svh::RowRide{a.p, a.p_esize, ctx->nch1, ctx->chunk1, a.c, ctx->ws.part,
+                          (int64_t)B * (gamma + 1) * ctx->nch1};
+    if ((st = check_launch(svh::launch_markov(ctx, m, stream), "Markov sampler")) != SV_OK) return st;
+    // 2. verification of that draft: the scan with the sampler's q
+    //    statistics, the correction / bonus weights of the rebuilt correction
+    //    rows summed per tile, the draw
     if ((st = check_launch(svh::launch_markov_verify_tail(ctx, a, m, stream), "fused verification")) != SV_OK)
         return st;
     return ok();

@@ -10,30 +10,29 @@
 // Per position k (strictly sequential; x_0 is the anchor token):
 //   k_markov_gemm    z[b, n] = base[b, k, n] + sum_r U[x_{k-1}(b), r] Wt[n, r]
 //                    computed transposed, z^T = Wt . U^T, with bf16 MFMA
-//                    (16x16x32, fp32 accumulate).  Workgroups of eight
-//                    wavefronts loop over 128-token tiles; each tile of Wt
-//                    (the transition matrix stored vocabulary-major, V rows
-//                    of R) is copied into a two-slot LDS ring by direct
-//                    global -> LDS loads and gives the A operand; the U rows
-//                    (or states) of the workgroup's 128 requests give the B
-//                    operand and stay in registers for the whole launch.  At
-//                    rank 256 a wavefront covers 32 requests x 64 rows of a
-//                    tile, so each A fragment read from LDS feeds two MFMAs.
-//                    Each accumulator lane holds 4 consecutive vocabulary
-//                    entries of one request, so the epilogue adds the base
-//                    logits and stores 16-byte runs of z without a detour
-//                    through LDS, and reduces per (request, 128-token tile)
-//                    the pair (max z*c, sum exp2(z*c - max)).  The next
-//                    tile's copy and base logits are requested a few
-//                    instructions at a time through the MFMAs and the
-//                    epilogue, so the small per-CU miss queue never blocks
-//                    the wavefront's arithmetic for long.
+//                    (16x16x32, fp32 accumulate).  One workgroup per CU of
+//                    eight compute and four loader wavefronts walks 64-token
+//                    tiles: the loaders copy each tile of Wt (the transition
+//                    matrix stored vocabulary-major, V rows of R) and the
+//                    tile's base logits straight from global memory into a
+//                    three-slot LDS ring, two tiles ahead; the compute
+//                    wavefronts hold the U rows (or states) of the
+//                    workgroup's 128 requests as B fragments in registers
+//                    for the whole launch, read the A fragments from LDS
+//                    (at rank 256 each feeds two MFMAs), add the base logits
+//                    and reduce per (request, tile) the pair (max z*c,
+//                    sum exp2(z*c - max)); z itself is stored only when the
+//                    caller asks for the draft logits.
 //   k_markov_draw    one 256-thread workgroup per request: the row maximum
 //                    of the tile pairs, the tile masses relative to it and
 //                    their fp64 prefix over the workgroup, the tile holding
-//                    u * Z, then that tile's 128 logits (read back, or rebuilt
+//                    u * Z, then that tile's 64 logits (read back, or rebuilt
 //                    by MFMA when no z rows are stored) scanned for the token
-//                    (inverse CDF in ascending token order).
+//                    (inverse CDF in ascending token order).  In the fused
+//                    draft -> verification path the launch carries further
+//                    workgroups that compute chunk statistics of the target
+//                    rows (they do not depend on the draft), using the memory
+//                    bandwidth the draw's few dependent round trips leave idle.
 //
 // RNN head ("DeepSeek DSpark 详解", section 03, and "DSpark: DeepSeek's bet
 // on speed that doesn't betray quality", section "A drafter that learns to
@@ -50,6 +49,7 @@
 
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_rowstats.h"
 
 namespace {
 
@@ -686,6 +686,9 @@ void k_markov_gemm(
     if (nt > 0) merge_parts((nt - 1) & 1, tile_of(nt - 1));
 }
 
+#ifndef SV_MARKOV_RIDE_WGS_PER_CU
+#define SV_MARKOV_RIDE_WGS_PER_CU 4   // riding target-row workgroups per CU in a draw launch
+#endif
 constexpr int kDrawThreads = 256;                                        // one workgroup per request
 constexpr int kDrawWaves = kDrawThreads / 64;
 constexpr int kDrawTilesPerThread = svh::kMarkovMaxTiles / kDrawThreads;  // tile pairs held per thread
@@ -906,8 +909,72 @@ __device__ int32_t select_token_in_tile(const svh::MarkovArgs &a, int k, int b, 
     return jj >= 0 ? (int32_t)(c0 + jj) : -1;
 }
 
+// The riding workgroups of one draw launch: workgroup w of nw takes items
+// first + w, first + w + nw, ... below end; item i is chunk i % nch1 of
+// target row i / nch1, reduced exactly as the row-statistics pass reduces it
+// (the same per-thread loads and fold order, the same workgroup merge) into
+// part[i].  When a chunk is one load batch per thread (bf16 chunks of at
+// most 32 KB) the next item's batch is requested before the current one is
+// folded, so each workgroup keeps its loads in flight through the
+// arithmetic.
+__device__ void ride_items(const svh::RowRide &r, int64_t V, int64_t first, int64_t end, int64_t nw)
+{
+    static_assert(kDrawThreads == svh::kRowstatsThreads, "the row-statistics workgroup shape");
+    constexpr int NB = svh::kRowstatsNB, NT = kDrawThreads;
+    __shared__ svk::MS red[2][NT / 64];   // alternating: a wavefront may start the next merge early
+    const bool nt = SV_ROWSTATS_NT_LOADS;
+    const int tid = threadIdx.x;
+    int par = 0;
+    auto plan = [&](int64_t item, auto esize) {
+        constexpr int ES = decltype(esize)::value;
+        const int64_t row = item / r.nch1;
+        const int64_t e0 = (item - row * r.nch1) * r.chunk1;
+        const int64_t e1 = e0 + r.chunk1 < V ? e0 + r.chunk1 : V;
+        return svk::chunk_plan<ES>((const char *)r.p + row * V * ES, e0, e1);
+    };
+    auto emit = [&](int64_t item, svk::MS t) {
+        const svk::MS tot = svk::block_merge<NT>(t, red[par]);
+        par ^= 1;
+        if (tid == 0) r.part[item] = make_float2(tot.m, tot.s);
+    };
+    if (r.pes == 2 && r.chunk1 * 2 + 16 <= (int64_t)NT * NB * 16) {
+        using E2 = std::integral_constant<int, 2>;
+        if (first >= end) return;
+        svk::ChunkPlan<2> cur = plan(first, E2{});
+        svk::u32x4 raw[NB];
+        svk::load_batch<2, NB, NT>(cur, tid, nt, raw);
+        for (int64_t item = first; item < end; item += nw) {
+            const int64_t nx = item + nw;
+            svk::ChunkPlan<2> nxt = cur;
+            svk::u32x4 rawn[NB];
+            if (nx < end) {
+                nxt = plan(nx, E2{});
+                svk::load_batch<2, NB, NT>(nxt, tid, nt, rawn);
+            }
+            svk::RunStats st = svk::run_start();
+            svk::fold_batch<2, NB>(raw, r.c, st);
+            emit(item, svk::run_finish<2>(cur, r.c, tid, st));
+            cur = nxt;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) raw[j] = rawn[j];
+        }
+    } else {
+        for (int64_t item = first; item < end; item += nw) {
+            svk::MS t;
+            if (r.pes == 2) {
+                const svk::ChunkPlan<2> pl = plan(item, std::integral_constant<int, 2>{});
+                t = svk::thread_stats<2, NB, NT>(pl.rowptr, pl.e0, pl.e1, r.c, nt, tid);
+            } else {
+                const svk::ChunkPlan<4> pl = plan(item, std::integral_constant<int, 4>{});
+                t = svk::thread_stats<4, NB, NT>(pl.rowptr, pl.e0, pl.e1, r.c, nt, tid);
+            }
+            emit(item, t);
+        }
+    }
+}
+
 // The draw at position k: one workgroup of four wavefronts per request.  All
-// threads choose the tile; its 128 logits come from the stored z rows (zin)
+// threads choose the tile; its 64 logits come from the stored z rows (zin)
 // or, without them (fused path), are rebuilt by the four wavefronts (two
 // 16-row blocks each) with the contraction's own arithmetic -- same A rows,
 // same k order, same base add -- so they equal, bit for bit, the values
@@ -918,10 +985,15 @@ template <int R>
 __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a, int k,
                                                               const float *__restrict__ zin, int64_t zstride,
                                                               const float2 *__restrict__ tile_part, int ntile,
-                                                              uint32_t *__restrict__ errword)
+                                                              uint32_t *__restrict__ errword, int64_t ride0,
+                                                              int64_t ride_n)
 {
     constexpr int KS = R / 32;
     constexpr int VBW = NVB / kDrawWaves;   // 16-row blocks per wavefront
+    if ((int)blockIdx.x >= a.B) {   // workgroups past the draws: riding target-row chunks
+        ride_items(a.ride, a.V, ride0 + ((int64_t)blockIdx.x - a.B), ride0 + ride_n, (int64_t)gridDim.x - a.B);
+        return;
+    }
     __shared__ DrawLDS L;
     __shared__ float zt[TN];
     __shared__ float hs[R];    // RNN head: the request's state
@@ -996,7 +1068,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
 //                 the first tile whose cumulative sum, rounded to binary32,
 //                 exceeds fp32(u' * fp32(Z)), else the last tile with weight
 //                 (inverse CDF in ascending token order, as the oracle's);
-//   the tile      its 128 weights with the residual epilogue's arithmetic:
+//   the tile      its 64 weights with the residual epilogue's arithmetic:
 //                 the draft logits rebuilt by MFMA as the Markov draw does
 //                 (same Wt rows, same k order, same base add), the target
 //                 logits read back, both weighed by resid_weight;
@@ -1237,15 +1309,22 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
     const int64_t zstride = a.q_logits ? (int64_t)a.gamma * a.V : a.V;
     const int vec = base_rows_aligned(a);
     const int zvec = (a.V % 4 == 0) && ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
+    // riding target-row chunks: an even share per draw
+    const int64_t ride_per = a.ride.items > 0 ? (a.ride.items + a.gamma - 1) / a.gamma : 0;
     for (int k = 1; k <= a.gamma; ++k) {
+        const int64_t r0 = ride_per * (k - 1);
+        const int64_t rn = a.ride.items - r0 < ride_per ? (a.ride.items - r0 > 0 ? a.ride.items - r0 : 0) : ride_per;
         float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
         hipLaunchKernelGGL((k_markov_gemm<R, 0>), dim3(gx, gy), dim3(NTG), 0, s, a, k, (const svh::ReqG *)nullptr,
                            zk, zstride, ctx->ws.mk_part, ntile, vec, zvec, ResidArgs{nullptr, nullptr}, 0);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
-        hipLaunchKernelGGL((k_markov_draw<R>), dim3(a.B), dim3(kDrawThreads), 0, s, a, k, (const float *)zk, zstride,
-                           (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword);
+        const int64_t cap = (int64_t)SV_MARKOV_RIDE_WGS_PER_CU * ctx->num_cu;
+        const int64_t nride = rn < cap ? rn : cap;
+        hipLaunchKernelGGL((k_markov_draw<R>), dim3((unsigned)(a.B + nride)), dim3(kDrawThreads), 0, s, a, k,
+                           (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword, r0,
+                           rn);
         svh::prof_end(ctx, s, slot);
     }
     return hipGetLastError();

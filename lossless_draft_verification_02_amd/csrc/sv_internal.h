@@ -220,6 +220,20 @@ struct StsTemps {
 hipError_t launch_schedule(sv_ctx *ctx, const float *conf, const StsTemps &sts, int B, int gamma, float sps_a,
                            float sps_k, int32_t *verify_len, double *expected, hipStream_t s);
 
+// Chunk statistics of the target rows carried by the draws of the fused
+// Markov draft -> verification path: item i is chunk i % nch1 of p row
+// i / nch1 ([B, gamma + 1] rows), written to part[i] as the row-statistics
+// pass would.  items == 0: nothing rides.
+struct RowRide {
+    const void *p;
+    int pes;               // 2 (bf16) or 4 (fp32)
+    int nch1;
+    int64_t chunk1;
+    float c;
+    float2 *part;
+    int64_t items;
+};
+
 struct MarkovArgs {
     const uint16_t *base;  // [B, gamma, V] bf16
     const uint16_t *U;     // [V, R]
@@ -235,7 +249,7 @@ struct MarkovArgs {
     float *q_logits;       // may be null
     float *lse_q;          // may be null
     // Fused draft -> verification: no z row is stored; the draw rebuilds the
-    // 128 logits of its chosen tile with the same MFMA sequence, and records
+    // 64 logits of its chosen tile with the same MFMA sequence, and records
     // per (request, position) the row's log2-sum-exp2 of z * c and the drawn
     // token's raw logit.
     bool fused;
@@ -248,6 +262,7 @@ struct MarkovArgs {
     const uint16_t *A;     // [R, R] bf16, linear-layer layout: A[j][r] takes state entry r into j
     uint16_t *hstate;      // [B, R] bf16 workspace
     uint16_t *states_out;  // [B, gamma, R] bf16 or null
+    RowRide ride;          // target-row statistics spread over the gamma draws
 };
 
 hipError_t launch_markov(sv_ctx *ctx, const MarkovArgs &a, hipStream_t s);
