@@ -981,7 +981,7 @@ __device__ void ride_items(const svh::RowRide &r, int64_t V, int64_t first, int6
 // reduced into the tile pairs; the B fragments of that rebuild are requested
 // before the tile choice.  Wavefront 0 then draws the token; for the RNN head
 // the four wavefronts advance the request's state.
-template <int R>
+template <int R, bool RIDE>
 __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a, int k,
                                                               const float *__restrict__ zin, int64_t zstride,
                                                               const float2 *__restrict__ tile_part, int ntile,
@@ -990,7 +990,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
 {
     constexpr int KS = R / 32;
     constexpr int VBW = NVB / kDrawWaves;   // 16-row blocks per wavefront
-    if ((int)blockIdx.x >= a.B) {   // workgroups past the draws: riding target-row chunks
+    if (RIDE && (int)blockIdx.x >= a.B) {   // workgroups past the draws: riding target-row chunks
         ride_items(a.ride, a.V, ride0 + ((int64_t)blockIdx.x - a.B), ride0 + ride_n, (int64_t)gridDim.x - a.B);
         return;
     }
@@ -1322,9 +1322,14 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
         const int64_t cap = (int64_t)SV_MARKOV_RIDE_WGS_PER_CU * ctx->num_cu;
         const int64_t nride = rn < cap ? rn : cap;
-        hipLaunchKernelGGL((k_markov_draw<R>), dim3((unsigned)(a.B + nride)), dim3(kDrawThreads), 0, s, a, k,
-                           (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword, r0,
-                           rn);
+        if (nride > 0)
+            hipLaunchKernelGGL((k_markov_draw<R, true>), dim3((unsigned)(a.B + nride)), dim3(kDrawThreads), 0, s, a,
+                               k, (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword,
+                               r0, rn);
+        else
+            hipLaunchKernelGGL((k_markov_draw<R, false>), dim3((unsigned)a.B), dim3(kDrawThreads), 0, s, a, k,
+                               (const float *)zk, zstride, (const float2 *)ctx->ws.mk_part, ntile, ctx->ws.errword,
+                               (int64_t)0, (int64_t)0);
         svh::prof_end(ctx, s, slot);
     }
     return hipGetLastError();
