@@ -38,6 +38,13 @@
 #include "sv_internal.h"
 #include "sv_rowstats.h"
 
+// The acceptance, fused-tail and selection kernels are latency-bound: one
+// wavefront's path through them (a few thousand instructions, run once per
+// request) sets their time, and its instruction fetches on a cold CU are a
+// good part of it, so they are compiled for size (measured: the one-launch
+// small call 14.1 -> 13.3 us, the others unchanged).
+#define SV_LATENCY_KERNEL __attribute__((minsize))
+
 namespace {
 
 using svk::u32x4;
@@ -351,12 +358,11 @@ __device__ void accept_eval(const svh::VerifyArgs &a, const float2 *__restrict__
 }
 
 template <int PES, int QES>
-__global__ __launch_bounds__(svk::kWave) void k_accept(svh::VerifyArgs a, const float2 *__restrict__ part,
-                                                       int nch1, const float *__restrict__ bm, int nseg,
-                                                       int stage, ReqG *__restrict__ req,
-                                                       float *__restrict__ lp2g, float *__restrict__ lq2g,
-                                                       double *__restrict__ wrun,
-                                                       uint32_t *__restrict__ errword)
+__global__ __launch_bounds__(svk::kWave)
+SV_LATENCY_KERNEL void k_accept(
+    svh::VerifyArgs a, const float2 *__restrict__ part, int nch1, const float *__restrict__ bm, int nseg,
+    int stage, ReqG *__restrict__ req, float *__restrict__ lp2g, float *__restrict__ lq2g,
+    double *__restrict__ wrun, uint32_t *__restrict__ errword)
 {
     __shared__ AcceptLDS s;
     const int b = a.b0 + (int)blockIdx.x;
@@ -816,9 +822,10 @@ __device__ int select_token_wave(const svh::VerifyArgs &a, int mode, float wmul,
 // bonus token from the segment sums (k_resid_sum's or block pass 2's) with
 // the fused tail's wavefront draw.
 template <int PES, int QES>
-__global__ __launch_bounds__(svk::kWave) void k_select(svh::VerifyArgs a, const ReqG *__restrict__ req,
-                                                       float *__restrict__ csum, const float *__restrict__ bm,
-                                                       int nseg, uint32_t *__restrict__ errword)
+__global__ __launch_bounds__(svk::kWave)
+SV_LATENCY_KERNEL void k_select(
+    svh::VerifyArgs a, const ReqG *__restrict__ req, float *__restrict__ csum, const float *__restrict__ bm,
+    int nseg, uint32_t *__restrict__ errword)
 {
     __shared__ int32_t xs[MAXG];
     const int b = a.b0 + (int)blockIdx.x;
@@ -897,12 +904,11 @@ __device__ void small_rowstats(const svh::VerifyArgs &a, int b, float2 *__restri
 }
 
 template <int PES, int QES, int NTT>
-__global__ __launch_bounds__(NTT, 4) void k_tail(svh::VerifyArgs a, float2 *__restrict__ part, int nch1,
-                                              const float *__restrict__ bm, int nseg, int stage,
-                                              const ReqG *__restrict__ pre,
-                                              float *__restrict__ lp2g, float *__restrict__ lq2g,
-                                              double *__restrict__ wrun, uint32_t *__restrict__ errword,
-                                              int small)
+__global__ __launch_bounds__(NTT, 4)
+SV_LATENCY_KERNEL void k_tail(
+    svh::VerifyArgs a, float2 *__restrict__ part, int nch1, const float *__restrict__ bm, int nseg, int stage,
+    const ReqG *__restrict__ pre, float *__restrict__ lp2g, float *__restrict__ lq2g, double *__restrict__ wrun,
+    uint32_t *__restrict__ errword, int small)
 {
     __shared__ AcceptLDS as;
     __shared__ ReqG r;
