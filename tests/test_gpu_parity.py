@@ -1062,9 +1062,25 @@ def check_markov_verify(ctx, mi, req, label):
     """Fused path against (a) the unfused GPU sampler, bit for bit on the
     draft, and (b) the oracle's draft followed by the oracle's verification."""
     d, lse, res = gpu_markov_verify(ctx, mi)
-    d2, _, lse2 = gpu_markov(ctx, mi, want_q=True)
+    d2, q2, lse2 = gpu_markov(ctx, mi, want_q=True)
     assert torch.equal(d, d2), "fused and unfused samplers drew different drafts"
     assert torch.equal(lse, lse2), "fused and unfused samplers report different normalisers"
+    # the target rows' statistics, which the fused path computes in workgroups
+    # riding in the draws, against token verification's own pass: the same
+    # per-thread order and workgroup merge, so equal bit for bit when that
+    # call runs the row pass (more than one chunk per row); a single-chunk row
+    # takes the one-launch route there, which merges per wavefront
+    B, gamma = d.shape
+    lp = torch.empty(B, gamma + 1, device="cuda")
+    acc2 = torch.empty(B, dtype=torch.int32, device="cuda")
+    out2 = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
+    L.spec_verify_run(ctx, mi.p, q2, d2, acc2, out2, temperature=mi.T, seed=WL.VERIFY_SEED, diag=dict(lse_p=lp))
+    torch.cuda.synchronize()
+    lp_f, lp_t = res["lse_p"], lp.cpu().numpy()
+    if mi.V > 16384:
+        assert np.array_equal(lp_f, lp_t, equal_nan=True), "fused and row-pass target statistics differ"
+    else:
+        assert np.allclose(lp_f, lp_t, rtol=0, atol=1e-5, equal_nan=True), np.nanmax(np.abs(lp_f - lp_t))
     o = oracle_markov(mi, req)
     rep = compare_markov(d.cpu().numpy()[req], lse.cpu().numpy()[req], None, o)
     _say(f"[{label} draft] {rep}")
