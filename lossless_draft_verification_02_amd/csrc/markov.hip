@@ -37,14 +37,15 @@
 // RNN head ("DeepSeek DSpark 详解", section 03, and "DSpark: DeepSeek's bet
 // on speed that doesn't betray quality", section "A drafter that learns to
 // doubt itself": the richer head variant carries a recurrent state over the
-// block's prefix, so a draw can use more of it than the previous token).  Same contraction and draw, with the bf16 state hb_k as the left
-// operand in place of U[x_{k-1}]: h_0 = 0, a_k = U[x_{k-1}] + A hb_{k-1}
-// (A in linear-layer layout [out, in]; fp32, sequential fused multiply-adds
-// over the state index starting from U[x_{k-1}]), hb_k = bf16(tanh(a_k)),
-// round to nearest even.  hb_1 =
-// bf16(tanh(U[x_0])) is formed wherever it is read; after drawing x_k the
-// draw's workgroup computes hb_{k+1} for its request (a 256 x 256 product,
-// A read from L2) and leaves it for the next position's contraction.
+// block's prefix, so a draw can use more of it than the previous token).
+// Same contraction and draw, with the bf16 state hb_k as the left operand in
+// place of U[x_{k-1}]: h_0 = 0, a_k = U[x_{k-1}] + A hb_{k-1} (A in
+// linear-layer layout [out, in]; fp32, sequential fused multiply-adds over
+// the state index starting from U[x_{k-1}]), hb_k = bf16(tanh(a_k)), round to
+// nearest even.  hb_1 = bf16(tanh(U[x_0])) is written to the state buffer by
+// a small kernel before position 1; after drawing x_k the draw's workgroup
+// computes hb_{k+1} for its request (a 256 x 256 product, A read from L2)
+// and leaves it for the next position's contraction.
 #include <type_traits>
 
 #include "sv_device.h"
@@ -91,9 +92,19 @@ __device__ __forceinline__ uint16_t rnn_first_state(const svh::MarkovArgs &a, in
     return f32_to_bf16(tanhf(bf16_to_f32(a.U[(int64_t)x * a.R + j])));
 }
 
+// hb_1 = bf16(tanh(U[x_0])) of every request into the state buffer, before
+// position 1: the contraction and the draw then read every state from it,
+// and neither carries the tanh code.
+__global__ void k_rnn_first_state(svh::MarkovArgs a)
+{
+    const int b = blockIdx.x;
+    for (int j = threadIdx.x; j < a.R; j += blockDim.x)
+        a.hstate[(int64_t)b * a.R + j] = rnn_first_state(a, b, j);
+}
+
 // The contraction's left operand for request m at position k, as the KS
 // fragments of lane group lg (entries 8 lg + 32 s .. + 7): U[x_{k-1}] for the
-// Markov head, the state hb_k for the RNN head.
+// Markov head, the state hb_k for the RNN head (hb_1 written beforehand).
 template <int R>
 __device__ __forceinline__ void head_fragments(const svh::MarkovArgs &a, int k, int m, int lg, bool act,
                                                bf16x8 (&ufr)[R / 32])
@@ -108,14 +119,6 @@ __device__ __forceinline__ void head_fragments(const svh::MarkovArgs &a, int k, 
         const uint16_t *urow = a.U + (int64_t)prev_token(a, k, m) * R + 8 * lg;
 #pragma unroll
         for (int s = 0; s < KS; ++s) ufr[s] = *(const bf16x8 *)(urow + 32 * s);
-    } else if (k == 1) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            uint16_t h[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = rnn_first_state(a, m, 8 * lg + 32 * s + e);
-            ufr[s] = __builtin_bit_cast(bf16x8, h);
-        }
     } else {
         const uint16_t *hrow = a.hstate + (int64_t)m * R + 8 * lg;
 #pragma unroll
@@ -145,7 +148,7 @@ __device__ void rnn_fill(const svh::MarkovArgs &a, int k, int b, float *hs, int 
         const int i = lane + 64 * q;
         if (i < PER) {
             const int j = part * PER + i;
-            const uint16_t hbits = k == 1 ? rnn_first_state(a, b, j) : hrow[j];
+            const uint16_t hbits = hrow[j];
             hs[j] = bf16_to_f32(hbits);
             if (a.states_out) a.states_out[((int64_t)b * a.gamma + (k - 1)) * R + j] = hbits;
         }
@@ -476,10 +479,12 @@ void k_markov_gemm(
                     copy_base_unaligned(brow[q], n0, a.V, sl + TL::BYTES, lw + NLW * q, lane);
             }
         };
+        // tile 0 alone first: at the start every CU's first copies compete
+        // for the memory system, and the compute wavefronts can begin as
+        // soon as one tile has landed; tile 1 follows while they multiply it
         if (nt > 0) issue(0);
+        __builtin_amdgcn_s_waitcnt(0);           // tile 0 landed (element copies: their LDS stores too)
         if (nt > 1) issue(1);
-        if (nt > 1 && vec) wait_vm<GS::PER>();   // tile 0 landed
-        else __builtin_amdgcn_s_waitcnt(0);     // (element copies: their LDS stores too)
         loader_barrier();
         for (int j = 0; j < nt; ++j) {
             const bool more = j + 2 < nt;
@@ -1311,6 +1316,7 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
     const int zvec = (a.V % 4 == 0) && ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
     // riding target-row chunks: an even share per draw
     const int64_t ride_per = a.ride.items > 0 ? (a.ride.items + a.gamma - 1) / a.gamma : 0;
+    if (a.A) hipLaunchKernelGGL(k_rnn_first_state, dim3(a.B), dim3(a.R < 256 ? a.R : 256), 0, s, a);
     for (int k = 1; k <= a.gamma; ++k) {
         const int64_t r0 = ride_per * (k - 1);
         const int64_t rn = a.ride.items - r0 < ride_per ? (a.ride.items - r0 > 0 ? a.ride.items - r0 : 0) : ride_per;
