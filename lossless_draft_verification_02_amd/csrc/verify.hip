@@ -903,24 +903,23 @@ __device__ void small_rowstats(const svh::VerifyArgs &a, int b, float2 *__restri
     }
 }
 
-template <int PES, int QES, int NTT>
+template <int PES, int QES, int NTT, bool SMALL>
 __global__ __launch_bounds__(NTT, 4)
 SV_LATENCY_KERNEL void k_tail(
-    svh::VerifyArgs a, float2 *__restrict__ part, int nch1, const float *__restrict__ bm, int nseg, int stage,
-    const ReqG *__restrict__ pre, float *__restrict__ lp2g, float *__restrict__ lq2g, double *__restrict__ wrun,
-    uint32_t *__restrict__ errword, int small)
+    svh::VerifyArgs a, float2 *__restrict__ part, int nch1, int nseg, uint32_t *__restrict__ errword)
 {
     __shared__ AcceptLDS as;
     __shared__ ReqG r;
     __shared__ float segsum[kTailMaxSeg];
     __shared__ int ybest;   // the draw's token (wavefront 0)
     const int b = a.b0 + (int)blockIdx.x;
-    if (small) {   // token verification of a small problem: its row statistics first
+    if constexpr (SMALL) {   // token verification of a small problem: its row statistics first
         small_rowstats<PES, QES, NTT / svk::kWave>(a, b, part);
         __syncthreads();
     }
     if (threadIdx.x < svk::kWave) {
-        accept_eval<PES, QES>(a, part, nch1, bm, nseg, stage, b, pre + b, &r, lp2g, lq2g, wrun, errword, as);
+        accept_eval<PES, QES>(a, part, nch1, nullptr, nseg, STAGE_TOKEN, b, nullptr, &r, nullptr, nullptr, nullptr,
+                              errword, as);
     }
     __syncthreads();
     if (r.flags) return;   // the request's error outputs are written
@@ -931,12 +930,8 @@ SV_LATENCY_KERNEL void k_tail(
     const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
 
     const float *sums = segsum;
-    if (sums_from_pass2(a, r)) {
-        sums = bm + ((int64_t)b * gamma + r.tau) * nseg;
-    } else {
-        segment_sums<PES, QES, NTT / svk::kWave>(a, prow, qrow, r.mode, r.wmul, r.lp2, r.lq2, nseg, segsum);
-        __syncthreads();
-    }
+    segment_sums<PES, QES, NTT / svk::kWave>(a, prow, qrow, r.mode, r.wmul, r.lp2, r.lq2, nseg, segsum);
+    __syncthreads();
     // the draw: wavefront 0 alone
     uint32_t flags = 0;
     double Z = 0.0;
@@ -993,18 +988,21 @@ void launch_sum_and_select(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
     svh::prof_end(ctx, s, slot);
 }
 
+// The fused tail (token rule): small = 1 adds the row statistics (one launch
+// for a small problem).
 template <int PES, int QES>
-void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int stage, int small = 0)
+void launch_fused_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s, int small = 0)
 {
     const int slot = svh::prof_begin(ctx, s, SV_KERNEL_TAIL);
-    if (a.nb <= ctx->num_cu || small)
-        hipLaunchKernelGGL((k_tail<PES, QES, NTT_WIDE>), dim3(a.nb), dim3(NTT_WIDE), 0, s, a, ctx->ws.part, ctx->nch1,
-                           (const float *)ctx->ws.bm, ctx->nseg, stage, (const ReqG *)ctx->ws.req, ctx->ws.lp2,
-                           ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword, small);
+    if (small)
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_WIDE, true>), dim3(a.nb), dim3(NTT_WIDE), 0, s, a, ctx->ws.part,
+                           ctx->nch1, ctx->nseg, ctx->ws.errword);
+    else if (a.nb <= ctx->num_cu)
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_WIDE, false>), dim3(a.nb), dim3(NTT_WIDE), 0, s, a, ctx->ws.part,
+                           ctx->nch1, ctx->nseg, ctx->ws.errword);
     else
-        hipLaunchKernelGGL((k_tail<PES, QES, NTT_NARROW>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a, ctx->ws.part,
-                           ctx->nch1, (const float *)ctx->ws.bm, ctx->nseg, stage, (const ReqG *)ctx->ws.req,
-                           ctx->ws.lp2, ctx->ws.lq2, ctx->ws.wrun, ctx->ws.errword, 0);
+        hipLaunchKernelGGL((k_tail<PES, QES, NTT_NARROW, false>), dim3(a.nb), dim3(NTT_NARROW), 0, s, a,
+                           ctx->ws.part, ctx->nch1, ctx->nseg, ctx->ws.errword);
     svh::prof_end(ctx, s, slot);
 }
 
@@ -1032,7 +1030,7 @@ inline bool fused_tail_fits(const sv_ctx *ctx, const svh::VerifyArgs &a)
 template <int PES, int QES>
 hipError_t token_single(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
 {
-    launch_fused_tail<PES, QES>(ctx, a, s, STAGE_TOKEN, 1);
+    launch_fused_tail<PES, QES>(ctx, a, s, 1);
     return hipGetLastError();
 }
 
@@ -1040,7 +1038,7 @@ template <int PES, int QES>
 hipError_t token_tail(sv_ctx *ctx, const svh::VerifyArgs &a, hipStream_t s)
 {
     if (fused_tail_fits(ctx, a)) {
-        launch_fused_tail<PES, QES>(ctx, a, s, STAGE_TOKEN);
+        launch_fused_tail<PES, QES>(ctx, a, s);
     } else {
         const int nseg = ctx->nseg;
         const int64_t nwg = (nseg + SPW - 1) / SPW;
