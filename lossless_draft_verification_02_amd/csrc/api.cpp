@@ -282,10 +282,9 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     const size_t o_rnnh = carve((size_t)max_batch * (max_rank > 0 ? max_rank : 1) * sizeof(uint16_t));
     const size_t o_tstate = carve(2 * (size_t)max_batch * svh::kTreeStateBytes);
     const size_t o_tseg = carve(2 * (size_t)max_batch * ctx->nseg * sizeof(float));
-    size_t o_mkpart = 0, o_mkprev = 0, o_mkq = 0, o_mklse = 0, o_mkzx = 0;
+    size_t o_mkpart = 0, o_mkq = 0, o_mklse = 0, o_mkzx = 0;
     if (max_rank > 0) {
         o_mkpart = carve((size_t)max_batch * ctx->ntile * sizeof(float2));
-        o_mkprev = carve((size_t)max_batch * sizeof(int32_t));
         o_mkq = carve((size_t)max_batch * (size_t)vocab * sizeof(float));
         o_mklse = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
         o_mkzx = carve((size_t)max_batch * (max_gamma > 0 ? max_gamma : 1) * sizeof(float));
@@ -318,7 +317,6 @@ sv_status spec_verify_create(sv_ctx **out, int device, int max_batch, int max_ga
     ctx->ws.tree_state = (void *)(b + o_tstate);
     ctx->ws.tree_seg = (float *)(b + o_tseg);
     ctx->ws.mk_part = max_rank > 0 ? (float2 *)(b + o_mkpart) : nullptr;
-    ctx->ws.mk_prev = max_rank > 0 ? (int32_t *)(b + o_mkprev) : nullptr;
     ctx->ws.mk_q = max_rank > 0 ? (float *)(b + o_mkq) : nullptr;
     ctx->ws.mk_lse2 = max_rank > 0 ? (float *)(b + o_mklse) : nullptr;
     ctx->ws.mk_zx = max_rank > 0 ? (float *)(b + o_mkzx) : nullptr;

@@ -74,7 +74,6 @@ struct Workspace {
     uint16_t *rnn_h;     // [max_batch, max_rank] bf16 RNN-head state
     float2 *mk_part;     // [max_batch * ntile] Markov tile (m, s) partials; after the
                          // fused path's draft, its correction / bonus tile sums (floats)
-    int32_t *mk_prev;    // [max_batch] Markov: token sampled at the previous position
     float *mk_q;         // [max_batch * V] Markov logits of the current position when
                          // the caller does not keep them
     float *mk_lse2;      // [max_batch * max_gamma] fused path: draft row log2-sum-exp2
