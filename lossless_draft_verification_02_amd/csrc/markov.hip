@@ -323,7 +323,13 @@ struct GemmShape {
     static constexpr int W_PER = TileLayout<R>::INSTR / NLW;   // copy instructions per loader, per tile
     static constexpr int B_PER = BASE_BYTES / 1024 / NLW;
     static constexpr int PER = W_PER + B_PER;
+    // the operand rows of the workgroup's MC requests, staged once in ring
+    // slots 1-2 before tile 1 uses them: UCH 16-byte chunks per row, UI copy
+    // instructions per loader
+    static constexpr int UCH = R / 8;
+    static constexpr int UI = MC * UCH / 64 / NLW;
     static_assert(NSET * RP == NCW && RP * VBW == NVB, "work split");
+    static_assert(MC * R * 2 <= 2 * SLOT && (MC * UCH) % (64 * NLW) == 0, "operand rows fit two ring slots");
     static_assert(TileLayout<R>::INSTR % NLW == 0 && (BASE_BYTES / 1024) % NLW == 0, "whole copy instructions");
 };
 
@@ -426,7 +432,14 @@ struct ResidArgs {
 // read while the current k-step's MFMAs run, and reduce it.  One workgroup
 // barrier per tile.  Per output the k-steps accumulate in ascending order
 // (the draws rebuild their tiles the same way).
-template <int R, int RES>
+//
+// STAGE (RNN head, draft mode): the operand rows are the state rows hb_k,
+// one contiguous row per request; the loaders copy each once into ring
+// slots 1-2 ahead of tile 0, and the compute wavefronts take them from
+// there, instead of each gathering its own (the Markov head's rows U[x]
+// stay with the compute wavefronts: their token reads would delay the
+// loaders' first tile).
+template <int R, int RES, bool STAGE>
 __global__ __launch_bounds__(NTG, 1)
 void k_markov_gemm(
     svh::MarkovArgs a, int k, const svh::ReqG *__restrict__ req, float *__restrict__ zout, int64_t zstride,
@@ -479,13 +492,37 @@ void k_markov_gemm(
                     copy_base_unaligned(brow[q], n0, a.V, sl + TL::BYTES, lw + NLW * q, lane);
             }
         };
-        // tile 0 alone first: at the start every CU's first copies compete
-        // for the memory system, and the compute wavefronts can begin as
-        // soon as one tile has landed; tile 1 follows while they multiply it
-        if (nt > 0) issue(0);
-        __builtin_amdgcn_s_waitcnt(0);           // tile 0 landed (element copies: their LDS stores too)
-        if (nt > 1) issue(1);
-        loader_barrier();
+        if constexpr (STAGE) {
+            // the RNN state rows first (each request's row once, into ring
+            // slots 1-2, 16-byte chunks swizzled as the compute wavefronts
+            // read them), then tile 0 alone: the compute wavefronts take the
+            // rows into registers while tile 0 lands, and tile 1 follows as
+            // soon as both are done
+#pragma unroll
+            for (int q = 0; q < GS::UI; ++q) {
+                const int ml = (64 * (lw + NLW * q) + lane) / GS::UCH, pos = lane % GS::UCH;
+                const int mm = mbase + ml < a.B ? mbase + ml : a.B - 1;
+                const int c = pos ^ (ml & (GS::UCH - 1));
+                __builtin_amdgcn_global_load_lds((const void *)(a.hstate + (int64_t)mm * R + 8 * c),
+                                                 (lds_void *)(ring + GS::SLOT + 1024 * (lw + NLW * q)), 16, 0, 0);
+            }
+            if (nt > 0) issue(0);
+            if (nt > 0 && vec) wait_vm<GS::PER>();   // the rows landed (tile 0 may be in flight)
+            else __builtin_amdgcn_s_waitcnt(0);
+            loader_barrier();                        // the compute wavefronts read the rows
+            __builtin_amdgcn_s_waitcnt(0);           // tile 0 landed (element copies: their LDS stores too)
+            loader_barrier();                        // rows read: slots 1-2 are free
+            if (nt > 1) issue(1);
+        } else {
+            // tile 0 alone first: at the start every CU's first copies
+            // compete for the memory system, and the compute wavefronts can
+            // begin as soon as one tile has landed; tile 1 follows while they
+            // multiply it
+            if (nt > 0) issue(0);
+            __builtin_amdgcn_s_waitcnt(0);   // tile 0 landed (element copies: their LDS stores too)
+            if (nt > 1) issue(1);
+            loader_barrier();
+        }
         for (int j = 0; j < nt; ++j) {
             const bool more = j + 2 < nt;
             if (more) issue(j + 2);
@@ -536,8 +573,10 @@ void k_markov_gemm(
         }
     }
     bf16x8 ufr[G][KS];
+    if constexpr (!STAGE) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) head_fragments<R>(a, km[g], m[g], lg, act[g], ufr[g]);
+        for (int g = 0; g < G; ++g) head_fragments<R>(a, km[g], m[g], lg, act[g], ufr[g]);
+    }
 
     // RP > 1: the pair (or weight sum) of (request, tile) from the row parts'
     // partials, written by the row-part-0 wavefronts once a barrier has passed
@@ -560,7 +599,19 @@ void k_markov_gemm(
         }
     };
 
-    svk::lds_barrier();   // tile 0 landed
+    if constexpr (STAGE) {
+        svk::lds_barrier();   // the state rows landed in slots 1-2
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int ml = q0 + 16 * g + li;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                ufr[g][s] = act[g] ? *(const bf16x8 *)(ring + GS::SLOT +
+                                                       16 * (ml * GS::UCH + ((lg + 4 * s) ^ (ml & (GS::UCH - 1)))))
+                                   : bf16x8{};
+        }
+    }
+    svk::lds_barrier();   // tile 0 landed (STAGE: the rows are read, the loaders may refill slots 1-2)
     for (int j = 0; j < nt; ++j) {
         const int tile = tile_of(j);
         const unsigned char *sl = slot_of(j);
@@ -1322,8 +1373,14 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
         const int64_t rn = a.ride.items - r0 < ride_per ? (a.ride.items - r0 > 0 ? a.ride.items - r0 : 0) : ride_per;
         float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        hipLaunchKernelGGL((k_markov_gemm<R, 0>), dim3(gx, gy), dim3(NTG), 0, s, a, k, (const svh::ReqG *)nullptr,
-                           zk, zstride, ctx->ws.mk_part, ntile, vec, zvec, ResidArgs{nullptr, nullptr}, 0);
+        if (a.A)
+            hipLaunchKernelGGL((k_markov_gemm<R, 0, true>), dim3(gx, gy), dim3(NTG), 0, s, a, k,
+                               (const svh::ReqG *)nullptr, zk, zstride, ctx->ws.mk_part, ntile, vec, zvec,
+                               ResidArgs{nullptr, nullptr}, 0);
+        else
+            hipLaunchKernelGGL((k_markov_gemm<R, 0, false>), dim3(gx, gy), dim3(NTG), 0, s, a, k,
+                               (const svh::ReqG *)nullptr, zk, zstride, ctx->ws.mk_part, ntile, vec, zvec,
+                               ResidArgs{nullptr, nullptr}, 0);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
         const int64_t cap = (int64_t)SV_MARKOV_RIDE_WGS_PER_CU * ctx->num_cu;
@@ -1354,7 +1411,7 @@ hipError_t launch_resid(sv_ctx *ctx, const svh::MarkovArgs &a, const svh::Verify
     // the draft's tile pairs are consumed: their buffer holds the tile sums
     float *tsum = (float *)ctx->ws.mk_part;
     int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_REBUILD);
-    hipLaunchKernelGGL((k_markov_gemm<R, PES>), dim3(gx, gy), dim3(NTG), 0, s, a, 0, req, (float *)nullptr, a.V,
+    hipLaunchKernelGGL((k_markov_gemm<R, PES, false>), dim3(gx, gy), dim3(NTG), 0, s, a, 0, req, (float *)nullptr, a.V,
                        (float2 *)nullptr, ntile, vec, 0, ResidArgs{v.p, tsum}, pvec);
     svh::prof_end(ctx, s, slot);
     slot = svh::prof_begin(ctx, s, SV_KERNEL_SELECT);
