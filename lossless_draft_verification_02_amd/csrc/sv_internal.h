@@ -171,6 +171,9 @@ struct ReqG {
 // Row-chunk and segment geometry of a context for vocabulary `vocab` and at
 // most `rows_max` verified rows per call (nch1, chunk1, nseg, ntile).
 void set_geometry(sv_ctx *ctx, int64_t vocab, int64_t rows_max);
+// Row-statistics chunks of about `target` elements (a multiple of 8) over a
+// row of `vocab`: their count and length.
+void chunk_geometry(int64_t vocab, int64_t target, int *nch1, int64_t *chunk1);
 // Argument checks and argument block of token verification (api.cpp), for
 // entry points defined in other files; set_error records a status and
 // message for spec_verify_last_error (SV_OK clears it).

@@ -941,7 +941,9 @@ def test_rnn_small(B, gamma, V, R, std, astd):
     _say(f"case: RNN B={B} gamma={gamma} V={V} R={R} std={std} A std={astd}")
     mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=std)
     A = WL.make_rnn_recurrence(R, "cuda", std=astd)
-    req = list(range(min(B, 12)))
+    # the first requests, and the last two (past 128 they sit in a second
+    # contraction workgroup row whose other state rows are clamped copies)
+    req = sorted(set(range(min(B, 12))) | {B - 2, B - 1} - {-1})
     with make_ctx(B, gamma, V, R) as ctx:
         d, lse, st = check_rnn(ctx, mi, A, req, f"rnn B={B} V={V} R={R}")
         d2, lse2, st2 = check_rnn(ctx, mi, A, req, f"rnn B={B} V={V} R={R} no q", want_q=False)
@@ -1066,18 +1068,31 @@ def check_markov_verify(ctx, mi, req, label):
     assert torch.equal(d, d2), "fused and unfused samplers drew different drafts"
     assert torch.equal(lse, lse2), "fused and unfused samplers report different normalisers"
     # the target rows' statistics, which the fused path computes in workgroups
-    # riding in the draws, against token verification's own pass: the same
-    # per-thread order and workgroup merge, so equal bit for bit when that
-    # call runs the row pass (more than one chunk per row); a single-chunk row
-    # takes the one-launch route there, which merges per wavefront
+    # riding in the draws (chunks of about 32K tokens), against token
+    # verification's own pass: the same per-thread order and workgroup merge,
+    # so equal bit for bit when that call runs the row pass on the same chunks
+    # (a context made with 32K-token chunks, more than one chunk per row); a
+    # single-chunk row takes the one-launch route there, which merges per
+    # wavefront, and other chunk lengths merge in another order
     B, gamma = d.shape
     lp = torch.empty(B, gamma + 1, device="cuda")
     acc2 = torch.empty(B, dtype=torch.int32, device="cuda")
     out2 = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
-    L.spec_verify_run(ctx, mi.p, q2, d2, acc2, out2, temperature=mi.T, seed=WL.VERIFY_SEED, diag=dict(lse_p=lp))
-    torch.cuda.synchronize()
+    old_env = os.environ.get("SPECVERIFY_ROWSTATS_CHUNK")
+    os.environ["SPECVERIFY_ROWSTATS_CHUNK"] = "32768"
+    try:
+        ctx32 = make_ctx(B, gamma, mi.V)
+    finally:
+        if old_env is None:
+            del os.environ["SPECVERIFY_ROWSTATS_CHUNK"]
+        else:
+            os.environ["SPECVERIFY_ROWSTATS_CHUNK"] = old_env
+    with ctx32:
+        L.spec_verify_run(ctx32, mi.p, q2, d2, acc2, out2, temperature=mi.T, seed=WL.VERIFY_SEED,
+                          diag=dict(lse_p=lp))
+        torch.cuda.synchronize()
     lp_f, lp_t = res["lse_p"], lp.cpu().numpy()
-    if mi.V > 16384:
+    if mi.V > 32768:
         assert np.array_equal(lp_f, lp_t, equal_nan=True), "fused and row-pass target statistics differ"
     else:
         assert np.allclose(lp_f, lp_t, rtol=0, atol=1e-5, equal_nan=True), np.nanmax(np.abs(lp_f - lp_t))
@@ -1137,7 +1152,7 @@ def test_rnn_random(case):
     _say(f"case: random RNN {case}: {c}")
     mi = WL.make_markov_inputs("cuda", B=c["B"], gamma=c["gamma"], V=c["V"], R=c["R"], uw_std=c["std"])
     A = WL.make_rnn_recurrence(c["R"], "cuda", std=c["astd"])
-    req = list(range(min(c["B"], 12)))
+    req = sorted(set(range(min(c["B"], 12))) | {c["B"] - 2, c["B"] - 1} - {-1})
     with make_ctx(c["B"], c["gamma"], c["V"], c["R"]) as ctx:
         d, lse, st = check_rnn(ctx, mi, A, req, f"random rnn {case}")
         d2, lse2, st2 = check_rnn(ctx, mi, A, req, f"random rnn {case} no q", want_q=False)
