@@ -495,19 +495,20 @@ __device__ __forceinline__ float seg_reduce(const SegRaw<PES, QES> &r, int mode,
 }
 
 // Segment sums of the correction / bonus weights of rows prow / qrow into
-// sums[kfirst, nseg), by NW wavefronts of the workgroup (wavefront wid takes
-// segments kfirst + wid, kfirst + wid + NW, ...).  Full segments of 16-byte aligned rows are
+// sums[kfirst, kend), by NW wavefronts of the workgroup (wavefront wid takes
+// segments kfirst + wid, kfirst + wid + NW, ...; kend is at most the row's
+// segment count).  Full segments of 16-byte aligned rows are
 // software-pipelined (unless both rows are fp32, where the second buffer would
 // spill): the next segment's vectors are requested before the current one is
 // reduced, so two segments per wavefront are in flight.
 template <int PES, int QES, int NW>
 __device__ void segment_sums(const svh::VerifyArgs &a, const char *prow, const char *qrow, int mode, float wmul,
-                             float lp2, float lq2, int nseg, float *sums, int kfirst = 0)
+                             float lp2, float lq2, int kend, float *sums, int kfirst = 0)
 {
     const int lane = threadIdx.x & (svk::kWave - 1), wid = threadIdx.x / svk::kWave;
     const bool aligned = (((uintptr_t)prow) & 15) == 0 && (mode || (((uintptr_t)qrow) & 15) == 0);
     const int nf = aligned ? (int)(a.V / SEG) : 0;
-    const int nfull = nf < nseg ? nf : nseg;   // segments [kfirst, nseg) only
+    const int nfull = nf < kend ? nf : kend;   // segments [kfirst, kend) only
     int k = kfirst + wid;
     if constexpr (PES == 4 && QES == 4) {
         // fp32 rows: a second register buffer does not fit; one segment at a time
@@ -529,7 +530,7 @@ __device__ void segment_sums(const svh::VerifyArgs &a, const char *prow, const c
         }
     }
     // the partial last segment, or every segment of unaligned rows
-    for (; k < nseg; k += NW) {
+    for (; k < kend; k += NW) {
         const int64_t s0 = (int64_t)k * SEG;
         const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
         const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, mode, wmul, lp2, lq2, a.c);
@@ -599,17 +600,16 @@ __global__ __launch_bounds__(NT) void k_resid_sum(svh::VerifyArgs a, const ReqG 
     const int nwg = (nseg + SPW - 1) / SPW;
     const int64_t wg = blockIdx.x;
     const int bl = (int)(wg / nwg);
-    const int sidx = (int)(wg - (int64_t)bl * nwg) * SPW + (int)(threadIdx.x / svk::kWave);
+    const int g = (int)(wg - (int64_t)bl * nwg);
     const int b = a.b0 + bl;
     const ReqG r = req[b];
-    if (r.flags || sums_from_pass2(a, r) || sidx >= nseg) return;
+    if (r.flags || sums_from_pass2(a, r)) return;
     const int G1 = a.gamma + 1;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
     const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
-    const int64_t s0 = (int64_t)sidx * SEG;
-    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
-    const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
-    if ((threadIdx.x & (svk::kWave - 1)) == 0) csum[(int64_t)b * nseg + sidx] = tot;
+    const int kfirst = g * SPW, kend = kfirst + SPW < nseg ? kfirst + SPW : nseg;
+    segment_sums<PES, QES, SPW>(a, prow, qrow, r.mode, r.wmul, r.lp2, r.lq2, kend, csum + (int64_t)b * nseg,
+                                kfirst);
 }
 
 // Token rule, split tail, acceptance and sums in one launch: grid (request,
@@ -640,15 +640,12 @@ __global__ __launch_bounds__(NT) void k_accept_sum(svh::VerifyArgs a, const floa
     __syncthreads();
     if (g == 0 && threadIdx.x == 0) req[b] = r;
     if (r.flags) return;
-    const int sidx = g * SPW + (int)(threadIdx.x / svk::kWave);
-    if (sidx >= nseg) return;
     const int G1 = a.gamma + 1;
     const char *prow = (const char *)a.p + ((int64_t)b * G1 + r.tau) * a.V * PES;
     const char *qrow = r.mode ? nullptr : correction_qrow<QES>(a, b, r.tau);
-    const int64_t s0 = (int64_t)sidx * SEG;
-    const int64_t s1 = s0 + SEG < a.V ? s0 + SEG : a.V;
-    const float tot = segment_weight_sum<PES, QES>(prow, qrow, s0, s1, r.mode, r.wmul, r.lp2, r.lq2, a.c);
-    if ((threadIdx.x & (svk::kWave - 1)) == 0) csum[(int64_t)b * nseg + sidx] = tot;
+    const int kfirst = g * SPW, kend = kfirst + SPW < nseg ? kfirst + SPW : nseg;
+    segment_sums<PES, QES, SPW>(a, prow, qrow, r.mode, r.wmul, r.lp2, r.lq2, kend, csum + (int64_t)b * nseg,
+                                kfirst);
 }
 
 // ---------------------------------------------------------------------------
