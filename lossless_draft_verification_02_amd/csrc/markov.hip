@@ -15,7 +15,9 @@
 //                    tiles: the loaders copy each tile of Wt (the transition
 //                    matrix stored vocabulary-major, V rows of R) and the
 //                    tile's base logits straight from global memory into a
-//                    three-slot LDS ring, two tiles ahead; the compute
+//                    three-slot LDS ring, two tiles ahead (from position 2
+//                    on, and for the RNN head, the operand rows first: the
+//                    previous draw left them contiguous); the compute
 //                    wavefronts hold the U rows (or states) of the
 //                    workgroup's 128 requests as B fragments in registers
 //                    for the whole launch, read the A fragments from LDS
@@ -28,7 +30,8 @@
 //                    their fp64 prefix over the workgroup, the tile holding
 //                    u * Z, then that tile's 64 logits (read back, or rebuilt
 //                    by MFMA when no z rows are stored) scanned for the token
-//                    (inverse CDF in ascending token order).  In the fused
+//                    (inverse CDF in ascending token order), and for the
+//                    Markov head copies U[x_k] for the next position.  In the fused
 //                    draft -> verification path the launch carries further
 //                    workgroups that compute chunk statistics of the target
 //                    rows (they do not depend on the draft), using the memory
@@ -433,12 +436,12 @@ struct ResidArgs {
 // barrier per tile.  Per output the k-steps accumulate in ascending order
 // (the draws rebuild their tiles the same way).
 //
-// STAGE (RNN head, draft mode): the operand rows are the state rows hb_k,
-// one contiguous row per request; the loaders copy each once into ring
-// slots 1-2 ahead of tile 0, and the compute wavefronts take them from
-// there, instead of each gathering its own (the Markov head's rows U[x]
-// stay with the compute wavefronts: their token reads would delay the
-// loaders' first tile).
+// STAGE (draft mode): the operand rows lie contiguous in hstate, one per
+// request -- the RNN head's states hb_k, or the Markov head's U[x_{k-1}]
+// that the previous position's draw left there -- and the loaders copy each
+// once into ring slots 1-2 ahead of tile 0; the compute wavefronts take them
+// from there instead of each gathering its own.  (Gathering U[x] by token in
+// the loaders instead put the token reads in front of their first tile.)
 template <int R, int RES, bool STAGE>
 __global__ __launch_bounds__(NTG, 1)
 void k_markov_gemm(
@@ -493,11 +496,11 @@ void k_markov_gemm(
             }
         };
         if constexpr (STAGE) {
-            // the RNN state rows first (each request's row once, into ring
-            // slots 1-2, 16-byte chunks swizzled as the compute wavefronts
-            // read them), then tile 0 alone: the compute wavefronts take the
-            // rows into registers while tile 0 lands, and tile 1 follows as
-            // soon as both are done
+            // the operand rows first (each request's row of hstate once,
+            // into ring slots 1-2, 16-byte chunks swizzled as the compute
+            // wavefronts read them), then tile 0 alone: the compute
+            // wavefronts take the rows into registers while tile 0 lands,
+            // and tile 1 follows as soon as both are done
 #pragma unroll
             for (int q = 0; q < GS::UI; ++q) {
                 const int ml = (64 * (lw + NLW * q) + lane) / GS::UCH, pos = lane % GS::UCH;
@@ -1029,6 +1032,19 @@ __device__ void ride_items(const svh::RowRide &r, int64_t V, int64_t first, int6
     }
 }
 
+// Markov head: the next position's operand row U[x_k] (row 0 for an invalid
+// or missing token, as prev_token reads it), copied by wavefront 0 to the
+// request's row of hstate, where the next contraction's loaders take it.
+template <int R>
+__device__ __forceinline__ void stage_next_row(const svh::MarkovArgs &a, int b, int32_t xk)
+{
+    static_assert(R % 8 == 0 && R / 8 <= 64, "one 16-byte chunk per lane");
+    const int lane = threadIdx.x & 63;
+    const int64_t x = (xk < 0 || (int64_t)xk >= a.V) ? 0 : xk;
+    if (lane < R / 8)
+        ((uint4 *)(a.hstate + (int64_t)b * R))[lane] = ((const uint4 *)(a.U + x * R))[lane];
+}
+
 // The draw at position k: one workgroup of four wavefronts per request.  All
 // threads choose the tile; its 64 logits come from the stored z rows (zin)
 // or, without them (fused path), are rebuilt by the four wavefronts (two
@@ -1060,7 +1076,13 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
     bf16x8 ufr[KS];
     if (!zin) head_fragments<R>(a, k, b, lg, true, ufr);   // the request's operand row in every B column
     SelState st;
-    if (!select_tile_wg(a, k, tile_part, ntile, errword, b, L, st)) return;   // the same in every thread
+    // Markov head with a state buffer: the draw leaves the next position's
+    // operand row there
+    const bool stage = !a.A && a.hstate && k < a.gamma;
+    if (!select_tile_wg(a, k, tile_part, ntile, errword, b, L, st)) {   // the same in every thread
+        if (stage && wid == 0) stage_next_row<R>(a, b, -1);
+        return;
+    }
     const int64_t c0 = (int64_t)st.ts * TN;
     const int ncols = (int)((a.V - c0) < TN ? (a.V - c0) : TN);
     if (zin) {
@@ -1106,6 +1128,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_markov_draw(svh::MarkovArgs a,
     if (wid == 0) {
         const int32_t xk = select_token_in_tile(a, k, b, st, zt, errword);
         if (lane == 0) xnew = xk;
+        if (stage) stage_next_row<R>(a, b, xk);
     }
     if (a.A) {   // RNN head: the four wavefronts advance the state together
         rnn_fill<R, kDrawWaves>(a, k, b, hs, wid);
@@ -1354,8 +1377,14 @@ inline int base_rows_aligned(const svh::MarkovArgs &a)
 }
 
 template <int R>
-hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s)
+hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &args, hipStream_t s)
 {
+    // The Markov head stages its operand rows too: from position 2 on, each
+    // draw leaves U[x_k] of its request in the state buffer (the RNN head's,
+    // unused here), and the contraction's loaders copy those rows as they do
+    // the RNN states.  Position 1's rows U[x_0] are gathered.
+    svh::MarkovArgs a = args;
+    if (!a.A) a.hstate = ctx->ws.rnn_h;
     const int ntile = ctx->ntile;
     const int gy = (a.B + MC - 1) / MC;
     int gx = ctx->num_cu / gy;   // one workgroup per CU (its tile ring fills most of the LDS)
@@ -1373,7 +1402,7 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &a, hipStream_t s
         const int64_t rn = a.ride.items - r0 < ride_per ? (a.ride.items - r0 > 0 ? a.ride.items - r0 : 0) : ride_per;
         float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        if (a.A)
+        if (a.A || k >= 2)
             hipLaunchKernelGGL((k_markov_gemm<R, 0, true>), dim3(gx, gy), dim3(NTG), 0, s, a, k,
                                (const svh::ReqG *)nullptr, zk, zstride, ctx->ws.mk_part, ntile, vec, zvec,
                                ResidArgs{nullptr, nullptr}, 0);
