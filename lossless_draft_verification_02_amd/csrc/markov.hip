@@ -603,7 +603,7 @@ void k_markov_gemm(
     };
 
     if constexpr (STAGE) {
-        svk::lds_barrier();   // the state rows landed in slots 1-2
+        svk::lds_barrier();   // the operand rows landed in slots 1-2
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int ml = q0 + 16 * g + li;
