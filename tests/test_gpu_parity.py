@@ -7,6 +7,7 @@ in seconds (several chunks and a ragged tail), and every workload at its full
 size in the launch configuration the benchmark times, compared on a sample
 of requests the oracle evaluates one by one.
 """
+import contextlib
 import os
 import subprocess
 
@@ -1060,9 +1061,26 @@ def gpu_markov_verify(ctx, mi, seed_d=WL.DRAFT_SEED, seed_v=WL.VERIFY_SEED, offs
     return d, lse, res
 
 
-def check_markov_verify(ctx, mi, req, label):
+@contextlib.contextmanager
+def rowstats_chunk_env(n):
+    """Contexts made inside take row-statistics chunks of about n tokens."""
+    key = "SPECVERIFY_ROWSTATS_CHUNK"
+    old = os.environ.get(key)
+    os.environ[key] = str(n)
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ[key]
+        else:
+            os.environ[key] = old
+
+
+def check_markov_verify(ctx, mi, req, label, ride_chunk=32768):
     """Fused path against (a) the unfused GPU sampler, bit for bit on the
-    draft, and (b) the oracle's draft followed by the oracle's verification."""
+    draft, and (b) the oracle's draft followed by the oracle's verification.
+    ride_chunk: the chunk length of the riding target-row statistics (32K
+    tokens, or the context's own chunks when longer)."""
     d, lse, res = gpu_markov_verify(ctx, mi)
     d2, q2, lse2 = gpu_markov(ctx, mi, want_q=True)
     assert torch.equal(d, d2), "fused and unfused samplers drew different drafts"
@@ -1078,21 +1096,14 @@ def check_markov_verify(ctx, mi, req, label):
     lp = torch.empty(B, gamma + 1, device="cuda")
     acc2 = torch.empty(B, dtype=torch.int32, device="cuda")
     out2 = torch.empty(B, gamma + 1, dtype=torch.int32, device="cuda")
-    old_env = os.environ.get("SPECVERIFY_ROWSTATS_CHUNK")
-    os.environ["SPECVERIFY_ROWSTATS_CHUNK"] = "32768"
-    try:
-        ctx32 = make_ctx(B, gamma, mi.V)
-    finally:
-        if old_env is None:
-            del os.environ["SPECVERIFY_ROWSTATS_CHUNK"]
-        else:
-            os.environ["SPECVERIFY_ROWSTATS_CHUNK"] = old_env
-    with ctx32:
-        L.spec_verify_run(ctx32, mi.p, q2, d2, acc2, out2, temperature=mi.T, seed=WL.VERIFY_SEED,
+    with rowstats_chunk_env(ride_chunk):
+        ctx_same = make_ctx(B, gamma, mi.V)
+    with ctx_same:
+        L.spec_verify_run(ctx_same, mi.p, q2, d2, acc2, out2, temperature=mi.T, seed=WL.VERIFY_SEED,
                           diag=dict(lse_p=lp))
         torch.cuda.synchronize()
     lp_f, lp_t = res["lse_p"], lp.cpu().numpy()
-    if mi.V > 32768:
+    if mi.V > ride_chunk:
         assert np.array_equal(lp_f, lp_t, equal_nan=True), "fused and row-pass target statistics differ"
     else:
         assert np.allclose(lp_f, lp_t, rtol=0, atol=1e-5, equal_nan=True), np.nanmax(np.abs(lp_f - lp_t))
@@ -1124,6 +1135,20 @@ def test_markov_verify_fused_small(B, gamma, V, R, std, p32):
         mi.p = mi.p.float()
     with make_ctx(B, gamma, V, R) as ctx:
         check_markov_verify(ctx, mi, list(range(B)), f"fused B={B} V={V} R={R}")
+
+
+def test_markov_verify_fused_context_chunks_longer():
+    """A context made with row-statistics chunks longer than the riding
+    statistics' 32K tokens keeps its own for them: the fused path's target
+    normalisers equal, bit for bit, that context's row pass (three chunks of
+    46,672 tokens per row), and the decisions match the oracle's."""
+    B, gamma, V, R = 8, 4, 140000, 128
+    _say(f"case: fused Markov -> verify, 64K-token context chunks, B={B} gamma={gamma} V={V} R={R}")
+    mi = WL.make_markov_inputs("cuda", B=B, gamma=gamma, V=V, R=R, uw_std=0.25)
+    with rowstats_chunk_env(65536):
+        ctx = make_ctx(B, gamma, V, R)
+    with ctx:
+        check_markov_verify(ctx, mi, list(range(B)), f"fused 64K chunks V={V}", ride_chunk=65536)
 
 
 def _random_markov_case(case, base_seed):
