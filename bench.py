@@ -236,6 +236,15 @@ def cpu_baseline_and_parity_markov(mi, offset, draft, gpu, single_budget_s=3.0, 
     return base, parity
 
 
+def _acceptance_by_position(acc, gamma):
+    """Per draft position i (0-based), the share of the requests with a valid
+    result whose accepted length exceeds i, i.e. that accepted token i."""
+    import numpy as np
+    a = np.asarray(acc)
+    a = a[a >= 0]
+    return [round(float((a > i).mean()), 4) for i in range(gamma)] if a.size else []
+
+
 def _gpu_outputs(acc, out):
     return {"accepted_len": acc.cpu().numpy().copy(), "out_tokens": out.cpu().numpy().copy()}
 
@@ -404,7 +413,8 @@ def bench_headline(args, L, WL):
                  roofline, cpu_baseline=cpu, parity=parity, call_roofline=call_roofline, tail_roofline=tail_roofline,
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
-                 mean_accepted=round(accepted, 4), wall_ms_per_step=round(wall_ms, 5), copy_probe=copy_probe,
+                 mean_accepted=round(accepted, 4), acceptance_by_position=_acceptance_by_position(a_all, gamma),
+                 wall_ms_per_step=round(wall_ms, 5), copy_probe=copy_probe,
                  env={"hip": torch.version.hip, "torch": torch.__version__,
                       "device": torch.cuda.get_device_name(0)})
 
@@ -443,6 +453,7 @@ def bench_token(args, L, WL, name, nsets):
                             "logits": str(vi.p.dtype).split(".")[-1], "temperature": vi.T, "input_sets": nsets},
                  _token_roofline(prof, vi, WL), cpu_baseline=cpu, parity=parity,
                  mean_accepted_last_step=round(accepted, 4),
+                 acceptance_by_position=_acceptance_by_position(gpu["accepted_len"], gamma),
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  us_per_call=round(ms * 1e3, 2),
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
@@ -508,6 +519,7 @@ def bench_block(args, L, WL):
                   "V": V, "logits": "bf16", "sps": "2000/(1+n/4096)", "input_sets": len(sets)},
                  _hbm_roofline("k_rowstats", alg, _mean_us(prof, "rowstats")), cpu_baseline=cpu, parity=parity,
                  mean_verify_len=round(positions / B, 4), mean_accepted_last_step=round(accepted, 4),
+                 acceptance_by_position=_acceptance_by_position(gpu["accepted_len"], gamma),
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]})
 
@@ -577,6 +589,7 @@ def bench_markov(args, L, WL):
                               "(p bf16; fused: no fp32 draft logits stored)",
                   "B": B, "gamma": gamma, "V": V, "R": R},
                  roof, cpu_baseline=cpu, parity=parity, mean_accepted_last_step=round(accepted, 4),
+                 acceptance_by_position=_acceptance_by_position(gpu["accepted_len"], gamma),
                  emitted_tokens_per_s=round(B * (accepted + 1) / (ms / 1e3), 1),
                  kernels_mean_us={k: round(_mean_us(prof, k), 2) for k, v in prof.items() if v[1]},
                  markov_ms_per_call=round((prof["markov_gemm"][0] + prof["markov_select"][0]) / args.steps, 4),
