@@ -15,9 +15,9 @@
 //                    tiles: the loaders copy each tile of Wt (the transition
 //                    matrix stored vocabulary-major, V rows of R) and the
 //                    tile's base logits straight from global memory into a
-//                    three-slot LDS ring, two tiles ahead (from position 2
-//                    on, and for the RNN head, the operand rows first: the
-//                    previous draw left them contiguous); the compute
+//                    three-slot LDS ring, two tiles ahead (the operand rows
+//                    first: the previous draw, or before position 1 a copy
+//                    kernel, left them contiguous); the compute
 //                    wavefronts hold the U rows (or states) of the
 //                    workgroup's 128 requests as B fragments in registers
 //                    for the whole launch, read the A fragments from LDS
@@ -438,10 +438,12 @@ struct ResidArgs {
 //
 // STAGE (draft mode): the operand rows lie contiguous in hstate, one per
 // request -- the RNN head's states hb_k, or the Markov head's U[x_{k-1}]
-// that the previous position's draw left there -- and the loaders copy each
-// once into ring slots 1-2 ahead of tile 0; the compute wavefronts take them
-// from there instead of each gathering its own.  (Gathering U[x] by token in
-// the loaders instead put the token reads in front of their first tile.)
+// that the previous position's draw (position 1: a small copy kernel) left
+// there -- and the loaders copy each once into ring slots 1-2 ahead of tile
+// 0; the compute wavefronts take them from there instead of each gathering
+// its own.  The residual mode gathers U[x_tau] by token in the compute
+// wavefronts.  (Gathering by token in the loaders instead put the token
+// reads in front of their first tile.)
 template <int R, int RES, bool STAGE>
 __global__ __launch_bounds__(NTG, 1)
 void k_markov_gemm(
@@ -1045,6 +1047,15 @@ __device__ __forceinline__ void stage_next_row(const svh::MarkovArgs &a, int b, 
         ((uint4 *)(a.hstate + (int64_t)b * R))[lane] = ((const uint4 *)(a.U + x * R))[lane];
 }
 
+// Markov head, before position 1: U[x_0] of every request into hstate, so
+// that position 1's contraction stages its operand rows as the later ones
+// do.  One wavefront per request.
+template <int R>
+__global__ __launch_bounds__(64) void k_markov_first_rows(svh::MarkovArgs a)
+{
+    stage_next_row<R>(a, (int)blockIdx.x, a.x0[blockIdx.x]);
+}
+
 // The draw at position k: one workgroup of four wavefronts per request.  All
 // threads choose the tile; its 64 logits come from the stored z rows (zin)
 // or, without them (fused path), are rebuilt by the four wavefronts (two
@@ -1379,10 +1390,10 @@ inline int base_rows_aligned(const svh::MarkovArgs &a)
 template <int R>
 hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &args, hipStream_t s)
 {
-    // The Markov head stages its operand rows too: from position 2 on, each
-    // draw leaves U[x_k] of its request in the state buffer (the RNN head's,
-    // unused here), and the contraction's loaders copy those rows as they do
-    // the RNN states.  Position 1's rows U[x_0] are gathered.
+    // The Markov head stages its operand rows too: a small kernel copies
+    // U[x_0] of every request into the state buffer (the RNN head's, unused
+    // here) before position 1, each draw then leaves U[x_k] there, and the
+    // contraction's loaders copy those rows as they do the RNN states.
     svh::MarkovArgs a = args;
     if (!a.A) a.hstate = ctx->ws.rnn_h;
     const int ntile = ctx->ntile;
@@ -1396,20 +1407,18 @@ hipError_t launch_positions(sv_ctx *ctx, const svh::MarkovArgs &args, hipStream_
     const int zvec = (a.V % 4 == 0) && ((((uintptr_t)(a.q_logits ? a.q_logits : ctx->ws.mk_q)) & 15) == 0);
     // riding target-row chunks: an even share per draw
     const int64_t ride_per = a.ride.items > 0 ? (a.ride.items + a.gamma - 1) / a.gamma : 0;
-    if (a.A) hipLaunchKernelGGL(k_rnn_first_state, dim3(a.B), dim3(a.R < 256 ? a.R : 256), 0, s, a);
+    if (a.A)
+        hipLaunchKernelGGL(k_rnn_first_state, dim3(a.B), dim3(a.R < 256 ? a.R : 256), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_markov_first_rows<R>), dim3(a.B), dim3(64), 0, s, a);
     for (int k = 1; k <= a.gamma; ++k) {
         const int64_t r0 = ride_per * (k - 1);
         const int64_t rn = a.ride.items - r0 < ride_per ? (a.ride.items - r0 > 0 ? a.ride.items - r0 : 0) : ride_per;
         float *zk = a.fused ? nullptr : (a.q_logits ? a.q_logits + (int64_t)(k - 1) * a.V : ctx->ws.mk_q);
         int slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_GEMM);
-        if (a.A || k >= 2)
-            hipLaunchKernelGGL((k_markov_gemm<R, 0, true>), dim3(gx, gy), dim3(NTG), 0, s, a, k,
-                               (const svh::ReqG *)nullptr, zk, zstride, ctx->ws.mk_part, ntile, vec, zvec,
-                               ResidArgs{nullptr, nullptr}, 0);
-        else
-            hipLaunchKernelGGL((k_markov_gemm<R, 0, false>), dim3(gx, gy), dim3(NTG), 0, s, a, k,
-                               (const svh::ReqG *)nullptr, zk, zstride, ctx->ws.mk_part, ntile, vec, zvec,
-                               ResidArgs{nullptr, nullptr}, 0);
+        hipLaunchKernelGGL((k_markov_gemm<R, 0, true>), dim3(gx, gy), dim3(NTG), 0, s, a, k,
+                           (const svh::ReqG *)nullptr, zk, zstride, ctx->ws.mk_part, ntile, vec, zvec,
+                           ResidArgs{nullptr, nullptr}, 0);
         svh::prof_end(ctx, s, slot);
         slot = svh::prof_begin(ctx, s, SV_KERNEL_MARKOV_SELECT);
         const int64_t cap = (int64_t)SV_MARKOV_RIDE_WGS_PER_CU * ctx->num_cu;
